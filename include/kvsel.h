@@ -1,0 +1,249 @@
+/*
+ * kvsel.h -- C ABI of the query-guided KV selection library (libkvsel.so),
+ * built for AMD Instinct MI355X (gfx950).
+ *
+ * The library runs the selection path shared by three methods:
+ *   [ACRE]       "Boosting Long-Context Management via Query-Guided Activation
+ *                 Refilling" (arXiv 2412.12486)
+ *   [CacheFocus] "CacheFocus: Dynamic Cache Re-Positioning for Efficient
+ *                 Retrieval-Augmented Generation" (arXiv 2502.11101)
+ *   [InfoFlow]   "InfoFlow KV: Information-Flow-Aware KV Recomputation for Long
+ *                 Context" (arXiv 2603.05353)
+ * in six calls: re-position -> score -> aggregate -> top-k -> gather/refill ->
+ * decode attention.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Tensor pointers are DEVICE pointers, owned by the caller.  The library
+ *   allocates nothing and keeps no state between calls; scratch memory is
+ *   passed in as (ws, ws_bytes) and sized by the *_workspace() queries.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *   default stream).  It returns KVSEL_OK once its kernels are enqueued.
+ * - Arguments are validated before anything is enqueued.  On a negative status
+ *   nothing was launched and no output was written; kvsel_last_error() gives a
+ *   message.  A fault during execution surfaces at the caller's next
+ *   synchronisation, as with any HIP kernel.
+ * - Caches are [B][N][H][D]: instance, cached row, kv head, head dim.  Within a
+ *   row the H*D elements are contiguous; rows and instances may be strided
+ *   (kvsel_cache.stride_n / stride_b, in elements, multiples of 8).  Pointers
+ *   must be 16-byte aligned.  Query blocks are contiguous [B][T][Hq][D] in the
+ *   cache dtype.  Per-row statistics are [B][Hq][T] (a "row" is one query head
+ *   and query token).  Hq must be a multiple of H; query head h reads kv head
+ *   h / (Hq / H).
+ * - Supported: head dim D in {64, 128}; dtype bf16 or fp32 (the query, the
+ *   cache and any second cache of one call share the dtype).  Attention
+ *   arithmetic is fp32 with fp32 accumulation; re-rotation is fp64.
+ * - A "unit" is unit_len consecutive cached rows: a chunk, a document, an L1
+ *   entry's L2 block, or a single token (unit_len = 1).  N must be a multiple
+ *   of unit_len; M = N / unit_len.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KVSEL_OK               0
+#define KVSEL_ERR_NULL        -1  /* a required pointer is NULL                  */
+#define KVSEL_ERR_SHAPE       -2  /* sizes are inconsistent or out of range      */
+#define KVSEL_ERR_DTYPE       -3  /* dtype is not bf16 / fp32                    */
+#define KVSEL_ERR_UNSUPPORTED -4  /* head dim, alignment or stride not supported */
+#define KVSEL_ERR_WORKSPACE   -5  /* workspace smaller than the query returned   */
+#define KVSEL_ERR_HIP         -6  /* the HIP runtime rejected a launch           */
+
+/* Element types of caches and query blocks. */
+#define KVSEL_BF16 0
+#define KVSEL_FP32 1
+
+/* Which dimensions form RoPE's 2-D slices: (i, i + D/2) or (2i, 2i + 1). */
+#define KVSEL_ROPE_HALF        0
+#define KVSEL_ROPE_INTERLEAVED 1
+
+/* Aggregation signal. */
+#define KVSEL_SIG_MASS  0  /* softmax attention weight                      */
+#define KVSEL_SIG_VNORM 1  /* attention weight x L2 norm of the value row    */
+
+/* A cache tensor [B][N][H][D]. */
+typedef struct kvsel_cache {
+  int64_t B;         /* instances (requests x layers, layers, ...)        */
+  int64_t N;         /* cached rows per instance                          */
+  int64_t H;         /* kv heads                                          */
+  int64_t D;         /* head dim: 64 or 128                               */
+  int64_t stride_b;  /* elements between instances, >= N * stride_n       */
+  int64_t stride_n;  /* elements between rows, >= H * D                   */
+  int32_t dtype;     /* KVSEL_BF16 or KVSEL_FP32                          */
+} kvsel_cache;
+
+/* One key/value segment of the cache read by the final attention pass. */
+typedef struct kvsel_segment {
+  const void* k;     /* device pointer, cache layout of `kc`              */
+  const void* v;     /* device pointer, same layout                       */
+  kvsel_cache kc;
+} kvsel_segment;
+
+/*
+ * kvsel_reposition -- cache re-positioning ([CacheFocus §2.3]: a rotation's
+ * inverse is its transpose, so a cached key is un-rotated and rotated again at
+ * its new position; [InfoFlow §4.2]: global position reconstruction
+ * g(t) = Delta_i + p_i(t); the rotation matrix is [InfoFlow §3.2]).
+ *
+ * Every row of unit u is rotated by delta[u] positions:
+ *   k_out = R(p_old + delta) R(p_old)^T k_in = R(delta) k_in,
+ * pair i turning by delta * theta_i with theta_i = rope_base^(-2i/D).  The
+ * angle and the 2x2 rotation are computed in fp64 and the result is rounded
+ * once to the cache dtype (nearest even).  Values are not touched (only keys
+ * carry RoPE).
+ *
+ *   k_in, k_out  cache `kc`; k_out may equal k_in (in place), else it must not
+ *                overlap k_in and uses the same strides.
+ *   unit_len     rows per unit (N % unit_len == 0).
+ *   delta        device int64: [M] shared by all instances, or [B][M] when
+ *                delta_per_instance != 0.  |delta| < 2^31.
+ *   rope_style   KVSEL_ROPE_HALF or KVSEL_ROPE_INTERLEAVED.
+ */
+int kvsel_reposition(const void* k_in, void* k_out, kvsel_cache kc,
+                     int64_t unit_len, const int64_t* delta,
+                     int32_t delta_per_instance, double rope_base,
+                     int32_t rope_style, hipStream_t stream);
+
+/*
+ * kvsel_score -- the query block attends the cached keys ([ACRE §2.4]:
+ * A = softmax(Q_q K^T / sqrt(d)); [ACRE §2.1 Eq. 4]).
+ *
+ * With l[b,h,j,t] = scale * q[b,j,h,:] . k[b,t,kv(h),:] and the softmax over
+ * all N cached rows of the instance (no mask), computes
+ *   row_max[b,h,j] = max_t l,   row_sum[b,h,j] = sum_t exp(l - row_max)
+ * and, per unit u, the partials
+ *   part[b,h,j,u] = (m_u, S_u),  m_u = max_{t in u} l,  S_u = sum_{t in u} exp(l - m_u).
+ *
+ *   q            [B][T][Hq][D], cache dtype.
+ *   k            keys in the scoring frame (after kvsel_reposition if any).
+ *   scale        usually 1/sqrt(D).
+ *   row_max, row_sum  fp32 [B][Hq][T]; both NULL or both set.
+ *   part         fp32 [B][Hq][T][M][2], or NULL.  Requires unit_len > 1.
+ *   At least one of (row_max, part) must be set.  When only `part` is set a
+ *   single kernel runs and needs no workspace.
+ *   ws           kvsel_score_workspace(...) bytes (may be 0 -> ws NULL).
+ */
+int kvsel_score(const void* q, int64_t T, int64_t Hq, const void* k,
+                kvsel_cache kc, float scale, int64_t unit_len, float* row_max,
+                float* row_sum, float* part, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+size_t kvsel_score_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T,
+                             int64_t unit_len, int32_t want_row_stats,
+                             int32_t want_part);
+
+/*
+ * kvsel_aggregate -- per-unit relevance from the softmax-normalised
+ * attention, with alpha = exp(l - row_max) / row_sum:
+ *   KVSEL_SIG_MASS:  S[g,u] = sum_{b in g} sum_h sum_j sum_{t in u} alpha
+ *                    ([ACRE §2.4 Eq. 15] pooling over heads and query tokens,
+ *                    as a sum: the mean times Hq*T, same ranking;
+ *                    [CacheFocus §2.4 footnote 3] document-wise accumulation)
+ *   KVSEL_SIG_VNORM: S[g,u] = sum_{b in g} sum_h sum_j sum_{t in u}
+ *                    alpha * ||v[b,t,kv(h),:]||_2
+ *                    ([InfoFlow §4.2] attention-norm token score s_j = sum_i A_ij)
+ * where group g is `group` consecutive instances (e.g. the layers whose scores
+ * are summed).  Output unit_score fp32 [B/group][M].
+ *
+ * Two paths:
+ *  - chunk path (signal MASS and part != NULL): combines the partials of
+ *    kvsel_score; q, k, v are not read and may be NULL; row_max/row_sum may be
+ *    NULL (derived from part; then workspace is needed).
+ *  - token path (otherwise): re-reads q and k (and v for VNORM) and needs
+ *    row_max/row_sum from kvsel_score; works for any unit_len >= 1.
+ */
+int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k,
+                    const void* v, kvsel_cache kc, float scale,
+                    const float* row_max, const float* row_sum,
+                    const float* part, int32_t signal, int64_t unit_len,
+                    int64_t group, float* unit_score, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T,
+                                 int64_t unit_len, int32_t chunk_path,
+                                 int32_t have_row_stats);
+
+/*
+ * kvsel_topk -- arg-top-k per row of scores ([ACRE §2.4 Eq. 16]
+ * I = argtop_k(S); [InfoFlow §4.2] global budget k).
+ *
+ * Order: score descending, ties by smaller index (-0.0 equals +0.0); NaN
+ * scores are not allowed.  The k kept indices are written in ASCENDING index
+ * order (the order-preserving refill of [ACRE Eq. 18-19]).
+ *   score  fp32 [G][M];  idx int32 [G][k];  val fp32 [G][k] (score of each
+ *   kept index, same order) or NULL.  0 <= k <= M, M < 2^31.  k == 0 is a
+ *   no-op.
+ */
+int kvsel_topk(const float* score, int64_t G, int64_t M, int64_t k,
+               int32_t* idx, float* val, hipStream_t stream);
+
+/*
+ * kvsel_gather -- copy the kept units into a compact cache ("refill",
+ * [ACRE §2.4 Eq. 18-19]; final cache of [CacheFocus §2.4]).
+ *
+ * Instance b uses index row b / idx_group of idx (int32 [B/idx_group][k],
+ * ascending, each in [0, M); a slot whose index is outside that range is
+ * skipped and its output rows are left as they were).  Unit u of the source is rows
+ * [u*unit_len, (u+1)*unit_len) -- with unit_len = l this is the L1-entry ->
+ * L2-block proxy map of [ACRE Eq. 11-12].
+ *
+ * Output layout:
+ *  - compact (proxy == NULL): dst [B][k*unit_len][H][D] contiguous, the kept
+ *    units in ascending order;
+ *  - nested (proxy != NULL, [ACRE Eq. 18-19]): dst [B][m + k*unit_len][H][D]
+ *    where m = proxy->N; walking the proxy (L1) entries j in order, a selected
+ *    entry is preceded by its unit of source rows, an unselected one stands
+ *    alone.  k_proxy / v_proxy use cache `*proxy` (same B, H, D, dtype).
+ *
+ * Re-positioning on the fly ([CacheFocus §2.5] "align"): when align_base >= 0
+ * the kept keys are rotated so that the r-th kept unit occupies positions
+ * align_base + r*unit_len + (0..unit_len-1); src_start (device int64 [M], or
+ * NULL = all 0) gives the position of each source unit's first row.  Values
+ * are copied unchanged.  Not available in nested mode.
+ *
+ *   v_src / v_dst (and v_proxy) may be NULL to gather keys only.
+ */
+int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc,
+                 int64_t unit_len, const int32_t* idx, int64_t k,
+                 int64_t idx_group, const int64_t* src_start,
+                 int64_t align_base, double rope_base, int32_t rope_style,
+                 const void* k_proxy, const void* v_proxy,
+                 const kvsel_cache* proxy, void* k_dst, void* v_dst,
+                 hipStream_t stream);
+
+/*
+ * kvsel_decode_attn -- one attention pass of the query rows over the compact
+ * cache ([ACRE §2.1 Eq. 4]; decoding on the refilled cache, [ACRE §2.4]).
+ *
+ *   o[b,j,h,:] = sum_t softmax_t(scale * q[b,j,h,:] . k_t) v_t
+ * over the concatenation of the n_seg segments (a HOST array; all share B, H,
+ * D and dtype with the query), no mask.  Output fp32 [B][T][Hq][D]; lse (fp32
+ * [B][Hq][T], natural log of sum_t exp(l)) or NULL.  1 <= n_seg <= 4; every
+ * segment has N >= 1.
+ *   ws  kvsel_decode_workspace(...) bytes (returns 0 for invalid arguments).
+ */
+int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale,
+                      const kvsel_segment* segs, int32_t n_seg, float* out,
+                      float* lse, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+size_t kvsel_decode_workspace(int64_t T, int64_t Hq, const kvsel_segment* segs,
+                              int32_t n_seg);
+
+/* Text of a status code; message of the last failed call on this thread. */
+const char* kvsel_status_str(int status);
+const char* kvsel_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+int kvsel_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

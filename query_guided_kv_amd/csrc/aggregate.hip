@@ -1,0 +1,194 @@
+// Per-unit relevance from the softmax-normalised attention.
+//   mass:  S[g,u] = sum_{b in g} sum_h sum_j sum_{t in u} alpha        (ACRE §2.4 Eq. 15,
+//          as a sum; CacheFocus §2.4 footnote 3)
+//   vnorm: S[g,u] = sum ... alpha * ||v[b,t,kv(h)]||_2                  (InfoFlow §4.2)
+// with alpha = exp(l - row_max) / row_sum.
+//
+// Chunk path: units are the score segments, so the per-unit sums follow from
+// the partials (m_u, S_u) without touching the cache again:
+//   sum_{t in u} alpha = S_u * exp(m_u - row_max) / row_sum.
+// Token path: the logits are recomputed from Q and K (a second streaming pass
+// over the keys, plus the values for the norm); each lane group owns one
+// cached row and loops over the query rows, so the sum over rows stays in
+// registers and needs no atomics.  Reductions have a fixed order, so results
+// are bitwise reproducible from run to run.
+#include "common.h"
+#include "internal.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void __launch_bounds__(kThreads)
+agg_chunk_kernel(const float* __restrict__ part, const float* __restrict__ row_max,
+                 const float* __restrict__ row_sum, int64_t rows_per_inst, int64_t M,
+                 int64_t group, int64_t mblocks, float* __restrict__ out) {
+  const int64_t gi = blockIdx.x / mblocks;
+  const int64_t u = (blockIdx.x % mblocks) * kThreads + threadIdx.x;
+  if (u >= M) return;
+  float acc = 0.0f;
+  for (int64_t bi = 0; bi < group; ++bi) {
+    const int64_t row0 = (gi * group + bi) * rows_per_inst;
+    for (int64_t r = 0; r < rows_per_inst; ++r) {
+      const int64_t row = row0 + r;
+      const float m = row_max[row];
+      const float inv_z = 1.0f / row_sum[row];
+      const float2 pu = *reinterpret_cast<const float2*>(part + (row * M + u) * 2);
+      acc += pu.y * exp2f((pu.x - m) * kLog2e) * inv_z;
+    }
+  }
+  out[gi * M + u] = acc;
+}
+
+constexpr int kQRows = 64;
+constexpr int kPad = 4;
+
+// per_token[b][t] = sum_h sum_j alpha[b,h,j,t] (* ||v[b,t,kv(h)]||)
+template <typename T, int D, int TPR, bool VNORM>
+__global__ void __launch_bounds__(kThreads)
+agg_token_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                 int64_t N, int H, int64_t stride_b, int64_t stride_n, int T_, int Hq,
+                 float scale2, const float* __restrict__ row_max,
+                 const float* __restrict__ row_sum, int64_t tiles,
+                 float* __restrict__ per_token) {
+  constexpr int TPB = kThreads / TPR;  // cached rows per block
+  constexpr int DPT = D / TPR;
+  __shared__ __align__(16) float qs[kQRows][D + kPad];
+  __shared__ float mz[kQRows][2];
+
+  const int64_t b = blockIdx.x / tiles;
+  const int64_t t = (blockIdx.x % tiles) * TPB + threadIdx.x / TPR;
+  const int p = threadIdx.x % TPR;
+  const bool t_ok = t < N;
+  const int G = Hq / H;
+  const int R = G * T_;
+  float acc = 0.0f;
+  for (int g = 0; g < H; ++g) {
+    float kf[DPT];
+    float vn = 1.0f;
+    {
+      const int64_t off = b * stride_b + (t_ok ? t : 0) * stride_n + static_cast<int64_t>(g) * D + p * DPT;
+      load_f32<T, DPT>(k + off, kf);
+      if constexpr (VNORM) {
+        float vf[DPT];
+        load_f32<T, DPT>(v + off, vf);
+        float ss = 0.0f;
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) ss += vf[d] * vf[d];
+        vn = sqrtf(group_sum<TPR>(ss));
+      }
+    }
+    float accg = 0.0f;
+    for (int r0 = 0; r0 < R; r0 += kQRows) {
+      const int nr = min(kQRows, R - r0);
+      __syncthreads();
+      for (int e = threadIdx.x; e < nr * D; e += kThreads) {
+        const int rr = e / D, d = e % D;
+        const int r = r0 + rr;
+        const int h = g * G + r / T_, j = r % T_;
+        qs[rr][d] = Elem<T>::to_f32(q[((b * T_ + j) * Hq + h) * D + d]);
+      }
+      for (int rr = threadIdx.x; rr < nr; rr += kThreads) {
+        const int r = r0 + rr;
+        const int h = g * G + r / T_, j = r % T_;
+        const int64_t row = (b * Hq + h) * T_ + j;
+        mz[rr][0] = row_max[row] * kLog2e;
+        mz[rr][1] = 1.0f / row_sum[row];
+      }
+      __syncthreads();
+      for (int rr = 0; rr < nr; ++rr) {
+        float dot = 0.0f;
+        if constexpr (DPT >= 4) {
+          const float4* qr = reinterpret_cast<const float4*>(&qs[rr][p * DPT]);
+#pragma unroll
+          for (int d4 = 0; d4 < DPT / 4; ++d4) {
+            const float4 qq = qr[d4];
+            dot += qq.x * kf[4 * d4] + qq.y * kf[4 * d4 + 1] + qq.z * kf[4 * d4 + 2] +
+                   qq.w * kf[4 * d4 + 3];
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) dot += qs[rr][p * DPT + d] * kf[d];
+        }
+        dot = group_sum<TPR>(dot);
+        accg += exp2f(dot * scale2 - mz[rr][0]) * mz[rr][1];
+      }
+    }
+    acc += accg * vn;
+  }
+  if (t_ok && p == 0) per_token[b * N + t] = acc;
+}
+
+// unit_score[g][u] = sum_{b in g} sum_{t in u} per_token[b][t], fixed order.
+__global__ void __launch_bounds__(kThreads)
+unit_sum_kernel(const float* __restrict__ per_token, int64_t N, int64_t unit_len, int64_t M,
+                int64_t group, int64_t mblocks, float* __restrict__ out) {
+  const int64_t gi = blockIdx.x / mblocks;
+  const int64_t u = (blockIdx.x % mblocks) * kThreads + threadIdx.x;
+  if (u >= M) return;
+  float acc = 0.0f;
+  for (int64_t bi = 0; bi < group; ++bi) {
+    const float* pt = per_token + (gi * group + bi) * N + u * unit_len;
+    for (int64_t t = 0; t < unit_len; ++t) acc += pt[t];
+  }
+  out[gi * M + u] = acc;
+}
+
+template <typename T, int D, int TPR>
+void launch_tok(const void* q, int64_t T_, int64_t Hq, const void* k, const void* v,
+                const kvsel_cache& kc, float scale2, const float* rm, const float* rs, int vnorm,
+                float* per_token, hipStream_t s) {
+  constexpr int TPB = kThreads / TPR;
+  const int64_t tiles = (kc.N + TPB - 1) / TPB;
+  const dim3 grid(static_cast<unsigned>(kc.B * tiles));
+  if (vnorm)
+    hipLaunchKernelGGL((agg_token_kernel<T, D, TPR, true>), grid, dim3(kThreads), 0, s,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), kc.N, static_cast<int>(kc.H), kc.stride_b,
+                       kc.stride_n, static_cast<int>(T_), static_cast<int>(Hq), scale2, rm, rs,
+                       tiles, per_token);
+  else
+    hipLaunchKernelGGL((agg_token_kernel<T, D, TPR, false>), grid, dim3(kThreads), 0, s,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), kc.N, static_cast<int>(kc.H), kc.stride_b,
+                       kc.stride_n, static_cast<int>(T_), static_cast<int>(Hq), scale2, rm, rs,
+                       tiles, per_token);
+}
+
+}  // namespace
+
+int launch_aggregate_chunks(const float* part, const float* row_max, const float* row_sum,
+                            int64_t B, int64_t Hq, int64_t T, int64_t M, int64_t group,
+                            float* unit_score, hipStream_t s) {
+  const int64_t mblocks = (M + kThreads - 1) / kThreads;
+  const int64_t G = B / group;
+  hipLaunchKernelGGL(agg_chunk_kernel, dim3(static_cast<unsigned>(G * mblocks)), dim3(kThreads), 0,
+                     s, part, row_max, row_sum, Hq * T, M, group, mblocks, unit_score);
+  return check_launch("kvsel_aggregate");
+}
+
+int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
+                            const kvsel_cache& kc, float scale, const float* row_max,
+                            const float* row_sum, int vnorm, float* per_token, hipStream_t s) {
+  const float scale2 = scale * kLog2e;
+  if (kc.dtype == KVSEL_BF16) {
+    if (kc.D == 128) launch_tok<bf16_t, 128, 4>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
+    else launch_tok<bf16_t, 64, 4>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
+  } else {
+    if (kc.D == 128) launch_tok<float, 128, 4>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
+    else launch_tok<float, 64, 4>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
+  }
+  return check_launch("kvsel_aggregate (token path)");
+}
+
+int launch_unit_sums(const float* per_token, int64_t B, int64_t N, int64_t unit_len,
+                     int64_t group, float* unit_score, hipStream_t s) {
+  const int64_t M = N / unit_len;
+  const int64_t mblocks = (M + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(unit_sum_kernel, dim3(static_cast<unsigned>((B / group) * mblocks)),
+                     dim3(kThreads), 0, s, per_token, N, unit_len, M, group, mblocks, unit_score);
+  return check_launch("kvsel_aggregate (unit sums)");
+}
+
+}  // namespace kvsel

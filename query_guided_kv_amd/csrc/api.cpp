@@ -1,0 +1,340 @@
+// C ABI of libkvsel: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before anything is enqueued; no call allocates
+// device memory.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+#include "kvsel.h"
+
+namespace kvsel {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return KVSEL_OK;
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return KVSEL_ERR_HIP;
+}
+
+namespace {
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const kvsel_cache& kc, const char* what) {
+  if (kc.dtype != KVSEL_BF16 && kc.dtype != KVSEL_FP32)
+    return fail(KVSEL_ERR_DTYPE, "%s: dtype %d is neither bf16 nor fp32", what, kc.dtype);
+  if (kc.B < 1 || kc.N < 1 || kc.H < 1)
+    return fail(KVSEL_ERR_SHAPE, "%s: B, N, H must be >= 1 (B=%lld N=%lld H=%lld)", what,
+                (long long)kc.B, (long long)kc.N, (long long)kc.H);
+  if (kc.D != 64 && kc.D != 128)
+    return fail(KVSEL_ERR_UNSUPPORTED, "%s: head dim %lld not in {64, 128}", what, (long long)kc.D);
+  if (kc.stride_n < kc.H * kc.D || kc.stride_b < kc.N * kc.stride_n)
+    return fail(KVSEL_ERR_SHAPE, "%s: strides too small for [N][H][D]", what);
+  if (kc.stride_n % 8 != 0 || kc.stride_b % 8 != 0)
+    return fail(KVSEL_ERR_UNSUPPORTED, "%s: strides must be multiples of 8 elements", what);
+  if (kc.B > (int64_t{1} << 24) || kc.N >= (int64_t{1} << 31))
+    return fail(KVSEL_ERR_SHAPE, "%s: B or N out of range", what);
+  return KVSEL_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(KVSEL_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(KVSEL_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  return KVSEL_OK;
+}
+
+int check_heads(int64_t T, int64_t Hq, const kvsel_cache& kc, const char* what) {
+  if (T < 1 || Hq < 1 || Hq % kc.H != 0)
+    return fail(KVSEL_ERR_SHAPE, "%s: need T >= 1 and Hq a multiple of H (T=%lld Hq=%lld H=%lld)",
+                what, (long long)T, (long long)Hq, (long long)kc.H);
+  if (Hq > 4096 || T > 65536 || (Hq / kc.H) * T > (int64_t{1} << 20))
+    return fail(KVSEL_ERR_SHAPE, "%s: query block too large", what);
+  return KVSEL_OK;
+}
+
+int check_units(const kvsel_cache& kc, int64_t unit_len, const char* what) {
+  if (unit_len < 1 || kc.N % unit_len != 0)
+    return fail(KVSEL_ERR_SHAPE, "%s: unit_len %lld must be >= 1 and divide N=%lld", what,
+                (long long)unit_len, (long long)kc.N);
+  return KVSEL_OK;
+}
+
+#define KVSEL_TRY(x)            \
+  do {                          \
+    const int rc_ = (x);        \
+    if (rc_ != KVSEL_OK) return rc_; \
+  } while (0)
+
+size_t score_ws(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len, bool stats,
+                bool part) {
+  if (!stats || (part && unit_len > 1)) return 0;
+  const int64_t nseg = (N + kTokenTile - 1) / kTokenTile;
+  return static_cast<size_t>(B * Hq * T * nseg * 2) * sizeof(float);
+}
+
+size_t aggregate_ws(int64_t B, int64_t N, int64_t Hq, int64_t T, bool chunk, bool have_stats) {
+  if (chunk) return have_stats ? 0 : static_cast<size_t>(2 * B * Hq * T) * sizeof(float);
+  return static_cast<size_t>(B * N) * sizeof(float);
+}
+
+int64_t decode_splits(const kvsel_segment* segs, int n_seg) {
+  int64_t n = 0;
+  for (int i = 0; i < n_seg; ++i) n += (segs[i].kc.N + kDecodeSplit - 1) / kDecodeSplit;
+  return n;
+}
+
+}  // namespace
+}  // namespace kvsel
+
+using namespace kvsel;
+
+extern "C" {
+
+int kvsel_version(void) { return 100; }
+
+const char* kvsel_last_error(void) { return kvsel::g_err; }
+
+const char* kvsel_status_str(int status) {
+  switch (status) {
+    case KVSEL_OK: return "ok";
+    case KVSEL_ERR_NULL: return "null pointer";
+    case KVSEL_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case KVSEL_ERR_DTYPE: return "unsupported dtype";
+    case KVSEL_ERR_UNSUPPORTED: return "unsupported head dim, alignment or stride";
+    case KVSEL_ERR_WORKSPACE: return "workspace too small";
+    case KVSEL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int kvsel_reposition(const void* k_in, void* k_out, kvsel_cache kc, int64_t unit_len,
+                     const int64_t* delta, int32_t delta_per_instance, double rope_base,
+                     int32_t rope_style, hipStream_t stream) {
+  KVSEL_TRY(check_ptr(k_in, "k_in"));
+  KVSEL_TRY(check_ptr(k_out, "k_out"));
+  if (delta == nullptr) return fail(KVSEL_ERR_NULL, "delta is NULL");
+  KVSEL_TRY(check_cache(kc, "kvsel_reposition"));
+  KVSEL_TRY(check_units(kc, unit_len, "kvsel_reposition"));
+  if (rope_style != KVSEL_ROPE_HALF && rope_style != KVSEL_ROPE_INTERLEAVED)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_reposition: unknown rope_style %d", rope_style);
+  if (!(rope_base > 1.0))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_reposition: rope_base must be > 1");
+  return launch_reposition(k_in, k_out, kc, unit_len, delta, delta_per_instance != 0, rope_base,
+                           rope_style, stream);
+}
+
+size_t kvsel_score_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len,
+                             int32_t want_row_stats, int32_t want_part) {
+  if (B < 1 || N < 1 || Hq < 1 || T < 1 || unit_len < 1) return 0;
+  return score_ws(B, N, Hq, T, unit_len, want_row_stats != 0, want_part != 0);
+}
+
+int kvsel_score(const void* q, int64_t T, int64_t Hq, const void* k, kvsel_cache kc, float scale,
+                int64_t unit_len, float* row_max, float* row_sum, float* part, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  KVSEL_TRY(check_ptr(q, "q"));
+  KVSEL_TRY(check_ptr(k, "k"));
+  KVSEL_TRY(check_cache(kc, "kvsel_score"));
+  KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_score"));
+  KVSEL_TRY(check_units(kc, unit_len, "kvsel_score"));
+  if ((row_max == nullptr) != (row_sum == nullptr))
+    return fail(KVSEL_ERR_NULL, "kvsel_score: row_max and row_sum must both be set or both NULL");
+  const bool stats = row_max != nullptr;
+  if (!stats && part == nullptr)
+    return fail(KVSEL_ERR_NULL, "kvsel_score: no output requested");
+  if (part != nullptr && unit_len < 2)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_score: per-unit partials need unit_len > 1");
+  const size_t need = score_ws(kc.B, kc.N, Hq, T, unit_len, stats, part != nullptr);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(KVSEL_ERR_WORKSPACE, "kvsel_score: workspace %zu < %zu bytes", ws_bytes, need);
+  const int64_t rows = kc.B * Hq * T;
+  if (part != nullptr) {
+    KVSEL_TRY(launch_score_partials(q, T, Hq, k, kc, scale, unit_len, part, 1, stream));
+    if (stats) return launch_rowstats(part, rows, kc.N / unit_len, 1, row_max, row_sum, stream);
+    return KVSEL_OK;
+  }
+  float* ms = static_cast<float*>(ws);
+  KVSEL_TRY(launch_score_partials(q, T, Hq, k, kc, scale, kTokenTile, ms, 0, stream));
+  return launch_rowstats(ms, rows, (kc.N + kTokenTile - 1) / kTokenTile, 0, row_max, row_sum,
+                         stream);
+}
+
+size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len,
+                                 int32_t chunk_path, int32_t have_row_stats) {
+  if (B < 1 || N < 1 || Hq < 1 || T < 1 || unit_len < 1) return 0;
+  return aggregate_ws(B, N, Hq, T, chunk_path != 0, have_row_stats != 0);
+}
+
+int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
+                    kvsel_cache kc, float scale, const float* row_max, const float* row_sum,
+                    const float* part, int32_t signal, int64_t unit_len, int64_t group,
+                    float* unit_score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  KVSEL_TRY(check_cache(kc, "kvsel_aggregate"));
+  KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_aggregate"));
+  KVSEL_TRY(check_units(kc, unit_len, "kvsel_aggregate"));
+  if (signal != KVSEL_SIG_MASS && signal != KVSEL_SIG_VNORM)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_aggregate: unknown signal %d", signal);
+  if (group < 1 || kc.B % group != 0)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_aggregate: group %lld must divide B=%lld",
+                (long long)group, (long long)kc.B);
+  if (unit_score == nullptr) return fail(KVSEL_ERR_NULL, "unit_score is NULL");
+  if ((row_max == nullptr) != (row_sum == nullptr))
+    return fail(KVSEL_ERR_NULL, "kvsel_aggregate: row_max and row_sum must both be set or both NULL");
+  const bool chunk = signal == KVSEL_SIG_MASS && part != nullptr;
+  const bool stats = row_max != nullptr;
+  const int64_t M = kc.N / unit_len;
+  const int64_t rows = kc.B * Hq * T;
+  const size_t need = aggregate_ws(kc.B, kc.N, Hq, T, chunk, stats);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(KVSEL_ERR_WORKSPACE, "kvsel_aggregate: workspace %zu < %zu bytes", ws_bytes, need);
+  if (chunk) {
+    if (unit_len < 2) return fail(KVSEL_ERR_SHAPE, "kvsel_aggregate: partials need unit_len > 1");
+    const float* rm = row_max;
+    const float* rs = row_sum;
+    if (!stats) {
+      float* w = static_cast<float*>(ws);
+      KVSEL_TRY(launch_rowstats(part, rows, M, 1, w, w + rows, stream));
+      rm = w;
+      rs = w + rows;
+    }
+    return launch_aggregate_chunks(part, rm, rs, kc.B, Hq, T, M, group, unit_score, stream);
+  }
+  KVSEL_TRY(check_ptr(q, "q"));
+  KVSEL_TRY(check_ptr(k, "k"));
+  if (signal == KVSEL_SIG_VNORM) KVSEL_TRY(check_ptr(v, "v"));
+  if (!stats)
+    return fail(KVSEL_ERR_NULL, "kvsel_aggregate: the token path needs row_max and row_sum");
+  float* per_token = static_cast<float*>(ws);
+  KVSEL_TRY(launch_aggregate_tokens(q, T, Hq, k, v, kc, scale, row_max, row_sum,
+                                    signal == KVSEL_SIG_VNORM, per_token, stream));
+  return launch_unit_sums(per_token, kc.B, kc.N, unit_len, group, unit_score, stream);
+}
+
+int kvsel_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,
+               hipStream_t stream) {
+  if (score == nullptr) return fail(KVSEL_ERR_NULL, "score is NULL");
+  if (G < 1 || M < 1 || M >= (int64_t{1} << 31) || G > (int64_t{1} << 31) - 1)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_topk: G=%lld M=%lld out of range", (long long)G,
+                (long long)M);
+  if (k < 0 || k > M)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_topk: k=%lld not in [0, M=%lld]", (long long)k,
+                (long long)M);
+  if (k == 0) return KVSEL_OK;
+  if (idx == nullptr) return fail(KVSEL_ERR_NULL, "idx is NULL");
+  return launch_topk(score, G, M, k, idx, val, stream);
+}
+
+int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc, int64_t unit_len,
+                 const int32_t* idx, int64_t k, int64_t idx_group, const int64_t* src_start,
+                 int64_t align_base, double rope_base, int32_t rope_style,
+                 const void* k_proxy, const void* v_proxy, const kvsel_cache* proxy,
+                 void* k_dst, void* v_dst, hipStream_t stream) {
+  KVSEL_TRY(check_ptr(k_src, "k_src"));
+  KVSEL_TRY(check_ptr(k_dst, "k_dst"));
+  if ((v_src == nullptr) != (v_dst == nullptr))
+    return fail(KVSEL_ERR_NULL, "kvsel_gather: v_src and v_dst must both be set or both NULL");
+  if (v_src != nullptr) {
+    KVSEL_TRY(check_ptr(v_src, "v_src"));
+    KVSEL_TRY(check_ptr(v_dst, "v_dst"));
+  }
+  KVSEL_TRY(check_cache(kc, "kvsel_gather"));
+  KVSEL_TRY(check_units(kc, unit_len, "kvsel_gather"));
+  const int64_t M = kc.N / unit_len;
+  if (k < 0 || k > M)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_gather: k=%lld not in [0, M=%lld]", (long long)k, (long long)M);
+  if (idx_group < 1 || kc.B % idx_group != 0)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_gather: idx_group must divide B");
+  if (k > 0 && idx == nullptr) return fail(KVSEL_ERR_NULL, "idx is NULL");
+  if (align_base >= 0) {
+    if (rope_style != KVSEL_ROPE_HALF && rope_style != KVSEL_ROPE_INTERLEAVED)
+      return fail(KVSEL_ERR_SHAPE, "kvsel_gather: unknown rope_style %d", rope_style);
+    if (!(rope_base > 1.0)) return fail(KVSEL_ERR_SHAPE, "kvsel_gather: rope_base must be > 1");
+    if (align_base + (M + 1) * unit_len >= (int64_t{1} << 31))
+      return fail(KVSEL_ERR_SHAPE, "kvsel_gather: aligned positions out of range");
+  }
+  int64_t dst_rows = k * unit_len;
+  if (proxy != nullptr) {
+    KVSEL_TRY(check_cache(*proxy, "kvsel_gather proxy"));
+    KVSEL_TRY(check_ptr(k_proxy, "k_proxy"));
+    if ((v_proxy == nullptr) != (v_src == nullptr))
+      return fail(KVSEL_ERR_NULL, "kvsel_gather: v_proxy must be set exactly when v_src is");
+    if (v_proxy != nullptr) KVSEL_TRY(check_ptr(v_proxy, "v_proxy"));
+    if (proxy->B != kc.B || proxy->H != kc.H || proxy->D != kc.D || proxy->dtype != kc.dtype)
+      return fail(KVSEL_ERR_SHAPE, "kvsel_gather: proxy cache must share B, H, D and dtype");
+    if (proxy->N != M)
+      return fail(KVSEL_ERR_SHAPE, "kvsel_gather: proxy has %lld entries, source has %lld units",
+                  (long long)proxy->N, (long long)M);
+    if (align_base >= 0)
+      return fail(KVSEL_ERR_UNSUPPORTED, "kvsel_gather: re-positioning is not available in nested mode");
+    dst_rows += proxy->N;
+  }
+  if (k > 0)
+    KVSEL_TRY(launch_gather(k_src, v_src, kc, unit_len, idx, k, idx_group, src_start, align_base,
+                            rope_base, rope_style, proxy != nullptr, dst_rows, k_dst, v_dst,
+                            stream));
+  if (proxy != nullptr)
+    return launch_proxy_copy(k_proxy, v_proxy, *proxy, unit_len, idx, k, idx_group, dst_rows,
+                             k_dst, v_dst, stream);
+  return KVSEL_OK;
+}
+
+size_t kvsel_decode_workspace(int64_t T, int64_t Hq, const kvsel_segment* segs, int32_t n_seg) {
+  if (segs == nullptr || n_seg < 1 || n_seg > kMaxSegments || T < 1 || Hq < 1) return 0;
+  for (int i = 0; i < n_seg; ++i)
+    if (segs[i].kc.N < 1 || segs[i].kc.B < 1 || segs[i].kc.D < 1) return 0;
+  const int64_t n_split = decode_splits(segs, n_seg);
+  return static_cast<size_t>(segs[0].kc.B * Hq * T * n_split * (2 + segs[0].kc.D)) * sizeof(float);
+}
+
+int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const kvsel_segment* segs,
+                      int32_t n_seg, float* out, float* lse, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  KVSEL_TRY(check_ptr(q, "q"));
+  if (out == nullptr) return fail(KVSEL_ERR_NULL, "out is NULL");
+  if (segs == nullptr) return fail(KVSEL_ERR_NULL, "segs is NULL");
+  if (n_seg < 1 || n_seg > kMaxSegments)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_decode_attn: n_seg=%d not in [1, %d]", n_seg, kMaxSegments);
+  const kvsel_cache& c0 = segs[0].kc;
+  DecodeSeg ds[kMaxSegments];
+  int64_t split = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    const kvsel_cache& c = segs[i].kc;
+    KVSEL_TRY(check_cache(c, "kvsel_decode_attn segment"));
+    KVSEL_TRY(check_ptr(segs[i].k, "segment k"));
+    KVSEL_TRY(check_ptr(segs[i].v, "segment v"));
+    if (c.B != c0.B || c.H != c0.H || c.D != c0.D || c.dtype != c0.dtype)
+      return fail(KVSEL_ERR_SHAPE, "kvsel_decode_attn: segments must share B, H, D and dtype");
+    ds[i] = DecodeSeg{segs[i].k, segs[i].v, c.N, c.stride_b, c.stride_n, split};
+    split += (c.N + kDecodeSplit - 1) / kDecodeSplit;
+  }
+  KVSEL_TRY(check_heads(T, Hq, c0, "kvsel_decode_attn"));
+  const size_t need = kvsel_decode_workspace(T, Hq, segs, n_seg);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(KVSEL_ERR_WORKSPACE, "kvsel_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
+  float* ws_ms = static_cast<float*>(ws);
+  float* ws_o = ws_ms + c0.B * Hq * T * split * 2;
+  return launch_decode(q, T, Hq, scale, ds, n_seg, c0.B, c0.H, c0.D, c0.dtype, split, out, lse,
+                       ws_ms, ws_o, stream);
+}
+
+}  // extern "C"

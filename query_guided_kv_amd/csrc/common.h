@@ -1,0 +1,209 @@
+// Device helpers shared by the kvsel kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvsel.h"
+
+namespace kvsel {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+using bf16_t = uint16_t;  // raw bfloat16 bit pattern
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Element access for the two cache dtypes.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPerVec = 4;  // elements per 16-byte vector
+  __device__ static __forceinline__ float load(const float* p) { return *p; }
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+  __device__ static __forceinline__ float from_f32(float x) { return x; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kPerVec = 8;
+  __device__ static __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ static __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+  __device__ static __forceinline__ bf16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// 16-byte vector unpacked to fp32 / packed from fp32.
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& raw, float* out) {
+  if constexpr (sizeof(T) == 4) {
+    out[0] = __uint_as_float(raw.x); out[1] = __uint_as_float(raw.y);
+    out[2] = __uint_as_float(raw.z); out[3] = __uint_as_float(raw.w);
+  } else {
+    out[0] = bf16_lo(raw.x); out[1] = bf16_hi(raw.x);
+    out[2] = bf16_lo(raw.y); out[3] = bf16_hi(raw.y);
+    out[4] = bf16_lo(raw.z); out[5] = bf16_hi(raw.z);
+    out[6] = bf16_lo(raw.w); out[7] = bf16_hi(raw.w);
+  }
+}
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float* in) {
+  uint4 r;
+  if constexpr (sizeof(T) == 4) {
+    r.x = __float_as_uint(in[0]); r.y = __float_as_uint(in[1]);
+    r.z = __float_as_uint(in[2]); r.w = __float_as_uint(in[3]);
+  } else {
+    r.x = f32_to_bf16(in[0]) | (static_cast<uint32_t>(f32_to_bf16(in[1])) << 16);
+    r.y = f32_to_bf16(in[2]) | (static_cast<uint32_t>(f32_to_bf16(in[3])) << 16);
+    r.z = f32_to_bf16(in[4]) | (static_cast<uint32_t>(f32_to_bf16(in[5])) << 16);
+    r.w = f32_to_bf16(in[6]) | (static_cast<uint32_t>(f32_to_bf16(in[7])) << 16);
+  }
+  return r;
+}
+
+// Load n contiguous elements (n * sizeof(T) a multiple of 16, 16-byte aligned)
+// as fp32.
+template <typename T, int n>
+__device__ __forceinline__ void load_f32(const T* p, float* out) {
+  constexpr int V = Elem<T>::kPerVec;
+  static_assert(n % V == 0, "slice must be whole 16-byte vectors");
+#pragma unroll
+  for (int i = 0; i < n / V; ++i) unpack16<T>(reinterpret_cast<const uint4*>(p)[i], out + i * V);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions inside groups of W consecutive lanes (W | 64).
+// DPP for W <= 16 (quad permutes and row mirrors), LDS crossbar beyond.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float dpp_half_mirror(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, false);  // lane i <- lane 7-i (per 8)
+}
+__device__ __forceinline__ float dpp_mirror(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, false);  // lane i <- lane 15-i (per 16)
+}
+
+// Sum over groups of W lanes; every lane of a group gets the group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "W");
+  if constexpr (W >= 2) x += dpp_xor1(x);
+  if constexpr (W >= 4) x += dpp_xor2(x);
+  if constexpr (W >= 8) x += dpp_half_mirror(x);
+  if constexpr (W >= 16) x += dpp_mirror(x);
+  if constexpr (W >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (W >= 2) x = fmaxf(x, dpp_xor1(x));
+  if constexpr (W >= 4) x = fmaxf(x, dpp_xor2(x));
+  if constexpr (W >= 8) x = fmaxf(x, dpp_half_mirror(x));
+  if constexpr (W >= 16) x = fmaxf(x, dpp_mirror(x));
+  if constexpr (W >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
+  if constexpr (W >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+// Merge of two softmax partials (m, s) in the log2 domain: s = sum 2^(l - m).
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
+  m = mn;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE: per-pair cos/sin of delta * theta_i in fp64, theta_i = base^(-2i/D).
+// The 2x2 rotation is also done in fp64 and rounded once to the cache dtype,
+// so a re-positioned key is the correctly rounded rotation of the stored one.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double2 rope_cs(int64_t delta, int i, int D, double base) {
+  const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(D));
+  const double ang = static_cast<double>(delta) * theta;
+  double s, c;
+  sincos(ang, &s, &c);
+  return make_double2(c, s);
+}
+
+// fp64 -> bf16 with one rounding to nearest even: round to fp32 toward zero,
+// make the last bit sticky (round to odd), then round fp32 -> bf16.  fp32
+// keeps more than two extra bits, so the two steps round like one.
+__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
+  float t = __double2float_rz(x);
+  if (static_cast<double>(t) != x) t = __uint_as_float(__float_as_uint(t) | 1u);
+  return f32_to_bf16(t);
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 pack16_f64(const double* in) {
+  uint4 r;
+  if constexpr (sizeof(T) == 4) {
+    r.x = __float_as_uint(__double2float_rn(in[0])); r.y = __float_as_uint(__double2float_rn(in[1]));
+    r.z = __float_as_uint(__double2float_rn(in[2])); r.w = __float_as_uint(__double2float_rn(in[3]));
+  } else {
+    r.x = f64_to_bf16(in[0]) | (static_cast<uint32_t>(f64_to_bf16(in[1])) << 16);
+    r.y = f64_to_bf16(in[2]) | (static_cast<uint32_t>(f64_to_bf16(in[3])) << 16);
+    r.z = f64_to_bf16(in[4]) | (static_cast<uint32_t>(f64_to_bf16(in[5])) << 16);
+    r.w = f64_to_bf16(in[6]) | (static_cast<uint32_t>(f64_to_bf16(in[7])) << 16);
+  }
+  return r;
+}
+
+// Rotate 16-byte vectors of a key row.  Half-split pairing: `ra` holds dims
+// [d0, d0 + V) and `rb` the partner dims [d0 + D/2, ...); interleaved: `ra`
+// holds V/2 whole pairs starting at dim d0 and `rb` is unused.  `cs` is the
+// row's table, indexed by pair.
+template <typename T, int STYLE>
+__device__ __forceinline__ void rope_rotate16(uint4& ra, uint4& rb, int d0, const double2* cs) {
+  constexpr int V = Elem<T>::kPerVec;
+  float a[V];
+  double oa[V];
+  unpack16<T>(ra, a);
+  if constexpr (STYLE == KVSEL_ROPE_HALF) {
+    float b[V];
+    double ob[V];
+    unpack16<T>(rb, b);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const double2 t = cs[d0 + e];
+      const double x = a[e], y = b[e];
+      oa[e] = fma(x, t.x, -y * t.y);
+      ob[e] = fma(x, t.y, y * t.x);
+    }
+    rb = pack16_f64<T>(ob);
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; e += 2) {
+      const double2 t = cs[(d0 + e) >> 1];
+      const double x = a[e], y = a[e + 1];
+      oa[e] = fma(x, t.x, -y * t.y);
+      oa[e + 1] = fma(x, t.y, y * t.x);
+    }
+  }
+  ra = pack16_f64<T>(oa);
+}
+
+// Record a launch failure; returns KVSEL_OK or KVSEL_ERR_HIP.
+int check_launch(const char* what);
+void set_error(const char* fmt, ...);
+
+}  // namespace kvsel

@@ -1,0 +1,399 @@
+// Final attention pass over the compact cache (ACRE §2.1 Eq. 4; decoding on
+// the refilled cache, ACRE §2.4).
+//
+// Split-K: the keys of every segment are cut into splits of kDecodeSplit rows;
+// one workgroup computes, for its split, each row's running max m, sum s and
+// unnormalised output o (online softmax in the log2 domain).  A merge kernel
+// combines the splits of a row with the usual rescaling and writes
+// o / s and lse = (m + log2 s) * ln 2.
+//
+// stream variant: bf16, few rows per kv head (decode).  Lanes own 32 bytes of
+// a key row and the matching 32 bytes of the value row; logits use packed bf16
+// dots and an 8-lane DPP reduction; the four waves' partials are merged
+// through LDS one wave at a time.
+// tile variant: any shape; keys and values staged through LDS as fp32.
+#include "common.h"
+#include "internal.h"
+
+namespace kvsel {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+struct SegTable {
+  const void* k[kMaxSegments];
+  const void* v[kMaxSegments];
+  int64_t N[kMaxSegments];
+  int64_t stride_b[kMaxSegments];
+  int64_t stride_n[kMaxSegments];
+  int64_t split_begin[kMaxSegments + 1];
+};
+
+// Which segment and key range a split covers.
+__device__ __forceinline__ int find_seg(const SegTable& st, int n_seg, int64_t sp) {
+  int sg = 0;
+  while (sg + 1 < n_seg && sp >= st.split_begin[sg + 1]) ++sg;
+  return sg;
+}
+
+// ---------------------------------------------------------------------------
+// stream variant
+// ---------------------------------------------------------------------------
+template <int D, int H, int R, int UNROLL>
+__global__ void __launch_bounds__(kThreads)
+decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t n_split,
+                     int T, int Hq, float scale2, float* __restrict__ ws_ms,
+                     float* __restrict__ ws_o) {
+  constexpr int LPH = D / 16;
+  constexpr int LPT = H * LPH;
+  constexpr int TPW = 64 / LPT;
+  static_assert(LPT <= 64 && 64 % LPT == 0, "row must tile a wave");
+  constexpr int ROWS = H * R;
+  __shared__ float red_o[ROWS][D];
+  __shared__ float red_ms[ROWS][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = lane / LPT;
+  const int g = (lane % LPT) / LPH;
+  const int c = lane % LPH;
+  const int64_t b = blockIdx.x / n_split;
+  const int64_t sp = blockIdx.x % n_split;
+  const int sg = find_seg(st, n_seg, sp);
+  const int64_t t_begin = (sp - st.split_begin[sg]) * kDecodeSplit;
+  const int64_t t_end = min(st.N[sg], t_begin + kDecodeSplit);
+  const int G = Hq / H;
+
+  uint32_t qv[R][8];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int h = g * G + r / T, j = r % T;
+    const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + c * 16);
+    const uint4 q0 = qp[0], q1 = qp[1];
+    qv[r][0] = q0.x; qv[r][1] = q0.y; qv[r][2] = q0.z; qv[r][3] = q0.w;
+    qv[r][4] = q1.x; qv[r][5] = q1.y; qv[r][6] = q1.z; qv[r][7] = q1.w;
+  }
+  float m[R], s[R], o[R][16];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY;
+    s[r] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) o[r][d] = 0.0f;
+  }
+
+  const int64_t off0 = g * D + c * 16;
+  const bf16_t* kb = static_cast<const bf16_t*>(st.k[sg]) + b * st.stride_b[sg] + off0;
+  const bf16_t* vb = static_cast<const bf16_t*>(st.v[sg]) + b * st.stride_b[sg] + off0;
+  const int64_t sn = st.stride_n[sg];
+  constexpr int STEP = kWaves * TPW;
+  for (int64_t t0 = t_begin + wave * TPW + slot; t0 < t_end; t0 += STEP * UNROLL) {
+    uint4 kr[UNROLL][2], vr[UNROLL][2];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t t = t0 + static_cast<int64_t>(u) * STEP;
+      if (t < t_end) {
+        const uint4* kp = reinterpret_cast<const uint4*>(kb + t * sn);
+        const uint4* vp = reinterpret_cast<const uint4*>(vb + t * sn);
+        kr[u][0] = kp[0]; kr[u][1] = kp[1];
+        vr[u][0] = vp[0]; vr[u][1] = vp[1];
+      } else {
+        kr[u][0] = kr[u][1] = vr[u][0] = vr[u][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float l2[UNROLL][R];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const uint32_t kw[8] = {kr[u][0].x, kr[u][0].y, kr[u][0].z, kr[u][0].w,
+                              kr[u][1].x, kr[u][1].y, kr[u][1].z, kr[u][1].w};
+      const bool valid = t0 + static_cast<int64_t>(u) * STEP < t_end;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) acc = dot2(qv[r][p], kw[p], acc);
+        acc = group_sum<LPH>(acc);
+        l2[u][r] = valid ? acc * scale2 : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float bm = l2[0][r];
+#pragma unroll
+      for (int u = 1; u < UNROLL; ++u) bm = fmaxf(bm, l2[u][r]);
+      const float mn = fmaxf(m[r], bm);
+      if (mn == -INFINITY) continue;
+      const float alpha = exp2f(m[r] - mn);
+      float pu[UNROLL];
+      float ps = 0.0f;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) { pu[u] = exp2f(l2[u][r] - mn); ps += pu[u]; }
+      s[r] = s[r] * alpha + ps;
+      m[r] = mn;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) o[r][d] *= alpha;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const uint32_t vw[8] = {vr[u][0].x, vr[u][0].y, vr[u][0].z, vr[u][0].w,
+                                vr[u][1].x, vr[u][1].y, vr[u][1].z, vr[u][1].w};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          o[r][2 * p] += pu[u] * bf16_lo(vw[p]);
+          o[r][2 * p + 1] += pu[u] * bf16_hi(vw[p]);
+        }
+      }
+    }
+  }
+
+  // merge the TPW row slots of the wave
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float m2 = __shfl_xor(m[r], off, 64);
+      const float s2 = __shfl_xor(s[r], off, 64);
+      const float mn = fmaxf(m[r], m2);
+      const float a1 = (m[r] == -INFINITY) ? 0.0f : exp2f(m[r] - mn);
+      const float a2 = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - mn);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) o[r][d] = o[r][d] * a1 + __shfl_xor(o[r][d], off, 64) * a2;
+      s[r] = s[r] * a1 + s2 * a2;
+      m[r] = mn;
+    }
+  }
+  // merge the waves through LDS, one wave after the other
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w && slot == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = g * R + r;
+        if (w == 0) {
+#pragma unroll
+          for (int d = 0; d < 16; ++d) red_o[row][c * 16 + d] = o[r][d];
+          if (c == 0) { red_ms[row][0] = m[r]; red_ms[row][1] = s[r]; }
+        } else {
+          const float m1 = red_ms[row][0], s1 = red_ms[row][1];
+          const float mn = fmaxf(m1, m[r]);
+          const float a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - mn);
+          const float a2 = (m[r] == -INFINITY) ? 0.0f : exp2f(m[r] - mn);
+#pragma unroll
+          for (int d = 0; d < 16; ++d)
+            red_o[row][c * 16 + d] = red_o[row][c * 16 + d] * a1 + o[r][d] * a2;
+          // every lane of the head has read red_ms before lane c == 0 updates it
+          __builtin_amdgcn_wave_barrier();
+          if (c == 0) { red_ms[row][0] = mn; red_ms[row][1] = s1 * a1 + s[r] * a2; }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < ROWS * (D + 2); i += kThreads) {
+    const int row = i / (D + 2), e = i % (D + 2);
+    const int gg = row / R, r = row % R;
+    const int h = gg * G + r / T, j = r % T;
+    const int64_t orow = (b * Hq + h) * T + j;
+    if (e < D) ws_o[(orow * n_split + sp) * D + e] = red_o[row][e];
+    else ws_ms[(orow * n_split + sp) * 2 + (e - D)] = red_ms[row][e - D];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tile variant
+// ---------------------------------------------------------------------------
+constexpr int kTileKeys = 32;
+constexpr int kPad = 4;
+
+template <typename T, int D, int TPR>
+__global__ void __launch_bounds__(kThreads)
+decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_split, int H,
+                   int T_, int Hq, float scale2, int64_t passes, float* __restrict__ ws_ms,
+                   float* __restrict__ ws_o) {
+  constexpr int RB = kThreads / TPR;
+  constexpr int DPT = D / TPR;
+  constexpr int V = Elem<T>::kPerVec;
+  __shared__ __align__(16) float ks[kTileKeys][D + kPad];
+  __shared__ __align__(16) float vs[kTileKeys][D + kPad];
+
+  int64_t x = blockIdx.x;
+  const int64_t sp = x % n_split; x /= n_split;
+  const int64_t pass = x % passes; x /= passes;
+  const int g = static_cast<int>(x % H);
+  const int64_t b = x / H;
+  const int sg = find_seg(st, n_seg, sp);
+  const int64_t t_begin = (sp - st.split_begin[sg]) * kDecodeSplit;
+  const int64_t t_end = min(st.N[sg], t_begin + kDecodeSplit);
+  const int G = Hq / H;
+  const int R = G * T_;
+  const int r = static_cast<int>(pass) * RB + threadIdx.x / TPR;
+  const int p = threadIdx.x % TPR;
+  const bool row_ok = r < R;
+  const int h = g * G + (row_ok ? r : 0) / T_, j = (row_ok ? r : 0) % T_;
+
+  float qf[DPT], o[DPT];
+  if (row_ok) {
+    const T* qp = q + ((b * T_ + j) * Hq + h) * D + p * DPT;
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) qf[d] = Elem<T>::to_f32(qp[d]);
+  } else {
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) qf[d] = 0.0f;
+  }
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) o[d] = 0.0f;
+  float m = -INFINITY, s = 0.0f;
+
+  const T* kb = static_cast<const T*>(st.k[sg]) + b * st.stride_b[sg] + static_cast<int64_t>(g) * D;
+  const T* vb = static_cast<const T*>(st.v[sg]) + b * st.stride_b[sg] + static_cast<int64_t>(g) * D;
+  const int64_t sn = st.stride_n[sg];
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) {
+    const int nt = static_cast<int>(min<int64_t>(kTileKeys, t_end - t0));
+    __syncthreads();
+    for (int e = threadIdx.x; e < nt * (D / V); e += kThreads) {
+      const int tt = e / (D / V), cc = e % (D / V);
+      float tk[V], tv[V];
+      unpack16<T>(*reinterpret_cast<const uint4*>(kb + (t0 + tt) * sn + cc * V), tk);
+      unpack16<T>(*reinterpret_cast<const uint4*>(vb + (t0 + tt) * sn + cc * V), tv);
+#pragma unroll
+      for (int y = 0; y < V; ++y) { ks[tt][cc * V + y] = tk[y]; vs[tt][cc * V + y] = tv[y]; }
+    }
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) acc += qf[d] * ks[tt][p * DPT + d];
+      const float l2 = group_sum<TPR>(acc) * scale2;
+      if (l2 > m) {
+        const float alpha = exp2f(m - l2);
+        s = s * alpha + 1.0f;
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) o[d] = o[d] * alpha + vs[tt][p * DPT + d];
+        m = l2;
+      } else {
+        const float pe = exp2f(l2 - m);
+        s += pe;
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) o[d] += pe * vs[tt][p * DPT + d];
+      }
+    }
+  }
+  if (row_ok) {
+    const int64_t orow = (b * Hq + h) * T_ + j;
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) ws_o[(orow * n_split + sp) * D + p * DPT + d] = o[d];
+    if (p == 0) {
+      ws_ms[(orow * n_split + sp) * 2] = m;
+      ws_ms[(orow * n_split + sp) * 2 + 1] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of the splits: one block of D threads per row
+// ---------------------------------------------------------------------------
+__global__ void decode_merge_kernel(const float* __restrict__ ws_ms, const float* __restrict__ ws_o,
+                                    int64_t n_split, int D, int T_, int Hq,
+                                    float* __restrict__ out, float* __restrict__ lse) {
+  const int64_t row = blockIdx.x;  // (b*Hq + h)*T + j
+  const int d = threadIdx.x;
+  float m = -INFINITY;
+  for (int64_t i = 0; i < n_split; ++i) m = fmaxf(m, ws_ms[(row * n_split + i) * 2]);
+  float s = 0.0f, acc = 0.0f;
+  for (int64_t i = 0; i < n_split; ++i) {
+    const float mi = ws_ms[(row * n_split + i) * 2];
+    if (mi == -INFINITY) continue;
+    const float a = exp2f(mi - m);
+    s += ws_ms[(row * n_split + i) * 2 + 1] * a;
+    acc += ws_o[(row * n_split + i) * D + d] * a;
+  }
+  const int64_t j = row % T_;
+  const int64_t h = (row / T_) % Hq;
+  const int64_t b = row / (static_cast<int64_t>(T_) * Hq);
+  out[((b * T_ + j) * Hq + h) * D + d] = acc / s;
+  if (lse != nullptr && d == 0) lse[row] = (m + log2f(s)) * kLn2;
+}
+
+template <int D, int H, int R>
+void launch_stream(const void* q, const SegTable& st, int n_seg, int64_t n_split, int64_t B,
+                   int64_t T, int64_t Hq, float scale2, float* ms, float* o, hipStream_t s) {
+  hipLaunchKernelGGL((decode_stream_kernel<D, H, R, 4>), dim3(static_cast<unsigned>(B * n_split)),
+                     dim3(kThreads), 0, s, static_cast<const bf16_t*>(q), st, n_seg, n_split,
+                     static_cast<int>(T), static_cast<int>(Hq), scale2, ms, o);
+}
+
+template <typename T, int D, int TPR>
+void launch_tile(const void* q, const SegTable& st, int n_seg, int64_t n_split, int64_t B,
+                 int64_t H, int64_t T_, int64_t Hq, float scale2, float* ms, float* o,
+                 hipStream_t s) {
+  constexpr int RB = kThreads / TPR;
+  const int64_t R = (Hq / H) * T_;
+  const int64_t passes = (R + RB - 1) / RB;
+  hipLaunchKernelGGL((decode_tile_kernel<T, D, TPR>),
+                     dim3(static_cast<unsigned>(B * H * passes * n_split)), dim3(kThreads), 0, s,
+                     static_cast<const T*>(q), st, n_seg, n_split, static_cast<int>(H),
+                     static_cast<int>(T_), static_cast<int>(Hq), scale2, passes, ms, o);
+}
+
+template <typename T, int D>
+void dispatch_tile(const void* q, const SegTable& st, int n_seg, int64_t n_split, int64_t B,
+                   int64_t H, int64_t T_, int64_t Hq, float scale2, float* ms, float* o,
+                   hipStream_t s) {
+  const int64_t R = (Hq / H) * T_;
+  if (R >= 64) launch_tile<T, D, 4>(q, st, n_seg, n_split, B, H, T_, Hq, scale2, ms, o, s);
+  else if (R >= 32) launch_tile<T, D, 8>(q, st, n_seg, n_split, B, H, T_, Hq, scale2, ms, o, s);
+  else if (R >= 16) launch_tile<T, D, 16>(q, st, n_seg, n_split, B, H, T_, Hq, scale2, ms, o, s);
+  else launch_tile<T, D, 32>(q, st, n_seg, n_split, B, H, T_, Hq, scale2, ms, o, s);
+}
+
+}  // namespace
+
+int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
+                  int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
+                  float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s) {
+  SegTable st{};
+  for (int i = 0; i < n_seg; ++i) {
+    st.k[i] = segs[i].k;
+    st.v[i] = segs[i].v;
+    st.N[i] = segs[i].N;
+    st.stride_b[i] = segs[i].stride_b;
+    st.stride_n[i] = segs[i].stride_n;
+    st.split_begin[i] = segs[i].split_begin;
+  }
+  st.split_begin[n_seg] = n_split;
+  const float scale2 = scale * kLog2e;
+  const int64_t R = (Hq / H) * T;
+  bool done = false;
+  if (stream_path_ok(dtype, H, D, R)) {
+#define KVSEL_DS(H_, R_) \
+  if (!done && H == H_ && R == R_) { launch_stream<128, H_, R_>(q, st, n_seg, n_split, B, T, Hq, scale2, ws_ms, ws_o, s); done = true; }
+    KVSEL_DS(8, 1) KVSEL_DS(8, 2) KVSEL_DS(8, 4) KVSEL_DS(8, 8)
+    KVSEL_DS(4, 1) KVSEL_DS(4, 2) KVSEL_DS(4, 4) KVSEL_DS(4, 8)
+    KVSEL_DS(2, 1) KVSEL_DS(2, 2) KVSEL_DS(2, 4) KVSEL_DS(2, 8)
+    KVSEL_DS(1, 1) KVSEL_DS(1, 2) KVSEL_DS(1, 4) KVSEL_DS(1, 8)
+#undef KVSEL_DS
+  }
+  if (!done) {
+    if (dtype == KVSEL_BF16) {
+      if (D == 128) dispatch_tile<bf16_t, 128>(q, st, n_seg, n_split, B, H, T, Hq, scale2, ws_ms, ws_o, s);
+      else dispatch_tile<bf16_t, 64>(q, st, n_seg, n_split, B, H, T, Hq, scale2, ws_ms, ws_o, s);
+    } else {
+      if (D == 128) dispatch_tile<float, 128>(q, st, n_seg, n_split, B, H, T, Hq, scale2, ws_ms, ws_o, s);
+      else dispatch_tile<float, 64>(q, st, n_seg, n_split, B, H, T, Hq, scale2, ws_ms, ws_o, s);
+    }
+  }
+  int rc = check_launch("kvsel_decode_attn");
+  if (rc != KVSEL_OK) return rc;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(static_cast<unsigned>(B * Hq * T)),
+                     dim3(static_cast<unsigned>(D)), 0, s, ws_ms, ws_o, n_split,
+                     static_cast<int>(D), static_cast<int>(T), static_cast<int>(Hq), out, lse);
+  return check_launch("kvsel_decode_attn (merge)");
+}
+
+}  // namespace kvsel

@@ -1,0 +1,75 @@
+// Host-side launchers behind the C ABI.  Arguments are validated by api.cpp
+// before any of these is called; each returns KVSEL_OK or KVSEL_ERR_HIP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvsel.h"
+
+namespace kvsel {
+
+// Maximum segments of one decode call.
+constexpr int kMaxSegments = 4;
+// Rows of one score / aggregate tile partial when unit_len == 1.
+constexpr int kTokenTile = 256;
+// Keys per split of the final attention pass.
+constexpr int kDecodeSplit = 512;
+
+int launch_reposition(const void* k_in, void* k_out, const kvsel_cache& kc, int64_t unit_len,
+                      const int64_t* delta, int per_instance, double base, int style,
+                      hipStream_t s);
+
+// Segment partials of the query block: for every row (b, h, j) and segment of
+// `seg_len` cached rows, (m, s) with m the max logit in log2 units and
+// s = sum 2^(l2 - m).  Written to ms[((b*Hq + h)*T + j)*nseg + seg][2].
+// When `natural` is set, m is converted to natural-log units on output (the
+// layout of kvsel_score's `part`).
+int launch_score_partials(const void* q, int64_t T, int64_t Hq, const void* k,
+                          const kvsel_cache& kc, float scale, int64_t seg_len, float* ms,
+                          int natural, hipStream_t s);
+
+// Row statistics from segment partials (log2 or natural units as written).
+int launch_rowstats(const float* ms, int64_t rows, int64_t nseg, int natural, float* row_max,
+                    float* row_sum, hipStream_t s);
+
+// Chunk path: unit_score[g][u] from natural-unit partials and row stats.
+int launch_aggregate_chunks(const float* part, const float* row_max, const float* row_sum,
+                            int64_t B, int64_t Hq, int64_t T, int64_t M, int64_t group,
+                            float* unit_score, hipStream_t s);
+
+// Token path: per_token[b][t] = sum_h sum_j alpha (* ||v||), then per unit/group sums.
+int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
+                            const kvsel_cache& kc, float scale, const float* row_max,
+                            const float* row_sum, int vnorm, float* per_token, hipStream_t s);
+int launch_unit_sums(const float* per_token, int64_t B, int64_t N, int64_t unit_len,
+                     int64_t group, float* unit_score, hipStream_t s);
+
+int launch_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,
+                hipStream_t s);
+
+int launch_gather(const void* k_src, const void* v_src, const kvsel_cache& kc, int64_t unit_len,
+                  const int32_t* idx, int64_t k, int64_t idx_group, const int64_t* src_start,
+                  int64_t align_base, double base, int style, int nested, int64_t dst_rows,
+                  void* k_dst, void* v_dst, hipStream_t s);
+int launch_proxy_copy(const void* k_proxy, const void* v_proxy, const kvsel_cache& proxy,
+                      int64_t unit_len, const int32_t* idx, int64_t k, int64_t idx_group,
+                      int64_t dst_rows, void* k_dst, void* v_dst, hipStream_t s);
+
+struct DecodeSeg {
+  const void* k;
+  const void* v;
+  int64_t N;
+  int64_t stride_b;
+  int64_t stride_n;
+  int64_t split_begin;  // index of this segment's first split
+};
+int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
+                  int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
+                  float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s);
+
+// Which score / decode path a shape takes (exposed for tests and docs).
+bool stream_path_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);
+
+}  // namespace kvsel

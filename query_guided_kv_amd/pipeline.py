@@ -1,0 +1,75 @@
+"""The selection path of each workload as a sequence of library calls.
+
+``run(w, inp)`` executes re-position -> score -> aggregate -> top-k ->
+gather/refill -> decode attention for one input batch on the GPU and returns
+every intermediate (device tensors), so that each call can be checked on its
+own.  Only argument preparation happens here; all tensor work is done by the
+HIP kernels behind :mod:`query_guided_kv_amd.kvsel`.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import host
+from . import kvsel as K
+
+
+def reposition_deltas(w, device) -> tuple:
+    """(delta tensor, re-positioning unit length) of workload ``w``, or (None, 0).
+    Keys are stored at unit-local positions 0..len-1."""
+    if w.reposition == "none":
+        return None, 0
+    if w.reposition == "global":            # InfoFlow KV §4.2, GLOBAL geometry
+        L = int(w.plants["chunk_len"])
+        return host.delta_tensor(host.chunk_offsets([L] * (w.N // L)), device), L
+    if w.reposition == "contiguous":        # chunks placed back to back
+        L = w.unit_len
+        return host.delta_tensor(host.chunk_offsets([L] * (w.N // L)), device), L
+    if w.reposition == "reuse_window":      # CacheFocus §2.3.1
+        L = w.unit_len
+        return host.delta_tensor(host.reuse_window_starts(w.N // L, L, w.window), device), L
+    raise ValueError(w.reposition)
+
+
+def run(w, inp: dict, row_stats: bool = True) -> dict:
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    dev = k.device
+    out = {}
+    delta, L = reposition_deltas(w, dev)
+    k_score = k
+    if delta is not None:
+        k_score = K.reposition(k, delta, L, rope_base=w.rope_base, style=w.rope_style)
+        out["k_rep"] = k_score
+    if w.unit_len > 1 and w.signal == "mass":
+        rm, rs, part = K.score(q, k_score, w.unit_len, w.scale, row_stats=row_stats, partials=True)
+        out.update(row_max=rm, row_sum=rs, part=part)
+        out["unit_score"] = K.aggregate(w.unit_len, w.group, "mass", part=part, row_max=rm,
+                                        row_sum=rs, k=k_score, scale=w.scale)
+    else:
+        rm, rs, _ = K.score(q, k_score, w.unit_len, w.scale, row_stats=True, partials=False)
+        out.update(row_max=rm, row_sum=rs)
+        out["unit_score"] = K.aggregate(w.unit_len, w.group, w.signal, q=q, k=k_score, v=v,
+                                        row_max=rm, row_sum=rs, scale=w.scale)
+    out["idx"] = K.topk(out["unit_score"], w.k)
+    if not w.decode:
+        return out
+    if w.refill_interval:                   # ACRE: L1 entry j -> its L2 block
+        gk, gv = K.gather(inp["l2_k"], inp["l2_v"], out["idx"], w.refill_interval, w.group)
+        segs = [(k, v), (gk, gv)]
+    elif w.align:                           # CacheFocus "align": contiguous final slots
+        gk, gv = K.gather(k, v, out["idx"], w.unit_len, w.group, align_base=0,
+                          rope_base=w.rope_base, style=w.rope_style)
+        segs = [(gk, gv)]
+    else:
+        gk, gv = K.gather(k_score, v, out["idx"], w.unit_len, w.group)
+        segs = [(gk, gv)]
+    out["k_gather"], out["v_gather"] = gk, gv
+    out["o"], out["lse"] = K.decode_attn(q, segs, w.scale)
+    return out
+
+
+def run_nested_refill(w, inp: dict, idx: torch.Tensor):
+    """ACRE Eq. 18-19 nested layout: each kept L1 entry preceded by its L2 block."""
+    return K.gather(inp["l2_k"], inp["l2_v"], idx, w.refill_interval, w.group,
+                    proxy_k=inp["k"], proxy_v=inp["v"])

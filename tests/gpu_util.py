@@ -1,0 +1,51 @@
+"""Helpers shared by the GPU parity tests."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle_pipeline import to64
+
+
+def device() -> torch.device:
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return torch.device("cuda:0")
+
+
+def announce(name: str, **kw) -> None:
+    """Name the case before any GPU work, so a fault can be traced to it."""
+    args = " ".join(f"{k}={v}" for k, v in kw.items())
+    print(f"[gpu-case] {name} {args}", file=sys.stderr, flush=True)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 values at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - 7)
+
+
+def assert_cache_close(got: torch.Tensor, want: np.ndarray, dtype: str, ref_norm=None):
+    """Re-rotated keys: bf16 within one ulp, >= 99.9% bit-equal; fp32 within
+    fp32 rounding of the row scale."""
+    g = to64(got)
+    assert g.shape == want.shape, (g.shape, want.shape)
+    if dtype == "bf16":
+        diff = np.abs(g - want)
+        assert np.all(diff <= bf16_ulp(want) * 1.0001), float(np.max(diff / bf16_ulp(want)))
+        assert np.mean(g == want) >= 0.999, float(np.mean(g == want))
+    else:
+        scale = np.abs(want).max(axis=-1, keepdims=True) if ref_norm is None else ref_norm
+        assert np.all(np.abs(g - want) <= 4e-7 * scale + 1e-30)
+
+
+def assert_rel(got, want, rel: float, atol: float = 0.0, what: str = ""):
+    g = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    err = np.abs(g - w)
+    bound = rel * np.abs(w) + atol
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside rel {rel} (worst {float(np.max(err - bound)):.3g})"
