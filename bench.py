@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of query-guided KV selection on one MI355X.
+
+One step is one pass of the whole hot path -- re-position (where the workload
+has it) -> score -> aggregate -> top-k -> gather/refill -> decode attention --
+over one batch of synthetic input that is already resident in HBM.  The
+default workload is batched serving: 16 requests x 8 layers = 128 independent
+caches of 131,072 tokens (GQA 32/8, head dim 128, bf16; 68.7 GB of K and V);
+each step draws a fresh one-token query per (request, layer), keeps the top 64
+chunks of 256 tokens, gathers them and runs decode attention over the 16,384
+kept rows.
+
+Prints one JSON line:
+  value       cached KV token-rows scored and selected per second (B x N per
+              step / step time);
+  roofline    the dominant kernel's algorithmic bytes per launch over its
+              average launch time (HIP events on its launch stream), against
+              MI355X's 8 TB/s; traffic is the HBM bytes the counters measured
+              for that kernel (null when no measurement matches the source);
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+DEFAULT_WORKLOAD = "serving_16req_8l_128k"
+PROFILES = os.path.join(ROOT, "profiles")
+# kernel sources whose hash keys a stored counter measurement
+KERNEL_SOURCES = {
+    "score": ["query_guided_kv_amd/csrc/score.hip", "query_guided_kv_amd/csrc/common.h"],
+    "reposition": ["query_guided_kv_amd/csrc/reposition.hip", "query_guided_kv_amd/csrc/common.h"],
+    "aggregate": ["query_guided_kv_amd/csrc/aggregate.hip", "query_guided_kv_amd/csrc/common.h"],
+    "gather": ["query_guided_kv_amd/csrc/gather.hip", "query_guided_kv_amd/csrc/common.h"],
+    "decode": ["query_guided_kv_amd/csrc/decode.hip", "query_guided_kv_amd/csrc/common.h"],
+    "topk": ["query_guided_kv_amd/csrc/topk.hip", "query_guided_kv_amd/csrc/common.h"],
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(stage: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def elem_bytes(w) -> int:
+    return 2 if w.dtype == "bf16" else 4
+
+
+def stage_bytes(w) -> dict:
+    """Algorithmic HBM bytes of one step, per stage: every distinct region
+    counted once (the scored keys read once, the values once if their norm is
+    needed, the re-positioned keys written once where they are a product, the
+    kept rows read once and the compact cache written once).  Re-reads are
+    implementation cost and are not counted."""
+    row = w.H * w.D * elem_bytes(w)
+    rows = w.B * w.N
+    out = {s: 0 for s in ("reposition", "score", "aggregate", "topk", "gather", "decode")}
+    if w.reposition != "none" and not w.align:
+        out["reposition"] = 2 * rows * row          # K read, K' written
+    else:
+        out["score"] += rows * row                  # keys read by the scoring pass
+    if w.signal == "vnorm":
+        out["aggregate"] += rows * row              # values read for their norms
+    out["topk"] = (w.B // w.group) * w.M * 4
+    if w.decode:
+        per_unit = w.refill_interval if w.refill_interval else w.unit_len
+        kept = w.B * w.k * per_unit * row
+        out["gather"] = 2 * 2 * kept                # K and V, read and written
+        if w.refill_interval:
+            out["decode"] = rows * row              # L1 values read by the final pass
+    return out
+
+
+def dominant_stage(w, sb: dict) -> str:
+    # the scoring pass streams the whole cache; with a fused re-rotation it is
+    # the re-position kernel that carries the cache bytes
+    return max(sb, key=lambda s: sb[s])
+
+
+def kernel_of(stage: str, w) -> str:
+    return {"reposition": "reposition_kernel", "score": "score_stream_kernel" if (
+        w.dtype == "bf16" and w.D == 128 and (w.Hq // w.H) * w.T in (1, 2, 4, 8)) else "score_tile_kernel",
+        "aggregate": "agg_token_kernel", "topk": "topk_kernel", "gather": "gather_kernel",
+        "decode": "decode_stream_kernel"}[stage]
+
+
+def stored_traffic(stage: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none for this kernel source."""
+    path = os.path.join(PROFILES, f"{stage}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = (s.strip() for s in line.split("=", 1))
+                vals[k] = v
+    if vals.get("source_hash") != source_hash(stage):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_queries(w, inp, n: int, seed: int, device):
+    from query_guided_kv_amd import synth
+    if w.recipe == "serving":
+        return [synth.serving_queries(w, inp["topic"], seed, s, device) for s in range(n)]
+    return [inp["q"]] * n
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0, max_instances: int = 8) -> dict:
+    """Time the fp64 oracle on whole instances of the workload (inputs copied to
+    host memory first, outside the timed region), single-threaded."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import pipeline as OP
+
+    if w.group > 1:
+        # one selection spans `group` instances (e.g. the layers of InfoFlow):
+        # time one instance's share of it and scale by the instance count
+        wi = w.scaled(B=1, group=1)
+    else:
+        wi = w.scaled(B=1, requests=1)
+    done, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        while done < min(max_instances, w.B) and elapsed < budget_s:
+            b = done
+            sub = {key: OP.to64(inp[key][b:b + 1]) for key in ("q", "k", "v")}
+            for key in ("l2_k", "l2_v"):
+                if key in inp:
+                    sub[key] = OP.to64(inp[key][b:b + 1])
+            t0 = time.perf_counter()
+            OP.run(wi, sub)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            log(f"cpu oracle: instance {b} done, {elapsed:.1f} s so far")
+    rows = done * w.N
+    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.B} instances ({w.N} cached rows each, whole path, "
+                      f"fp64 numpy, 1 thread), {elapsed:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB streaming kernel (counter scale reference)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the selection path is data-parallel over independent caches; see the "
+              "sharding notes of the design)", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    from query_guided_kv_amd import kvsel as K
+    from query_guided_kv_amd import pipeline, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible MI355X GPU", file=sys.stderr)
+        return 2
+    K.load()                                   # fails loudly if the library is missing
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    log(f"workload {w.name}: B={w.B} N={w.N} Hq/H={w.Hq}/{w.H} D={w.D} T={w.T} {w.dtype}")
+
+    if args.copy_probe:
+        # a plain streaming kernel of known size: 1 GiB read, 1 GiB written
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy probe: 3 x (1 GiB read + 1 GiB written) done")
+
+    t0 = time.perf_counter()
+    inp = synth.generate(w, args.seed, dev)
+    torch.cuda.synchronize()
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    queries = make_queries(w, inp, args.warmup + args.steps, args.seed, dev)
+    path = pipeline.Path(w, inp)
+
+    for i in range(args.warmup):
+        path(queries[i])
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warm-up steps done")
+
+    sb = stage_bytes(w)
+    dom = dominant_stage(w, sb)
+    marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for s in path.stages} for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        path(queries[args.warmup + i], marks[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    log(f"{args.steps} timed steps: {total_ms:.2f} ms on the GPU clock, {wall * 1e3:.2f} ms wall")
+
+    stage_ms = {s: statistics.mean(m[s][0].elapsed_time(m[s][1]) for m in marks)
+                for s in path.stages}
+    dom_ms = stage_ms[dom]
+    achieved = sb[dom] / (dom_ms * 1e-3) / 1e9
+    traffic = stored_traffic(dom, w.name)
+    rows = w.B * w.N
+    path_bytes = sum(sb.values())
+
+    result = {
+        "metric": "cached KV tokens scored+selected per second",
+        "value": rows / (ms_step * 1e-3),
+        "unit": "token-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, planted relevant units; no datasets or weights)",
+        "config": {"workload": w.name, "instances": w.B, "cached_rows_per_instance": w.N,
+                   "q_heads": w.Hq, "kv_heads": w.H, "head_dim": w.D, "query_tokens": w.T,
+                   "unit_len": w.unit_len, "kept_units": w.k, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": kernel_of(dom, w), "stage": dom,
+                     "algorithmic_bytes_per_launch": sb[dom], "avg_launch_ms": dom_ms},
+        "path_hbm": {"algorithmic_bytes_per_step": path_bytes,
+                     "achieved_GBps": path_bytes / (ms_step * 1e-3) / 1e9,
+                     "frac": path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "stages_ms": stage_ms,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

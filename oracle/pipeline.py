@@ -10,11 +10,14 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-import oracle as O
+from . import kvsel_oracle as O
 
 
-def to64(t: torch.Tensor) -> np.ndarray:
-    """Exact float64 copy of a (bf16 / fp32) torch tensor."""
+def to64(t) -> np.ndarray:
+    """Exact float64 copy of a (bf16 / fp32) torch tensor; numpy arrays pass
+    through as float64."""
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64, copy=False)
     return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
 
 

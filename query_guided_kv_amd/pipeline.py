@@ -73,3 +73,86 @@ def run_nested_refill(w, inp: dict, idx: torch.Tensor):
     """ACRE Eq. 18-19 nested layout: each kept L1 entry preceded by its L2 block."""
     return K.gather(inp["l2_k"], inp["l2_v"], idx, w.refill_interval, w.group,
                     proxy_k=inp["k"], proxy_v=inp["v"])
+
+
+class Path:
+    """One workload's hot path with every argument prepared once.
+
+    ``path(q)`` runs re-position -> score -> aggregate -> top-k -> gather ->
+    decode attention for one query block with the fewest launches each step
+    needs (chunk workloads: one scoring kernel that emits only the per-unit
+    partials, row statistics derived inside the aggregate call).  ``marks``
+    maps a stage name to a (start, end) pair of torch.cuda.Event recorded on
+    the launch stream around that stage.
+    """
+
+    STAGES = ("reposition", "score", "aggregate", "topk", "gather", "decode")
+
+    def __init__(self, w, inp: dict):
+        self.w = w
+        self.k, self.v = inp["k"], inp["v"]
+        self.l2 = (inp.get("l2_k"), inp.get("l2_v"))
+        dev = self.k.device
+        self.delta, self.delta_len = reposition_deltas(w, dev)
+        self.k_rep = torch.empty_like(self.k) if self.delta is not None else None
+        self.chunk = w.unit_len > 1 and w.signal == "mass"
+        self.stages = tuple(s for s in self.STAGES
+                            if (s != "reposition" or self.delta is not None)
+                            and (s not in ("gather", "decode") or w.decode))
+
+    def __call__(self, q: torch.Tensor, marks: dict = None) -> dict:
+        w = self.w
+        ev = marks or {}
+
+        def mark(stage, i):
+            pair = ev.get(stage)
+            if pair is not None:
+                pair[i].record()
+
+        out = {}
+        k_score = self.k
+        if self.delta is not None:
+            mark("reposition", 0)
+            K.reposition(self.k, self.delta, self.delta_len, out=self.k_rep,
+                         rope_base=w.rope_base, style=w.rope_style)
+            mark("reposition", 1)
+            k_score = self.k_rep
+            out["k_rep"] = k_score
+        if self.chunk:
+            mark("score", 0)
+            _, _, part = K.score(q, k_score, w.unit_len, w.scale, row_stats=False, partials=True)
+            mark("score", 1)
+            mark("aggregate", 0)
+            out["unit_score"] = K.aggregate(w.unit_len, w.group, "mass", part=part,
+                                            cache_shape=tuple(k_score.shape), q=q)
+            mark("aggregate", 1)
+        else:
+            mark("score", 0)
+            rm, rs, _ = K.score(q, k_score, w.unit_len, w.scale, row_stats=True, partials=False)
+            mark("score", 1)
+            mark("aggregate", 0)
+            out["unit_score"] = K.aggregate(w.unit_len, w.group, w.signal, q=q, k=k_score,
+                                            v=self.v, row_max=rm, row_sum=rs, scale=w.scale)
+            mark("aggregate", 1)
+        mark("topk", 0)
+        out["idx"] = K.topk(out["unit_score"], w.k)
+        mark("topk", 1)
+        if not w.decode:
+            return out
+        mark("gather", 0)
+        if w.refill_interval:
+            gk, gv = K.gather(self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group)
+            segs = [(self.k, self.v), (gk, gv)]
+        elif w.align:
+            gk, gv = K.gather(self.k, self.v, out["idx"], w.unit_len, w.group, align_base=0,
+                              rope_base=w.rope_base, style=w.rope_style)
+            segs = [(gk, gv)]
+        else:
+            gk, gv = K.gather(k_score, self.v, out["idx"], w.unit_len, w.group)
+            segs = [(gk, gv)]
+        mark("gather", 1)
+        out["k_gather"], out["v_gather"] = gk, gv
+        mark("decode", 0)
+        out["o"], out["lse"] = K.decode_attn(q, segs, w.scale)
+        mark("decode", 1)
+        return out

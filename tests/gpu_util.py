@@ -7,7 +7,7 @@ import sys
 import numpy as np
 import torch
 
-from oracle_pipeline import to64
+from oracle.pipeline import to64
 
 
 def device() -> torch.device:

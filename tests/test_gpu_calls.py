@@ -14,7 +14,7 @@ import torch
 
 import oracle as O
 from gpu_util import announce, assert_cache_close, assert_rel, device
-from oracle_pipeline import to64
+from oracle.pipeline import to64
 from query_guided_kv_amd import kvsel as K
 
 pytestmark = pytest.mark.gpu

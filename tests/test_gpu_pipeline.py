@@ -1,0 +1,211 @@
+"""GPU parity of the whole selection path, workload by workload.
+
+Each workload runs through ``pipeline.Path`` -- the launch sequence the
+benchmark times -- and is compared with the oracle run step by step on the
+same seeded inputs:
+
+* kept index sets bit-exact.  The oracle's relative gap at the top-k cut is
+  asserted first (>= 1e-2, planted relevant units); a smaller margin would make
+  the case invalid, not passed;
+* unit scores within relative 2e-3;
+* re-positioned keys within one bf16 ulp, >= 99.9% bit-equal (fp32: rounding
+  of the row scale);
+* gathered caches bit-exact (aligned keys: as re-positioned keys);
+* decode outputs within 5e-3 absolute.
+
+Small sizes are checked in full.  The full-size workloads are checked on
+sampled instances (or layers) that the oracle computes one at a time, plus
+properties that hold at any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import announce, assert_cache_close, assert_rel, device
+from oracle import pipeline as OP
+from query_guided_kv_amd import kvsel as K
+from query_guided_kv_amd import pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-2
+
+SMALL = {
+    "tiny": lambda: synth.workload("tiny_mha4_d64_fp32_8x128"),
+    "docs_small": lambda: synth.workload(
+        "llama2_7b_32docs_x512", N=4096, Hq=8, H=8, T=8, k=4, window=1024,
+        plants={"primary": 2, "primary_scale": 1.5, "secondary": 2, "secondary_scale": 1.25}),
+    "bilayer_small": lambda: synth.workload(
+        "acre_bilayer_l1_16k_l2_128k", N=2048, k=256,
+        plants={"planted": 256, "gamma": 1.0, "l1_noise_std": 0.1}),
+    "infoflow_small": lambda: synth.workload(
+        "infoflow_32l_64x1024", B=4, N=8192, group=4, k=1228,
+        plants={"chunk_len": 1024, "chunks": 1, "chunk_scale": 1.5, "tokens": 204,
+                "token_scale": 1.3}),
+    "serving_small": lambda: synth.workload(
+        "serving_16req_8l_128k", B=4, requests=2, N=16384, k=8,
+        plants={"chunks": 8, "gamma": 1.0, "query_topic": 2.0}),
+}
+
+
+def check_against_oracle(w, got: dict, want: dict, planted=None):
+    for g, m in enumerate(want["margin"]):
+        assert m >= MARGIN, f"oracle margin {m:.3g} at the cut of group {g}: invalid case"
+    if planted is not None:
+        for g in range(len(planted)):
+            assert np.array_equal(want["idx"][g], planted[g]), "oracle misses the planted set"
+    idx = got["idx"].cpu().numpy().astype(np.int64)
+    assert np.array_equal(idx, want["idx"]), "kept index sets differ"
+    assert_rel(got["unit_score"], want["unit_score"], 2e-3, 0.0, "unit_score")
+    if "k_rep" in want:
+        assert_cache_close(got["k_rep"], want["k_rep"], w.dtype)
+    if not w.decode:
+        return
+    if w.align:
+        assert_cache_close(got["k_gather"], want["k_gather"], w.dtype)
+    else:
+        assert np.array_equal(OP.to64(got["k_gather"]), want["k_gather"]), "gathered keys"
+    assert np.array_equal(OP.to64(got["v_gather"]), want["v_gather"]), "gathered values"
+    assert_rel(got["o"], want["o"], 0.0, 5e-3, "decode output")
+    assert_rel(got["lse"], want["lse"], 0.0, 2e-3, "lse")
+
+
+@pytest.mark.parametrize("name,seed", [("tiny", s) for s in range(5)] +
+                         [("docs_small", 0), ("docs_small", 1), ("bilayer_small", 0),
+                          ("bilayer_small", 2), ("infoflow_small", 0), ("infoflow_small", 1),
+                          ("serving_small", 0)])
+def test_path_small(name, seed):
+    w = SMALL[name]()
+    announce("path_small", workload=name, seed=seed, B=w.B, N=w.N)
+    dev = device()
+    inp = synth.generate(w, seed, dev)
+    got = pipeline.Path(w, inp)(inp["q"])
+    torch.cuda.synchronize()
+    want = OP.run(w, inp)
+    check_against_oracle(w, got, want, inp["planted"])
+
+
+def test_path_serving_steps_fresh_queries():
+    """Several decode steps with fresh queries through one Path: each step's
+    selection and output match the oracle on that step's query."""
+    w = SMALL["serving_small"]()
+    announce("path_serving_steps", B=w.B, N=w.N)
+    dev = device()
+    inp = synth.generate(w, 3, dev)
+    path = pipeline.Path(w, inp)
+    for step in range(3):
+        q = synth.serving_queries(w, inp["topic"], 3, step, dev)
+        got = path(q)
+        torch.cuda.synchronize()
+        want = OP.run(w, dict(inp, q=q))
+        check_against_oracle(w, got, want, inp["planted"])
+
+
+def test_path_run_matches_lean_path():
+    """The per-stage run (row statistics and partials both requested) and the
+    lean benchmark path (partials only, statistics derived) agree exactly on
+    the selection and closely on the scores."""
+    w = SMALL["serving_small"]()
+    announce("path_run_vs_lean")
+    dev = device()
+    inp = synth.generate(w, 1, dev)
+    a = pipeline.run(w, inp)
+    b = pipeline.Path(w, inp)(inp["q"])
+    torch.cuda.synchronize()
+    assert torch.equal(a["idx"], b["idx"])
+    assert_rel(b["unit_score"], OP.to64(a["unit_score"]), 1e-5, 0.0, "scores")
+    assert torch.equal(a["o"], b["o"])
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+
+def test_full_docs_llama2_shaped():
+    w = synth.workload("llama2_7b_32docs_x512")
+    announce("full", workload=w.name, seed=0)
+    dev = device()
+    inp = synth.generate(w, 0, dev)
+    got = pipeline.Path(w, inp)(inp["q"])
+    torch.cuda.synchronize()
+    want = OP.run(w, inp)
+    check_against_oracle(w, got, want, inp["planted"])
+
+
+def test_full_bilayer_refill():
+    w = synth.workload("acre_bilayer_l1_16k_l2_128k")
+    announce("full", workload=w.name, seed=0)
+    dev = device()
+    inp = synth.generate(w, 0, dev)
+    got = pipeline.Path(w, inp)(inp["q"])
+    torch.cuda.synchronize()
+    want = OP.run(w, inp)
+    check_against_oracle(w, got, want, inp["planted"])
+    # the nested layout of the refilled cache (L2 block before its L1 entry)
+    nk, nv = pipeline.run_nested_refill(w, inp, got["idx"])
+    torch.cuda.synchronize()
+    from oracle import kvsel_oracle as O
+    for kk, src1, src2 in ((nk, "k", "l2_k"), (nv, "v", "l2_v")):
+        want_n = O.refill_nested(OP.to64(inp[src1][0]), OP.to64(inp[src2][0]),
+                                 want["idx"][0], w.refill_interval)
+        assert np.array_equal(OP.to64(kk[0]), want_n)
+
+
+def test_full_infoflow_sampled_layers():
+    """32 layers x 65,536 tokens.  The selection sums all layers; the oracle
+    computes two sampled layers in full, and the summed scores are checked
+    against the per-layer GPU scores (any-size property) and the plants."""
+    w = synth.workload("infoflow_32l_64x1024")
+    announce("full", workload=w.name, seed=0)
+    dev = device()
+    inp = synth.generate(w, 0, dev)
+    path = pipeline.Path(w, inp)
+    got = path(inp["q"])
+    torch.cuda.synchronize()
+    # the selection is the planted set, an exact top-k of the GPU's own scores
+    idx = got["idx"].cpu().numpy().astype(np.int64)[0]
+    assert np.array_equal(idx, inp["planted"][0])
+    s = got["unit_score"].cpu().numpy()[0].astype(np.float64)
+    kept = np.zeros(w.N, bool)
+    kept[idx] = True
+    assert s[kept].min() > s[~kept].max() * (1 + MARGIN)
+    # per-layer scores of the GPU (same kernels, group 1) sum to the selection scores
+    rm, rs, _ = K.score(inp["q"], got["k_rep"], 1, w.scale, row_stats=True, partials=False)
+    per_layer = K.aggregate(1, 1, "vnorm", q=inp["q"], k=got["k_rep"], v=inp["v"],
+                            row_max=rm, row_sum=rs, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_rel(per_layer.double().sum(0, keepdim=True).cpu().numpy(), s[None], 1e-4, 0.0,
+               "sum over layers")
+    # two sampled layers against the oracle, in full
+    wl = w.scaled(B=1, group=1)
+    for layer in (0, 23):
+        sub = {key: inp[key][layer:layer + 1] for key in ("q", "k", "v")}
+        want = OP.run(wl, sub)
+        assert_cache_close(got["k_rep"][layer:layer + 1], want["k_rep"], w.dtype)
+        assert_rel(rm[layer:layer + 1], want["row_max"], 2e-3, 2e-3, "row_max")
+        assert_rel(rs[layer:layer + 1], want["row_sum"], 2e-3, 0.0, "row_sum")
+        assert_rel(per_layer[layer:layer + 1], want["unit_score"], 2e-3, 0.0, "layer scores")
+
+
+def test_full_serving_sampled_instances():
+    """16 requests x 8 layers x 131,072 tokens (68.7 GB), the benchmark's
+    launch configuration; the oracle checks sampled instances in full."""
+    w = synth.workload("serving_16req_8l_128k")
+    announce("full", workload=w.name, seed=0)
+    dev = device()
+    inp = synth.generate(w, 0, dev)
+    path = pipeline.Path(w, inp)
+    q = synth.serving_queries(w, inp["topic"], 0, 5, dev)
+    got = path(q)
+    torch.cuda.synchronize()
+    idx = got["idx"].cpu().numpy().astype(np.int64)
+    for b in range(w.B):
+        assert np.array_equal(idx[b], inp["planted"][b]), f"instance {b}"
+    wi = w.scaled(B=1, requests=1)
+    for b in (0, 77, 127):
+        sub = {"q": q[b:b + 1], "k": inp["k"][b:b + 1], "v": inp["v"][b:b + 1]}
+        want = OP.run(wi, sub)
+        one = {key: got[key][b:b + 1] for key in ("idx", "unit_score", "k_gather", "v_gather",
+                                                   "o", "lse")}
+        check_against_oracle(wi, one, want, [inp["planted"][b]])
