@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "gather": ["query_guided_kv_amd/csrc/gather.hip", "query_guided_kv_amd/csrc/common.h"],
     "decode": ["query_guided_kv_amd/csrc/decode.hip", "query_guided_kv_amd/csrc/common.h"],
     "topk": ["query_guided_kv_amd/csrc/topk.hip", "query_guided_kv_amd/csrc/common.h"],
+    "gather_decode": ["query_guided_kv_amd/csrc/decode.hip", "query_guided_kv_amd/csrc/common.h"],
 }
 
 
@@ -75,6 +76,7 @@ def stage_bytes(w) -> dict:
     row = w.H * w.D * elem_bytes(w)
     rows = w.B * w.N
     out = {s: 0 for s in ("reposition", "score", "aggregate", "topk", "gather", "decode")}
+    fused = w.decode and not w.align
     if w.reposition != "none" and not w.align:
         out["reposition"] = 2 * rows * row          # K read, K' written
     else:
@@ -88,6 +90,10 @@ def stage_bytes(w) -> dict:
         out["gather"] = 2 * 2 * kept                # K and V, read and written
         if w.refill_interval:
             out["decode"] = rows * row              # L1 values read by the final pass
+    if fused:                                       # one call: refill + attention
+        out["gather_decode"] = out.pop("gather") + out.pop("decode")
+    elif not w.decode:
+        del out["gather"], out["decode"]
     return out
 
 
@@ -101,7 +107,7 @@ def kernel_of(stage: str, w) -> str:
     return {"reposition": "reposition_kernel", "score": "score_stream_kernel" if (
         w.dtype == "bf16" and w.D == 128 and (w.Hq // w.H) * w.T in (1, 2, 4, 8)) else "score_tile_kernel",
         "aggregate": "agg_token_kernel", "topk": "topk_kernel", "gather": "gather_kernel",
-        "decode": "decode_stream_kernel"}[stage]
+        "decode": "decode_stream_kernel", "gather_decode": "decode_stream_kernel (gathering)"}[stage]
 
 
 def stored_traffic(stage: str, workload: str):

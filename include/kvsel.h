@@ -236,6 +236,44 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale,
 size_t kvsel_decode_workspace(int64_t T, int64_t Hq, const kvsel_segment* segs,
                               int32_t n_seg);
 
+/*
+ * kvsel_gather_decode -- refill and the final attention pass in one call
+ * ([ACRE §2.4 Eq. 18-19] refill of the kept entries, then decoding over the
+ * refilled cache, [ACRE §2.4] and [ACRE §2.1 Eq. 4]).
+ *
+ * Same result as kvsel_gather in the compact layout (no re-positioning, no
+ * proxy cache) into (k_dst, v_dst), followed by kvsel_decode_attn over the
+ * segments extra[0 .. n_extra) plus that compact cache.  Where the shape
+ * allows it (bf16, head dim 128, H in {1,2,4,8} and (Hq / H) * T in
+ * {1,2,4,8}) one kernel reads every kept row once, writes it to the compact
+ * cache and attends to it from registers; otherwise the kernels of the two
+ * separate calls run back to back.
+ *
+ *   q, T, Hq, scale   as in kvsel_decode_attn.
+ *   k_src, v_src, kc, unit_len, idx, k, idx_group   as in kvsel_gather.  Every
+ *                     index must lie in [0, M); a slot outside that range is
+ *                     never read from or written to, and the output is then
+ *                     unspecified.
+ *   k_dst, v_dst      compact cache [B][k * unit_len][H][D], contiguous (may
+ *                     be NULL when k == 0).
+ *   extra, n_extra    HOST array of 0 .. 3 further segments attended as they
+ *                     are (e.g. the L1 cache of [ACRE]); same B, H, D, dtype.
+ *                     k == 0 needs at least one extra segment.
+ *   out, lse          as in kvsel_decode_attn.
+ *   ws                kvsel_gather_decode_workspace(...) bytes.
+ */
+int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale,
+                        const void* k_src, const void* v_src, kvsel_cache kc,
+                        int64_t unit_len, const int32_t* idx, int64_t k,
+                        int64_t idx_group, void* k_dst, void* v_dst,
+                        const kvsel_segment* extra, int32_t n_extra,
+                        float* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+size_t kvsel_gather_decode_workspace(int64_t T, int64_t Hq, kvsel_cache kc,
+                                     int64_t unit_len, int64_t k,
+                                     const kvsel_segment* extra,
+                                     int32_t n_extra);
+
 /* Text of a status code; message of the last failed call on this thread. */
 const char* kvsel_status_str(int status);
 const char* kvsel_last_error(void);

@@ -337,4 +337,94 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const k
                        ws_ms, ws_o, stream);
 }
 
+size_t kvsel_gather_decode_workspace(int64_t T, int64_t Hq, kvsel_cache kc, int64_t unit_len,
+                                     int64_t k, const kvsel_segment* extra, int32_t n_extra) {
+  if (T < 1 || Hq < 1 || unit_len < 1 || k < 0 || n_extra < 0 || n_extra >= kMaxSegments ||
+      (n_extra > 0 && extra == nullptr))
+    return 0;
+  kvsel_segment segs[kMaxSegments];
+  int n = 0;
+  for (int i = 0; i < n_extra; ++i) segs[n++] = extra[i];
+  if (k > 0) {
+    const int64_t rows = k * unit_len;
+    segs[n++] = kvsel_segment{nullptr, nullptr,
+                              kvsel_cache{kc.B, rows, kc.H, kc.D, rows * kc.H * kc.D,
+                                          kc.H * kc.D, kc.dtype}};
+  }
+  if (n == 0) return 0;
+  return kvsel_decode_workspace(T, Hq, segs, n);
+}
+
+int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const void* k_src,
+                        const void* v_src, kvsel_cache kc, int64_t unit_len, const int32_t* idx,
+                        int64_t k, int64_t idx_group, void* k_dst, void* v_dst,
+                        const kvsel_segment* extra, int32_t n_extra, float* out, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  KVSEL_TRY(check_ptr(q, "q"));
+  KVSEL_TRY(check_ptr(k_src, "k_src"));
+  KVSEL_TRY(check_ptr(v_src, "v_src"));
+  if (k > 0) {  // an empty compact cache may have no storage
+    KVSEL_TRY(check_ptr(k_dst, "k_dst"));
+    KVSEL_TRY(check_ptr(v_dst, "v_dst"));
+  }
+  if (out == nullptr) return fail(KVSEL_ERR_NULL, "out is NULL");
+  KVSEL_TRY(check_cache(kc, "kvsel_gather_decode"));
+  KVSEL_TRY(check_units(kc, unit_len, "kvsel_gather_decode"));
+  KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_gather_decode"));
+  const int64_t M = kc.N / unit_len;
+  if (k < 0 || k > M)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_gather_decode: k=%lld not in [0, M=%lld]", (long long)k,
+                (long long)M);
+  if (idx_group < 1 || kc.B % idx_group != 0)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_gather_decode: idx_group must divide B");
+  if (k > 0 && idx == nullptr) return fail(KVSEL_ERR_NULL, "idx is NULL");
+  if (n_extra < 0 || n_extra >= kMaxSegments)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_gather_decode: n_extra=%d not in [0, %d]", n_extra,
+                kMaxSegments - 1);
+  if (n_extra > 0 && extra == nullptr) return fail(KVSEL_ERR_NULL, "extra is NULL");
+  if (k == 0 && n_extra == 0)
+    return fail(KVSEL_ERR_SHAPE, "kvsel_gather_decode: nothing to attend (k = 0, no extra segment)");
+  const int64_t rows = k * unit_len;
+  kvsel_segment segs[kMaxSegments];
+  int n = 0;
+  for (int i = 0; i < n_extra; ++i) segs[n++] = extra[i];
+  if (k > 0)
+    segs[n++] = kvsel_segment{k_dst, v_dst,
+                              kvsel_cache{kc.B, rows, kc.H, kc.D, rows * kc.H * kc.D,
+                                          kc.H * kc.D, kc.dtype}};
+  for (int i = 0; i < n_extra; ++i) {
+    const kvsel_cache& c = extra[i].kc;
+    KVSEL_TRY(check_cache(c, "kvsel_gather_decode extra segment"));
+    KVSEL_TRY(check_ptr(extra[i].k, "extra segment k"));
+    KVSEL_TRY(check_ptr(extra[i].v, "extra segment v"));
+    if (c.B != kc.B || c.H != kc.H || c.D != kc.D || c.dtype != kc.dtype)
+      return fail(KVSEL_ERR_SHAPE, "kvsel_gather_decode: segments must share B, H, D and dtype");
+  }
+  const size_t need = kvsel_decode_workspace(T, Hq, segs, n);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(KVSEL_ERR_WORKSPACE, "kvsel_gather_decode: workspace %zu < %zu bytes", ws_bytes,
+                need);
+  if (k > 0 && stream_path_ok(kc.dtype, kc.H, kc.D, (Hq / kc.H) * T)) {
+    // one pass: each kept row is read once, copied to the compact cache and attended
+    DecodeSeg ds[kMaxSegments];
+    int64_t split = 0;
+    for (int i = 0; i < n; ++i) {
+      const bool g = i == n - 1;
+      ds[i] = DecodeSeg{g ? k_src : segs[i].k, g ? v_src : segs[i].v, segs[i].kc.N,
+                        g ? kc.stride_b : segs[i].kc.stride_b,
+                        g ? kc.stride_n : segs[i].kc.stride_n, split};
+      split += (segs[i].kc.N + kDecodeSplit - 1) / kDecodeSplit;
+    }
+    const DecodeGather gather{n - 1, idx, unit_len, k, idx_group, M, k_dst, v_dst};
+    float* ws_ms = static_cast<float*>(ws);
+    float* ws_o = ws_ms + kc.B * Hq * T * split * 2;
+    return launch_decode(q, T, Hq, scale, ds, n, kc.B, kc.H, kc.D, kc.dtype, split, out, lse,
+                         ws_ms, ws_o, stream, &gather);
+  }
+  if (k > 0)
+    KVSEL_TRY(launch_gather(k_src, v_src, kc, unit_len, idx, k, idx_group, nullptr, -1, 0.0,
+                            KVSEL_ROPE_HALF, 0, rows, k_dst, v_dst, stream));
+  return kvsel_decode_attn(q, T, Hq, scale, segs, n, out, lse, ws, ws_bytes, stream);
+}
+
 }  // extern "C"

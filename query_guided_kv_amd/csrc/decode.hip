@@ -35,6 +35,14 @@ struct SegTable {
   int64_t stride_b[kMaxSegments];
   int64_t stride_n[kMaxSegments];
   int64_t split_begin[kMaxSegments + 1];
+  // At most one segment is gathered on the fly: its row t is source row
+  // idx[t / unit_len] * unit_len + t % unit_len of (k, v) above, and the kernel
+  // also writes that row to row t of the compact destination (k_dst, v_dst).
+  int gather_seg;            // -1 when no segment is gathered
+  const int32_t* idx;        // [B / idx_group][n_kept], kept unit ids
+  int64_t unit_len, n_kept, idx_group, n_units;
+  void* k_dst;
+  void* v_dst;
 };
 
 // Which segment and key range a split covers.
@@ -72,6 +80,21 @@ decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64
   const int64_t t_end = min(st.N[sg], t_begin + kDecodeSplit);
   const int G = Hq / H;
 
+  // gathered segment: the kept unit ids that this split's rows come from
+  __shared__ int32_t s_unit[kDecodeSplit];
+  const bool gathered = sg == st.gather_seg;
+  int64_t u_first = 0;
+  if (gathered) {
+    u_first = t_begin / st.unit_len;
+    const int64_t nu = (t_end - 1) / st.unit_len - u_first + 1;
+    const int32_t* ib = st.idx + (b / st.idx_group) * st.n_kept + u_first;
+    for (int64_t i = threadIdx.x; i < nu; i += kThreads) {
+      const int32_t u = ib[i];
+      s_unit[i] = (u >= 0 && u < st.n_units) ? u : -1;
+    }
+  }
+  __syncthreads();
+
   uint32_t qv[R][8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -94,19 +117,42 @@ decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64
   const bf16_t* kb = static_cast<const bf16_t*>(st.k[sg]) + b * st.stride_b[sg] + off0;
   const bf16_t* vb = static_cast<const bf16_t*>(st.v[sg]) + b * st.stride_b[sg] + off0;
   const int64_t sn = st.stride_n[sg];
+  constexpr int64_t ROW = static_cast<int64_t>(H) * D;  // elements of a compact row
+  bf16_t* kd = gathered ? static_cast<bf16_t*>(st.k_dst) + b * st.N[sg] * ROW + off0 : nullptr;
+  bf16_t* vd = gathered ? static_cast<bf16_t*>(st.v_dst) + b * st.N[sg] * ROW + off0 : nullptr;
   constexpr int STEP = kWaves * TPW;
   for (int64_t t0 = t_begin + wave * TPW + slot; t0 < t_end; t0 += STEP * UNROLL) {
     uint4 kr[UNROLL][2], vr[UNROLL][2];
+    bool ok[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t t = t0 + static_cast<int64_t>(u) * STEP;
-      if (t < t_end) {
-        const uint4* kp = reinterpret_cast<const uint4*>(kb + t * sn);
-        const uint4* vp = reinterpret_cast<const uint4*>(vb + t * sn);
+      ok[u] = t < t_end;
+      int64_t src = t;
+      if (gathered && ok[u]) {
+        const int64_t r = t / st.unit_len;
+        const int32_t unit = s_unit[r - u_first];
+        ok[u] = unit >= 0;
+        src = static_cast<int64_t>(unit) * st.unit_len + (t - r * st.unit_len);
+      }
+      if (ok[u]) {
+        const uint4* kp = reinterpret_cast<const uint4*>(kb + src * sn);
+        const uint4* vp = reinterpret_cast<const uint4*>(vb + src * sn);
         kr[u][0] = kp[0]; kr[u][1] = kp[1];
         vr[u][0] = vp[0]; vr[u][1] = vp[1];
       } else {
         kr[u][0] = kr[u][1] = vr[u][0] = vr[u][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (gathered) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (!ok[u]) continue;
+        const int64_t t = t0 + static_cast<int64_t>(u) * STEP;
+        uint4* kq = reinterpret_cast<uint4*>(kd + t * ROW);
+        uint4* vq = reinterpret_cast<uint4*>(vd + t * ROW);
+        kq[0] = kr[u][0]; kq[1] = kr[u][1];
+        vq[0] = vr[u][0]; vq[1] = vr[u][1];
       }
     }
     float l2[UNROLL][R];
@@ -114,7 +160,7 @@ decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64
     for (int u = 0; u < UNROLL; ++u) {
       const uint32_t kw[8] = {kr[u][0].x, kr[u][0].y, kr[u][0].z, kr[u][0].w,
                               kr[u][1].x, kr[u][1].y, kr[u][1].z, kr[u][1].w};
-      const bool valid = t0 + static_cast<int64_t>(u) * STEP < t_end;
+      const bool valid = ok[u];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float acc = 0.0f;
@@ -356,8 +402,25 @@ void dispatch_tile(const void* q, const SegTable& st, int n_seg, int64_t n_split
 
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
                   int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
-                  float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s) {
+                  float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s,
+                  const DecodeGather* gather) {
   SegTable st{};
+  st.gather_seg = -1;
+  if (gather != nullptr) {
+    // only the streaming variant gathers on the fly
+    if (!stream_path_ok(dtype, H, D, (Hq / H) * T)) {
+      set_error("kvsel: fused gather is not available for this shape");
+      return KVSEL_ERR_UNSUPPORTED;
+    }
+    st.gather_seg = gather->seg;
+    st.idx = gather->idx;
+    st.unit_len = gather->unit_len;
+    st.n_kept = gather->n_kept;
+    st.idx_group = gather->idx_group;
+    st.n_units = gather->n_units;
+    st.k_dst = gather->k_dst;
+    st.v_dst = gather->v_dst;
+  }
   for (int i = 0; i < n_seg; ++i) {
     st.k[i] = segs[i].k;
     st.v[i] = segs[i].v;

@@ -65,9 +65,24 @@ struct DecodeSeg {
   int64_t stride_n;
   int64_t split_begin;  // index of this segment's first split
 };
+// Segment `seg` of a decode call read through a kept-unit index list: its row t
+// is source row idx[b / idx_group][t / unit_len] * unit_len + t % unit_len, and
+// the kernel also copies it to row t of the compact cache (k_dst, v_dst,
+// [B][n_kept * unit_len][H][D]).  Streaming variant only.
+struct DecodeGather {
+  int seg;
+  const int32_t* idx;
+  int64_t unit_len;
+  int64_t n_kept;
+  int64_t idx_group;
+  int64_t n_units;
+  void* k_dst;
+  void* v_dst;
+};
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
                   int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
-                  float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s);
+                  float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s,
+                  const DecodeGather* gather = nullptr);
 
 // Which score / decode path a shape takes (exposed for tests and docs).
 bool stream_path_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);

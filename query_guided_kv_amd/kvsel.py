@@ -59,6 +59,11 @@ _SIGNATURES = {
     "kvsel_decode_attn": (ctypes.c_int, [_P, _I64, _I64, _F, ctypes.POINTER(Segment), _I32, _P,
                                          _P, _P, _SZ, _P]),
     "kvsel_decode_workspace": (_SZ, [_I64, _I64, ctypes.POINTER(Segment), _I32]),
+    "kvsel_gather_decode": (ctypes.c_int, [_P, _I64, _I64, _F, _P, _P, Cache, _I64, _P, _I64, _I64,
+                                           _P, _P, ctypes.POINTER(Segment), _I32, _P, _P, _P, _SZ,
+                                           _P]),
+    "kvsel_gather_decode_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, ctypes.POINTER(Segment),
+                                            _I32]),
     "kvsel_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kvsel_last_error": (ctypes.c_char_p, []),
     "kvsel_version": (ctypes.c_int, []),
@@ -238,3 +243,30 @@ def decode_attn(q: torch.Tensor, segments: Sequence[Tuple[torch.Tensor, torch.Te
     _check(lib.kvsel_decode_attn(_ptr(q), T, Hq, scale, segs, len(segments), _ptr(out), _ptr(lse),
                                  _ptr(ws), need, _stream(q.device)))
     return out, lse
+
+
+def gather_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                  unit_len: int, idx_group: int = 1,
+                  extra: Sequence[Tuple[torch.Tensor, torch.Tensor]] = (),
+                  scale: Optional[float] = None, want_lse: bool = True):
+    """kvsel_gather_decode -> (k_dst, v_dst, o, lse): the compact cache of the
+    kept units and one attention pass over ``extra`` segments plus that cache."""
+    lib = load()
+    B, T, Hq, D = q.shape
+    _, N, H, _ = k.shape
+    kk = idx.shape[1]
+    scale = 1.0 / D ** 0.5 if scale is None else scale
+    kd = torch.empty((B, kk * unit_len, H, D), dtype=k.dtype, device=k.device)
+    vd = torch.empty_like(kd)
+    n_extra = len(extra)
+    segs = (Segment * max(1, n_extra))(*[Segment(a.data_ptr(), b.data_ptr(), cache_desc(a))
+                                         for a, b in extra])
+    kc = cache_desc(k)
+    need = lib.kvsel_gather_decode_workspace(T, Hq, kc, unit_len, kk, segs, n_extra)
+    ws = _workspace(need, q.device)
+    out = _empty((B, T, Hq, D), q.device)
+    lse = _empty((B, Hq, T), q.device) if want_lse else None
+    _check(lib.kvsel_gather_decode(_ptr(q), T, Hq, scale, _ptr(k), _ptr(v), kc, unit_len,
+                                   _ptr(idx), kk, idx_group, _ptr(kd), _ptr(vd), segs, n_extra,
+                                   _ptr(out), _ptr(lse), _ptr(ws), need, _stream(q.device)))
+    return kd, vd, out, lse

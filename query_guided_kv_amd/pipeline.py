@@ -86,7 +86,7 @@ class Path:
     the launch stream around that stage.
     """
 
-    STAGES = ("reposition", "score", "aggregate", "topk", "gather", "decode")
+    STAGES = ("reposition", "score", "aggregate", "topk", "gather", "decode", "gather_decode")
 
     def __init__(self, w, inp: dict):
         self.w = w
@@ -96,9 +96,12 @@ class Path:
         self.delta, self.delta_len = reposition_deltas(w, dev)
         self.k_rep = torch.empty_like(self.k) if self.delta is not None else None
         self.chunk = w.unit_len > 1 and w.signal == "mass"
+        # without re-positioning on the way, gather and decode are one call
+        split = w.decode and w.align
         self.stages = tuple(s for s in self.STAGES
                             if (s != "reposition" or self.delta is not None)
-                            and (s not in ("gather", "decode") or w.decode))
+                            and (s not in ("gather", "decode") or split)
+                            and (s != "gather_decode" or (w.decode and not split)))
 
     def __call__(self, q: torch.Tensor, marks: dict = None) -> dict:
         w = self.w
@@ -139,20 +142,27 @@ class Path:
         mark("topk", 1)
         if not w.decode:
             return out
-        mark("gather", 0)
-        if w.refill_interval:
-            gk, gv = K.gather(self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group)
-            segs = [(self.k, self.v), (gk, gv)]
-        elif w.align:
+        if w.align:
+            # re-positioned copy, then attention over it
+            mark("gather", 0)
             gk, gv = K.gather(self.k, self.v, out["idx"], w.unit_len, w.group, align_base=0,
                               rope_base=w.rope_base, style=w.rope_style)
-            segs = [(gk, gv)]
+            mark("gather", 1)
+            mark("decode", 0)
+            out["o"], out["lse"] = K.decode_attn(q, [(gk, gv)], w.scale)
+            mark("decode", 1)
         else:
-            gk, gv = K.gather(k_score, self.v, out["idx"], w.unit_len, w.group)
-            segs = [(gk, gv)]
-        mark("gather", 1)
+            # refill and attention in one call (one pass over the kept rows
+            # where the shape allows it)
+            mark("gather_decode", 0)
+            if w.refill_interval:       # ACRE: L1 entry j -> its L2 block, L1 kept as a segment
+                gk, gv, o, lse = K.gather_decode(q, self.l2[0], self.l2[1], out["idx"],
+                                                 w.refill_interval, w.group,
+                                                 extra=[(self.k, self.v)], scale=w.scale)
+            else:
+                gk, gv, o, lse = K.gather_decode(q, k_score, self.v, out["idx"], w.unit_len,
+                                                 w.group, scale=w.scale)
+            mark("gather_decode", 1)
+            out["o"], out["lse"] = o, lse
         out["k_gather"], out["v_gather"] = gk, gv
-        mark("decode", 0)
-        out["o"], out["lse"] = K.decode_attn(q, segs, w.scale)
-        mark("decode", 1)
         return out

@@ -165,3 +165,30 @@ def test_decode_validation(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         K.load(str(tmp_path / "missing.so"))
+
+
+def test_gather_decode_validation(lib):
+    p = ctypes.c_void_p(FAKE)
+    kc = cache(B=2, N=1024, H=8, D=128)
+    ext = (K.Segment * 1)(K.Segment(FAKE, FAKE, cache(B=2, N=100, H=8)))
+    bad = (K.Segment * 1)(K.Segment(FAKE, FAKE, cache(B=2, N=100, H=4)))
+    call = lambda k=4, unit=256, T=1, Hq=32, group=1, segs=None, n=0, idx=FAKE, ws=1 << 40, out=FAKE, vsrc=FAKE: \
+        lib.kvsel_gather_decode(p, T, Hq, 0.1, p, vsrc and ctypes.c_void_p(vsrc), kc, unit,
+                                idx and ctypes.c_void_p(idx), k, group, p, p, segs, n,
+                                out and ctypes.c_void_p(out), None, p, ws, None)
+    assert call(k=5) == SHAPE                      # M = 4
+    assert call(unit=300) == SHAPE
+    assert call(Hq=30) == SHAPE
+    assert call(group=3) == SHAPE
+    assert call(idx=0) == NULL
+    assert call(vsrc=0) == NULL
+    assert call(out=0) == NULL
+    assert call(k=0) == SHAPE                      # nothing to attend
+    assert call(n=4, segs=ext) == SHAPE            # at most 3 extra segments
+    assert call(n=1, segs=None) == NULL
+    assert call(n=1, segs=bad) == SHAPE            # extra segment with other H
+    need = lib.kvsel_gather_decode_workspace(1, 32, kc, 256, 4, ext, 1)
+    splits = (100 + 511) // 512 + (4 * 256 + 511) // 512
+    assert need == 2 * 32 * 1 * splits * (2 + 128) * 4
+    assert call(n=1, segs=ext, ws=need - 1) == WS
+    assert lib.kvsel_gather_decode_workspace(1, 32, kc, 256, 0, None, 0) == 0

@@ -274,3 +274,47 @@ def test_decode(case):
     wo, wl = O.decode_attention(to64(q), [(to64(a), to64(b)) for a, b in segs], 1.0 / np.sqrt(D))
     assert_rel(o, wo, 0.0, 5e-3, "o")
     assert_rel(lse, wl, 0.0, 2e-3, "lse")
+
+
+# --------------------------------------------------------------------------
+# kvsel_gather_decode (refill + final attention pass in one call)
+# --------------------------------------------------------------------------
+GD_CASES = [
+    # name, dtype, B, H, Hq, T, D, unit, M, kept, idx_group, extra N list
+    ("fused_R4_chunks", "bf16", 3, 8, 32, 1, 128, 256, 12, 5, 1, ()),
+    ("fused_R2_tokens_group_extra", "bf16", 4, 4, 8, 1, 128, 1, 1000, 300, 2, (77,)),
+    ("fused_R8_ragged_two_extra", "bf16", 2, 2, 16, 1, 128, 3, 400, 171, 1, (513, 40)),
+    ("tile_R448_refill_extra", "bf16", 1, 4, 28, 16, 128, 8, 300, 37, 1, (300,)),
+    ("tile_fp32_d64", "fp32", 2, 4, 4, 16, 64, 64, 10, 3, 1, ()),
+    ("fused_k0_extra_only", "bf16", 2, 8, 32, 1, 128, 256, 4, 0, 1, (600,)),
+]
+
+
+@pytest.mark.parametrize("case", GD_CASES, ids=[c[0] for c in GD_CASES])
+def test_gather_decode(case):
+    name, dtype, B, H, Hq, T, D, unit, M, kept, group, extra_n = case
+    announce("gather_decode", case=name)
+    dev = device()
+    N = M * unit
+    q = rnd((B, T, Hq, D), dtype, 50)
+    k = rnd((B, N, H, D), dtype, 51, 1.5)
+    v = rnd((B, N, H, D), dtype, 52)
+    extra = [(rnd((B, n, H, D), dtype, 60 + i, 1.5), rnd((B, n, H, D), dtype, 70 + i))
+             for i, n in enumerate(extra_n)]
+    rng = np.random.default_rng(kept + M)
+    idx = np.stack([np.sort(rng.choice(M, kept, replace=False)) for _ in range(B // group)])
+    idx_t = torch.from_numpy(idx).int().to(dev).reshape(B // group, kept)
+    kd, vd, o, lse = K.gather_decode(q.to(dev), k.to(dev), v.to(dev), idx_t, unit, group,
+                                     extra=[(a.to(dev), b.to(dev)) for a, b in extra])
+    torch.cuda.synchronize()
+    wk, wv = O.gather(to64(k), to64(v), idx, unit, group)
+    assert np.array_equal(to64(kd), wk) and np.array_equal(to64(vd), wv)
+    segs = [(to64(a), to64(b)) for a, b in extra] + ([(wk, wv)] if kept else [])
+    wo, wl = O.decode_attention(to64(q), segs, 1.0 / np.sqrt(D))
+    assert_rel(o, wo, 0.0, 5e-3, "o")
+    assert_rel(lse, wl, 0.0, 2e-3, "lse")
+    # the separate calls give the same output
+    segs_d = [(a.to(dev), b.to(dev)) for a, b in extra] + ([(kd, vd)] if kept else [])
+    o2, lse2 = K.decode_attn(q.to(dev), segs_d)
+    torch.cuda.synchronize()
+    assert_rel(o2, to64(o), 0.0, 1e-5, "o vs separate calls")
