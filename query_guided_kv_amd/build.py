@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvsel.so")
 
-SOURCES = ["api.cpp", "reposition.hip", "score.hip", "aggregate.hip", "topk.hip",
-           "gather.hip", "decode.hip"]
+SOURCES = ["api.cpp", "reposition.hip", "score.hip", "score_mfma.hip", "aggregate.hip",
+           "aggregate_mfma.hip", "topk.hip", "gather.hip", "decode.hip"]
 
 ARCH = os.environ.get("KVSEL_ARCH", "gfx950")
 

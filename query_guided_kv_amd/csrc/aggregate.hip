@@ -172,6 +172,10 @@ int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k,
                             const kvsel_cache& kc, float scale, const float* row_max,
                             const float* row_sum, int vnorm, float* per_token, hipStream_t s) {
   const float scale2 = scale * kLog2e;
+  if (aggregate_mfma_ok(kc.dtype, (Hq / kc.H) * T)) {
+    launch_aggregate_mfma(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
+    return check_launch("kvsel_aggregate (token path)");
+  }
   if (kc.dtype == KVSEL_BF16) {
     if (kc.D == 128) launch_tok<bf16_t, 128, 4>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
     else launch_tok<bf16_t, 64, 4>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);

@@ -1,0 +1,211 @@
+// Token-path aggregation on the matrix cores (bf16 caches with >= 16 query
+// rows per kv head):
+//   per_token[b][t] = sum_h sum_j alpha[b,h,j,t]            (mass)
+//   per_token[b][t] = sum_h sum_j alpha[b,h,j,t] * ||v[b,t,kv(h)]||_2   (vnorm)
+// with alpha = exp(l - row_max) / row_sum (ACRE §2.4 Eq. 15 as a sum;
+// InfoFlow §4.2, s_j = sum_i A_ij with A_ij read as attention weight times
+// value norm).
+//
+// A workgroup owns a range of cached rows of one instance and loops over the kv
+// heads (and row passes for very tall query blocks).  For every 64-key tile of
+// K staged in LDS it recomputes the logits with v_mfma_f32_16x16x32_bf16 (the
+// same operand layout as score_mfma.hip), forms alpha with one exp per logit,
+// sums it over the lane's rows, over the four lane quads (shuffles) and over
+// the waves that split the rows (LDS), then scales by the value norm of the
+// head.  The per-token totals stay in LDS across heads and are written once:
+// a fixed summation order, no atomics.
+#include "common.h"
+#include "internal.h"
+#include "mfma.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTileKeys = kMfmaTileKeys;
+constexpr int kPad = kMfmaPad;
+constexpr int kMaxRange = 1024;   // cached rows per workgroup
+
+template <int D, int RBW, int NWR, bool VNORM>
+__global__ void __launch_bounds__(kThreads)
+agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                const bf16_t* __restrict__ v, int64_t N, int H, int64_t stride_b,
+                int64_t stride_n, int T, int Hq, float scale2, const float* __restrict__ row_max,
+                const float* __restrict__ row_sum, int64_t range, int64_t ranges, int passes,
+                float* __restrict__ per_token) {
+  constexpr int KS = D / 32;
+  constexpr int KROW = D + kPad;
+  constexpr int NWK = kWaves / NWR;
+  constexpr int KBW = (kTileKeys / 16) / NWK;
+  constexpr int VPT = kTileKeys * D / 8 / kThreads;
+  constexpr int ROWS_PASS = NWR * RBW * 16;
+  __shared__ __align__(16) bf16_t kt[kTileKeys * KROW];
+  __shared__ float vn[kTileKeys];
+  __shared__ float part[kWaves][kTileKeys];
+  __shared__ float tot[kMaxRange];
+
+  const int64_t b = blockIdx.x / ranges;
+  const int64_t t_begin = (blockIdx.x % ranges) * range;
+  const int64_t t_end = min(N, t_begin + range);
+  const int G = Hq / H;
+  const int R = G * T;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wr = wave % NWR, wk = wave / NWR;
+  const int col = lane & 15, quad = lane >> 4;
+
+  for (int i = threadIdx.x; i < range; i += kThreads) tot[i] = 0.0f;
+
+  for (int g = 0; g < H; ++g) {
+    const bf16_t* kb = k + b * stride_b + static_cast<int64_t>(g) * D;
+    const bf16_t* vb = v + b * stride_b + static_cast<int64_t>(g) * D;
+    for (int pass = 0; pass < passes; ++pass) {
+      // query fragments and row statistics of this wave's row blocks; rows
+      // past R get zero weight
+      uint4 qa[RBW][KS];
+      float m2[RBW][4], iz[RBW][4];
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        const int rb = pass * NWR * RBW + wr + i * NWR;
+        const int r = rb * 16 + col;
+        if (r < R) {
+          const int h = g * G + r / T, j = r % T;
+          const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + quad * 8);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) qa[i][s] = qp[s * 4];
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) qa[i][s] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int rr = rb * 16 + quad * 4 + vv;
+          if (rr < R) {
+            const int h = g * G + rr / T, j = rr % T;
+            const int64_t row = (b * Hq + h) * T + j;
+            m2[i][vv] = row_max[row] * kLog2e;
+            iz[i][vv] = 1.0f / row_sum[row];
+          } else {
+            m2[i][vv] = 0.0f;
+            iz[i][vv] = 0.0f;
+          }
+        }
+      }
+
+      for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) {
+        __syncthreads();  // previous tile's kt / vn / part fully used
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+          const int e = threadIdx.x + i * kThreads;
+          const int key = e / (D / 8), ch = e % (D / 8);
+          const uint4 w4 = (t0 + key < t_end)
+                               ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * stride_n + ch * 8)
+                               : make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = w4;
+        }
+        if constexpr (VNORM) {
+          // 4 consecutive lanes per key, D/4 dims each
+          const int key = threadIdx.x >> 2, qd = threadIdx.x & 3;
+          float ss = 0.0f;
+          if (t0 + key < t_end) {
+            float f[D / 4];
+            load_f32<bf16_t, D / 4>(vb + (t0 + key) * stride_n + qd * (D / 4), f);
+#pragma unroll
+            for (int d = 0; d < D / 4; ++d) ss = fmaf(f[d], f[d], ss);
+          }
+          ss = group_sum<4>(ss);
+          if (qd == 0) vn[key] = sqrtf(ss);
+        }
+        __syncthreads();
+
+        float c[KBW];
+#pragma unroll
+        for (int jb = 0; jb < KBW; ++jb) {
+          const int key = (wk + jb * NWK) * 16 + col;
+          uint4 bk[KS];
+#pragma unroll
+          for (int st = 0; st < KS; ++st)
+            bk[st] = *reinterpret_cast<const uint4*>(&kt[key * KROW + st * 32 + quad * 8]);
+          float sum = 0.0f;
+#pragma unroll
+          for (int i = 0; i < RBW; ++i) {
+            f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < KS; ++st) a = mfma16x16x32(qa[i][st], bk[st], a);
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+              sum = fmaf(__builtin_amdgcn_exp2f(fmaf(a[vv], scale2, -m2[i][vv])), iz[i][vv], sum);
+          }
+          sum += __shfl_xor(sum, 16, 64);
+          sum += __shfl_xor(sum, 32, 64);
+          c[jb] = sum;
+        }
+        if (quad == 0) {
+#pragma unroll
+          for (int jb = 0; jb < KBW; ++jb) part[wave][(wk + jb * NWK) * 16 + col] = c[jb];
+        }
+        __syncthreads();
+        if (threadIdx.x < kTileKeys) {
+          const int key = threadIdx.x;
+          const int owner = (key / 16) % NWK;  // the waves (wr, owner) computed this key
+          float s = 0.0f;
+#pragma unroll
+          for (int w = 0; w < NWR; ++w) s += part[w + owner * NWR][key];
+          if (VNORM) s *= vn[key];
+          if (t0 + key < t_end) tot[t0 - t_begin + key] += s;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < t_end - t_begin; i += kThreads) per_token[b * N + t_begin + i] = tot[i];
+}
+
+template <int D, int RBW, int NWR>
+void launch(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
+            const kvsel_cache& kc, float scale2, const float* rm, const float* rs, int vnorm,
+            int passes, float* per_token, hipStream_t s) {
+  // enough workgroups to fill the chip: the range shrinks for small caches
+  int64_t range = (kc.B * kc.N / 1024) / kTileKeys * kTileKeys;
+  range = range < kTileKeys ? kTileKeys : (range > kMaxRange ? kMaxRange : range);
+  const int64_t ranges = (kc.N + range - 1) / range;
+  const dim3 grid(static_cast<unsigned>(kc.B * ranges));
+#define KVSEL_AM(VN)                                                                         \
+  hipLaunchKernelGGL((agg_mfma_kernel<D, RBW, NWR, VN>), grid, dim3(kThreads), 0, s,          \
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),            \
+                     static_cast<const bf16_t*>(v), kc.N, static_cast<int>(kc.H), kc.stride_b, \
+                     kc.stride_n, static_cast<int>(T), static_cast<int>(Hq), scale2, rm, rs,   \
+                     range, ranges, passes, per_token)
+  if (vnorm) KVSEL_AM(true); else KVSEL_AM(false);
+#undef KVSEL_AM
+}
+
+template <int D>
+void dispatch(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
+              const kvsel_cache& kc, float scale2, const float* rm, const float* rs, int vnorm,
+              float* per_token, hipStream_t s) {
+  const MfmaRowPlan p = mfma_row_plan((Hq / kc.H) * T);
+#define KVSEL_AD(RBW, NWR) \
+  if (p.rbw == RBW && p.nwr == NWR) \
+    return launch<D, RBW, NWR>(q, T, Hq, k, v, kc, scale2, rm, rs, vnorm, p.passes, per_token, s);
+  KVSEL_AD(1, 1) KVSEL_AD(1, 2) KVSEL_AD(1, 4) KVSEL_AD(2, 4) KVSEL_AD(4, 4)
+#undef KVSEL_AD
+}
+
+}  // namespace
+
+bool aggregate_mfma_ok(int dtype, int64_t rows_per_kv) {
+  return dtype == KVSEL_BF16 && rows_per_kv >= 16;
+}
+
+void launch_aggregate_mfma(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
+                           const kvsel_cache& kc, float scale2, const float* row_max,
+                           const float* row_sum, int vnorm, float* per_token, hipStream_t s) {
+  if (kc.D == 128)
+    dispatch<128>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
+  else
+    dispatch<64>(q, T, Hq, k, v, kc, scale2, row_max, row_sum, vnorm, per_token, s);
+}
+
+}  // namespace kvsel

@@ -30,6 +30,14 @@ int launch_score_partials(const void* q, int64_t T, int64_t Hq, const void* k,
                           const kvsel_cache& kc, float scale, int64_t seg_len, float* ms,
                           int natural, hipStream_t s);
 
+// Matrix-core variant of launch_score_partials (bf16, >= 16 query rows per kv
+// head, segments a multiple of 64 cached rows); score_mfma_ok tells whether it
+// applies.
+bool score_mfma_ok(int dtype, int64_t rows_per_kv, int64_t seg_len);
+void launch_score_mfma(const void* q, int64_t T, int64_t Hq, const void* k,
+                       const kvsel_cache& kc, float scale2, int64_t seg_len, int64_t nseg,
+                       float* ms, int natural, hipStream_t s);
+
 // Row statistics from segment partials (log2 or natural units as written).
 int launch_rowstats(const float* ms, int64_t rows, int64_t nseg, int natural, float* row_max,
                     float* row_sum, hipStream_t s);
@@ -43,6 +51,12 @@ int launch_aggregate_chunks(const float* part, const float* row_max, const float
 int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
                             const kvsel_cache& kc, float scale, const float* row_max,
                             const float* row_sum, int vnorm, float* per_token, hipStream_t s);
+// Matrix-core variant of launch_aggregate_tokens (bf16, >= 16 query rows per
+// kv head); aggregate_mfma_ok tells whether it applies.
+bool aggregate_mfma_ok(int dtype, int64_t rows_per_kv);
+void launch_aggregate_mfma(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
+                           const kvsel_cache& kc, float scale2, const float* row_max,
+                           const float* row_sum, int vnorm, float* per_token, hipStream_t s);
 int launch_unit_sums(const float* per_token, int64_t B, int64_t N, int64_t unit_len,
                      int64_t group, float* unit_score, hipStream_t s);
 

@@ -34,9 +34,59 @@ constexpr int kWaves = kThreads / 64;
 // ---------------------------------------------------------------------------
 // stream path
 // ---------------------------------------------------------------------------
-// Lane layout: LPH = D/16 lanes per kv head (16 dims = 32 bytes each), LPT =
-// H*LPH lanes per cached row, TPW = 64/LPT rows per wave step.
-template <int D, int H, int R, int UNROLL>
+// Lane layout: LPH = D/16 = 8 lanes per kv head (16 dims = 32 bytes each),
+// LPT = H*LPH lanes per cached row, TPW = 64/LPT rows per wave step.  A wave
+// step covers U rows per slot (U*TPW*waves rows per workgroup step).
+//
+// After the packed-bf16 dot products each lane holds partial sums of V = U*R
+// (key, query row) pairs.  A reduce-scatter over the 8 lanes of the head (see
+// reduce_scatter8) leaves every lane with V/8 complete logits of ONE query row,
+// so the softmax update runs once per logit instead of once per lane.
+//
+// Lane c of a head group (bits b0 b1 b2) owns index block j = 4*b2 + 2*b0 + b1,
+// i.e. the V/8 pairs idx = r*U + u in [j*V/8, (j+1)*V/8): query row
+// r = j*V/(8U), keys u = (j*V/8) % U + 0 .. V/8-1.
+
+// Reduce-scatter of V values over the 8 lanes of a head group: three butterfly
+// levels (partners: lane i <-> 7-i, then xor 1, then xor 2).  At each level a
+// lane keeps the half of its current values picked by one lane-id bit (b2, b0,
+// b1 in turn), adds the partner's copy of that half and drops the other half.
+template <int V>
+__device__ __forceinline__ void reduce_scatter8(float (&x)[V], int c) {
+  static_assert(V % 8 == 0, "8 lanes need at least 8 values");
+  const bool h2 = (c & 4) != 0, h0 = (c & 1) != 0, h1 = (c & 2) != 0;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    const float keep = h2 ? x[i + V / 2] : x[i];
+    const float send = h2 ? x[i] : x[i + V / 2];
+    x[i] = keep + dpp_half_mirror(send);
+  }
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) {
+    const float keep = h0 ? x[i + V / 4] : x[i];
+    const float send = h0 ? x[i] : x[i + V / 4];
+    x[i] = keep + dpp_xor1(send);
+  }
+#pragma unroll
+  for (int i = 0; i < V / 8; ++i) {
+    const float keep = h1 ? x[i + V / 8] : x[i];
+    const float send = h1 ? x[i] : x[i + V / 8];
+    x[i] = keep + dpp_xor2(send);
+  }
+}
+
+// Merge of softmax partials (log2 domain) with the lane holding the same query
+// row: PARTNER 0 = xor 2, 1 = xor 1, 2 = half mirror.
+template <int PARTNER>
+__device__ __forceinline__ void merge_lane(float& m, float& s) {
+  float m2, s2;
+  if constexpr (PARTNER == 0) { m2 = dpp_xor2(m); s2 = dpp_xor2(s); }
+  else if constexpr (PARTNER == 1) { m2 = dpp_xor1(m); s2 = dpp_xor1(s); }
+  else { m2 = dpp_half_mirror(m); s2 = dpp_half_mirror(s); }
+  merge_ms(m, s, m2, s2);
+}
+
+template <int D, int H, int R, int U>
 __global__ void __launch_bounds__(kThreads)
 score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int64_t N,
                     int64_t stride_b, int64_t stride_n, int T, int Hq, float scale2,
@@ -44,7 +94,11 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   constexpr int LPH = D / 16;
   constexpr int LPT = H * LPH;
   constexpr int TPW = 64 / LPT;
+  constexpr int V = U * R;        // (key, row) pairs per lane and step
+  constexpr int VL = V / 8;       // complete logits per lane after the scatter
+  static_assert(LPH == 8, "head dim 128: 8 lanes per head");
   static_assert(LPT <= 64 && 64 % LPT == 0, "row must tile a wave");
+  static_assert(V % 8 == 0 && VL <= U, "need 8 <= U*R <= 8*U");
   __shared__ float red[kWaves][H * R][2];
 
   const int lane = threadIdx.x & 63;
@@ -55,87 +109,109 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   const int64_t b = blockIdx.x / nseg;
   const int64_t seg = blockIdx.x % nseg;
   const int G = Hq / H;
+  // the block of (row, key) pairs this lane owns after the scatter
+  const int j = ((c >> 2) & 1) * 4 + (c & 1) * 2 + ((c >> 1) & 1);
+  const int own_r = (j * VL) / U;
+  const int own_u = (j * VL) % U;
 
   // query slices of this lane's kv head: R rows x 16 dims (8 packed pairs)
   uint32_t qv[R][8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int h = g * G + r / T, j = r % T;
-    const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + c * 16);
+    const int h = g * G + r / T, jj = r % T;
+    const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + jj) * Hq + h) * D + c * 16);
     const uint4 q0 = qp[0], q1 = qp[1];
     qv[r][0] = q0.x; qv[r][1] = q0.y; qv[r][2] = q0.z; qv[r][3] = q0.w;
     qv[r][4] = q1.x; qv[r][5] = q1.y; qv[r][6] = q1.z; qv[r][7] = q1.w;
   }
 
-  float m[R], s[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) { m[r] = -INFINITY; s[r] = 0.0f; }
+  float m = -INFINITY, s = 0.0f;  // softmax partial of row own_r over this lane's keys
 
   const int64_t t_begin = seg * seg_len;
   const int64_t t_end = min(N, t_begin + seg_len);
   const bf16_t* kb = k + b * stride_b + g * D + c * 16;
   constexpr int STEP = kWaves * TPW;
-  for (int64_t t0 = t_begin + wave * TPW + slot; t0 < t_end; t0 += STEP * UNROLL) {
-    uint4 kr[UNROLL][2];
+
+  // logits of U rows (t0 + u*STEP) from their loaded slices; rows with
+  // u >= n_valid are masked out
+  auto consume = [&](const uint4 (&kr)[U][2], int n_valid) {
+    float x[V];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t t = t0 + static_cast<int64_t>(u) * STEP;
-      if (t < t_end) {
-        const uint4* kp = reinterpret_cast<const uint4*>(kb + t * stride_n);
-        kr[u][0] = kp[0];
-        kr[u][1] = kp[1];
-      } else {
-        kr[u][0] = make_uint4(0, 0, 0, 0);
-        kr[u][1] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    float l2[UNROLL][R];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint32_t kw[8] = {kr[u][0].x, kr[u][0].y, kr[u][0].z, kr[u][0].w,
                               kr[u][1].x, kr[u][1].y, kr[u][1].z, kr[u][1].w};
-      const bool valid = t0 + static_cast<int64_t>(u) * STEP < t_end;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float acc = 0.0f;
 #pragma unroll
         for (int p = 0; p < 8; ++p) acc = dot2(qv[r][p], kw[p], acc);
-        acc = group_sum<LPH>(acc);
-        l2[u][r] = valid ? acc * scale2 : -INFINITY;
+        x[r * U + u] = acc;
       }
     }
+    reduce_scatter8<V>(x, c);
+    float l[VL];
+    float bm = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float bm = l2[0][r];
+    for (int e = 0; e < VL; ++e) {
+      l[e] = (own_u + e < n_valid) ? x[e] * scale2 : -INFINITY;
+      bm = fmaxf(bm, l[e]);
+    }
+    const float mn = fmaxf(m, bm);
+    if (mn != -INFINITY) {
+      float acc = s * __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
-      for (int u = 1; u < UNROLL; ++u) bm = fmaxf(bm, l2[u][r]);
-      const float mn = fmaxf(m[r], bm);
-      if (mn != -INFINITY) {
-        float acc = s[r] * exp2f(m[r] - mn);
+      for (int e = 0; e < VL; ++e) acc += __builtin_amdgcn_exp2f(l[e] - mn);
+      s = acc;
+      m = mn;
+    }
+  };
+  auto load = [&](uint4 (&kr)[U][2], int64_t t0) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) acc += exp2f(l2[u][r] - mn);
-        s[r] = acc;
-        m[r] = mn;
+    for (int u = 0; u < U; ++u) {
+      const uint4* kp = reinterpret_cast<const uint4*>(kb + (t0 + static_cast<int64_t>(u) * STEP) * stride_n);
+      kr[u][0] = kp[0];
+      kr[u][1] = kp[1];
+    }
+  };
+
+  int64_t t0 = t_begin + wave * TPW + slot;
+  const int64_t full_end = t_end - static_cast<int64_t>(U - 1) * STEP;  // t0 < full_end: U rows valid
+  for (; t0 < full_end; t0 += static_cast<int64_t>(STEP) * U) {
+    uint4 cur[U][2];
+    load(cur, t0);
+    consume(cur, U);
+  }
+  if (t0 < t_end) {  // ragged tail: fewer than U rows left for this slot
+    const int n_valid = static_cast<int>((t_end - t0 + STEP - 1) / STEP);
+    uint4 cur[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < n_valid) {
+        const uint4* kp = reinterpret_cast<const uint4*>(kb + (t0 + static_cast<int64_t>(u) * STEP) * stride_n);
+        cur[u][0] = kp[0];
+        cur[u][1] = kp[1];
+      } else {
+        cur[u][0] = cur[u][1] = make_uint4(0, 0, 0, 0);
       }
     }
+    consume(cur, n_valid);
   }
 
-  // merge the TPW row slots of the wave (lanes LPT apart)
+  // lanes of the head group that own the same query row
+  if constexpr (R <= 4) merge_lane<0>(m, s);
+  if constexpr (R <= 2) merge_lane<1>(m, s);
+  if constexpr (R <= 1) merge_lane<2>(m, s);
+  // the TPW row slots of the wave (lanes LPT apart)
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float m2 = __shfl_xor(m[r], off, 64);
-      const float s2 = __shfl_xor(s[r], off, 64);
-      merge_ms(m[r], s[r], m2, s2);
-    }
+    const float m2 = __shfl_xor(m, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    merge_ms(m, s, m2, s2);
   }
-  if (slot == 0 && c == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      red[wave][g * R + r][0] = m[r];
-      red[wave][g * R + r][1] = s[r];
-    }
+  // one lane per (head, row) publishes: the owner of the row's first keys
+  if (slot == 0 && own_u == 0) {
+    red[wave][g * R + own_r][0] = m;
+    red[wave][g * R + own_r][1] = s;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < H * R; i += kThreads) {
@@ -143,8 +219,8 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) merge_ms(mm, ss, red[w][i][0], red[w][i][1]);
     const int gg = i / R, r = i % R;
-    const int h = gg * G + r / T, j = r % T;
-    float* o = ms + (((b * Hq + h) * T + j) * nseg + seg) * 2;
+    const int h = gg * G + r / T, jj = r % T;
+    float* o = ms + (((b * Hq + h) * T + jj) * nseg + seg) * 2;
     o[0] = natural ? mm * kLn2 : mm;
     o[1] = ss;
   }
@@ -266,11 +342,17 @@ rowstat_kernel(const float* __restrict__ ms, int64_t rows, int64_t nseg, int nat
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
+// rows per slot and step: at least 8 (key, row) pairs per lane.  (Double
+// buffering the loads in registers and 8 rows per step measured the same on
+// MI355X: the stream runs at the memory system's rate either way.)
+template <int R> constexpr int stream_unroll() { return R >= 2 ? 4 : 8; }
+
 template <int D, int H, int R>
 void launch_stream(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
                    float scale2, int64_t seg_len, int64_t nseg, float* ms, int natural,
                    hipStream_t s) {
-  hipLaunchKernelGGL((score_stream_kernel<D, H, R, 4>), dim3(static_cast<unsigned>(kc.B * nseg)),
+  hipLaunchKernelGGL((score_stream_kernel<D, H, R, stream_unroll<R>()>),
+                     dim3(static_cast<unsigned>(kc.B * nseg)),
                      dim3(kThreads), 0, s, static_cast<const bf16_t*>(q),
                      static_cast<const bf16_t*>(k), kc.N, kc.stride_b, kc.stride_n,
                      static_cast<int>(T), static_cast<int>(Hq), scale2, seg_len, nseg, ms,
@@ -322,6 +404,10 @@ int launch_score_partials(const void* q, int64_t T, int64_t Hq, const void* k,
     KVSEL_SS(2, 1) KVSEL_SS(2, 2) KVSEL_SS(2, 4) KVSEL_SS(2, 8)
     KVSEL_SS(1, 1) KVSEL_SS(1, 2) KVSEL_SS(1, 4) KVSEL_SS(1, 8)
 #undef KVSEL_SS
+  }
+  if (score_mfma_ok(kc.dtype, R, seg_len)) {
+    launch_score_mfma(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, s);
+    return check_launch("kvsel_score");
   }
   if (kc.dtype == KVSEL_BF16) {
     if (kc.D == 128) dispatch_tile<bf16_t, 128>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, s);

@@ -86,6 +86,12 @@ SCORE_CASES = [
     ("tile_R448_ragged", "bf16", 1, 1000, 2, 14, 64, 128, 1),
     ("tile_R3_d64", "bf16", 2, 700, 2, 2, 3, 64, 1),
     ("tile_R64_fp32_d128", "fp32", 1, 1536, 2, 8, 16, 128, 96),
+    # matrix-core path: bf16, >= 16 rows per kv head, segments of 64k rows
+    ("mfma_R16_d64_chunks", "bf16", 1, 640, 2, 4, 8, 64, 64),
+    ("mfma_R24_d64_chunks", "bf16", 2, 1536, 2, 6, 8, 64, 128),
+    ("mfma_R64_chunks", "bf16", 2, 4096, 8, 16, 32, 128, 256),
+    ("mfma_R128_tokens_ragged", "bf16", 2, 2000, 4, 16, 32, 128, 1),
+    ("mfma_R300_two_passes_ragged", "bf16", 1, 700, 1, 10, 30, 128, 1),
 ]
 
 
@@ -121,6 +127,11 @@ AGG_CASES = [
     ("token_vnorm_group", "bf16", 4, 1200, 2, 8, 8, 128, 1, 4, "vnorm", "token"),
     ("token_vnorm_units_fp32", "fp32", 2, 640, 4, 4, 16, 64, 5, 2, "vnorm", "token"),
     ("token_mass_units_d64", "bf16", 2, 768, 2, 4, 3, 64, 256, 1, "mass", "token"),
+    # matrix-core token path: bf16, >= 16 rows per kv head
+    ("mfma_vnorm_R128_ragged_group", "bf16", 2, 1100, 4, 16, 32, 128, 1, 2, "vnorm", "token"),
+    ("mfma_mass_R300_two_passes", "bf16", 1, 700, 1, 10, 30, 128, 1, 1, "mass", "token"),
+    ("mfma_vnorm_R16_d64_units", "bf16", 2, 640, 2, 4, 8, 64, 5, 2, "vnorm", "token"),
+    ("mfma_mass_R64", "bf16", 3, 512, 2, 16, 8, 128, 1, 1, "mass", "token"),
 ]
 
 
