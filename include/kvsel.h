@@ -156,9 +156,10 @@ size_t kvsel_score_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T,
  * Two paths:
  *  - chunk path (signal MASS and part != NULL): combines the partials of
  *    kvsel_score; q, k, v are not read and may be NULL; row_max/row_sum may be
- *    NULL (derived from part; then workspace is needed).
+ *    NULL (then derived from part).
  *  - token path (otherwise): re-reads q and k (and v for VNORM) and needs
  *    row_max/row_sum from kvsel_score; works for any unit_len >= 1.
+ *   ws           kvsel_aggregate_workspace(...) bytes (both paths need one).
  */
 int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k,
                     const void* v, kvsel_cache kc, float scale,

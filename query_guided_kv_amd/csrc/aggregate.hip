@@ -20,25 +20,54 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Chunk path, stage 1: workgroup (g, row chunk, unit chunk); 64 units x 4 row
+// lanes; each lane sums every 4th row of the chunk, the four lanes merge in
+// LDS.  Writes out[g][u] directly when one chunk covers the group's rows,
+// else a partial ws[(g * n_rc + rc) * M + u] for stage 2.
+constexpr int kAggUnits = 64;
+constexpr int kAggRowLanes = kThreads / kAggUnits;
+constexpr int kAggChunkRows = 64;
+
 __global__ void __launch_bounds__(kThreads)
 agg_chunk_kernel(const float* __restrict__ part, const float* __restrict__ row_max,
-                 const float* __restrict__ row_sum, int64_t rows_per_inst, int64_t M,
-                 int64_t group, int64_t mblocks, float* __restrict__ out) {
-  const int64_t gi = blockIdx.x / mblocks;
-  const int64_t u = (blockIdx.x % mblocks) * kThreads + threadIdx.x;
-  if (u >= M) return;
+                 const float* __restrict__ row_sum, int64_t rows_per_g, int64_t M, int64_t n_rc,
+                 int64_t n_uc, float* __restrict__ dst) {
+  __shared__ float red[kAggRowLanes][kAggUnits];
+  const int64_t uc = blockIdx.x % n_uc;
+  const int64_t rc = (blockIdx.x / n_uc) % n_rc;
+  const int64_t gi = blockIdx.x / (n_uc * n_rc);
+  const int ul = threadIdx.x % kAggUnits, rl = threadIdx.x / kAggUnits;
+  const int64_t u = uc * kAggUnits + ul;
+  const int64_t r0 = rc * kAggChunkRows;
+  const int64_t r1 = min(rows_per_g, r0 + kAggChunkRows);
   float acc = 0.0f;
-  for (int64_t bi = 0; bi < group; ++bi) {
-    const int64_t row0 = (gi * group + bi) * rows_per_inst;
-    for (int64_t r = 0; r < rows_per_inst; ++r) {
-      const int64_t row = row0 + r;
-      const float m = row_max[row];
-      const float inv_z = 1.0f / row_sum[row];
+  if (u < M) {
+    for (int64_t r = r0 + rl; r < r1; r += kAggRowLanes) {
+      const int64_t row = gi * rows_per_g + r;
       const float2 pu = *reinterpret_cast<const float2*>(part + (row * M + u) * 2);
-      acc += pu.y * exp2f((pu.x - m) * kLog2e) * inv_z;
+      acc += pu.y * exp2f((pu.x - row_max[row]) * kLog2e) / row_sum[row];
     }
   }
-  out[gi * M + u] = acc;
+  red[rl][ul] = acc;
+  __syncthreads();
+  if (rl == 0 && u < M) {
+    float t = red[0][ul];
+#pragma unroll
+    for (int i = 1; i < kAggRowLanes; ++i) t += red[i][ul];
+    dst[(gi * n_rc + rc) * M + u] = t;
+  }
+}
+
+// Chunk path, stage 2: out[g][u] = sum over row chunks, in order.
+__global__ void __launch_bounds__(kThreads)
+agg_chunk_sum_kernel(const float* __restrict__ ws, int64_t G, int64_t M, int64_t n_rc,
+                     float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= G * M) return;
+  const int64_t gi = i / M, u = i % M;
+  float t = 0.0f;
+  for (int64_t rc = 0; rc < n_rc; ++rc) t += ws[(gi * n_rc + rc) * M + u];
+  out[i] = t;
 }
 
 constexpr int kQRows = 64;
@@ -160,12 +189,26 @@ void launch_tok(const void* q, int64_t T_, int64_t Hq, const void* k, const void
 
 int launch_aggregate_chunks(const float* part, const float* row_max, const float* row_sum,
                             int64_t B, int64_t Hq, int64_t T, int64_t M, int64_t group,
-                            float* unit_score, hipStream_t s) {
-  const int64_t mblocks = (M + kThreads - 1) / kThreads;
+                            float* unit_score, float* ws, hipStream_t s) {
   const int64_t G = B / group;
-  hipLaunchKernelGGL(agg_chunk_kernel, dim3(static_cast<unsigned>(G * mblocks)), dim3(kThreads), 0,
-                     s, part, row_max, row_sum, Hq * T, M, group, mblocks, unit_score);
+  const int64_t rows_per_g = group * Hq * T;
+  const int64_t n_rc = (rows_per_g + kAggChunkRows - 1) / kAggChunkRows;
+  const int64_t n_uc = (M + kAggUnits - 1) / kAggUnits;
+  float* dst = n_rc == 1 ? unit_score : ws;
+  hipLaunchKernelGGL(agg_chunk_kernel, dim3(static_cast<unsigned>(G * n_rc * n_uc)),
+                     dim3(kThreads), 0, s, part, row_max, row_sum, rows_per_g, M, n_rc, n_uc, dst);
+  if (n_rc > 1) {
+    const int rc = check_launch("kvsel_aggregate");
+    if (rc != KVSEL_OK) return rc;
+    hipLaunchKernelGGL(agg_chunk_sum_kernel, dim3(static_cast<unsigned>((G * M + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, ws, G, M, n_rc, unit_score);
+  }
   return check_launch("kvsel_aggregate");
+}
+
+size_t aggregate_chunk_ws_floats(int64_t B, int64_t Hq, int64_t T, int64_t M) {
+  // any group: (B / group) * ceil(group * Hq * T / 64) <= ceil(B * Hq * T / 64) + B
+  return static_cast<size_t>(((B * Hq * T + kAggChunkRows - 1) / kAggChunkRows + B) * M);
 }
 
 int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,

@@ -92,8 +92,13 @@ size_t score_ws(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len, b
   return static_cast<size_t>(B * Hq * T * nseg * 2) * sizeof(float);
 }
 
-size_t aggregate_ws(int64_t B, int64_t N, int64_t Hq, int64_t T, bool chunk, bool have_stats) {
-  if (chunk) return have_stats ? 0 : static_cast<size_t>(2 * B * Hq * T) * sizeof(float);
+// chunk path: [derived row stats: 2 * B*Hq*T] [row-chunk sums]; token path:
+// per-token sums B*N
+size_t aggregate_ws(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len, bool chunk,
+                    bool have_stats) {
+  if (chunk)
+    return (static_cast<size_t>(have_stats ? 0 : 2 * B * Hq * T) +
+            aggregate_chunk_ws_floats(B, Hq, T, N / unit_len)) * sizeof(float);
   return static_cast<size_t>(B * N) * sizeof(float);
 }
 
@@ -182,7 +187,7 @@ int kvsel_score(const void* q, int64_t T, int64_t Hq, const void* k, kvsel_cache
 size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len,
                                  int32_t chunk_path, int32_t have_row_stats) {
   if (B < 1 || N < 1 || Hq < 1 || T < 1 || unit_len < 1) return 0;
-  return aggregate_ws(B, N, Hq, T, chunk_path != 0, have_row_stats != 0);
+  return aggregate_ws(B, N, Hq, T, unit_len, chunk_path != 0, have_row_stats != 0);
 }
 
 int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
@@ -204,20 +209,21 @@ int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const v
   const bool stats = row_max != nullptr;
   const int64_t M = kc.N / unit_len;
   const int64_t rows = kc.B * Hq * T;
-  const size_t need = aggregate_ws(kc.B, kc.N, Hq, T, chunk, stats);
+  const size_t need = aggregate_ws(kc.B, kc.N, Hq, T, unit_len, chunk, stats);
   if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(KVSEL_ERR_WORKSPACE, "kvsel_aggregate: workspace %zu < %zu bytes", ws_bytes, need);
   if (chunk) {
     if (unit_len < 2) return fail(KVSEL_ERR_SHAPE, "kvsel_aggregate: partials need unit_len > 1");
     const float* rm = row_max;
     const float* rs = row_sum;
+    float* w = static_cast<float*>(ws);
     if (!stats) {
-      float* w = static_cast<float*>(ws);
       KVSEL_TRY(launch_rowstats(part, rows, M, 1, w, w + rows, stream));
       rm = w;
       rs = w + rows;
+      w += 2 * rows;
     }
-    return launch_aggregate_chunks(part, rm, rs, kc.B, Hq, T, M, group, unit_score, stream);
+    return launch_aggregate_chunks(part, rm, rs, kc.B, Hq, T, M, group, unit_score, w, stream);
   }
   KVSEL_TRY(check_ptr(q, "q"));
   KVSEL_TRY(check_ptr(k, "k"));

@@ -14,6 +14,7 @@
 // tile variant: any shape; keys and values staged through LDS as fp32.
 #include "common.h"
 #include "internal.h"
+#include "mfma.h"
 
 namespace kvsel {
 namespace {
@@ -342,6 +343,189 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
 }
 
 // ---------------------------------------------------------------------------
+// matrix-core variant: bf16, >= 16 query rows per kv head
+// ---------------------------------------------------------------------------
+// Flash decoding with v_mfma_f32_16x16x32_bf16 (lane layout in mfma.h):
+//   S^T = K Q^T  (A = 16 keys x 32 dims from the LDS K tile, B = 32 dims x 16
+//                 query rows held in registers): lane l gets query row l%16
+//                 and keys 4*(l/16) .. +3 of the key block;
+//   O^T += V^T P^T  (A = 16 dims x 32 keys from a transposed LDS V tile,
+//                 B = the lane's own probabilities, rounded to bf16): the 32
+//                 keys of two key blocks, in the order the lane holds them.
+// The running max, sum and output of a query row all live in the lanes with
+// l%16 == row, so rescaling is lane-local; the max and the final sum are
+// reduced across the four lane quads.  Waves split the query rows; blocks with
+// fewer than four row blocks launch fewer waves, taller ones run in passes.
+template <int D, int RBW>
+__global__ void __launch_bounds__(256)
+decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t n_split, int H,
+                   int T_, int Hq, float scale2, int passes, float* __restrict__ ws_ms,
+                   float* __restrict__ ws_o) {
+  constexpr int TK = kMfmaTileKeys;
+  constexpr int KS = D / 32;
+  constexpr int KROW = D + kMfmaPad;
+  constexpr int VROW = TK + 8;          // transposed V: dims x keys (+16 bytes)
+  constexpr int CB = D / 16;            // output column blocks
+  __shared__ __align__(16) bf16_t kt[TK * KROW];
+  __shared__ __align__(16) bf16_t vt[D * VROW];
+
+  const int nthreads = blockDim.x;
+  const int nwaves = nthreads / 64;
+  int64_t x = blockIdx.x;
+  const int64_t sp = x % n_split; x /= n_split;
+  const int pass = static_cast<int>(x % passes); x /= passes;
+  const int g = static_cast<int>(x % H);
+  const int64_t b = x / H;
+  const int sg = find_seg(st, n_seg, sp);
+  const int64_t t_begin = (sp - st.split_begin[sg]) * kDecodeSplit;
+  const int64_t t_end = min(st.N[sg], t_begin + kDecodeSplit);
+  const int G = Hq / H;
+  const int R = G * T_;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const bf16_t* kb = static_cast<const bf16_t*>(st.k[sg]) + b * st.stride_b[sg] + static_cast<int64_t>(g) * D;
+  const bf16_t* vb = static_cast<const bf16_t*>(st.v[sg]) + b * st.stride_b[sg] + static_cast<int64_t>(g) * D;
+  const int64_t sn = st.stride_n[sg];
+
+  // query fragments (B operand: query row col of the row block, 8 dims per k-step)
+  uint4 qb[RBW][KS];
+  int rb[RBW];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    rb[i] = (pass * nwaves + wave) * RBW + i;
+    const int r = rb[i] * 16 + col;
+    if (r < R) {
+      const int h = g * G + r / T_, j = r % T_;
+      const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T_ + j) * Hq + h) * D + quad * 8);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) qb[i][s2] = qp[s2 * 4];
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) qb[i][s2] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  float m[RBW], s[RBW];
+  f32x4_t o[RBW][CB];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    m[i] = -INFINITY;
+    s[i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) o[i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += TK) {
+    __syncthreads();
+    // stage K (row-major) and V (transposed); rows past the end are zero
+    for (int e = threadIdx.x; e < TK * (D / 8); e += nthreads) {
+      const int key = e / (D / 8), ch = e % (D / 8);
+      uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
+      if (t0 + key < t_end) {
+        kw = *reinterpret_cast<const uint4*>(kb + (t0 + key) * sn + ch * 8);
+        vw = *reinterpret_cast<const uint4*>(vb + (t0 + key) * sn + ch * 8);
+      }
+      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kw;
+      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        vt[(ch * 8 + 2 * p) * VROW + key] = static_cast<bf16_t>(vv[p] & 0xffffu);
+        vt[(ch * 8 + 2 * p + 1) * VROW + key] = static_cast<bf16_t>(vv[p] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // K fragments of the four key blocks (A operand)
+    uint4 ka[4][KS];
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        ka[kb4][s2] = *reinterpret_cast<const uint4*>(&kt[(kb4 * 16 + col) * KROW + s2 * 32 + quad * 8]);
+    // V^T fragments: dim row c*16 + col, keys (pair*32) + {4*quad .. +3, 16 + 4*quad .. +3}
+    uint4 va[2][CB];
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const bf16_t* vr = &vt[(c * 16 + col) * VROW + pr * 32 + quad * 4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        va[pr][c] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      f32x4_t sv[4];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) a = mfma16x16x32(ka[kb4][s2], qb[i][s2], a);
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv)
+          if (t0 + kb4 * 16 + quad * 4 + vv >= t_end) a[vv] = -INFINITY;
+        sv[kb4] = a;
+      }
+      float tmax = sv[0][0];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) tmax = fmaxf(tmax, sv[kb4][vv]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m[i], tmax * scale2);
+      if (mn == -INFINITY) continue;  // whole tile masked (cannot happen for valid rows)
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
+      m[i] = mn;
+      float ps = 0.0f;
+      uint32_t pk[4][2];  // bf16 pairs of the probabilities, per key block
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        float p[4];
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          p[vv] = __builtin_amdgcn_exp2f(fmaf(sv[kb4][vv], scale2, -mn));
+          ps += p[vv];
+        }
+        pk[kb4][0] = f32_to_bf16(p[0]) | (static_cast<uint32_t>(f32_to_bf16(p[1])) << 16);
+        pk[kb4][1] = f32_to_bf16(p[2]) | (static_cast<uint32_t>(f32_to_bf16(p[3])) << 16);
+      }
+      s[i] = s[i] * alpha + ps;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) o[i][c] *= alpha;
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const uint4 pb = make_uint4(pk[2 * pr][0], pk[2 * pr][1], pk[2 * pr + 1][0], pk[2 * pr + 1][1]);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) o[i][c] = mfma16x16x32(va[pr][c], pb, o[i][c]);
+      }
+    }
+  }
+
+  // publish: lane l holds query row rb*16 + l%16, dims c*16 + 4*quad .. +3
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    float st_sum = s[i];
+    st_sum += __shfl_xor(st_sum, 16, 64);
+    st_sum += __shfl_xor(st_sum, 32, 64);
+    const int r = rb[i] * 16 + col;
+    if (r >= R) continue;
+    const int h = g * G + r / T_, j = r % T_;
+    const int64_t orow = (b * Hq + h) * T_ + j;
+    float* wo = ws_o + (orow * n_split + sp) * D;
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+      *reinterpret_cast<float4*>(wo + c * 16 + quad * 4) =
+          make_float4(o[i][c][0], o[i][c][1], o[i][c][2], o[i][c][3]);
+    if (quad == 0) {
+      ws_ms[(orow * n_split + sp) * 2] = m[i];
+      ws_ms[(orow * n_split + sp) * 2 + 1] = st_sum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // merge of the splits: one block of D threads per row
 // ---------------------------------------------------------------------------
 __global__ void decode_merge_kernel(const float* __restrict__ ws_ms, const float* __restrict__ ws_o,
@@ -441,6 +625,24 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
     KVSEL_DS(2, 1) KVSEL_DS(2, 2) KVSEL_DS(2, 4) KVSEL_DS(2, 8)
     KVSEL_DS(1, 1) KVSEL_DS(1, 2) KVSEL_DS(1, 4) KVSEL_DS(1, 8)
 #undef KVSEL_DS
+  }
+  if (!done && dtype == KVSEL_BF16 && R >= 16) {
+    const MfmaRowPlan p = mfma_row_plan(R);
+    const int64_t rbs = (R + 15) / 16;
+    // row blocks per wave: at most 2 (output accumulators live in registers)
+    const int rbw = rbs >= 8 ? 2 : 1;
+    const int nwaves = static_cast<int>(rbs < 4 ? rbs : 4);
+    const int passes = static_cast<int>((rbs + nwaves * rbw - 1) / (nwaves * rbw));
+    (void)p;
+    const dim3 grid(static_cast<unsigned>(B * H * passes * n_split)), block(64 * nwaves);
+#define KVSEL_DM(D_, RBW_) \
+    hipLaunchKernelGGL((decode_mfma_kernel<D_, RBW_>), grid, block, 0, s, static_cast<const bf16_t*>(q), st, \
+                       n_seg, n_split, static_cast<int>(H), static_cast<int>(T), static_cast<int>(Hq), scale2, \
+                       passes, ws_ms, ws_o)
+    if (D == 128) { if (rbw == 2) KVSEL_DM(128, 2); else KVSEL_DM(128, 1); }
+    else { if (rbw == 2) KVSEL_DM(64, 2); else KVSEL_DM(64, 1); }
+#undef KVSEL_DM
+    done = true;
   }
   if (!done) {
     if (dtype == KVSEL_BF16) {

@@ -43,9 +43,11 @@ int launch_rowstats(const float* ms, int64_t rows, int64_t nseg, int natural, fl
                     float* row_sum, hipStream_t s);
 
 // Chunk path: unit_score[g][u] from natural-unit partials and row stats.
+// `ws` holds aggregate_chunk_ws_floats(B, Hq, T, M) floats of row-chunk sums.
 int launch_aggregate_chunks(const float* part, const float* row_max, const float* row_sum,
                             int64_t B, int64_t Hq, int64_t T, int64_t M, int64_t group,
-                            float* unit_score, hipStream_t s);
+                            float* unit_score, float* ws, hipStream_t s);
+size_t aggregate_chunk_ws_floats(int64_t B, int64_t Hq, int64_t T, int64_t M);
 
 // Token path: per_token[b][t] = sum_h sum_j alpha (* ||v||), then per unit/group sums.
 int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,

@@ -123,6 +123,7 @@ AGG_CASES = [
     # name, dtype, B, N, H, Hq, T, D, unit, group, signal, path
     ("chunk_mass_stats", "bf16", 4, 2048, 8, 32, 1, 128, 256, 1, "mass", "chunk"),
     ("chunk_mass_derived_group2", "bf16", 4, 2048, 4, 8, 4, 128, 128, 2, "mass", "chunk_nostats"),
+    ("chunk_mass_many_rows_units", "bf16", 2, 8192, 4, 16, 16, 128, 64, 2, "mass", "chunk"),
     ("token_mass_l1", "bf16", 1, 1500, 4, 28, 4, 128, 1, 1, "mass", "token"),
     ("token_vnorm_group", "bf16", 4, 1200, 2, 8, 8, 128, 1, 4, "vnorm", "token"),
     ("token_vnorm_units_fp32", "fp32", 2, 640, 4, 4, 16, 64, 5, 2, "vnorm", "token"),
@@ -269,6 +270,10 @@ DECODE_CASES = [
     ("tile_R448_two_segs", "bf16", 1, (700, 600), 4, 28, 64, 128),
     ("tile_R32_bf16", "bf16", 1, (1100,), 4, 4, 32, 128),
     ("tile_R3_d64", "bf16", 2, (513, 5), 2, 2, 3, 64),
+    # matrix-core path: bf16, >= 16 rows per kv head
+    ("mfma_R16_d64_two_segs", "bf16", 2, (700, 77), 2, 4, 8, 64),
+    ("mfma_R128_ragged", "bf16", 1, (1300,), 4, 16, 32, 128),
+    ("mfma_R300_d64_three_passes", "bf16", 1, (530, 40), 1, 10, 30, 64),
 ]
 
 
