@@ -42,6 +42,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # kernel sources whose hash keys a stored counter measurement
 KERNEL_SOURCES = {
     "score": ["query_guided_kv_amd/csrc/score.hip", "query_guided_kv_amd/csrc/common.h"],
+    "score_mfma": ["query_guided_kv_amd/csrc/score_mfma.hip", "query_guided_kv_amd/csrc/mfma.h",
+                   "query_guided_kv_amd/csrc/common.h"],
     "reposition": ["query_guided_kv_amd/csrc/reposition.hip", "query_guided_kv_amd/csrc/common.h"],
     "aggregate": ["query_guided_kv_amd/csrc/aggregate.hip", "query_guided_kv_amd/csrc/common.h"],
     "gather": ["query_guided_kv_amd/csrc/gather.hip", "query_guided_kv_amd/csrc/common.h"],
@@ -75,12 +77,11 @@ def stage_bytes(w) -> dict:
     implementation cost and are not counted."""
     row = w.H * w.D * elem_bytes(w)
     rows = w.B * w.N
-    out = {s: 0 for s in ("reposition", "score", "aggregate", "topk", "gather", "decode")}
+    out = {s: 0 for s in ("score", "aggregate", "topk", "gather", "decode")}
     fused = w.decode and not w.align
+    out["score"] = rows * row                       # keys read by the scoring pass
     if w.reposition != "none" and not w.align:
-        out["reposition"] = 2 * rows * row          # K read, K' written
-    else:
-        out["score"] += rows * row                  # keys read by the scoring pass
+        out["score"] += rows * row                  # re-positioned keys written (a product)
     if w.signal == "vnorm":
         out["aggregate"] += rows * row              # values read for their norms
     out["topk"] = (w.B // w.group) * w.M * 4
@@ -98,15 +99,16 @@ def stage_bytes(w) -> dict:
 
 
 def dominant_stage(w, sb: dict) -> str:
-    # the scoring pass streams the whole cache; with a fused re-rotation it is
-    # the re-position kernel that carries the cache bytes
     return max(sb, key=lambda s: sb[s])
 
 
 def kernel_of(stage: str, w) -> str:
-    return {"reposition": "reposition_kernel", "score": "score_stream_kernel" if (
-        w.dtype == "bf16" and w.D == 128 and (w.Hq // w.H) * w.T in (1, 2, 4, 8)) else "score_tile_kernel",
-        "aggregate": "agg_token_kernel", "topk": "topk_kernel", "gather": "gather_kernel",
+    rows = (w.Hq // w.H) * w.T
+    score = ("score_stream_kernel" if w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
+             else "score_mfma_kernel" if w.dtype == "bf16" and rows >= 16 else "score_tile_kernel")
+    return {"score": score,
+        "aggregate": "agg_mfma_kernel" if w.dtype == "bf16" and rows >= 16 else "agg_token_kernel",
+        "topk": "topk_kernel", "gather": "gather_kernel",
         "decode": "decode_stream_kernel", "gather_decode": "decode_stream_kernel (gathering)"}[stage]
 
 

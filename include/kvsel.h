@@ -141,6 +141,39 @@ size_t kvsel_score_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T,
                              int32_t want_part);
 
 /*
+ * kvsel_score_reposition -- kvsel_reposition followed by kvsel_score on the
+ * re-positioned keys, in one pass where the shape allows it ([CacheFocus §2.3]
+ * re-positions the cached keys before the query-document attention;
+ * [InfoFlow §4.2] scores after global position reconstruction).
+ *
+ * Same results as kvsel_reposition(k -> k_out, rot_unit_len, delta, ...) and
+ * then kvsel_score(q, ..., k_out, ...): the keys are rotated with the same
+ * fp64 arithmetic and single rounding, so the scores are those of the
+ * rounded re-positioned keys.  Where bf16 query blocks have >= 16 rows per kv
+ * head, the scoring segment (unit_len with `part`, else 256) and rot_unit_len
+ * are multiples of 64, the rotation happens while the keys are staged for
+ * scoring: the keys are read once, and k_out (when not NULL) receives the
+ * re-positioned keys.  Otherwise the two passes run, through k_out or, when
+ * it is NULL, through the tail of the workspace.
+ *   k_out        NULL or a cache with the layout of `kc`; must not overlap k.
+ *   rot_unit_len, delta, delta_per_instance, rope_base, rope_style
+ *                as unit_len, delta, ... of kvsel_reposition.
+ *   ws           kvsel_score_reposition_workspace(..., have_k_out) bytes.
+ *   other arguments as for kvsel_score.
+ */
+int kvsel_score_reposition(const void* q, int64_t T, int64_t Hq, const void* k,
+                           void* k_out, kvsel_cache kc, float scale,
+                           int64_t unit_len, int64_t rot_unit_len,
+                           const int64_t* delta, int32_t delta_per_instance,
+                           double rope_base, int32_t rope_style,
+                           float* row_max, float* row_sum, float* part,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+size_t kvsel_score_reposition_workspace(int64_t T, int64_t Hq, kvsel_cache kc,
+                                        int64_t unit_len, int64_t rot_unit_len,
+                                        int32_t want_row_stats, int32_t want_part,
+                                        int32_t have_k_out);
+
+/*
  * kvsel_aggregate -- per-unit relevance from the softmax-normalised
  * attention, with alpha = exp(l - row_max) / row_sum:
  *   KVSEL_SIG_MASS:  S[g,u] = sum_{b in g} sum_h sum_j sum_{t in u} alpha

@@ -154,34 +154,124 @@ size_t kvsel_score_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_
   return score_ws(B, N, Hq, T, unit_len, want_row_stats != 0, want_part != 0);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Re-positioning that a scoring call applies on the fly.
+struct ScoreRotArgs {
+  void* k_out;
+  int64_t unit_len;
+  const int64_t* delta;
+  int per_instance;
+  double base;
+  int style;
+};
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of kvsel_score_reposition: the scoring workspace, plus room for
+// the re-positioned keys when they cannot be formed on the fly and the caller
+// keeps none.
+size_t score_rot_ws(int64_t T, int64_t Hq, const kvsel_cache& kc, int64_t unit_len,
+                    int64_t rot_unit_len, bool stats, bool part, bool have_k_out) {
+  const size_t base = score_ws(kc.B, kc.N, Hq, T, unit_len, stats, part);
+  const int64_t seg_len = part ? unit_len : kTokenTile;
+  const bool fused = score_mfma_rot_ok(kc.dtype, (Hq / kc.H) * T, seg_len, rot_unit_len);
+  if (fused || have_k_out) return base;
+  const size_t esz = kc.dtype == KVSEL_BF16 ? 2 : 4;
+  return round256(base) + static_cast<size_t>(kc.B * kc.stride_b) * esz;
+}
+
+int score_impl(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
+               float scale, int64_t unit_len, float* row_max, float* row_sum, float* part,
+               void* ws, size_t ws_bytes, hipStream_t stream, const ScoreRotArgs* rot,
+               const char* what) {
+  KVSEL_TRY(check_ptr(q, "q"));
+  KVSEL_TRY(check_ptr(k, "k"));
+  KVSEL_TRY(check_cache(kc, what));
+  KVSEL_TRY(check_heads(T, Hq, kc, what));
+  KVSEL_TRY(check_units(kc, unit_len, what));
+  if ((row_max == nullptr) != (row_sum == nullptr))
+    return fail(KVSEL_ERR_NULL, "%s: row_max and row_sum must both be set or both NULL", what);
+  const bool stats = row_max != nullptr;
+  if (!stats && part == nullptr) return fail(KVSEL_ERR_NULL, "%s: no output requested", what);
+  if (part != nullptr && unit_len < 2)
+    return fail(KVSEL_ERR_SHAPE, "%s: per-unit partials need unit_len > 1", what);
+  const size_t need = rot == nullptr
+                          ? score_ws(kc.B, kc.N, Hq, T, unit_len, stats, part != nullptr)
+                          : score_rot_ws(T, Hq, kc, unit_len, rot->unit_len, stats,
+                                         part != nullptr, rot->k_out != nullptr);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(KVSEL_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, need);
+  const int64_t rows = kc.B * Hq * T;
+  const int64_t seg_len = part != nullptr ? unit_len : kTokenTile;
+  const int64_t nseg = (kc.N + seg_len - 1) / seg_len;
+  float* ms = part != nullptr ? part : static_cast<float*>(ws);
+  const int natural = part != nullptr ? 1 : 0;
+  if (rot != nullptr) {
+    if (score_mfma_rot_ok(kc.dtype, (Hq / kc.H) * T, seg_len, rot->unit_len)) {
+      launch_score_mfma_rot(q, T, Hq, k, rot->k_out, kc, scale, seg_len, nseg, ms,
+                            natural, rot->unit_len, rot->delta, rot->per_instance, rot->base,
+                            rot->style, stream);
+      KVSEL_TRY(check_launch(what));
+    } else {
+      // separate passes; without k_out the keys go to the workspace tail
+      void* kp = rot->k_out;
+      if (kp == nullptr)
+        kp = static_cast<char*>(ws) +
+             round256(score_ws(kc.B, kc.N, Hq, T, unit_len, stats, part != nullptr));
+      KVSEL_TRY(launch_reposition(k, kp, kc, rot->unit_len, rot->delta, rot->per_instance,
+                                  rot->base, rot->style, stream));
+      KVSEL_TRY(launch_score_partials(q, T, Hq, kp, kc, scale, seg_len, ms, natural, stream));
+    }
+  } else {
+    KVSEL_TRY(launch_score_partials(q, T, Hq, k, kc, scale, seg_len, ms, natural, stream));
+  }
+  if (stats) return launch_rowstats(ms, rows, nseg, natural, row_max, row_sum, stream);
+  return KVSEL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int kvsel_score(const void* q, int64_t T, int64_t Hq, const void* k, kvsel_cache kc, float scale,
                 int64_t unit_len, float* row_max, float* row_sum, float* part, void* ws,
                 size_t ws_bytes, hipStream_t stream) {
-  KVSEL_TRY(check_ptr(q, "q"));
-  KVSEL_TRY(check_ptr(k, "k"));
-  KVSEL_TRY(check_cache(kc, "kvsel_score"));
-  KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_score"));
-  KVSEL_TRY(check_units(kc, unit_len, "kvsel_score"));
-  if ((row_max == nullptr) != (row_sum == nullptr))
-    return fail(KVSEL_ERR_NULL, "kvsel_score: row_max and row_sum must both be set or both NULL");
-  const bool stats = row_max != nullptr;
-  if (!stats && part == nullptr)
-    return fail(KVSEL_ERR_NULL, "kvsel_score: no output requested");
-  if (part != nullptr && unit_len < 2)
-    return fail(KVSEL_ERR_SHAPE, "kvsel_score: per-unit partials need unit_len > 1");
-  const size_t need = score_ws(kc.B, kc.N, Hq, T, unit_len, stats, part != nullptr);
-  if (need > 0 && (ws == nullptr || ws_bytes < need))
-    return fail(KVSEL_ERR_WORKSPACE, "kvsel_score: workspace %zu < %zu bytes", ws_bytes, need);
-  const int64_t rows = kc.B * Hq * T;
-  if (part != nullptr) {
-    KVSEL_TRY(launch_score_partials(q, T, Hq, k, kc, scale, unit_len, part, 1, stream));
-    if (stats) return launch_rowstats(part, rows, kc.N / unit_len, 1, row_max, row_sum, stream);
-    return KVSEL_OK;
+  return score_impl(q, T, Hq, k, kc, scale, unit_len, row_max, row_sum, part, ws, ws_bytes,
+                    stream, nullptr, "kvsel_score");
+}
+
+size_t kvsel_score_reposition_workspace(int64_t T, int64_t Hq, kvsel_cache kc, int64_t unit_len,
+                                        int64_t rot_unit_len, int32_t want_row_stats,
+                                        int32_t want_part, int32_t have_k_out) {
+  if (T < 1 || Hq < 1 || kc.B < 1 || kc.N < 1 || kc.H < 1 || unit_len < 1 || rot_unit_len < 1)
+    return 0;
+  return score_rot_ws(T, Hq, kc, unit_len, rot_unit_len, want_row_stats != 0, want_part != 0,
+                      have_k_out != 0);
+}
+
+int kvsel_score_reposition(const void* q, int64_t T, int64_t Hq, const void* k, void* k_out,
+                           kvsel_cache kc, float scale, int64_t unit_len, int64_t rot_unit_len,
+                           const int64_t* delta, int32_t delta_per_instance, double rope_base,
+                           int32_t rope_style, float* row_max, float* row_sum, float* part,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* what = "kvsel_score_reposition";
+  if (delta == nullptr) return fail(KVSEL_ERR_NULL, "delta is NULL");
+  if (k_out != nullptr) {
+    KVSEL_TRY(check_ptr(k_out, "k_out"));
+    if (k_out == k) return fail(KVSEL_ERR_SHAPE, "%s: k_out must not overlap k", what);
   }
-  float* ms = static_cast<float*>(ws);
-  KVSEL_TRY(launch_score_partials(q, T, Hq, k, kc, scale, kTokenTile, ms, 0, stream));
-  return launch_rowstats(ms, rows, (kc.N + kTokenTile - 1) / kTokenTile, 0, row_max, row_sum,
-                         stream);
+  KVSEL_TRY(check_cache(kc, what));
+  KVSEL_TRY(check_units(kc, rot_unit_len, what));
+  if (rope_style != KVSEL_ROPE_HALF && rope_style != KVSEL_ROPE_INTERLEAVED)
+    return fail(KVSEL_ERR_SHAPE, "%s: unknown rope_style %d", what, rope_style);
+  if (!(rope_base > 1.0)) return fail(KVSEL_ERR_SHAPE, "%s: rope_base must be > 1", what);
+  const ScoreRotArgs rot{k_out, rot_unit_len, delta, delta_per_instance != 0, rope_base,
+                         rope_style};
+  return score_impl(q, T, Hq, k, kc, scale, unit_len, row_max, row_sum, part, ws, ws_bytes,
+                    stream, &rot, what);
 }
 
 size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len,

@@ -22,12 +22,16 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+// Two fp32 values -> a packed bf16 pair (lo, hi), one instruction.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const bf16x2_hw_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element access for the two cache dtypes.
@@ -65,10 +69,10 @@ __device__ __forceinline__ uint4 pack16(const float* in) {
     r.x = __float_as_uint(in[0]); r.y = __float_as_uint(in[1]);
     r.z = __float_as_uint(in[2]); r.w = __float_as_uint(in[3]);
   } else {
-    r.x = f32_to_bf16(in[0]) | (static_cast<uint32_t>(f32_to_bf16(in[1])) << 16);
-    r.y = f32_to_bf16(in[2]) | (static_cast<uint32_t>(f32_to_bf16(in[3])) << 16);
-    r.z = f32_to_bf16(in[4]) | (static_cast<uint32_t>(f32_to_bf16(in[5])) << 16);
-    r.w = f32_to_bf16(in[6]) | (static_cast<uint32_t>(f32_to_bf16(in[7])) << 16);
+    r.x = pack2_bf16(in[0], in[1]);
+    r.y = pack2_bf16(in[2], in[3]);
+    r.z = pack2_bf16(in[4], in[5]);
+    r.w = pack2_bf16(in[6], in[7]);
   }
   return r;
 }
@@ -144,13 +148,22 @@ __device__ __forceinline__ double2 rope_cs(int64_t delta, int i, int D, double b
   return make_double2(c, s);
 }
 
-// fp64 -> bf16 with one rounding to nearest even: round to fp32 toward zero,
-// make the last bit sticky (round to odd), then round fp32 -> bf16.  fp32
-// keeps more than two extra bits, so the two steps round like one.
+// fp64 -> bf16 with one rounding to nearest even.  The hardware fp64 -> fp32
+// conversion rounds to nearest; rounding that fp32 value to bf16 gives the
+// correctly rounded result unless it landed exactly halfway between two bf16
+// values while the fp64 value did not (every bf16 midpoint is an fp32 value,
+// and any other fp32 value lies on the same side of the midpoints as x).  In
+// that case the fp32 value moves one ulp toward x, which fixes the direction.
+__device__ __forceinline__ float f64_to_bf16_ready(double x) {
+  const float t = static_cast<float>(x);
+  const uint32_t u = __float_as_uint(t);
+  const double back = static_cast<double>(t);
+  const bool fix = ((u & 0xffffu) == 0x8000u) & (back != x);
+  const uint32_t step = fabs(x) > fabs(back) ? 1u : 0xffffffffu;
+  return __uint_as_float(fix ? u + step : u);
+}
 __device__ __forceinline__ bf16_t f64_to_bf16(double x) {
-  float t = __double2float_rz(x);
-  if (static_cast<double>(t) != x) t = __uint_as_float(__float_as_uint(t) | 1u);
-  return f32_to_bf16(t);
+  return f32_to_bf16(f64_to_bf16_ready(x));
 }
 
 template <typename T>
@@ -160,10 +173,10 @@ __device__ __forceinline__ uint4 pack16_f64(const double* in) {
     r.x = __float_as_uint(__double2float_rn(in[0])); r.y = __float_as_uint(__double2float_rn(in[1]));
     r.z = __float_as_uint(__double2float_rn(in[2])); r.w = __float_as_uint(__double2float_rn(in[3]));
   } else {
-    r.x = f64_to_bf16(in[0]) | (static_cast<uint32_t>(f64_to_bf16(in[1])) << 16);
-    r.y = f64_to_bf16(in[2]) | (static_cast<uint32_t>(f64_to_bf16(in[3])) << 16);
-    r.z = f64_to_bf16(in[4]) | (static_cast<uint32_t>(f64_to_bf16(in[5])) << 16);
-    r.w = f64_to_bf16(in[6]) | (static_cast<uint32_t>(f64_to_bf16(in[7])) << 16);
+    r.x = pack2_bf16(f64_to_bf16_ready(in[0]), f64_to_bf16_ready(in[1]));
+    r.y = pack2_bf16(f64_to_bf16_ready(in[2]), f64_to_bf16_ready(in[3]));
+    r.z = pack2_bf16(f64_to_bf16_ready(in[4]), f64_to_bf16_ready(in[5]));
+    r.w = pack2_bf16(f64_to_bf16_ready(in[6]), f64_to_bf16_ready(in[7]));
   }
   return r;
 }

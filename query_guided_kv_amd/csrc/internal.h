@@ -37,6 +37,13 @@ bool score_mfma_ok(int dtype, int64_t rows_per_kv, int64_t seg_len);
 void launch_score_mfma(const void* q, int64_t T, int64_t Hq, const void* k,
                        const kvsel_cache& kc, float scale2, int64_t seg_len, int64_t nseg,
                        float* ms, int natural, hipStream_t s);
+// Same, scoring the keys re-positioned on the fly (units of rot_len rows, a
+// multiple of 64, rotated by delta[u]); k_out (or NULL) receives them.
+bool score_mfma_rot_ok(int dtype, int64_t rows_per_kv, int64_t seg_len, int64_t rot_len);
+void launch_score_mfma_rot(const void* q, int64_t T, int64_t Hq, const void* k, void* k_out,
+                           const kvsel_cache& kc, float scale, int64_t seg_len, int64_t nseg,
+                           float* ms, int natural, int64_t rot_len, const int64_t* delta,
+                           int per_instance, double base, int style, hipStream_t s);
 
 // Row statistics from segment partials (log2 or natural units as written).
 int launch_rowstats(const float* ms, int64_t rows, int64_t nseg, int natural, float* row_max,

@@ -36,13 +36,27 @@ __device__ __forceinline__ void merge_cols(float& m, float& s) {
   merge_ms(m, s, dpp_mirror(m), dpp_mirror(s));
 }
 
-// D: head dim; RBW: row blocks per wave; NWR: waves across row blocks.
-template <int D, int RBW, int NWR>
+// Re-positioning fused into the staging of K (kvsel_score_reposition): every
+// unit of rot_len cached rows (a multiple of the tile) is rotated by delta[u]
+// positions with the same fp64 arithmetic and single rounding as
+// kvsel_reposition, so the scored keys are bit-identical to that call's
+// output; with WRITE the re-positioned keys are also stored to kout.
+struct ScoreRot {
+  const int64_t* delta;      // [M] or [B][M] (delta_stride_b = M)
+  int64_t delta_stride_b;
+  int64_t rot_len;
+  double base;
+  bf16_t* kout;              // same layout as k, or NULL
+};
+
+// D: head dim; RBW: row blocks per wave; NWR: waves across row blocks;
+// ROT: 0 none, 1 half-split pairs, 2 interleaved pairs; WRITE: store K'.
+template <int D, int RBW, int NWR, int ROT, bool WRITE>
 __global__ void __launch_bounds__(kThreads)
 score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int64_t N, int H,
                   int64_t stride_b, int64_t stride_n, int T, int Hq, float scale2,
                   int64_t seg_len, int64_t nseg, int64_t segs_per_block, int64_t groups,
-                  int passes, float* __restrict__ ms, int natural) {
+                  int passes, float* __restrict__ ms, int natural, ScoreRot rot) {
   constexpr int KS = D / 32;                 // MFMA k-steps
   constexpr int KROW = D + kPad;             // staged row stride (elements)
   constexpr int NWK = kWaves / NWR;          // waves across key blocks
@@ -51,6 +65,7 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   constexpr int ROWS_PASS = NWR * RBW * 16;
   __shared__ __align__(16) bf16_t kt[kTileKeys * KROW];
   __shared__ float red[NWK][ROWS_PASS][2];
+  __shared__ double2 cs[ROT ? D / 2 : 1];
 
   int64_t x = blockIdx.x;
   const int64_t grp = x % groups; x /= groups;
@@ -86,25 +101,55 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   const int64_t t_end = min(N, seg1 * seg_len);
   const bf16_t* kb = k + b * stride_b + static_cast<int64_t>(g) * D;
 
-  // staging of one tile: thread e moves vectors e, e + 256, ... of the tile
+  // staging of one tile.  Vector i of a thread is (key, chunk) of item
+  // e = tid + (i / P) * 256 (P = 2 with half-split rotation: chunk c and its
+  // partner c + D/16 travel together; else P = 1 and item e is chunk e).
+  constexpr int P = ROT == 1 ? 2 : 1;
+  constexpr int CPK = D / 8 / P;  // items per key
+  auto item = [&](int i, int& key, int& ch) {
+    const int e = threadIdx.x + (i / P) * kThreads;
+    key = e / CPK;
+    ch = e % CPK + (i % P) * (D / 16);
+  };
   auto fetch = [&](uint4 (&v)[VPT], int64_t t0) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int key = e / (D / 8), ch = e % (D / 8);
+      int key, ch;
+      item(i, key, ch);
       v[i] = (t0 + key < t_end)
                  ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * stride_n + ch * 8)
                  : make_uint4(0, 0, 0, 0);
     }
   };
-  auto stash = [&](const uint4 (&v)[VPT]) {
+  const bool write_out = WRITE && pass == 0;
+  auto stash = [&](uint4 (&v)[VPT], int64_t t0) {
+    if constexpr (ROT == 1) {
+#pragma unroll
+      for (int i = 0; i < VPT; i += 2) {
+        int key, ch;
+        item(i, key, ch);
+        rope_rotate16<bf16_t, KVSEL_ROPE_HALF>(v[i], v[i + 1], ch * 8, cs);
+      }
+    } else if constexpr (ROT == 2) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        int key, ch;
+        item(i, key, ch);
+        uint4 unused;
+        rope_rotate16<bf16_t, KVSEL_ROPE_INTERLEAVED>(v[i], unused, ch * 8, cs);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int key = e / (D / 8), ch = e % (D / 8);
+      int key, ch;
+      item(i, key, ch);
       *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = v[i];
+      if (write_out && t0 + key < t_end)
+        *reinterpret_cast<uint4*>(rot.kout + b * stride_b + (t0 + key) * stride_n +
+                                  static_cast<int64_t>(g) * D + ch * 8) = v[i];
     }
   };
+  int64_t cs_unit = -1;
 
   float m[RBW][4], s[RBW][4];
 #pragma unroll
@@ -116,7 +161,16 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   if (t_begin < t_end) fetch(nxt, t_begin);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) {
     __syncthreads();               // previous tile fully read
-    stash(nxt);
+    if constexpr (ROT != 0) {
+      const int64_t u = t0 / rot.rot_len;  // a tile lies inside one unit
+      if (u != cs_unit) {
+        const int64_t delta = rot.delta[b * rot.delta_stride_b + u];
+        for (int i = threadIdx.x; i < D / 2; i += kThreads) cs[i] = rope_cs(delta, i, D, rot.base);
+        cs_unit = u;
+        __syncthreads();
+      }
+    }
+    stash(nxt, t0);
     __syncthreads();
     if (t0 + kTileKeys < t_end) fetch(nxt, t0 + kTileKeys);  // in flight during the math
 
@@ -201,29 +255,31 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   }
 }
 
-template <int D, int RBW, int NWR>
+template <int D, int RBW, int NWR, int ROT, bool WRITE>
 void launch(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
             float scale2, int64_t seg_len, int64_t nseg, int64_t spb, int passes, float* ms,
-            int natural, hipStream_t s) {
+            int natural, const ScoreRot& rot, hipStream_t s) {
   const int64_t groups = (nseg + spb - 1) / spb;
   const int64_t blocks = kc.B * kc.H * passes * groups;
-  hipLaunchKernelGGL((score_mfma_kernel<D, RBW, NWR>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kThreads), 0, s, static_cast<const bf16_t*>(q),
-                     static_cast<const bf16_t*>(k), kc.N, static_cast<int>(kc.H), kc.stride_b,
-                     kc.stride_n, static_cast<int>(T), static_cast<int>(Hq), scale2, seg_len, nseg,
-                     spb, groups, passes, ms, natural);
+  hipLaunchKernelGGL((score_mfma_kernel<D, RBW, NWR, ROT, WRITE>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), kc.N,
+                     static_cast<int>(kc.H), kc.stride_b, kc.stride_n, static_cast<int>(T),
+                     static_cast<int>(Hq), scale2, seg_len, nseg, spb, groups, passes, ms, natural,
+                     rot);
 }
 
-template <int D>
+template <int D, int ROT, bool WRITE>
 void dispatch(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
               float scale2, int64_t seg_len, int64_t nseg, float* ms, int natural,
-              hipStream_t s) {
+              const ScoreRot& rot, hipStream_t s) {
   const MfmaRowPlan p = mfma_row_plan((Hq / kc.H) * T);
   // about 1024 keys per workgroup: segments of 256 go four to a block
   const int64_t spb = seg_len >= 1024 ? 1 : 1024 / seg_len;
-#define KVSEL_SM(RBW, NWR) \
-  if (p.rbw == RBW && p.nwr == NWR) \
-    return launch<D, RBW, NWR>(q, T, Hq, k, kc, scale2, seg_len, nseg, spb, p.passes, ms, natural, s);
+#define KVSEL_SM(RBW, NWR)                                                                 \
+  if (p.rbw == RBW && p.nwr == NWR)                                                        \
+    return launch<D, RBW, NWR, ROT, WRITE>(q, T, Hq, k, kc, scale2, seg_len, nseg, spb,    \
+                                           p.passes, ms, natural, rot, s);
   KVSEL_SM(1, 1) KVSEL_SM(1, 2) KVSEL_SM(1, 4) KVSEL_SM(2, 4) KVSEL_SM(4, 4)
 #undef KVSEL_SM
 }
@@ -234,13 +290,37 @@ bool score_mfma_ok(int dtype, int64_t rows_per_kv, int64_t seg_len) {
   return dtype == KVSEL_BF16 && rows_per_kv >= 16 && seg_len % kTileKeys == 0;
 }
 
+bool score_mfma_rot_ok(int dtype, int64_t rows_per_kv, int64_t seg_len, int64_t rot_len) {
+  return score_mfma_ok(dtype, rows_per_kv, seg_len) && rot_len % kTileKeys == 0;
+}
+
 void launch_score_mfma(const void* q, int64_t T, int64_t Hq, const void* k,
                        const kvsel_cache& kc, float scale2, int64_t seg_len, int64_t nseg,
                        float* ms, int natural, hipStream_t s) {
+  const ScoreRot none{nullptr, 0, 1, 0.0, nullptr};
   if (kc.D == 128)
-    dispatch<128>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, s);
+    dispatch<128, 0, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, none, s);
   else
-    dispatch<64>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, s);
+    dispatch<64, 0, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, none, s);
+}
+
+void launch_score_mfma_rot(const void* q, int64_t T, int64_t Hq, const void* k, void* k_out,
+                           const kvsel_cache& kc, float scale, int64_t seg_len, int64_t nseg,
+                           float* ms, int natural, int64_t rot_len, const int64_t* delta,
+                           int per_instance, double base, int style, hipStream_t s) {
+  const float scale2 = scale * kLog2e;
+  const ScoreRot rot{delta, per_instance ? kc.N / rot_len : 0, rot_len, base,
+                     static_cast<bf16_t*>(k_out)};
+  const bool w = k_out != nullptr;
+#define KVSEL_SR(D_, ST)                                                                   \
+  if (w) dispatch<D_, ST, true>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, rot, s); \
+  else dispatch<D_, ST, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, rot, s);
+  if (kc.D == 128) {
+    if (style == KVSEL_ROPE_HALF) { KVSEL_SR(128, 1) } else { KVSEL_SR(128, 2) }
+  } else {
+    if (style == KVSEL_ROPE_HALF) { KVSEL_SR(64, 1) } else { KVSEL_SR(64, 2) }
+  }
+#undef KVSEL_SR
 }
 
 }  // namespace kvsel

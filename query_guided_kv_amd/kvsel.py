@@ -50,6 +50,9 @@ _SIGNATURES = {
     "kvsel_reposition": (ctypes.c_int, [_P, _P, Cache, _I64, _P, _I32, _D, _I32, _P]),
     "kvsel_score": (ctypes.c_int, [_P, _I64, _I64, _P, Cache, _F, _I64, _P, _P, _P, _P, _SZ, _P]),
     "kvsel_score_workspace": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I32, _I32]),
+    "kvsel_score_reposition": (ctypes.c_int, [_P, _I64, _I64, _P, _P, Cache, _F, _I64, _I64, _P,
+                                              _I32, _D, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "kvsel_score_reposition_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, _I32, _I32, _I32]),
     "kvsel_aggregate": (ctypes.c_int, [_P, _I64, _I64, _P, _P, Cache, _F, _P, _P, _P, _I32, _I64,
                                        _I64, _P, _P, _SZ, _P]),
     "kvsel_aggregate_workspace": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I32, _I32]),
@@ -163,6 +166,36 @@ def score(q: torch.Tensor, k: torch.Tensor, unit_len: int, scale: Optional[float
     ws = _workspace(need, dev)
     _check(lib.kvsel_score(_ptr(q), T, Hq, _ptr(k), cache_desc(k), scale, unit_len, _ptr(rm),
                            _ptr(rs), _ptr(part), _ptr(ws), need, _stream(dev)))
+    return rm, rs, part
+
+
+def score_reposition(q: torch.Tensor, k: torch.Tensor, delta: torch.Tensor, rot_unit_len: int,
+                     unit_len: int, k_out: Optional[torch.Tensor] = None,
+                     scale: Optional[float] = None, row_stats: bool = True,
+                     partials: bool = True, rope_base: float = 10000.0, style: str = "half"):
+    """kvsel_score_reposition -> (row_max, row_sum, part) of the keys rotated by
+    delta[u] per unit of ``rot_unit_len`` rows; ``k_out`` (same shape and strides
+    as ``k``) receives the re-positioned keys when given."""
+    lib = load()
+    B, T, Hq, D = q.shape
+    N = k.shape[1]
+    scale = 1.0 / D ** 0.5 if scale is None else scale
+    dev = k.device
+    if k_out is not None and (k_out.shape != k.shape or k_out.stride() != k.stride()):
+        raise KvselError(-2, "k_out must match k in shape and strides")
+    rm = _empty((B, Hq, T), dev) if row_stats else None
+    rs = _empty((B, Hq, T), dev) if row_stats else None
+    part = _empty((B, Hq, T, N // unit_len, 2), dev) if partials else None
+    kc = cache_desc(k)
+    need = lib.kvsel_score_reposition_workspace(T, Hq, kc, unit_len, rot_unit_len,
+                                                int(row_stats), int(partials),
+                                                int(k_out is not None))
+    ws = _workspace(need, dev)
+    per = 1 if delta.dim() == 2 else 0
+    _check(lib.kvsel_score_reposition(_ptr(q), T, Hq, _ptr(k), _ptr(k_out), kc, scale, unit_len,
+                                      rot_unit_len, _ptr(delta), per, rope_base, ROPE[style],
+                                      _ptr(rm), _ptr(rs), _ptr(part), _ptr(ws), need,
+                                      _stream(dev)))
     return rm, rs, part
 
 

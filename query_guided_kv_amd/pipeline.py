@@ -86,7 +86,7 @@ class Path:
     the launch stream around that stage.
     """
 
-    STAGES = ("reposition", "score", "aggregate", "topk", "gather", "decode", "gather_decode")
+    STAGES = ("score", "aggregate", "topk", "gather", "decode", "gather_decode")
 
     def __init__(self, w, inp: dict):
         self.w = w
@@ -94,13 +94,15 @@ class Path:
         self.l2 = (inp.get("l2_k"), inp.get("l2_v"))
         dev = self.k.device
         self.delta, self.delta_len = reposition_deltas(w, dev)
-        self.k_rep = torch.empty_like(self.k) if self.delta is not None else None
+        # re-positioned keys are kept where later steps read them; the aligned
+        # gather re-positions from the stored keys instead
+        keep = self.delta is not None and not w.align
+        self.k_rep = torch.empty_like(self.k) if keep else None
         self.chunk = w.unit_len > 1 and w.signal == "mass"
         # without re-positioning on the way, gather and decode are one call
         split = w.decode and w.align
         self.stages = tuple(s for s in self.STAGES
-                            if (s != "reposition" or self.delta is not None)
-                            and (s not in ("gather", "decode") or split)
+                            if (s not in ("gather", "decode") or split)
                             and (s != "gather_decode" or (w.decode and not split)))
 
     def __call__(self, q: torch.Tensor, marks: dict = None) -> dict:
@@ -113,17 +115,22 @@ class Path:
                 pair[i].record()
 
         out = {}
-        k_score = self.k
-        if self.delta is not None:
-            mark("reposition", 0)
-            K.reposition(self.k, self.delta, self.delta_len, out=self.k_rep,
-                         rope_base=w.rope_base, style=w.rope_style)
-            mark("reposition", 1)
-            k_score = self.k_rep
-            out["k_rep"] = k_score
+        k_score = self.k if self.k_rep is None else self.k_rep
+
+        def score(stats: bool, partials: bool):
+            # re-positioning happens inside the scoring call (one read of K)
+            if self.delta is None:
+                return K.score(q, self.k, w.unit_len, w.scale, row_stats=stats, partials=partials)
+            return K.score_reposition(q, self.k, self.delta, self.delta_len, w.unit_len,
+                                      k_out=self.k_rep, scale=w.scale, row_stats=stats,
+                                      partials=partials, rope_base=w.rope_base,
+                                      style=w.rope_style)
+
+        if self.k_rep is not None:
+            out["k_rep"] = self.k_rep
         if self.chunk:
             mark("score", 0)
-            _, _, part = K.score(q, k_score, w.unit_len, w.scale, row_stats=False, partials=True)
+            _, _, part = score(False, True)
             mark("score", 1)
             mark("aggregate", 0)
             out["unit_score"] = K.aggregate(w.unit_len, w.group, "mass", part=part,
@@ -131,7 +138,7 @@ class Path:
             mark("aggregate", 1)
         else:
             mark("score", 0)
-            rm, rs, _ = K.score(q, k_score, w.unit_len, w.scale, row_stats=True, partials=False)
+            rm, rs, _ = score(True, False)
             mark("score", 1)
             mark("aggregate", 0)
             out["unit_score"] = K.aggregate(w.unit_len, w.group, w.signal, q=q, k=k_score,

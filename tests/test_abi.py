@@ -194,3 +194,25 @@ def test_gather_decode_validation(lib):
     assert need == 2 * 32 * 1 * splits * (2 + 128) * 4
     assert call(n=1, segs=ext, ws=need - 1) == WS
     assert lib.kvsel_gather_decode_workspace(1, 32, kc, 256, 0, None, 0) == 0
+
+
+def test_score_reposition_validation(lib):
+    p = ctypes.c_void_p(FAKE)
+    kc = cache(B=2, N=1024, H=8, D=128)
+    call = lambda rot=256, style=0, base=10000.0, delta=FAKE, kout=None, unit=256: lib.kvsel_score_reposition(
+        p, 1, 32, p, kout, kc, 0.088, unit, rot, delta and ctypes.c_void_p(delta), 0, base, style,
+        p, p, p, p, 1 << 40, None)
+    assert call(delta=0) == NULL
+    assert call(rot=300) == SHAPE
+    assert call(style=3) == SHAPE
+    assert call(base=1.0) == SHAPE
+    assert call(kout=p) == SHAPE                  # k_out overlapping k
+    assert call(kout=ctypes.c_void_p(MISALIGNED)) == UNSUP
+    # streaming shape without k_out: the re-positioned keys go to the workspace
+    base_ws = lib.kvsel_score_workspace(2, 1024, 32, 1, 256, 1, 1)
+    need = lib.kvsel_score_reposition_workspace(1, 32, kc, 256, 256, 1, 1, 0)
+    assert need == (base_ws + 255) // 256 * 256 + 2 * 1024 * 8 * 128 * 2
+    assert lib.kvsel_score_reposition_workspace(1, 32, kc, 256, 256, 1, 1, 1) == base_ws
+    # matrix-core shape (32 rows per kv head): fused, no extra room
+    assert lib.kvsel_score_reposition_workspace(32, 32, kc, 256, 256, 1, 1, 0) == \
+        lib.kvsel_score_workspace(2, 1024, 32, 32, 256, 1, 1)

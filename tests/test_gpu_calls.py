@@ -334,3 +334,50 @@ def test_gather_decode(case):
     o2, lse2 = K.decode_attn(q.to(dev), segs_d)
     torch.cuda.synchronize()
     assert_rel(o2, to64(o), 0.0, 1e-5, "o vs separate calls")
+
+
+# --------------------------------------------------------------------------
+# kvsel_score_reposition (re-position + score, fused where the shape allows)
+# --------------------------------------------------------------------------
+SR_CASES = [
+    # name, dtype, B, N, H, Hq, T, D, unit (score), rot_unit, style, per_inst, keep
+    ("fused_chunks_half_nokeep", "bf16", 1, 4096, 4, 8, 8, 128, 512, 512, "half", False, False),
+    ("fused_tokens_half_keep_ragged", "bf16", 2, 2112, 2, 8, 16, 128, 1, 64, "half", True, True),
+    ("fused_tokens_interleaved_d64", "bf16", 2, 1024, 2, 4, 8, 64, 1, 256, "interleaved", False, True),
+    ("fused_R300_passes_keep", "bf16", 1, 1280, 1, 10, 30, 128, 1, 128, "half", False, True),
+    ("stream_R4_nokeep_uses_ws", "bf16", 2, 2048, 8, 32, 1, 128, 256, 256, "half", False, False),
+    ("fp32_two_pass_keep", "fp32", 1, 1024, 4, 4, 16, 64, 128, 128, "half", False, True),
+]
+
+
+@pytest.mark.parametrize("case", SR_CASES, ids=[c[0] for c in SR_CASES])
+def test_score_reposition(case):
+    name, dtype, B, N, H, Hq, T, D, unit, rot, style, per_inst, keep = case
+    announce("score_reposition", case=name)
+    dev = device()
+    q = rnd((B, T, Hq, D), dtype, 80).to(dev)
+    k = rnd((B, N, H, D), dtype, 81, 1.5).to(dev)
+    M = N // rot
+    rng = np.random.default_rng(9)
+    delta = torch.from_numpy(rng.integers(0, 66000, size=(B, M) if per_inst else (M,))).to(dev)
+    chunk = unit > 1
+    k_out = torch.empty_like(k) if keep else None
+    rm, rs, part = K.score_reposition(q, k, delta, rot, unit, k_out=k_out, row_stats=True,
+                                      partials=chunk, style=style)
+    # reference: the two separate calls
+    k_ref = K.reposition(k, delta, rot, style=style)
+    rm2, rs2, part2 = K.score(q, k_ref, unit, row_stats=True, partials=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(rm, rm2) and torch.equal(rs, rs2)
+    if chunk:
+        assert torch.equal(part, part2)
+    if keep:
+        assert torch.equal(k_out, k_ref)
+    # and the oracle on the re-positioned keys
+    p_old = np.tile(np.arange(rot), M)
+    dl = delta.cpu().numpy() if per_inst else np.broadcast_to(delta.cpu().numpy(), (B, M))
+    p_new = p_old[None] + np.repeat(dl, rot, axis=1)
+    want_k = O.reposition(to64(k), np.broadcast_to(p_old, (B, N)), p_new, 10000.0, style, dtype)
+    m, Z, _ = O.score(to64(q), want_k, 1.0 / np.sqrt(D), 1)
+    assert_rel(rm, m, 2e-3, 2e-3, "row_max")
+    assert_rel(rs, Z, 2e-3, 0.0, "row_sum")

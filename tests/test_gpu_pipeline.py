@@ -58,7 +58,7 @@ def check_against_oracle(w, got: dict, want: dict, planted=None):
     idx = got["idx"].cpu().numpy().astype(np.int64)
     assert np.array_equal(idx, want["idx"]), "kept index sets differ"
     assert_rel(got["unit_score"], want["unit_score"], 2e-3, 0.0, "unit_score")
-    if "k_rep" in want:
+    if "k_rep" in got:   # kept where later steps read them
         assert_cache_close(got["k_rep"], want["k_rep"], w.dtype)
     if not w.decode:
         return
