@@ -40,16 +40,17 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 DEFAULT_WORKLOAD = "serving_16req_8l_128k"
 PROFILES = os.path.join(ROOT, "profiles")
 # kernel sources whose hash keys a stored counter measurement
+_C = "query_guided_kv_amd/csrc/"
 KERNEL_SOURCES = {
-    "score": ["query_guided_kv_amd/csrc/score.hip", "query_guided_kv_amd/csrc/common.h"],
-    "score_mfma": ["query_guided_kv_amd/csrc/score_mfma.hip", "query_guided_kv_amd/csrc/mfma.h",
-                   "query_guided_kv_amd/csrc/common.h"],
-    "reposition": ["query_guided_kv_amd/csrc/reposition.hip", "query_guided_kv_amd/csrc/common.h"],
-    "aggregate": ["query_guided_kv_amd/csrc/aggregate.hip", "query_guided_kv_amd/csrc/common.h"],
-    "gather": ["query_guided_kv_amd/csrc/gather.hip", "query_guided_kv_amd/csrc/common.h"],
-    "decode": ["query_guided_kv_amd/csrc/decode.hip", "query_guided_kv_amd/csrc/common.h"],
-    "topk": ["query_guided_kv_amd/csrc/topk.hip", "query_guided_kv_amd/csrc/common.h"],
-    "gather_decode": ["query_guided_kv_amd/csrc/decode.hip", "query_guided_kv_amd/csrc/common.h"],
+    "score_stream_kernel": [_C + "score.hip", _C + "common.h"],
+    "score_tile_kernel": [_C + "score.hip", _C + "common.h"],
+    "score_mfma_kernel": [_C + "score_mfma.hip", _C + "mfma.h", _C + "common.h"],
+    "agg_mfma_kernel": [_C + "aggregate_mfma.hip", _C + "mfma.h", _C + "common.h"],
+    "agg_token_kernel": [_C + "aggregate.hip", _C + "common.h"],
+    "topk_kernel": [_C + "topk.hip", _C + "common.h"],
+    "gather_kernel": [_C + "gather.hip", _C + "common.h"],
+    "decode_stream_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
+    "decode_mfma_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
 }
 
 
@@ -57,9 +58,9 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash(stage: str) -> str:
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[stage]:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -103,19 +104,22 @@ def dominant_stage(w, sb: dict) -> str:
 
 
 def kernel_of(stage: str, w) -> str:
+    """Name of the kernel that carries a stage's bytes for workload w."""
     rows = (w.Hq // w.H) * w.T
-    score = ("score_stream_kernel" if w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
-             else "score_mfma_kernel" if w.dtype == "bf16" and rows >= 16 else "score_tile_kernel")
-    return {"score": score,
-        "aggregate": "agg_mfma_kernel" if w.dtype == "bf16" and rows >= 16 else "agg_token_kernel",
-        "topk": "topk_kernel", "gather": "gather_kernel",
-        "decode": "decode_stream_kernel", "gather_decode": "decode_stream_kernel (gathering)"}[stage]
+    stream = w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
+    mfma = w.dtype == "bf16" and rows >= 16
+    return {"score": "score_stream_kernel" if stream else
+                     "score_mfma_kernel" if mfma else "score_tile_kernel",
+            "aggregate": "agg_mfma_kernel" if mfma else "agg_token_kernel",
+            "topk": "topk_kernel", "gather": "gather_kernel",
+            "decode": "decode_mfma_kernel" if mfma else "decode_stream_kernel",
+            "gather_decode": "decode_stream_kernel" if stream else "gather_kernel"}[stage]
 
 
-def stored_traffic(stage: str, workload: str):
+def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed counter summary, or None when
-    there is none for this kernel source."""
-    path = os.path.join(PROFILES, f"{stage}_{workload}_traffic.txt")
+    there is none for this kernel's current source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -124,7 +128,7 @@ def stored_traffic(stage: str, workload: str):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = (s.strip() for s in line.split("=", 1))
                 vals[k] = v
-    if vals.get("source_hash") != source_hash(stage):
+    if vals.get("source_hash") != source_hash(kernel):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -247,7 +251,8 @@ def main() -> int:
                 for s in path.stages}
     dom_ms = stage_ms[dom]
     achieved = sb[dom] / (dom_ms * 1e-3) / 1e9
-    traffic = stored_traffic(dom, w.name)
+    kernel = kernel_of(dom, w)
+    traffic = stored_traffic(kernel, w.name)
     rows = w.B * w.N
     path_bytes = sum(sb.values())
 
@@ -269,7 +274,7 @@ def main() -> int:
                    "unit_len": w.unit_len, "kept_units": w.k, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": kernel_of(dom, w), "stage": dom,
+                     "kernel": kernel, "stage": dom,
                      "algorithmic_bytes_per_launch": sb[dom], "avg_launch_ms": dom_ms},
         "path_hbm": {"algorithmic_bytes_per_step": path_bytes,
                      "achieved_GBps": path_bytes / (ms_step * 1e-3) / 1e9,
