@@ -274,8 +274,10 @@ void dispatch(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_c
               float scale2, int64_t seg_len, int64_t nseg, float* ms, int natural,
               const ScoreRot& rot, hipStream_t s) {
   const MfmaRowPlan p = mfma_row_plan((Hq / kc.H) * T);
-  // about 1024 keys per workgroup: segments of 256 go four to a block
-  const int64_t spb = seg_len >= 1024 ? 1 : 1024 / seg_len;
+  // up to 1024 keys per workgroup (segments of 256 go four to a block), fewer
+  // when that leaves under ~2048 workgroups for the 256 CUs
+  int64_t spb = seg_len >= 1024 ? 1 : 1024 / seg_len;
+  while (spb > 1 && kc.B * kc.H * p.passes * ((nseg + spb - 1) / spb) < 2048) spb /= 2;
 #define KVSEL_SM(RBW, NWR)                                                                 \
   if (p.rbw == RBW && p.nwr == NWR)                                                        \
     return launch<D, RBW, NWR, ROT, WRITE>(q, T, Hq, k, kc, scale2, seg_len, nseg, spb,    \

@@ -51,36 +51,90 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
   pb = sb[wave] + ib - b;
 }
 
+// Pick the digit of the k-th largest key from a 256-bin histogram (one wave,
+// threadIdx.x < 64): lane l owns bins 255-4l .. 252-4l (high to low); an
+// exclusive scan of the lanes' counts gives the number of keys in higher bins,
+// and the one bin with above < rank <= above + count publishes the new prefix
+// and the rank left inside that bin.
+__device__ __forceinline__ void select_bin(const uint32_t* h, uint32_t rank, uint32_t prefix,
+                                           int shift, uint32_t* sh_prefix, uint32_t* sh_rank) {
+  const int lane = threadIdx.x;
+  uint32_t c[4], tot = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = h[255 - 4 * lane - j];
+    tot += c[j];
+  }
+  uint32_t incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  uint32_t above = incl - tot;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (above < rank && rank <= above + c[j]) {
+      *sh_prefix = prefix | (static_cast<uint32_t>(255 - 4 * lane - j) << shift);
+      *sh_rank = rank - above;
+    }
+    above += c[j];
+  }
+}
+
+// Count `bin` into this wave's histogram.  Scores of one row share most of
+// their leading bits, so the lanes of a wave mostly hit the same bin: the
+// lanes with the first active lane's bin add their count once (ballot +
+// popcount), the rest add one by one.  Integer counts: exact in any order.
+__device__ __forceinline__ void count_bin(uint32_t* hist, uint32_t bin, bool active) {
+  const uint64_t act = __ballot(active);
+  if (act == 0) return;
+  const int first = __builtin_ctzll(act);
+  const uint32_t lead = __shfl(bin, first, 64);
+  const bool same = active && bin == lead;
+  const uint64_t grp = __ballot(same);
+  const int lane = threadIdx.x & 63;
+  if (lane == first) atomicAdd(&hist[lead], static_cast<uint32_t>(__popcll(grp)));
+  if (active && !same) atomicAdd(&hist[bin], 1u);
+}
+
 __global__ void __launch_bounds__(kThreads)
 topk_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* __restrict__ idx,
             float* __restrict__ val) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kWaves][256];
   __shared__ uint32_t sh_prefix, sh_rank;
   __shared__ uint32_t scan_a[kWaves], scan_b[kWaves];
   const float* s = score + static_cast<int64_t>(blockIdx.x) * M;
   int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
   float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
+  const int wave = threadIdx.x >> 6;
 
-  // 1. radix select of the k-th largest key
+  // 1. radix select of the k-th largest key, 8 bits per pass, one histogram
+  //    per wave merged in a fixed order
   uint32_t prefix = 0, mask = 0, rank = static_cast<uint32_t>(k);
   for (int shift = 24; shift >= 0; shift -= 8) {
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+    for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < M; i += kThreads) {
-      const uint32_t key = order_key(s[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t above = 0;
-      int bin = 255;
-      for (; bin > 0; --bin) {
-        if (above + hist[bin] >= rank) break;
-        above += hist[bin];
+    const int64_t rounds = (M + kThreads - 1) / kThreads;
+    for (int64_t rd = 0; rd < rounds; ++rd) {
+      const int64_t i = rd * kThreads + threadIdx.x;
+      uint32_t key = 0;
+      bool act = false;
+      if (i < M) {
+        key = order_key(s[i]);
+        act = (key & mask) == prefix;
       }
-      sh_rank = rank - above;
-      sh_prefix = prefix | (static_cast<uint32_t>(bin) << shift);
+      count_bin(hist[wave], (key >> shift) & 255u, act);
     }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) t += hist[w][threadIdx.x];
+      hist[0][threadIdx.x] = t;   // each thread reads and writes its own bin only
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) select_bin(hist[0], rank, prefix, shift, &sh_prefix, &sh_rank);
     __syncthreads();
     rank = sh_rank;
     prefix = sh_prefix;
@@ -120,12 +174,89 @@ topk_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* __re
   }
 }
 
+// Rows of up to 64 * 1024 scores: each thread keeps its contiguous slice of
+// KPT keys in registers, so the four radix passes and the ordered compaction
+// read the scores once.
+template <int KPT>
+__global__ void __launch_bounds__(kThreads)
+topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* __restrict__ idx,
+                float* __restrict__ val) {
+  __shared__ uint32_t hist[kWaves][256];
+  __shared__ uint32_t sh_prefix, sh_rank;
+  __shared__ uint32_t scan_a[kWaves], scan_b[kWaves];
+  const float* s = score + static_cast<int64_t>(blockIdx.x) * M;
+  int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
+  float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
+  const int wave = threadIdx.x >> 6;
+  const int64_t i0 = static_cast<int64_t>(threadIdx.x) * KPT;
+
+  uint32_t key[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) key[e] = i0 + e < M ? order_key(s[i0 + e]) : 0u;
+
+  uint32_t prefix = 0, mask = 0, rank = static_cast<uint32_t>(k);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+      count_bin(hist[wave], (key[e] >> shift) & 255u, i0 + e < M && (key[e] & mask) == prefix);
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) t += hist[w][threadIdx.x];
+      hist[0][threadIdx.x] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) select_bin(hist[0], rank, prefix, shift, &sh_prefix, &sh_rank);
+    __syncthreads();
+    rank = sh_rank;
+    prefix = sh_prefix;
+    mask |= 255u << shift;
+  }
+  const uint32_t kstar = prefix;
+  const uint32_t need_eq = rank;
+
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const bool in = i0 + e < M;
+    n_gt += in && key[e] > kstar;
+    n_eq += in && key[e] == kstar;
+  }
+  uint32_t gt_before, eq_before;
+  block_exclusive_scan2(n_gt, n_eq, gt_before, eq_before, scan_a, scan_b);
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    if (i0 + e >= M) break;
+    if (key[e] > kstar) {
+      const uint32_t pos = gt_before + min(eq_before, need_eq);
+      out_i[pos] = static_cast<int32_t>(i0 + e);
+      if (out_v) out_v[pos] = s[i0 + e];
+      ++gt_before;
+    } else if (key[e] == kstar) {
+      if (eq_before < need_eq) {
+        const uint32_t pos = gt_before + eq_before;
+        out_i[pos] = static_cast<int32_t>(i0 + e);
+        if (out_v) out_v[pos] = s[i0 + e];
+      }
+      ++eq_before;
+    }
+  }
+}
+
 }  // namespace
 
 int launch_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,
                 hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(G)), dim3(kThreads), 0, s, score, M,
-                     k, idx, val);
+  const dim3 grid(static_cast<unsigned>(G)), block(kThreads);
+  const int64_t per = (M + kThreads - 1) / kThreads;
+#define KVSEL_TK(KPT) \
+  if (per <= KPT) { hipLaunchKernelGGL(topk_reg_kernel<KPT>, grid, block, 0, s, score, M, k, idx, val); return check_launch("kvsel_topk"); }
+  KVSEL_TK(1) KVSEL_TK(2) KVSEL_TK(4) KVSEL_TK(8) KVSEL_TK(16) KVSEL_TK(32) KVSEL_TK(64)
+#undef KVSEL_TK
+  hipLaunchKernelGGL(topk_kernel, grid, block, 0, s, score, M, k, idx, val);
   return check_launch("kvsel_topk");
 }
 
