@@ -57,14 +57,44 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
   for (int i = threadIdx.x; i < range; i += kThreads) tot[i] = 0.0f;
 
-  for (int g = 0; g < H; ++g) {
+  // one flat sequence of (kv head, row pass, 64-key tile) items; the next
+  // item's K slice (and V slice for the norms) is in flight during the math
+  constexpr int VV = D / 32;  // 16-byte vectors of V per thread (4 lanes per key)
+  const int64_t n_tiles = (t_end - t_begin + kTileKeys - 1) / kTileKeys;
+  const int64_t n_items = static_cast<int64_t>(H) * passes * n_tiles;
+  uint4 kn[VPT], vr[VNORM ? VV : 1];
+  auto fetch = [&](int64_t it) {
+    const int g = static_cast<int>(it / (passes * n_tiles));
+    const int64_t t0 = t_begin + (it % n_tiles) * kTileKeys;
     const bf16_t* kb = k + b * stride_b + static_cast<int64_t>(g) * D;
-    const bf16_t* vb = v + b * stride_b + static_cast<int64_t>(g) * D;
-    for (int pass = 0; pass < passes; ++pass) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int key = e / (D / 8), ch = e % (D / 8);
+      kn[i] = (t0 + key < t_end) ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * stride_n + ch * 8)
+                                 : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (VNORM) {
+      const bf16_t* vb = v + b * stride_b + static_cast<int64_t>(g) * D;
+      const int key = threadIdx.x >> 2, qd = threadIdx.x & 3;
+#pragma unroll
+      for (int i = 0; i < VV; ++i)
+        vr[i] = (t0 + key < t_end)
+                    ? *reinterpret_cast<const uint4*>(vb + (t0 + key) * stride_n + qd * (D / 4) + i * 8)
+                    : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  uint4 qa[RBW][KS];
+  float m2[RBW][4], iz[RBW][4];
+  if (n_items > 0) fetch(0);
+  for (int64_t it = 0; it < n_items; ++it) {
+    const int g = static_cast<int>(it / (passes * n_tiles));
+    const int pass = static_cast<int>((it / n_tiles) % passes);
+    const int64_t t0 = t_begin + (it % n_tiles) * kTileKeys;
+    if (it % n_tiles == 0) {
       // query fragments and row statistics of this wave's row blocks; rows
       // past R get zero weight
-      uint4 qa[RBW][KS];
-      float m2[RBW][4], iz[RBW][4];
 #pragma unroll
       for (int i = 0; i < RBW; ++i) {
         const int rb = pass * NWR * RBW + wr + i * NWR;
@@ -73,10 +103,10 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           const int h = g * G + r / T, j = r % T;
           const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + quad * 8);
 #pragma unroll
-          for (int s = 0; s < KS; ++s) qa[i][s] = qp[s * 4];
+          for (int s2 = 0; s2 < KS; ++s2) qa[i][s2] = qp[s2 * 4];
         } else {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) qa[i][s] = make_uint4(0, 0, 0, 0);
+          for (int s2 = 0; s2 < KS; ++s2) qa[i][s2] = make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) {
@@ -92,70 +122,65 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           }
         }
       }
+    }
 
-      for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) {
-        __syncthreads();  // previous tile's kt / vn / part fully used
+    __syncthreads();  // previous tile's kt / vn / part fully used
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-          const int e = threadIdx.x + i * kThreads;
-          const int key = e / (D / 8), ch = e % (D / 8);
-          const uint4 w4 = (t0 + key < t_end)
-                               ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * stride_n + ch * 8)
-                               : make_uint4(0, 0, 0, 0);
-          *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = w4;
-        }
-        if constexpr (VNORM) {
-          // 4 consecutive lanes per key, D/4 dims each
-          const int key = threadIdx.x >> 2, qd = threadIdx.x & 3;
-          float ss = 0.0f;
-          if (t0 + key < t_end) {
-            float f[D / 4];
-            load_f32<bf16_t, D / 4>(vb + (t0 + key) * stride_n + qd * (D / 4), f);
+    for (int i = 0; i < VPT; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int key = e / (D / 8), ch = e % (D / 8);
+      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
+    }
+    if constexpr (VNORM) {
+      float ss = 0.0f;
 #pragma unroll
-            for (int d = 0; d < D / 4; ++d) ss = fmaf(f[d], f[d], ss);
-          }
-          ss = group_sum<4>(ss);
-          if (qd == 0) vn[key] = sqrtf(ss);
-        }
-        __syncthreads();
-
-        float c[KBW];
+      for (int i = 0; i < VV; ++i) {
+        float f[8];
+        unpack16<bf16_t>(vr[i], f);
 #pragma unroll
-        for (int jb = 0; jb < KBW; ++jb) {
-          const int key = (wk + jb * NWK) * 16 + col;
-          uint4 bk[KS];
-#pragma unroll
-          for (int st = 0; st < KS; ++st)
-            bk[st] = *reinterpret_cast<const uint4*>(&kt[key * KROW + st * 32 + quad * 8]);
-          float sum = 0.0f;
-#pragma unroll
-          for (int i = 0; i < RBW; ++i) {
-            f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < KS; ++st) a = mfma16x16x32(qa[i][st], bk[st], a);
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv)
-              sum = fmaf(__builtin_amdgcn_exp2f(fmaf(a[vv], scale2, -m2[i][vv])), iz[i][vv], sum);
-          }
-          sum += __shfl_xor(sum, 16, 64);
-          sum += __shfl_xor(sum, 32, 64);
-          c[jb] = sum;
-        }
-        if (quad == 0) {
-#pragma unroll
-          for (int jb = 0; jb < KBW; ++jb) part[wave][(wk + jb * NWK) * 16 + col] = c[jb];
-        }
-        __syncthreads();
-        if (threadIdx.x < kTileKeys) {
-          const int key = threadIdx.x;
-          const int owner = (key / 16) % NWK;  // the waves (wr, owner) computed this key
-          float s = 0.0f;
-#pragma unroll
-          for (int w = 0; w < NWR; ++w) s += part[w + owner * NWR][key];
-          if (VNORM) s *= vn[key];
-          if (t0 + key < t_end) tot[t0 - t_begin + key] += s;
-        }
+        for (int d = 0; d < 8; ++d) ss = fmaf(f[d], f[d], ss);
       }
+      ss = group_sum<4>(ss);
+      if ((threadIdx.x & 3) == 0) vn[threadIdx.x >> 2] = sqrtf(ss);
+    }
+    __syncthreads();
+    if (it + 1 < n_items) fetch(it + 1);
+
+    float c[KBW];
+#pragma unroll
+    for (int jb = 0; jb < KBW; ++jb) {
+      const int key = (wk + jb * NWK) * 16 + col;
+      uint4 bk[KS];
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        bk[st] = *reinterpret_cast<const uint4*>(&kt[key * KROW + st * 32 + quad * 8]);
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) a = mfma16x16x32(qa[i][st], bk[st], a);
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv)
+          sum = fmaf(__builtin_amdgcn_exp2f(fmaf(a[vv], scale2, -m2[i][vv])), iz[i][vv], sum);
+      }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      c[jb] = sum;
+    }
+    if (quad == 0) {
+#pragma unroll
+      for (int jb = 0; jb < KBW; ++jb) part[wave][(wk + jb * NWK) * 16 + col] = c[jb];
+    }
+    __syncthreads();
+    if (threadIdx.x < kTileKeys) {
+      const int key = threadIdx.x;
+      const int owner = (key / 16) % NWK;  // the waves (wr, owner) computed this key
+      float s2 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NWR; ++w) s2 += part[w + owner * NWR][key];
+      if (VNORM) s2 *= vn[key];
+      if (t0 + key < t_end) tot[t0 - t_begin + key] += s2;
     }
   }
   __syncthreads();
