@@ -173,10 +173,23 @@ __device__ __forceinline__ uint4 pack16_f64(const double* in) {
     r.x = __float_as_uint(__double2float_rn(in[0])); r.y = __float_as_uint(__double2float_rn(in[1]));
     r.z = __float_as_uint(__double2float_rn(in[2])); r.w = __float_as_uint(__double2float_rn(in[3]));
   } else {
-    r.x = pack2_bf16(f64_to_bf16_ready(in[0]), f64_to_bf16_ready(in[1]));
-    r.y = pack2_bf16(f64_to_bf16_ready(in[2]), f64_to_bf16_ready(in[3]));
-    r.z = pack2_bf16(f64_to_bf16_ready(in[4]), f64_to_bf16_ready(in[5]));
-    r.w = pack2_bf16(f64_to_bf16_ready(in[6]), f64_to_bf16_ready(in[7]));
+    // round to fp32 first; only a value that landed exactly on a bf16
+    // midpoint (probability ~2^-16) needs the one-ulp fix of f64_to_bf16_ready
+    float t[8];
+    bool tie = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      t[e] = static_cast<float>(in[e]);
+      tie |= (__float_as_uint(t[e]) & 0xffffu) == 0x8000u;
+    }
+    if (tie) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = f64_to_bf16_ready(in[e]);
+    }
+    r.x = pack2_bf16(t[0], t[1]);
+    r.y = pack2_bf16(t[2], t[3]);
+    r.z = pack2_bf16(t[4], t[5]);
+    r.w = pack2_bf16(t[6], t[7]);
   }
   return r;
 }
