@@ -102,10 +102,14 @@ size_t aggregate_ws(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_le
   return static_cast<size_t>(B * N) * sizeof(float);
 }
 
-int64_t decode_splits(const kvsel_segment* segs, int n_seg) {
+int64_t decode_splits(const kvsel_segment* segs, int n_seg, int64_t split_len) {
   int64_t n = 0;
-  for (int i = 0; i < n_seg; ++i) n += (segs[i].kc.N + kDecodeSplit - 1) / kDecodeSplit;
+  for (int i = 0; i < n_seg; ++i) n += (segs[i].kc.N + split_len - 1) / split_len;
   return n;
+}
+
+int64_t split_len_of(int64_t T, int64_t Hq, const kvsel_cache& c) {
+  return decode_split_len(c.dtype, c.H, c.D, c.H > 0 ? (Hq / c.H) * T : 1);
 }
 
 }  // namespace
@@ -398,7 +402,7 @@ size_t kvsel_decode_workspace(int64_t T, int64_t Hq, const kvsel_segment* segs, 
   if (segs == nullptr || n_seg < 1 || n_seg > kMaxSegments || T < 1 || Hq < 1) return 0;
   for (int i = 0; i < n_seg; ++i)
     if (segs[i].kc.N < 1 || segs[i].kc.B < 1 || segs[i].kc.D < 1) return 0;
-  const int64_t n_split = decode_splits(segs, n_seg);
+  const int64_t n_split = decode_splits(segs, n_seg, split_len_of(T, Hq, segs[0].kc));
   return static_cast<size_t>(segs[0].kc.B * Hq * T * n_split * (2 + segs[0].kc.D)) * sizeof(float);
 }
 
@@ -421,7 +425,7 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const k
     if (c.B != c0.B || c.H != c0.H || c.D != c0.D || c.dtype != c0.dtype)
       return fail(KVSEL_ERR_SHAPE, "kvsel_decode_attn: segments must share B, H, D and dtype");
     ds[i] = DecodeSeg{segs[i].k, segs[i].v, c.N, c.stride_b, c.stride_n, split};
-    split += (c.N + kDecodeSplit - 1) / kDecodeSplit;
+    split += (c.N + split_len_of(T, Hq, c0) - 1) / split_len_of(T, Hq, c0);
   }
   KVSEL_TRY(check_heads(T, Hq, c0, "kvsel_decode_attn"));
   const size_t need = kvsel_decode_workspace(T, Hq, segs, n_seg);
@@ -509,7 +513,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
       ds[i] = DecodeSeg{g ? k_src : segs[i].k, g ? v_src : segs[i].v, segs[i].kc.N,
                         g ? kc.stride_b : segs[i].kc.stride_b,
                         g ? kc.stride_n : segs[i].kc.stride_n, split};
-      split += (segs[i].kc.N + kDecodeSplit - 1) / kDecodeSplit;
+      split += (segs[i].kc.N + split_len_of(T, Hq, kc) - 1) / split_len_of(T, Hq, kc);
     }
     const DecodeGather gather{n - 1, idx, unit_len, k, idx_group, M, k_dst, v_dst};
     float* ws_ms = static_cast<float*>(ws);

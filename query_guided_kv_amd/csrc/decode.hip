@@ -36,6 +36,7 @@ struct SegTable {
   int64_t stride_b[kMaxSegments];
   int64_t stride_n[kMaxSegments];
   int64_t split_begin[kMaxSegments + 1];
+  int64_t split_len;         // keys per split (decode_split_len)
   // At most one segment is gathered on the fly: its row t is source row
   // idx[t / unit_len] * unit_len + t % unit_len of (k, v) above, and the kernel
   // also writes that row to row t of the compact destination (k_dst, v_dst).
@@ -77,8 +78,8 @@ decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64
   const int64_t b = blockIdx.x / n_split;
   const int64_t sp = blockIdx.x % n_split;
   const int sg = find_seg(st, n_seg, sp);
-  const int64_t t_begin = (sp - st.split_begin[sg]) * kDecodeSplit;
-  const int64_t t_end = min(st.N[sg], t_begin + kDecodeSplit);
+  const int64_t t_begin = (sp - st.split_begin[sg]) * st.split_len;
+  const int64_t t_end = min(st.N[sg], t_begin + st.split_len);
   const int G = Hq / H;
 
   // gathered segment: the kept unit ids that this split's rows come from
@@ -275,8 +276,8 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
   const int g = static_cast<int>(x % H);
   const int64_t b = x / H;
   const int sg = find_seg(st, n_seg, sp);
-  const int64_t t_begin = (sp - st.split_begin[sg]) * kDecodeSplit;
-  const int64_t t_end = min(st.N[sg], t_begin + kDecodeSplit);
+  const int64_t t_begin = (sp - st.split_begin[sg]) * st.split_len;
+  const int64_t t_end = min(st.N[sg], t_begin + st.split_len);
   const int G = Hq / H;
   const int R = G * T_;
   const int r = static_cast<int>(pass) * RB + threadIdx.x / TPR;
@@ -356,8 +357,8 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
 // l%16 == row, so rescaling is lane-local; the max and the final sum are
 // reduced across the four lane quads.  Waves split the query rows; blocks with
 // fewer than four row blocks launch fewer waves, taller ones run in passes.
-template <int D, int RBW>
-__global__ void __launch_bounds__(256)
+template <int D, int RBW, int NW>
+__global__ void __launch_bounds__(64 * NW)
 decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t n_split, int H,
                    int T_, int Hq, float scale2, int passes, float* __restrict__ ws_ms,
                    float* __restrict__ ws_o) {
@@ -366,19 +367,23 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   constexpr int KROW = D + kMfmaPad;
   constexpr int VROW = TK + 8;          // transposed V: dims x keys (+16 bytes)
   constexpr int CB = D / 16;            // output column blocks
+  constexpr int KG = TK / 4;            // groups of 4 keys
+  constexpr int NT = 64 * NW;
+  constexpr int KV = TK * (D / 8) / NT;    // K vectors per thread and tile
+  constexpr int VITEMS = KG * (D / 8);     // V items (4 keys x 8 dims) per tile
+  constexpr int VI = (VITEMS + NT - 1) / NT;
   __shared__ __align__(16) bf16_t kt[TK * KROW];
   __shared__ __align__(16) bf16_t vt[D * VROW];
 
-  const int nthreads = blockDim.x;
-  const int nwaves = nthreads / 64;
+  const int nwaves = NW;
   int64_t x = blockIdx.x;
   const int64_t sp = x % n_split; x /= n_split;
   const int pass = static_cast<int>(x % passes); x /= passes;
   const int g = static_cast<int>(x % H);
   const int64_t b = x / H;
   const int sg = find_seg(st, n_seg, sp);
-  const int64_t t_begin = (sp - st.split_begin[sg]) * kDecodeSplit;
-  const int64_t t_end = min(st.N[sg], t_begin + kDecodeSplit);
+  const int64_t t_begin = (sp - st.split_begin[sg]) * st.split_len;
+  const int64_t t_end = min(st.N[sg], t_begin + st.split_len);
   const int G = Hq / H;
   const int R = G * T_;
   const int lane = threadIdx.x & 63;
@@ -415,90 +420,129 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     for (int c = 0; c < CB; ++c) o[i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
+  // the next tile's K and V rows are in flight while this tile computes
+  uint4 kn[KV], vn4[VI][4];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int e = threadIdx.x + i * NT;
+      const int key = e / (D / 8), ch = e % (D / 8);
+      kn[i] = (t0 + key < t_end) ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * sn + ch * 8)
+                                 : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int e = threadIdx.x + i * NT;
+      const int kg = e % KG, ch = e / KG;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = t0 + kg * 4 + j;
+        vn4[i][j] = (e < VITEMS && t < t_end) ? *reinterpret_cast<const uint4*>(vb + t * sn + ch * 8)
+                                              : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  if (t_begin < t_end) fetch(t_begin);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TK) {
     __syncthreads();
-    // stage K (row-major) and V (transposed); rows past the end are zero
-    for (int e = threadIdx.x; e < TK * (D / 8); e += nthreads) {
+    // K row-major: item (key, 16-byte chunk); rows past the end are zero
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int e = threadIdx.x + i * NT;
       const int key = e / (D / 8), ch = e % (D / 8);
-      uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-      if (t0 + key < t_end) {
-        kw = *reinterpret_cast<const uint4*>(kb + (t0 + key) * sn + ch * 8);
-        vw = *reinterpret_cast<const uint4*>(vb + (t0 + key) * sn + ch * 8);
+      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
+    }
+    // V transposed: item (4 consecutive keys, 8-dim chunk) -> eight 8-byte runs
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int e = threadIdx.x + i * NT;
+      if (e >= VITEMS) break;
+      const int kg = e % KG, ch = e / KG;
+      uint32_t w[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[j][0] = vn4[i][j].x; w[j][1] = vn4[i][j].y; w[j][2] = vn4[i][j].z; w[j][3] = vn4[i][j].w;
       }
-      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kw;
-      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        vt[(ch * 8 + 2 * p) * VROW + key] = static_cast<bf16_t>(vv[p] & 0xffffu);
-        vt[(ch * 8 + 2 * p + 1) * VROW + key] = static_cast<bf16_t>(vv[p] >> 16);
+        // dims ch*8 + 2p (low halves) and ch*8 + 2p + 1 (high halves)
+        const uint2 lo = make_uint2((w[0][p] & 0xffffu) | (w[1][p] << 16),
+                                    (w[2][p] & 0xffffu) | (w[3][p] << 16));
+        const uint2 hi = make_uint2((w[0][p] >> 16) | (w[1][p] & 0xffff0000u),
+                                    (w[2][p] >> 16) | (w[3][p] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&vt[(ch * 8 + 2 * p) * VROW + kg * 4]) = lo;
+        *reinterpret_cast<uint2*>(&vt[(ch * 8 + 2 * p + 1) * VROW + kg * 4]) = hi;
       }
     }
     __syncthreads();
+    if (t0 + TK < t_end) fetch(t0 + TK);
 
-    // K fragments of the four key blocks (A operand)
-    uint4 ka[4][KS];
+    // S^T blocks: key block outer, so one K fragment serves every row block
+    f32x4_t sv[RBW][4];
 #pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4)
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      uint4 ka[KS];
 #pragma unroll
       for (int s2 = 0; s2 < KS; ++s2)
-        ka[kb4][s2] = *reinterpret_cast<const uint4*>(&kt[(kb4 * 16 + col) * KROW + s2 * 32 + quad * 8]);
-    // V^T fragments: dim row c*16 + col, keys (pair*32) + {4*quad .. +3, 16 + 4*quad .. +3}
-    uint4 va[2][CB];
+        ka[s2] = *reinterpret_cast<const uint4*>(&kt[(kb4 * 16 + col) * KROW + s2 * 32 + quad * 8]);
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const bf16_t* vr = &vt[(c * 16 + col) * VROW + pr * 32 + quad * 4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-        va[pr][c] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      f32x4_t sv[4];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
+      for (int i = 0; i < RBW; ++i) {
         f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) a = mfma16x16x32(ka[kb4][s2], qb[i][s2], a);
+        for (int s2 = 0; s2 < KS; ++s2) a = mfma16x16x32(ka[s2], qb[i][s2], a);
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv)
           if (t0 + kb4 * 16 + quad * 4 + vv >= t_end) a[vv] = -INFINITY;
-        sv[kb4] = a;
+        sv[i][kb4] = a;
       }
-      float tmax = sv[0][0];
+    }
+    // online softmax per row block; probabilities packed to bf16 pairs
+    uint32_t pk[RBW][4][2];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      float tmax = sv[i][0][0];
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) tmax = fmaxf(tmax, sv[kb4][vv]);
+        for (int vv = 0; vv < 4; ++vv) tmax = fmaxf(tmax, sv[i][kb4][vv]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mn = fmaxf(m[i], tmax * scale2);
-      if (mn == -INFINITY) continue;  // whole tile masked (cannot happen for valid rows)
-      const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
-      m[i] = mn;
+      // a fully masked tile only happens past a row's last key: nothing to add
+      const bool live = mn != -INFINITY;
+      const float alpha = live ? __builtin_amdgcn_exp2f(m[i] - mn) : 1.0f;
       float ps = 0.0f;
-      uint32_t pk[4][2];  // bf16 pairs of the probabilities, per key block
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4) {
         float p[4];
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) {
-          p[vv] = __builtin_amdgcn_exp2f(fmaf(sv[kb4][vv], scale2, -mn));
+          p[vv] = live ? __builtin_amdgcn_exp2f(fmaf(sv[i][kb4][vv], scale2, -mn)) : 0.0f;
           ps += p[vv];
         }
-        pk[kb4][0] = f32_to_bf16(p[0]) | (static_cast<uint32_t>(f32_to_bf16(p[1])) << 16);
-        pk[kb4][1] = f32_to_bf16(p[2]) | (static_cast<uint32_t>(f32_to_bf16(p[3])) << 16);
+        pk[i][kb4][0] = pack2_bf16(p[0], p[1]);
+        pk[i][kb4][1] = pack2_bf16(p[2], p[3]);
       }
+      if (live) m[i] = mn;
       s[i] = s[i] * alpha + ps;
 #pragma unroll
       for (int c = 0; c < CB; ++c) o[i][c] *= alpha;
+    }
+    // O^T += V^T P^T: one V^T fragment serves every row block
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const uint4 pb = make_uint4(pk[2 * pr][0], pk[2 * pr][1], pk[2 * pr + 1][0], pk[2 * pr + 1][1]);
+    for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
-        for (int c = 0; c < CB; ++c) o[i][c] = mfma16x16x32(va[pr][c], pb, o[i][c]);
+      for (int c = 0; c < CB; ++c) {
+        const bf16_t* vr = &vt[(c * 16 + col) * VROW + pr * 32 + quad * 4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          const uint4 pb = make_uint4(pk[i][2 * pr][0], pk[i][2 * pr][1], pk[i][2 * pr + 1][0],
+                                      pk[i][2 * pr + 1][1]);
+          o[i][c] = mfma16x16x32(va, pb, o[i][c]);
+        }
       }
     }
   }
@@ -584,12 +628,21 @@ void dispatch_tile(const void* q, const SegTable& st, int n_seg, int64_t n_split
 
 }  // namespace
 
+int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv) {
+  (void)H;
+  (void)D;
+  // the matrix-core variant runs tall query blocks: longer splits leave fewer
+  // (m, s, o) partials to write and merge
+  return dtype == KVSEL_BF16 && rows_per_kv >= 16 ? 1024 : kDecodeSplit;
+}
+
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
                   int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
                   float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s,
                   const DecodeGather* gather) {
   SegTable st{};
   st.gather_seg = -1;
+  st.split_len = decode_split_len(dtype, H, D, (Hq / H) * T);
   if (gather != nullptr) {
     // only the streaming variant gathers on the fly
     if (!stream_path_ok(dtype, H, D, (Hq / H) * T)) {
@@ -627,20 +680,18 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
 #undef KVSEL_DS
   }
   if (!done && dtype == KVSEL_BF16 && R >= 16) {
-    const MfmaRowPlan p = mfma_row_plan(R);
+    // one row block per wave; two waves for up to two row blocks, eight for
+    // 16 or more, else four; taller query blocks run in passes
     const int64_t rbs = (R + 15) / 16;
-    // row blocks per wave: at most 2 (output accumulators live in registers)
-    const int rbw = rbs >= 8 ? 2 : 1;
-    const int nwaves = static_cast<int>(rbs < 4 ? rbs : 4);
-    const int passes = static_cast<int>((rbs + nwaves * rbw - 1) / (nwaves * rbw));
-    (void)p;
+    const int nwaves = rbs <= 2 ? 2 : (rbs >= 16 ? 8 : 4);
+    const int passes = static_cast<int>((rbs + nwaves - 1) / nwaves);
     const dim3 grid(static_cast<unsigned>(B * H * passes * n_split)), block(64 * nwaves);
-#define KVSEL_DM(D_, RBW_) \
-    hipLaunchKernelGGL((decode_mfma_kernel<D_, RBW_>), grid, block, 0, s, static_cast<const bf16_t*>(q), st, \
+#define KVSEL_DM(D_, NW_) \
+    hipLaunchKernelGGL((decode_mfma_kernel<D_, 1, NW_>), grid, block, 0, s, static_cast<const bf16_t*>(q), st, \
                        n_seg, n_split, static_cast<int>(H), static_cast<int>(T), static_cast<int>(Hq), scale2, \
                        passes, ws_ms, ws_o)
-    if (D == 128) { if (rbw == 2) KVSEL_DM(128, 2); else KVSEL_DM(128, 1); }
-    else { if (rbw == 2) KVSEL_DM(64, 2); else KVSEL_DM(64, 1); }
+    if (D == 128) { if (nwaves == 2) KVSEL_DM(128, 2); else if (nwaves == 8) KVSEL_DM(128, 8); else KVSEL_DM(128, 4); }
+    else { if (nwaves == 2) KVSEL_DM(64, 2); else if (nwaves == 8) KVSEL_DM(64, 8); else KVSEL_DM(64, 4); }
 #undef KVSEL_DM
     done = true;
   }

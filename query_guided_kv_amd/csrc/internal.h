@@ -14,7 +14,8 @@ namespace kvsel {
 constexpr int kMaxSegments = 4;
 // Rows of one score / aggregate tile partial when unit_len == 1.
 constexpr int kTokenTile = 256;
-// Keys per split of the final attention pass.
+// Keys per split of the final attention pass (streaming and tile variants;
+// decode_split_len gives the length a call actually uses).
 constexpr int kDecodeSplit = 512;
 
 int launch_reposition(const void* k_in, void* k_out, const kvsel_cache& kc, int64_t unit_len,
@@ -102,6 +103,7 @@ struct DecodeGather {
   void* k_dst;
   void* v_dst;
 };
+int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
                   int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
                   float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s,
