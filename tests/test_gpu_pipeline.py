@@ -209,3 +209,54 @@ def test_full_serving_sampled_instances():
         one = {key: got[key][b:b + 1] for key in ("idx", "unit_score", "k_gather", "v_gather",
                                                    "o", "lse")}
         check_against_oracle(wi, one, want, [inp["planted"][b]])
+
+
+# ---------------------------------------------------------------------------
+# degenerate cases of the method
+# ---------------------------------------------------------------------------
+
+def check_tied_or_full(w, got: dict, want: dict):
+    """Index sets bit-exact (the tie rule makes them unique), scores and
+    outputs to tolerance; no margin requirement."""
+    idx = got["idx"].cpu().numpy().astype(np.int64)
+    assert np.array_equal(idx, want["idx"]), "kept index sets differ"
+    assert_rel(got["unit_score"], want["unit_score"], 2e-3, 0.0, "unit_score")
+    if w.decode:
+        assert_rel(got["o"], want["o"], 0.0, 5e-3, "decode output")
+        assert_rel(got["lse"], want["lse"], 0.0, 2e-3, "lse")
+
+
+@pytest.mark.parametrize("name", ["serving_small", "docs_small", "bilayer_small", "tiny"])
+def test_path_zero_query_all_tied(name):
+    """q = 0: every logit is 0, the attention is uniform and every unit's
+    score is the same number, so the kept set is the k lowest indices
+    ([ACRE Eq. 16] under the tie rule) and the output is the mean value row."""
+    w = SMALL[name]()
+    announce("path_zero_query", workload=name)
+    dev = device()
+    inp = synth.generate(w, 0, dev)
+    inp["q"] = torch.zeros_like(inp["q"])
+    got = pipeline.Path(w, inp)(inp["q"])
+    torch.cuda.synchronize()
+    want = OP.run(w, inp)
+    for g in range(len(want["idx"])):
+        assert np.array_equal(want["idx"][g], np.arange(w.k)), "oracle tie rule"
+    s = got["unit_score"].cpu().numpy()
+    assert np.all(s == s[:, :1]), "GPU scores are not exactly tied"
+    check_tied_or_full(w, got, want)
+
+
+@pytest.mark.parametrize("name", ["serving_small", "docs_small"])
+def test_path_keep_every_unit(name):
+    """k = M: the compact cache is the whole cache (in unit order), so the
+    final pass is full attention over every cached row."""
+    base = SMALL[name]()
+    w = base.scaled(k=base.M)
+    announce("path_keep_all", workload=name, k=w.k)
+    dev = device()
+    inp = synth.generate(w, 1, dev)
+    got = pipeline.Path(w, inp)(inp["q"])
+    torch.cuda.synchronize()
+    want = OP.run(w, inp)
+    assert np.array_equal(got["idx"].cpu().numpy(), np.tile(np.arange(w.M), (w.B // w.group, 1)))
+    check_tied_or_full(w, got, want)
