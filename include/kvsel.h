@@ -10,7 +10,9 @@
  *   [InfoFlow]   "InfoFlow KV: Information-Flow-Aware KV Recomputation for Long
  *                 Context" (arXiv 2603.05353)
  * in six calls: re-position -> score -> aggregate -> top-k -> gather/refill ->
- * decode attention.
+ * decode attention, plus two calls that fuse neighbouring steps with results
+ * defined as those of the pair they replace (kvsel_score_reposition,
+ * kvsel_gather_decode).
  *
  * Conventions for every call
  * --------------------------
@@ -31,8 +33,10 @@
  *   and query token).  Hq must be a multiple of H; query head h reads kv head
  *   h / (Hq / H).
  * - Supported: head dim D in {64, 128}; dtype bf16 or fp32 (the query, the
- *   cache and any second cache of one call share the dtype).  Attention
- *   arithmetic is fp32 with fp32 accumulation; re-rotation is fp64.
+ *   cache and any second cache of one call share the dtype).  Dot products of
+ *   the cache dtype's operands accumulate in fp32 (packed bf16 dots or the
+ *   matrix cores for bf16); softmax arithmetic is fp32; re-rotation is fp64
+ *   with one rounding to the cache dtype.
  * - A "unit" is unit_len consecutive cached rows: a chunk, a document, an L1
  *   entry's L2 block, or a single token (unit_len = 1).  N must be a multiple
  *   of unit_len; M = N / unit_len.
@@ -260,7 +264,10 @@ int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc,
  * over the concatenation of the n_seg segments (a HOST array; all share B, H,
  * D and dtype with the query), no mask.  Output fp32 [B][T][Hq][D]; lse (fp32
  * [B][Hq][T], natural log of sum_t exp(l)) or NULL.  1 <= n_seg <= 4; every
- * segment has N >= 1.
+ * segment has N >= 1.  For bf16 query blocks with >= 16 rows per kv head the
+ * pass runs on the matrix cores and the attention weights exp(l - max) are
+ * rounded to bf16 before they multiply V (the sum that normalises them is
+ * fp32).
  *   ws  kvsel_decode_workspace(...) bytes (returns 0 for invalid arguments).
  */
 int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale,

@@ -597,7 +597,9 @@ __global__ void decode_merge_kernel(const float* __restrict__ ws_ms, const float
 template <int D, int H, int R>
 void launch_stream(const void* q, const SegTable& st, int n_seg, int64_t n_split, int64_t B,
                    int64_t T, int64_t Hq, float scale2, float* ms, float* o, hipStream_t s) {
-  hipLaunchKernelGGL((decode_stream_kernel<D, H, R, 4>), dim3(static_cast<unsigned>(B * n_split)),
+  // 8 rows in flight per slot measured ~3.5% faster than 4 on the serving
+  // shape (<= 4 query rows per kv head); 8 query rows keep 4
+  hipLaunchKernelGGL((decode_stream_kernel<D, H, R, (R >= 8 ? 4 : 8)>), dim3(static_cast<unsigned>(B * n_split)),
                      dim3(kThreads), 0, s, static_cast<const bf16_t*>(q), st, n_seg, n_split,
                      static_cast<int>(T), static_cast<int>(Hq), scale2, ms, o);
 }
