@@ -13,10 +13,12 @@ kept rows.
 Prints one JSON line:
   value       cached KV token-rows scored and selected per second (B x N per
               step / step time);
-  roofline    the dominant kernel's algorithmic bytes per launch over its
-              average launch time (HIP events on its launch stream), against
-              MI355X's 8 TB/s; traffic is the HBM bytes the counters measured
-              for that kernel (null when no measurement matches the source);
+  roofline    the dominant (longest) stage's kernel: its algorithmic bytes (or
+              flops, where it runs on the matrix cores above the bf16 ridge)
+              per launch over its average launch time (HIP events on its
+              launch stream), against MI355X's 8 TB/s (or 2.5 PFLOP/s bf16);
+              traffic is the HBM bytes the counters measured for that kernel
+              (null when no measurement matches the source);
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -37,6 +39,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak, vendor figure
+MFMA_RIDGE = MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop per byte
 DEFAULT_WORKLOAD = "serving_16req_8l_128k"
 PROFILES = os.path.join(ROOT, "profiles")
 # kernel sources whose hash keys a stored counter measurement
@@ -70,50 +74,72 @@ def elem_bytes(w) -> int:
     return 2 if w.dtype == "bf16" else 4
 
 
-def stage_bytes(w) -> dict:
-    """Algorithmic HBM bytes of one step, per stage: every distinct region
-    counted once (the scored keys read once, the values once if their norm is
-    needed, the re-positioned keys written once where they are a product, the
-    kept rows read once and the compact cache written once).  Re-reads are
-    implementation cost and are not counted."""
+def one_pass_decode(w) -> bool:
+    """True where refill and decode attention run as one kernel (the streaming
+    decode reads each kept row through the index, writes it to the compact
+    cache and attends to it): bf16, head dim 128, <= 8 kv heads and 1, 2, 4
+    or 8 query rows per kv head."""
+    rows = (w.Hq // w.H) * w.T
+    return w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8) and w.H in (1, 2, 4, 8)
+
+
+def mfma_shape(w) -> bool:
+    """Shapes whose scoring and decode run on the matrix cores."""
+    return w.dtype == "bf16" and (w.Hq // w.H) * w.T >= 16
+
+
+def stage_work(w) -> dict:
+    """Algorithmic work of one step, per stage: ``(bytes, flops)``.
+
+    Bytes count every distinct region once (the scored keys read once, the
+    values once if their norm is needed, the re-positioned keys written once
+    where they are a product, the kept rows read once and the compact cache
+    written once); re-reads are implementation cost.  Flops are the products
+    the stage needs: 2 per multiply-add of the query-key logits (scoring) and
+    of both attention products (decode); re-computation is not counted."""
     row = w.H * w.D * elem_bytes(w)
     rows = w.B * w.N
-    out = {s: 0 for s in ("score", "aggregate", "topk", "gather", "decode")}
-    fused = w.decode and not w.align
-    out["score"] = rows * row                       # keys read by the scoring pass
+    qk = 2 * w.B * w.Hq * w.T * w.N * w.D          # one pass of query x cached keys
+    out = {"score": [rows * row, qk]}
     if w.reposition != "none" and not w.align:
-        out["score"] += rows * row                  # re-positioned keys written (a product)
-    if w.signal == "vnorm":
-        out["aggregate"] += rows * row              # values read for their norms
-    out["topk"] = (w.B // w.group) * w.M * 4
+        out["score"][0] += rows * row               # re-positioned keys written (a product)
+    out["aggregate"] = [rows * row if w.signal == "vnorm" else 0, 0]   # values for their norms
+    out["topk"] = [(w.B // w.group) * w.M * 4, 0]
     if w.decode:
         per_unit = w.refill_interval if w.refill_interval else w.unit_len
-        kept = w.B * w.k * per_unit * row
-        out["gather"] = 2 * 2 * kept                # K and V, read and written
-        if w.refill_interval:
-            out["decode"] = rows * row              # L1 values read by the final pass
-    if fused:                                       # one call: refill + attention
-        out["gather_decode"] = out.pop("gather") + out.pop("decode")
-    elif not w.decode:
-        del out["gather"], out["decode"]
-    return out
+        kept_rows = w.k * per_unit
+        keys = kept_rows + (w.N if w.refill_interval else 0)   # ACRE attends L1 + refilled rows
+        gather = [2 * 2 * w.B * kept_rows * row, 0]            # K and V, read and written
+        decode = [(w.B * w.N * row if w.refill_interval else 0),  # L1 values (keys: scoring)
+                  4 * w.B * w.Hq * w.T * keys * w.D]
+        if one_pass_decode(w) and not w.align:                 # one call: refill + attention
+            out["gather_decode"] = [gather[0] + decode[0], decode[1]]
+        else:
+            out["gather"], out["decode"] = gather, decode
+    return {s: tuple(v) for s, v in out.items()}
 
 
-def dominant_stage(w, sb: dict) -> str:
-    return max(sb, key=lambda s: sb[s])
+def stage_bound(stage: str, w, work) -> tuple:
+    """(bound, algorithmic quantity, peak, unit) of a stage: the matrix cores
+    where the stage runs on them and its flops per algorithmic byte exceed the
+    bf16 ridge of MI355X (2.5 PFLOP/s over 8 TB/s = 312.5), else HBM."""
+    nbytes, flops = work
+    if mfma_shape(w) and stage in ("score", "decode") and flops > MFMA_RIDGE * max(nbytes, 1):
+        return "mfma", flops / 1e12, MFMA_BF16_TFLOPS, "TFLOP/s"
+    return "hbm", nbytes / 1e9, HBM_PEAK_GBPS, "GB/s"
 
 
 def kernel_of(stage: str, w) -> str:
-    """Name of the kernel that carries a stage's bytes for workload w."""
+    """Name of the kernel that carries a stage's work for workload w."""
     rows = (w.Hq // w.H) * w.T
     stream = w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
-    mfma = w.dtype == "bf16" and rows >= 16
+    mfma = mfma_shape(w)
     return {"score": "score_stream_kernel" if stream else
                      "score_mfma_kernel" if mfma else "score_tile_kernel",
             "aggregate": "agg_mfma_kernel" if mfma else "agg_token_kernel",
             "topk": "topk_kernel", "gather": "gather_kernel",
             "decode": "decode_mfma_kernel" if mfma else "decode_stream_kernel",
-            "gather_decode": "decode_stream_kernel" if stream else "gather_kernel"}[stage]
+            "gather_decode": "decode_stream_kernel"}[stage]
 
 
 def stored_traffic(kernel: str, workload: str):
@@ -230,8 +256,7 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"{args.warmup} warm-up steps done")
 
-    sb = stage_bytes(w)
-    dom = dominant_stage(w, sb)
+    work = stage_work(w)
     marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for s in path.stages} for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -249,12 +274,14 @@ def main() -> int:
 
     stage_ms = {s: statistics.mean(m[s][0].elapsed_time(m[s][1]) for m in marks)
                 for s in path.stages}
+    dom = max(path.stages, key=lambda s: stage_ms[s])     # the stage that takes longest
     dom_ms = stage_ms[dom]
-    achieved = sb[dom] / (dom_ms * 1e-3) / 1e9
+    bound, quantity, peak, unit = stage_bound(dom, w, work[dom])
+    achieved = quantity / (dom_ms * 1e-3)
     kernel = kernel_of(dom, w)
     traffic = stored_traffic(kernel, w.name)
     rows = w.B * w.N
-    path_bytes = sum(sb.values())
+    path_bytes = sum(b for b, _ in work.values())
 
     result = {
         "metric": "cached KV tokens scored+selected per second",
@@ -272,10 +299,10 @@ def main() -> int:
         "config": {"workload": w.name, "instances": w.B, "cached_rows_per_instance": w.N,
                    "q_heads": w.Hq, "kv_heads": w.H, "head_dim": w.D, "query_tokens": w.T,
                    "unit_len": w.unit_len, "kept_units": w.k, "seed": args.seed},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": kernel, "stage": dom,
-                     "algorithmic_bytes_per_launch": sb[dom], "avg_launch_ms": dom_ms},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic, "kernel": kernel,
+                     "stage": dom, "algorithmic_bytes_per_launch": work[dom][0],
+                     "algorithmic_flops_per_launch": work[dom][1], "avg_launch_ms": dom_ms},
         "path_hbm": {"algorithmic_bytes_per_step": path_bytes,
                      "achieved_GBps": path_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},

@@ -99,8 +99,13 @@ class Path:
         keep = self.delta is not None and not w.align
         self.k_rep = torch.empty_like(self.k) if keep else None
         self.chunk = w.unit_len > 1 and w.signal == "mass"
-        # without re-positioning on the way, gather and decode are one call
-        split = w.decode and w.align
+        # refill and attention are one call where one kernel does both (it
+        # reads each kept row once); the aligned gather re-positions on the way
+        rows = (w.Hq // w.H) * w.T
+        one_pass = (w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
+                    and w.H in (1, 2, 4, 8))
+        split = w.decode and (w.align or not one_pass)
+        self.split = split
         self.stages = tuple(s for s in self.STAGES
                             if (s not in ("gather", "decode") or split)
                             and (s != "gather_decode" or (w.decode and not split)))
@@ -149,18 +154,23 @@ class Path:
         mark("topk", 1)
         if not w.decode:
             return out
-        if w.align:
-            # re-positioned copy, then attention over it
+        if self.split:
+            # the copy (re-positioned for "align"), then attention over it
             mark("gather", 0)
-            gk, gv = K.gather(self.k, self.v, out["idx"], w.unit_len, w.group, align_base=0,
-                              rope_base=w.rope_base, style=w.rope_style)
+            if w.align:
+                gk, gv = K.gather(self.k, self.v, out["idx"], w.unit_len, w.group, align_base=0,
+                                  rope_base=w.rope_base, style=w.rope_style)
+            elif w.refill_interval:     # ACRE: L1 entry j -> its L2 block
+                gk, gv = K.gather(self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group)
+            else:
+                gk, gv = K.gather(k_score, self.v, out["idx"], w.unit_len, w.group)
             mark("gather", 1)
             mark("decode", 0)
-            out["o"], out["lse"] = K.decode_attn(q, [(gk, gv)], w.scale)
+            segs = [(self.k, self.v), (gk, gv)] if w.refill_interval else [(gk, gv)]
+            out["o"], out["lse"] = K.decode_attn(q, segs, w.scale)
             mark("decode", 1)
         else:
-            # refill and attention in one call (one pass over the kept rows
-            # where the shape allows it)
+            # refill and attention in one pass over the kept rows
             mark("gather_decode", 0)
             if w.refill_interval:       # ACRE: L1 entry j -> its L2 block, L1 kept as a segment
                 gk, gv, o, lse = K.gather_decode(q, self.l2[0], self.l2[1], out["idx"],
