@@ -43,7 +43,8 @@ __all__ = [
     "reposition", "logits", "attention_weights", "score", "combine_partials",
     "aggregate", "acre_mean_pool", "topk", "gather", "gather_aligned",
     "refill_nested", "decode_attention", "acre_k", "cf_group_size",
-    "cf_reuse_count", "cf_doc_starts", "cf_k_prune", "if_chunk_offsets",
+    "cf_reuse_count", "cf_doc_starts", "cf_k_prune", "cf_prune_layers",
+    "cf_keep_schedule", "cf_progressive_prune", "cf_final_cache", "if_chunk_offsets",
     "if_global_positions", "if_budget",
 ]
 
@@ -75,11 +76,14 @@ def round_bf16(x) -> np.ndarray:
 
 
 def round_to(x, dtype: str) -> np.ndarray:
-    """Round to the cache dtype ("bf16" or "fp32"), ties to even; float64 out."""
+    """Round to the cache dtype ("bf16" or "fp32"), ties to even; float64 out.
+    "fp64" leaves the values as they are."""
     if dtype == "bf16":
         return round_bf16(x)
     if dtype == "fp32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "fp64":     # no rounding (exact checks of the arithmetic)
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -446,6 +450,125 @@ def cf_k_prune(k: int, k_finish: int, L: int, n: int) -> float:
     """[CacheFocus App. C]: caches pruned per pruning layer,
     ``(k - k_finish) / (L / n)`` (L layers, pruning every n-th layer)."""
     return (k - k_finish) / (L / n)
+
+
+def cf_prune_layers(L: int, n: int) -> list:
+    """[CacheFocus §2.4]: a pruning operation runs at every n-th layer of the
+    pre-fill.  With layers counted from 0 these are layers n-1, 2n-1, ...;
+    ``L // n`` of them."""
+    return [l for l in range(L) if (l + 1) % n == 0]
+
+
+def cf_keep_schedule(k: int, k_finish: int, L: int, n: int) -> list:
+    """Caches left after each pruning layer.
+
+    [CacheFocus App. C]: each pruning layer removes ``k_prune = (k - k_finish) /
+    (L / n)`` caches, so that ``k_finish`` remain after the last one (worked
+    example: L=28, n=4, k=40, k_finish=5 gives 5).  Reading where that is not a
+    whole number: with P = ``L // n`` pruning layers, ``k - floor(p (k - k_finish)
+    / P)`` caches remain after the p-th, which removes exactly k_prune each time
+    when it is whole, leaves k_finish after the last, and otherwise spreads the
+    remainder so that no two pruning layers differ by more than one cache.
+    """
+    P = len(cf_prune_layers(L, n))
+    return [k - (p * (k - k_finish)) // P for p in range(1, P + 1)]
+
+
+def cf_progressive_prune(q_layers, k_layers, doc_len: int, scale: float, n: int,
+                         k_finish: int, window: int, base: float = 10000.0,
+                         style: str = "half", dtype: str = "bf16",
+                         score_after_last_prune: bool = True) -> dict:
+    """Layer-Adaptive Cache Pruning of [CacheFocus §2.4] for one request.
+
+    ``q_layers``: ``[L][T][Hq][D]``, the query block of every layer (already at
+    its positions); ``k_layers``: ``[L][k * doc_len][H][D]``, the k retrieved
+    document caches of every layer, document i in rows ``[i*doc_len,
+    (i+1)*doc_len)``, each stored at document-local positions ``0 .. doc_len-1``
+    ([CacheFocus §2.2]: every document cache is pre-computed on its own).
+
+    At every layer l:
+
+    1. the caches of the current cache IDs (ascending: the retrieval order) are
+       concatenated and re-positioned: the j-th gets the start position of
+       slot j under adaptive re-positioning (:func:`cf_doc_starts` with the
+       positional range ``window``, [CacheFocus §2.3.1]), token t of it goes
+       from position t to ``start_j + t`` (:func:`reposition`);
+    2. the layer's query attends the whole concatenation (:func:`attention_weights`);
+    3. the attention is accumulated document-wise ([CacheFocus §2.4 fn. 3]:
+       summed over heads, query tokens and the document's tokens) and added to
+       the document's running total.  Reading: the relevance S a pruning layer
+       uses is this total over all layers so far (the footnote's progressive
+       accumulation), not the pruning layer's own attention alone;
+    4. at a pruning layer (:func:`cf_prune_layers`), only the
+       :func:`cf_keep_schedule` count of caches with the largest totals stay
+       (ties: smaller cache ID), kept in ascending ID order.
+
+    After the last layer the remaining IDs are listed two ways ([CacheFocus
+    §2.5]): "align", ascending ID (positions follow continuity), and "sort",
+    by total with the most relevant last, i.e. nearest the query that follows
+    the caches (reading of the attention-guided allocation, after [CacheFocus
+    §2.5]'s point that relevant documents near the query help).  Layers after
+    the last pruning layer only change the "sort" order; with
+    ``score_after_last_prune=False`` they are not scored.
+
+    Returns a dict: ``ids`` (IDs present at each layer), ``mass`` (each
+    layer's document-wise attention, in the order of ``ids``), ``total``
+    (running totals after each layer, same order), ``starts`` (slot start
+    positions at each layer), ``final_align``, ``final_sort`` and
+    ``final_total`` (totals of ``final_align``).
+    """
+    q_layers = np.asarray(q_layers, dtype=np.float64)
+    k_layers = np.asarray(k_layers, dtype=np.float64)
+    L = q_layers.shape[0]
+    k = k_layers.shape[1] // doc_len
+    prune_at = dict(zip(cf_prune_layers(L, n), cf_keep_schedule(k, k_finish, L, n)))
+    last_prune = max(prune_at) if prune_at else -1
+    ids = np.arange(k, dtype=np.int64)
+    total = np.zeros(k, dtype=np.float64)          # by cache ID
+    out = {"ids": [], "mass": [], "total": [], "starts": []}
+    for l in range(L):
+        m = ids.size
+        if l > last_prune and not score_after_last_prune:
+            break
+        rows = (ids[:, None] * doc_len + np.arange(doc_len)[None, :]).reshape(-1)
+        starts = cf_doc_starts(m, doc_len, window)
+        p_old = np.tile(np.arange(doc_len), m)
+        p_new = np.repeat(starts, doc_len) + p_old
+        k_rep = reposition(k_layers[l][rows], p_old, p_new, base, style, dtype)
+        A = attention_weights(q_layers[l][None], k_rep[None], scale)[0]     # [Hq][T][m*doc_len]
+        mass = A.reshape(A.shape[0], A.shape[1], m, doc_len).sum(axis=(0, 1, 3))
+        total[ids] += mass
+        out["ids"].append(ids.copy())
+        out["mass"].append(mass)
+        out["total"].append(total[ids].copy())
+        out["starts"].append(starts)
+        if l in prune_at:
+            keep = topk(total[ids][None], prune_at[l])[0]     # positions in the current list
+            ids = ids[keep]
+    out["final_align"] = ids.copy()
+    by_relevance = np.lexsort((ids, -total[ids]))             # most relevant first
+    out["final_sort"] = ids[by_relevance[::-1]].copy()
+    out["final_total"] = total[ids].copy()
+    return out
+
+
+def cf_final_cache(k_layers, v_layers, final_ids, doc_len: int, start: int = 0,
+                   base: float = 10000.0, style: str = "half", dtype: str = "bf16"):
+    """The combined final cache of [CacheFocus §2.4]: for every layer, the
+    caches of ``final_ids`` (in that order) concatenated and re-positioned to
+    contiguous positions ``start + r * doc_len + t`` (slot r, token t; §2.5
+    assigns the remaining caches new consecutive positions).  Keys stored at
+    document-local positions; values are copied.  Returns ``(K, V)`` of shape
+    ``[L][len(final_ids) * doc_len][H][D]``."""
+    k_layers = np.asarray(k_layers, dtype=np.float64)
+    v_layers = np.asarray(v_layers, dtype=np.float64)
+    ids = np.asarray(final_ids, dtype=np.int64)
+    rows = (ids[:, None] * doc_len + np.arange(doc_len)[None, :]).reshape(-1)
+    p_old = np.tile(np.arange(doc_len), ids.size)
+    p_new = start + np.arange(ids.size * doc_len)
+    K = np.stack([reposition(k_layers[l][rows], p_old, p_new, base, style, dtype)
+                  for l in range(k_layers.shape[0])])
+    return K, v_layers[:, rows].copy()
 
 
 def if_chunk_offsets(chunk_lens: Iterable[int]) -> np.ndarray:
