@@ -44,7 +44,8 @@ __all__ = [
     "aggregate", "acre_mean_pool", "topk", "gather", "gather_aligned",
     "refill_nested", "decode_attention", "acre_k", "cf_group_size",
     "cf_reuse_count", "cf_doc_starts", "cf_k_prune", "cf_prune_layers",
-    "cf_keep_schedule", "cf_progressive_prune", "cf_final_cache", "if_chunk_offsets",
+    "cf_keep_schedule", "cf_progressive_prune", "cf_final_cache", "take", "order",
+    "if_chunk_offsets",
     "if_global_positions", "if_budget",
 ]
 
@@ -549,6 +550,38 @@ def cf_progressive_prune(q_layers, k_layers, doc_len: int, scale: float, n: int,
     by_relevance = np.lexsort((ids, -total[ids]))             # most relevant first
     out["final_sort"] = ids[by_relevance[::-1]].copy()
     out["final_total"] = total[ids].copy()
+    return out
+
+
+def take(src, idx) -> np.ndarray:
+    """Composition of index lists, ``out[g][j] = src[g][idx[g][j]]``
+    ([CacheFocus §2.4]: the cache IDs left after a pruning layer are the kept
+    positions of the current ID list).  ``-1`` where an index is outside
+    ``[0, m)``."""
+    src = np.asarray(src, dtype=np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
+    out = np.full(idx.shape, -1, dtype=np.int64)
+    for g in range(idx.shape[0]):
+        ok = (idx[g] >= 0) & (idx[g] < src.shape[1])
+        out[g, ok] = src[g, idx[g, ok]]
+    return out
+
+
+def order(scores, idx, descending: bool = True) -> np.ndarray:
+    """The given indices of each row listed by score ([CacheFocus §2.5]
+    attention-guided "sort" allocation).  Order: score descending, then index
+    ascending (the tie rule of :func:`topk`), then position in the given list;
+    ``descending=False`` lists the exact reverse (most relevant last).  An
+    index outside ``[0, M)`` ranks below every valid one."""
+    s = np.asarray(scores, dtype=np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    out = np.empty_like(idx)
+    for g in range(idx.shape[0]):
+        ok = (idx[g] >= 0) & (idx[g] < s.shape[1])
+        sc = np.where(ok, s[g, np.clip(idx[g], 0, s.shape[1] - 1)], 0.0)
+        pos = np.arange(idx.shape[1])
+        rank = np.lexsort((pos, idx[g], -sc, ~ok))        # last key is primary
+        out[g] = idx[g, rank] if descending else idx[g, rank[::-1]]
     return out
 
 

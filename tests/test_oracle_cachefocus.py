@@ -208,3 +208,40 @@ def test_layers_after_the_last_prune_only_change_the_order():
                                score_after_last_prune=False)
     assert list(a["final_align"]) == list(b["final_align"])
     assert len(a["mass"]) == 5 and len(b["mass"]) == 4
+
+
+def test_take_composes_index_lists():
+    src = np.array([[10, 11, 12, 13], [20, 21, 22, 23]])
+    idx = np.array([[3, 0], [1, 9]])
+    np.testing.assert_array_equal(O.take(src, idx), [[13, 10], [21, -1]])
+    # composing with the identity changes nothing; composing twice is composing the
+    # composed positions
+    ident = np.tile(np.arange(4), (2, 1))
+    np.testing.assert_array_equal(O.take(src, ident), src)
+    a = np.array([[2, 3, 1], [0, 2, 3]])
+    b = np.array([[2, 0], [1, 1]])
+    np.testing.assert_array_equal(O.take(O.take(src, a), b), O.take(src, O.take(a, b)))
+
+
+def test_order_lists_by_score():
+    rng = np.random.default_rng(8)
+    s = rng.random((3, 50))
+    idx = O.topk(s, 12)                                   # ascending index order
+    desc = O.order(s, idx, descending=True)
+    for g in range(3):
+        assert sorted(desc[g]) == sorted(idx[g])
+        vals = s[g, desc[g]]
+        assert np.all(np.diff(vals) <= 0)
+        assert desc[g, 0] == np.argmax(s[g])
+        # the k largest, largest first: the same list as a full descending sort
+        assert list(desc[g]) == list(np.argsort(-s[g], kind="stable")[:12])
+    np.testing.assert_array_equal(O.order(s, idx, descending=False), desc[:, ::-1])
+
+
+def test_order_ties_and_invalid_entries():
+    s = np.array([[1.0, 2.0, 2.0, 0.0, -0.0]])
+    # ties: smaller index first; -0.0 ties +0.0; repeated entries keep list order;
+    # out-of-range entries come last
+    idx = np.array([[4, 2, 7, 1, 3, 2]])
+    np.testing.assert_array_equal(O.order(s, idx), [[1, 2, 2, 3, 4, 7]])
+    np.testing.assert_array_equal(O.order(s, idx, descending=False), [[7, 4, 3, 2, 2, 1]])
