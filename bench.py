@@ -119,18 +119,52 @@ def stage_work(w) -> dict:
     return {s: tuple(v) for s, v in out.items()}
 
 
+def prune_scored_units(w) -> int:
+    """Documents scored per request over the layer loop of a pruning workload
+    (every layer scores the documents still present; layers after the last
+    pruning layer are scored only for the "sort" order)."""
+    from query_guided_kv_amd import host
+    prune = dict(zip(host.prune_layers(w.layers, w.prune_every),
+                     host.keep_schedule(w.M, w.k, w.layers, w.prune_every)))
+    last = max(prune) if prune else -1
+    n_scored = w.layers if w.allocation == "sort" else last + 1
+    m, total = w.M, 0
+    for l in range(n_scored):
+        total += m
+        m = prune.get(l, m)
+    return total
+
+
+def prune_stage_work(w) -> dict:
+    """(bytes, flops) per stage of the layer-wise pruning path: the select loop
+    reads the present documents' keys once per scored layer; the final gather
+    reads and writes the survivors' K and V for every layer; the decode pass
+    attends them (its reads are the gather's writes, counted there)."""
+    row = w.H * w.D * elem_bytes(w)
+    scored_rows = w.requests * prune_scored_units(w) * w.unit_len
+    kept_rows = w.B * w.k * w.unit_len
+    return {"select": (scored_rows * row, 2 * scored_rows * (w.Hq // w.H) * w.T * w.H * w.D),
+            "final_gather": (2 * 2 * kept_rows * row, 0),
+            "decode": (0, 4 * w.B * w.Hq * 1 * w.k * w.unit_len * w.D)}
+
+
 def stage_bound(stage: str, w, work) -> tuple:
     """(bound, algorithmic quantity, peak, unit) of a stage: the matrix cores
     where the stage runs on them and its flops per algorithmic byte exceed the
     bf16 ridge of MI355X (2.5 PFLOP/s over 8 TB/s = 312.5), else HBM."""
     nbytes, flops = work
-    if mfma_shape(w) and stage in ("score", "decode") and flops > MFMA_RIDGE * max(nbytes, 1):
+    rows = (w.Hq // w.H) * (1 if (w.recipe == "cachefocus" and stage == "decode") else w.T)
+    on_mfma = w.dtype == "bf16" and rows >= 16 and stage in ("score", "decode", "select")
+    if on_mfma and flops > MFMA_RIDGE * max(nbytes, 1):
         return "mfma", flops / 1e12, MFMA_BF16_TFLOPS, "TFLOP/s"
     return "hbm", nbytes / 1e9, HBM_PEAK_GBPS, "GB/s"
 
 
 def kernel_of(stage: str, w) -> str:
     """Name of the kernel that carries a stage's work for workload w."""
+    if w.recipe == "cachefocus":
+        return {"select": "score_mfma_kernel" if mfma_shape(w) else "score_stream_kernel",
+                "final_gather": "gather_kernel", "decode": "decode_tile_kernel"}[stage]
     rows = (w.Hq // w.H) * w.T
     stream = w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
     mfma = mfma_shape(w)
@@ -167,6 +201,29 @@ def make_queries(w, inp, n: int, seed: int, device):
     if w.recipe == "serving":
         return [synth.serving_queries(w, inp["topic"], seed, s, device) for s in range(n)]
     return [inp["q"]] * n
+
+
+def cpu_baseline_prune(w, inp, layers: int = 8) -> dict:
+    """The fp64 oracle's layer loop on request 0, first ``layers`` layers
+    (two pruning layers at n = 4), single-threaded; rate in scored token-rows
+    per second."""
+    from threadpoolctl import threadpool_limits
+    from oracle import kvsel_oracle as O
+    from oracle import pipeline as OP
+
+    L = min(layers, w.layers)
+    q = OP.to64(inp["q"][:L, 0])
+    k = OP.to64(inp["k"][:L])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        res = O.cf_progressive_prune(q, k, w.unit_len, w.scale, w.prune_every, w.k, w.window,
+                                     w.rope_base, w.rope_style, w.dtype)
+        elapsed = time.perf_counter() - t0
+    rows = sum(ids.size for ids in res["ids"]) * w.unit_len
+    log(f"cpu oracle: {L} layers of request 0 in {elapsed:.1f} s")
+    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"request 0, layers 0-{L - 1} of the pruning loop ({rows} scored "
+                      f"token-rows; fp64 numpy, 1 thread), {elapsed:.1f} s"}
 
 
 def cpu_baseline(w, inp, budget_s: float = 12.0, max_instances: int = 8) -> dict:
@@ -248,15 +305,20 @@ def main() -> int:
     inp = synth.generate(w, args.seed, dev)
     torch.cuda.synchronize()
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
-    queries = make_queries(w, inp, args.warmup + args.steps, args.seed, dev)
-    path = pipeline.Path(w, inp)
+    prune = w.recipe == "cachefocus"
+    path = pipeline.make_path(w, inp)
+    if prune:
+        step = lambda i, m=None: path(inp["q"], inp["q_dec"], m)
+    else:
+        queries = make_queries(w, inp, args.warmup + args.steps, args.seed, dev)
+        step = lambda i, m=None: path(queries[i], m)
 
     for i in range(args.warmup):
-        path(queries[i])
+        step(i)
     torch.cuda.synchronize()
     log(f"{args.warmup} warm-up steps done")
 
-    work = stage_work(w)
+    work = prune_stage_work(w) if prune else stage_work(w)
     marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for s in path.stages} for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -264,7 +326,7 @@ def main() -> int:
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        path(queries[args.warmup + i], marks[i])
+        step(args.warmup + i, marks[i])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -280,7 +342,9 @@ def main() -> int:
     achieved = quantity / (dom_ms * 1e-3)
     kernel = kernel_of(dom, w)
     traffic = stored_traffic(kernel, w.name)
-    rows = w.B * w.N
+    # token-rows scored per step: every cached row once, or for the pruning
+    # loop the rows of the documents present at each scored layer
+    rows = w.requests * prune_scored_units(w) * w.unit_len if prune else w.B * w.N
     path_bytes = sum(b for b, _ in work.values())
 
     result = {
@@ -296,9 +360,13 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded, planted relevant units; no datasets or weights)",
-        "config": {"workload": w.name, "instances": w.B, "cached_rows_per_instance": w.N,
-                   "q_heads": w.Hq, "kv_heads": w.H, "head_dim": w.D, "query_tokens": w.T,
-                   "unit_len": w.unit_len, "kept_units": w.k, "seed": args.seed},
+        "config": dict({"workload": w.name, "instances": w.B, "cached_rows_per_instance": w.N,
+                        "q_heads": w.Hq, "kv_heads": w.H, "head_dim": w.D,
+                        "query_tokens": w.T, "unit_len": w.unit_len, "kept_units": w.k,
+                        "seed": args.seed},
+                       **({"requests": w.requests, "layers": w.layers,
+                           "prune_every": w.prune_every, "allocation": w.allocation,
+                           "scored_rows_per_step": rows} if prune else {})),
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "kernel": kernel,
                      "stage": dom, "algorithmic_bytes_per_launch": work[dom][0],
@@ -310,7 +378,7 @@ def main() -> int:
     }
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w, inp)
+        result["cpu_baseline"] = cpu_baseline_prune(w, inp) if prune else cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -12,7 +12,10 @@
  * in six calls: re-position -> score -> aggregate -> top-k -> gather/refill ->
  * decode attention, plus two calls that fuse neighbouring steps with results
  * defined as those of the pair they replace (kvsel_score_reposition,
- * kvsel_gather_decode).
+ * kvsel_gather_decode).  Three more serve CacheFocus's layer-wise pruning
+ * (§2.4-2.5): kvsel_score_units scores a list of units of a cache, re-positioned
+ * to their slots, without copying them; kvsel_take composes index lists;
+ * kvsel_order lists a kept set by score.
  *
  * Conventions for every call
  * --------------------------
@@ -178,6 +181,44 @@ size_t kvsel_score_reposition_workspace(int64_t T, int64_t Hq, kvsel_cache kc,
                                         int32_t have_k_out);
 
 /*
+ * kvsel_score_units -- kvsel_score_reposition over a list of units of the
+ * cache: instance b scores the cache formed by concatenating, in list order,
+ * the n_units units units[b][0..n_units) of its own cache (unit_len rows each),
+ * with virtual unit j re-positioned by delta[j] (delta_per_instance: by
+ * delta[b][j]) positions, or not re-positioned when delta is NULL.  This is
+ * one layer of [CacheFocus §2.4]: the caches of the current cache IDs are
+ * concatenated, re-positioned (§2.3 / §2.3.1: each cache to its slot's
+ * start) and attended by the query.
+ *
+ * Results are those of copying the listed units into a compact cache of
+ * n_units * unit_len rows, kvsel_reposition on it with unit_len and delta,
+ * then kvsel_score: row_max/row_sum [B][Hq][T] over the n_units * unit_len
+ * scored rows, part [B][Hq][T][n_units][2] (segment j = virtual unit j).
+ * Where bf16 query blocks have >= 16 rows per kv head and unit_len (and the
+ * scoring segment, unit_len with part, else 256) is a multiple of 64, the
+ * listed units are read in place, rotated while staged and scored in one
+ * kernel (no copy); otherwise the copy goes through the workspace.
+ *   kc           the source caches (B instances of kc.N rows, any strides).
+ *   units        int32 [B][n_units]; each entry in [0, kc.N / unit_len)
+ *                (repeats allowed).  An entry outside that range reads no
+ *                memory; its rows' contribution is unspecified.
+ *   delta        int64 [n_units] or [B][n_units], or NULL; rope_base > 1 and
+ *                rope_style as kvsel_reposition when set.
+ *   ws           kvsel_score_units_workspace(...) bytes (may be 0 -> ws NULL).
+ *   other arguments as for kvsel_score.
+ */
+int kvsel_score_units(const void* q, int64_t T, int64_t Hq, const void* k,
+                      kvsel_cache kc, float scale, int64_t unit_len,
+                      const int32_t* units, int64_t n_units,
+                      const int64_t* delta, int32_t delta_per_instance,
+                      double rope_base, int32_t rope_style, float* row_max,
+                      float* row_sum, float* part, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+size_t kvsel_score_units_workspace(int64_t T, int64_t Hq, kvsel_cache kc,
+                                   int64_t unit_len, int64_t n_units,
+                                   int32_t want_row_stats, int32_t want_part);
+
+/*
  * kvsel_aggregate -- per-unit relevance from the softmax-normalised
  * attention, with alpha = exp(l - row_max) / row_sum:
  *   KVSEL_SIG_MASS:  S[g,u] = sum_{b in g} sum_h sum_j sum_{t in u} alpha
@@ -188,7 +229,10 @@ size_t kvsel_score_reposition_workspace(int64_t T, int64_t Hq, kvsel_cache kc,
  *                    alpha * ||v[b,t,kv(h),:]||_2
  *                    ([InfoFlow §4.2] attention-norm token score s_j = sum_i A_ij)
  * where group g is `group` consecutive instances (e.g. the layers whose scores
- * are summed).  Output unit_score fp32 [B/group][M].
+ * are summed).  Output unit_score fp32 [B/group][M].  With accumulate != 0
+ * the result is added to what unit_score holds (a running total over calls,
+ * [CacheFocus §2.4 footnote 3]: document-wise attention accumulated layer by
+ * layer); the call's own sum is formed first, in a fixed order, then added.
  *
  * Two paths:
  *  - chunk path (signal MASS and part != NULL): combines the partials of
@@ -202,8 +246,8 @@ int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k,
                     const void* v, kvsel_cache kc, float scale,
                     const float* row_max, const float* row_sum,
                     const float* part, int32_t signal, int64_t unit_len,
-                    int64_t group, float* unit_score, void* ws,
-                    size_t ws_bytes, hipStream_t stream);
+                    int64_t group, float* unit_score, int32_t accumulate,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
 size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T,
                                  int64_t unit_len, int32_t chunk_path,
                                  int32_t have_row_stats);
@@ -216,11 +260,44 @@ size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T,
  * scores are not allowed.  The k kept indices are written in ASCENDING index
  * order (the order-preserving refill of [ACRE Eq. 18-19]).
  *   score  fp32 [G][M];  idx int32 [G][k];  val fp32 [G][k] (score of each
- *   kept index, same order) or NULL.  0 <= k <= M, M < 2^31.  k == 0 is a
- *   no-op.
+ *   kept index, same order) or NULL.  0 <= k <= M, M < 2^31, G < 2^21.
+ *   k == 0 is a no-op.
  */
 int kvsel_topk(const float* score, int64_t G, int64_t M, int64_t k,
                int32_t* idx, float* val, hipStream_t stream);
+
+/*
+ * kvsel_take -- out[g][j] = src[g][idx[g][j]] for j < k: composes two index
+ * lists, e.g. the positions kvsel_topk kept in the current list of cache IDs
+ * with that list, giving the cache IDs left after a pruning layer
+ * ([CacheFocus §2.4]).
+ *   src   int32 [G][m];  idx int32 [G][k];  out int32 [G][k], not overlapping
+ *   src or idx.  An idx entry outside [0, m) gives -1.  G * k < 2^31.
+ *   k == 0 is a no-op.
+ */
+int kvsel_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx,
+               int64_t k, int32_t* out, hipStream_t stream);
+
+/*
+ * kvsel_order -- list k given indices of each row by their scores
+ * ([CacheFocus §2.5] attention-guided "sort" allocation: the remaining caches
+ * are placed in order of their aggregated attention).
+ *
+ * Rank of an entry = number of entries before it in the order (score
+ * descending, index ascending, list position ascending): the same order as
+ * kvsel_topk, made total.  descending != 0: idx_out[g][r] is the entry of
+ * rank r (most relevant first); descending == 0: the exact reverse (most
+ * relevant last, i.e. nearest a query that follows the caches).
+ *   score    fp32 [G][M];  idx int32 [G][k] (entries in [0, M); an entry
+ *            outside ranks as the lowest score and gets value 0).
+ *   idx_out  int32 [G][k], not overlapping idx;  val_out fp32 [G][k] (the
+ *            score of each listed index) or NULL.  k == 0 is a no-op.
+ *   G * ceil(k / 256) < 2^23.  Cost: k^2 comparisons per row (meant for
+ *   kept sets, not whole caches).
+ */
+int kvsel_order(const float* score, int64_t G, int64_t M, const int32_t* idx,
+                int64_t k, int32_t descending, int32_t* idx_out,
+                float* val_out, hipStream_t stream);
 
 /*
  * kvsel_gather -- copy the kept units into a compact cache ("refill",

@@ -22,8 +22,9 @@ constexpr int kThreads = 256;
 
 // Chunk path, stage 1: workgroup (g, row chunk, unit chunk); 64 units x 4 row
 // lanes; each lane sums every 4th row of the chunk, the four lanes merge in
-// LDS.  Writes out[g][u] directly when one chunk covers the group's rows,
-// else a partial ws[(g * n_rc + rc) * M + u] for stage 2.
+// LDS.  Writes out[g][u] directly when one chunk covers the group's rows
+// (added to the value there with `accumulate`), else a partial
+// ws[(g * n_rc + rc) * M + u] for stage 2.
 constexpr int kAggUnits = 64;
 constexpr int kAggRowLanes = kThreads / kAggUnits;
 constexpr int kAggChunkRows = 64;
@@ -31,7 +32,7 @@ constexpr int kAggChunkRows = 64;
 __global__ void __launch_bounds__(kThreads)
 agg_chunk_kernel(const float* __restrict__ part, const float* __restrict__ row_max,
                  const float* __restrict__ row_sum, int64_t rows_per_g, int64_t M, int64_t n_rc,
-                 int64_t n_uc, float* __restrict__ dst) {
+                 int64_t n_uc, int accumulate, float* __restrict__ dst) {
   __shared__ float red[kAggRowLanes][kAggUnits];
   const int64_t uc = blockIdx.x % n_uc;
   const int64_t rc = (blockIdx.x / n_uc) % n_rc;
@@ -54,20 +55,22 @@ agg_chunk_kernel(const float* __restrict__ part, const float* __restrict__ row_m
     float t = red[0][ul];
 #pragma unroll
     for (int i = 1; i < kAggRowLanes; ++i) t += red[i][ul];
-    dst[(gi * n_rc + rc) * M + u] = t;
+    float* o = dst + (gi * n_rc + rc) * M + u;
+    *o = accumulate ? *o + t : t;
   }
 }
 
-// Chunk path, stage 2: out[g][u] = sum over row chunks, in order.
+// Chunk path, stage 2: out[g][u] = sum over row chunks, in order (added to
+// out[g][u] with `accumulate`).
 __global__ void __launch_bounds__(kThreads)
 agg_chunk_sum_kernel(const float* __restrict__ ws, int64_t G, int64_t M, int64_t n_rc,
-                     float* __restrict__ out) {
+                     int accumulate, float* __restrict__ out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= G * M) return;
   const int64_t gi = i / M, u = i % M;
   float t = 0.0f;
   for (int64_t rc = 0; rc < n_rc; ++rc) t += ws[(gi * n_rc + rc) * M + u];
-  out[i] = t;
+  out[i] = accumulate ? out[i] + t : t;
 }
 
 constexpr int kQRows = 64;
@@ -149,10 +152,11 @@ agg_token_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   if (t_ok && p == 0) per_token[b * N + t] = acc;
 }
 
-// unit_score[g][u] = sum_{b in g} sum_{t in u} per_token[b][t], fixed order.
+// unit_score[g][u] = sum_{b in g} sum_{t in u} per_token[b][t], fixed order
+// (added to unit_score[g][u] with `accumulate`).
 __global__ void __launch_bounds__(kThreads)
 unit_sum_kernel(const float* __restrict__ per_token, int64_t N, int64_t unit_len, int64_t M,
-                int64_t group, int64_t mblocks, float* __restrict__ out) {
+                int64_t group, int64_t mblocks, int accumulate, float* __restrict__ out) {
   const int64_t gi = blockIdx.x / mblocks;
   const int64_t u = (blockIdx.x % mblocks) * kThreads + threadIdx.x;
   if (u >= M) return;
@@ -161,7 +165,7 @@ unit_sum_kernel(const float* __restrict__ per_token, int64_t N, int64_t unit_len
     const float* pt = per_token + (gi * group + bi) * N + u * unit_len;
     for (int64_t t = 0; t < unit_len; ++t) acc += pt[t];
   }
-  out[gi * M + u] = acc;
+  out[gi * M + u] = accumulate ? out[gi * M + u] + acc : acc;
 }
 
 template <typename T, int D, int TPR>
@@ -189,19 +193,20 @@ void launch_tok(const void* q, int64_t T_, int64_t Hq, const void* k, const void
 
 int launch_aggregate_chunks(const float* part, const float* row_max, const float* row_sum,
                             int64_t B, int64_t Hq, int64_t T, int64_t M, int64_t group,
-                            float* unit_score, float* ws, hipStream_t s) {
+                            float* unit_score, int accumulate, float* ws, hipStream_t s) {
   const int64_t G = B / group;
   const int64_t rows_per_g = group * Hq * T;
   const int64_t n_rc = (rows_per_g + kAggChunkRows - 1) / kAggChunkRows;
   const int64_t n_uc = (M + kAggUnits - 1) / kAggUnits;
   float* dst = n_rc == 1 ? unit_score : ws;
   hipLaunchKernelGGL(agg_chunk_kernel, dim3(static_cast<unsigned>(G * n_rc * n_uc)),
-                     dim3(kThreads), 0, s, part, row_max, row_sum, rows_per_g, M, n_rc, n_uc, dst);
+                     dim3(kThreads), 0, s, part, row_max, row_sum, rows_per_g, M, n_rc, n_uc,
+                     n_rc == 1 ? accumulate : 0, dst);
   if (n_rc > 1) {
     const int rc = check_launch("kvsel_aggregate");
     if (rc != KVSEL_OK) return rc;
     hipLaunchKernelGGL(agg_chunk_sum_kernel, dim3(static_cast<unsigned>((G * M + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, s, ws, G, M, n_rc, unit_score);
+                       dim3(kThreads), 0, s, ws, G, M, n_rc, accumulate, unit_score);
   }
   return check_launch("kvsel_aggregate");
 }
@@ -230,11 +235,12 @@ int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k,
 }
 
 int launch_unit_sums(const float* per_token, int64_t B, int64_t N, int64_t unit_len,
-                     int64_t group, float* unit_score, hipStream_t s) {
+                     int64_t group, float* unit_score, int accumulate, hipStream_t s) {
   const int64_t M = N / unit_len;
   const int64_t mblocks = (M + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(unit_sum_kernel, dim3(static_cast<unsigned>((B / group) * mblocks)),
-                     dim3(kThreads), 0, s, per_token, N, unit_len, M, group, mblocks, unit_score);
+                     dim3(kThreads), 0, s, per_token, N, unit_len, M, group, mblocks, accumulate,
+                     unit_score);
   return check_launch("kvsel_aggregate (unit sums)");
 }
 

@@ -40,6 +40,12 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// do the byte ranges [a, a + na) and [b, b + nb) share a byte?
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
 int check_cache(const kvsel_cache& kc, const char* what) {
   if (kc.dtype != KVSEL_BF16 && kc.dtype != KVSEL_FP32)
     return fail(KVSEL_ERR_DTYPE, "%s: dtype %d is neither bf16 nor fp32", what, kc.dtype);
@@ -187,6 +193,23 @@ size_t score_rot_ws(int64_t T, int64_t Hq, const kvsel_cache& kc, int64_t unit_l
   return round256(base) + static_cast<size_t>(kc.B * kc.stride_b) * esz;
 }
 
+// kvsel_score_units takes the matrix-core scorer, which reads the listed
+// units in place, when a unit is a whole number of 64-key tiles; otherwise the
+// units are copied to the workspace first.
+bool score_units_mfma(int dtype, int64_t rows_per_kv, int64_t seg_len, int64_t unit_len) {
+  return score_mfma_ok(dtype, rows_per_kv, seg_len) && unit_len % kMfmaTileKeys == 0;
+}
+
+size_t score_units_ws(int64_t T, int64_t Hq, const kvsel_cache& kc, int64_t unit_len,
+                      int64_t n_units, bool stats, bool part) {
+  const int64_t nv = n_units * unit_len;
+  const size_t base = score_ws(kc.B, nv, Hq, T, unit_len, stats, part);
+  const int64_t seg_len = part ? unit_len : kTokenTile;
+  if (kc.H < 1 || score_units_mfma(kc.dtype, (Hq / kc.H) * T, seg_len, unit_len)) return base;
+  const size_t esz = kc.dtype == KVSEL_BF16 ? 2 : 4;
+  return round256(base) + static_cast<size_t>(kc.B * nv * kc.H * kc.D) * esz;
+}
+
 int score_impl(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
                float scale, int64_t unit_len, float* row_max, float* row_sum, float* part,
                void* ws, size_t ws_bytes, hipStream_t stream, const ScoreRotArgs* rot,
@@ -278,6 +301,69 @@ int kvsel_score_reposition(const void* q, int64_t T, int64_t Hq, const void* k, 
                     stream, &rot, what);
 }
 
+size_t kvsel_score_units_workspace(int64_t T, int64_t Hq, kvsel_cache kc, int64_t unit_len,
+                                   int64_t n_units, int32_t want_row_stats, int32_t want_part) {
+  if (T < 1 || Hq < 1 || kc.B < 1 || kc.H < 1 || unit_len < 1 || n_units < 1) return 0;
+  return score_units_ws(T, Hq, kc, unit_len, n_units, want_row_stats != 0, want_part != 0);
+}
+
+int kvsel_score_units(const void* q, int64_t T, int64_t Hq, const void* k, kvsel_cache kc,
+                      float scale, int64_t unit_len, const int32_t* units, int64_t n_units,
+                      const int64_t* delta, int32_t delta_per_instance, double rope_base,
+                      int32_t rope_style, float* row_max, float* row_sum, float* part, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  const char* what = "kvsel_score_units";
+  KVSEL_TRY(check_ptr(q, "q"));
+  KVSEL_TRY(check_ptr(k, "k"));
+  if (units == nullptr) return fail(KVSEL_ERR_NULL, "units is NULL");
+  KVSEL_TRY(check_cache(kc, what));
+  KVSEL_TRY(check_heads(T, Hq, kc, what));
+  KVSEL_TRY(check_units(kc, unit_len, what));
+  if (n_units < 1 || n_units * unit_len >= (int64_t{1} << 31))
+    return fail(KVSEL_ERR_SHAPE, "%s: n_units=%lld out of range", what, (long long)n_units);
+  if (delta != nullptr) {
+    if (rope_style != KVSEL_ROPE_HALF && rope_style != KVSEL_ROPE_INTERLEAVED)
+      return fail(KVSEL_ERR_SHAPE, "%s: unknown rope_style %d", what, rope_style);
+    if (!(rope_base > 1.0)) return fail(KVSEL_ERR_SHAPE, "%s: rope_base must be > 1", what);
+  }
+  if ((row_max == nullptr) != (row_sum == nullptr))
+    return fail(KVSEL_ERR_NULL, "%s: row_max and row_sum must both be set or both NULL", what);
+  const bool stats = row_max != nullptr;
+  if (!stats && part == nullptr) return fail(KVSEL_ERR_NULL, "%s: no output requested", what);
+  if (part != nullptr && unit_len < 2)
+    return fail(KVSEL_ERR_SHAPE, "%s: per-unit partials need unit_len > 1", what);
+  const size_t need = score_units_ws(T, Hq, kc, unit_len, n_units, stats, part != nullptr);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(KVSEL_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, need);
+  const int64_t nv = n_units * unit_len;  // scored rows per instance
+  const int64_t rows = kc.B * Hq * T;
+  const int64_t seg_len = part != nullptr ? unit_len : kTokenTile;
+  const int64_t nseg = (nv + seg_len - 1) / seg_len;
+  float* ms = part != nullptr ? part : static_cast<float*>(ws);
+  const int natural = part != nullptr ? 1 : 0;
+  const int per_instance = delta_per_instance != 0;
+  if (score_units_mfma(kc.dtype, (Hq / kc.H) * T, seg_len, unit_len)) {
+    const UnitMap map{units, n_units, unit_len, kc.N / unit_len};
+    launch_score_mfma_units(q, T, Hq, k, kc, map, scale, seg_len, nseg, ms, natural, delta,
+                            per_instance, rope_base, rope_style, stream);
+    KVSEL_TRY(check_launch(what));
+  } else {
+    // copy the listed units to the workspace tail, re-position them there,
+    // then score the copy
+    const kvsel_cache kv{kc.B, nv, kc.H, kc.D, nv * kc.H * kc.D, kc.H * kc.D, kc.dtype};
+    void* kp = static_cast<char*>(ws) +
+               round256(score_ws(kc.B, nv, Hq, T, unit_len, stats, part != nullptr));
+    KVSEL_TRY(launch_gather(k, nullptr, kc, unit_len, units, n_units, 1, nullptr, -1, 0.0,
+                            KVSEL_ROPE_HALF, 0, nv, kp, nullptr, stream));
+    if (delta != nullptr)
+      KVSEL_TRY(launch_reposition(kp, kp, kv, unit_len, delta, per_instance, rope_base,
+                                  rope_style, stream));
+    KVSEL_TRY(launch_score_partials(q, T, Hq, kp, kv, scale, seg_len, ms, natural, stream));
+  }
+  if (stats) return launch_rowstats(ms, rows, nseg, natural, row_max, row_sum, stream);
+  return KVSEL_OK;
+}
+
 size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_len,
                                  int32_t chunk_path, int32_t have_row_stats) {
   if (B < 1 || N < 1 || Hq < 1 || T < 1 || unit_len < 1) return 0;
@@ -287,7 +373,8 @@ size_t kvsel_aggregate_workspace(int64_t B, int64_t N, int64_t Hq, int64_t T, in
 int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
                     kvsel_cache kc, float scale, const float* row_max, const float* row_sum,
                     const float* part, int32_t signal, int64_t unit_len, int64_t group,
-                    float* unit_score, void* ws, size_t ws_bytes, hipStream_t stream) {
+                    float* unit_score, int32_t accumulate, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
   KVSEL_TRY(check_cache(kc, "kvsel_aggregate"));
   KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_aggregate"));
   KVSEL_TRY(check_units(kc, unit_len, "kvsel_aggregate"));
@@ -317,7 +404,8 @@ int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const v
       rs = w + rows;
       w += 2 * rows;
     }
-    return launch_aggregate_chunks(part, rm, rs, kc.B, Hq, T, M, group, unit_score, w, stream);
+    return launch_aggregate_chunks(part, rm, rs, kc.B, Hq, T, M, group, unit_score,
+                                   accumulate != 0, w, stream);
   }
   KVSEL_TRY(check_ptr(q, "q"));
   KVSEL_TRY(check_ptr(k, "k"));
@@ -327,13 +415,15 @@ int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const v
   float* per_token = static_cast<float*>(ws);
   KVSEL_TRY(launch_aggregate_tokens(q, T, Hq, k, v, kc, scale, row_max, row_sum,
                                     signal == KVSEL_SIG_VNORM, per_token, stream));
-  return launch_unit_sums(per_token, kc.B, kc.N, unit_len, group, unit_score, stream);
+  return launch_unit_sums(per_token, kc.B, kc.N, unit_len, group, unit_score, accumulate != 0,
+                          stream);
 }
 
 int kvsel_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,
                hipStream_t stream) {
   if (score == nullptr) return fail(KVSEL_ERR_NULL, "score is NULL");
-  if (G < 1 || M < 1 || M >= (int64_t{1} << 31) || G > (int64_t{1} << 31) - 1)
+  // one 1024-thread workgroup per row: G * 1024 work-items fit in 32 bits
+  if (G < 1 || M < 1 || M >= (int64_t{1} << 31) || G >= (int64_t{1} << 21))
     return fail(KVSEL_ERR_SHAPE, "kvsel_topk: G=%lld M=%lld out of range", (long long)G,
                 (long long)M);
   if (k < 0 || k > M)
@@ -342,6 +432,36 @@ int kvsel_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx
   if (k == 0) return KVSEL_OK;
   if (idx == nullptr) return fail(KVSEL_ERR_NULL, "idx is NULL");
   return launch_topk(score, G, M, k, idx, val, stream);
+}
+
+int kvsel_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx, int64_t k,
+               int32_t* out, hipStream_t stream) {
+  // one work-item per output element: G * k must fit the dispatch's 32-bit size
+  if (G < 1 || m < 1 || m >= (int64_t{1} << 31) || k < 0 || k >= (int64_t{1} << 31) ||
+      G >= (int64_t{1} << 31) || G * k >= (int64_t{1} << 31))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_take: G=%lld m=%lld k=%lld out of range", (long long)G,
+                (long long)m, (long long)k);
+  if (k == 0) return KVSEL_OK;
+  if (src == nullptr || idx == nullptr || out == nullptr)
+    return fail(KVSEL_ERR_NULL, "kvsel_take: src, idx and out must be set");
+  if (overlap(out, G * k * 4, src, G * m * 4) || overlap(out, G * k * 4, idx, G * k * 4))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_take: out must not overlap src or idx");
+  return launch_take(src, G, m, idx, k, out, stream);
+}
+
+int kvsel_order(const float* score, int64_t G, int64_t M, const int32_t* idx, int64_t k,
+                int32_t descending, int32_t* idx_out, float* val_out, hipStream_t stream) {
+  if (G < 1 || M < 1 || M >= (int64_t{1} << 31) || k < 0 || k >= (int64_t{1} << 31))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_order: G=%lld M=%lld k=%lld out of range", (long long)G,
+                (long long)M, (long long)k);
+  if (G >= (int64_t{1} << 31) || G * ((k + 255) / 256) >= (int64_t{1} << 23))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_order: too many rows");  // 256 work-items per block
+  if (k == 0) return KVSEL_OK;
+  if (score == nullptr || idx == nullptr || idx_out == nullptr)
+    return fail(KVSEL_ERR_NULL, "kvsel_order: score, idx and idx_out must be set");
+  if (overlap(idx_out, G * k * 4, idx, G * k * 4))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_order: idx_out must not overlap idx");
+  return launch_order(score, G, M, idx, k, descending != 0, idx_out, val_out, stream);
 }
 
 int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc, int64_t unit_len,

@@ -130,8 +130,8 @@ __device__ __forceinline__ float group_max(float x) {
 // Merge of two softmax partials (m, s) in the log2 domain: s = sum 2^(l - m).
 __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) return;  // both empty
-  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
+  const float ref = mn == -INFINITY ? 0.0f : mn;  // both empty: stays (-inf, 0), no branch
+  s = s * exp2f(m - ref) + s2 * exp2f(m2 - ref);
   m = mn;
 }
 
@@ -196,10 +196,11 @@ __device__ __forceinline__ uint4 pack16_f64(const double* in) {
 
 // Rotate 16-byte vectors of a key row.  Half-split pairing: `ra` holds dims
 // [d0, d0 + V) and `rb` the partner dims [d0 + D/2, ...); interleaved: `ra`
-// holds V/2 whole pairs starting at dim d0 and `rb` is unused.  `cs` is the
-// row's table, indexed by pair.
-template <typename T, int STYLE>
-__device__ __forceinline__ void rope_rotate16(uint4& ra, uint4& rb, int d0, const double2* cs) {
+// holds V/2 whole pairs starting at dim d0 and `rb` is unused.  cs_at(e)
+// gives the cos/sin of the pair that element e of `ra` belongs to (from an
+// LDS table or from registers).
+template <typename T, int STYLE, typename CsAt>
+__device__ __forceinline__ void rope_rotate16_with(uint4& ra, uint4& rb, CsAt cs_at) {
   constexpr int V = Elem<T>::kPerVec;
   float a[V];
   double oa[V];
@@ -210,7 +211,7 @@ __device__ __forceinline__ void rope_rotate16(uint4& ra, uint4& rb, int d0, cons
     unpack16<T>(rb, b);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const double2 t = cs[d0 + e];
+      const double2 t = cs_at(e);
       const double x = a[e], y = b[e];
       oa[e] = fma(x, t.x, -y * t.y);
       ob[e] = fma(x, t.y, y * t.x);
@@ -219,13 +220,23 @@ __device__ __forceinline__ void rope_rotate16(uint4& ra, uint4& rb, int d0, cons
   } else {
 #pragma unroll
     for (int e = 0; e < V; e += 2) {
-      const double2 t = cs[(d0 + e) >> 1];
+      const double2 t = cs_at(e);
       const double x = a[e], y = a[e + 1];
       oa[e] = fma(x, t.x, -y * t.y);
       oa[e + 1] = fma(x, t.y, y * t.x);
     }
   }
   ra = pack16_f64<T>(oa);
+}
+
+// cs_at(e) = cos/sin of the pair of element e of the vector that starts at
+// dimension d0: cs[d0 + e] (half-split) or cs[(d0 + e) / 2] (interleaved).
+template <typename T, int STYLE>
+__device__ __forceinline__ void rope_rotate16(uint4& ra, uint4& rb, int d0, const double2* cs) {
+  if constexpr (STYLE == KVSEL_ROPE_HALF)
+    rope_rotate16_with<T, STYLE>(ra, rb, [&](int e) { return cs[d0 + e]; });
+  else
+    rope_rotate16_with<T, STYLE>(ra, rb, [&](int e) { return cs[(d0 + e) >> 1]; });
 }
 
 // Record a launch failure; returns KVSEL_OK or KVSEL_ERR_HIP.

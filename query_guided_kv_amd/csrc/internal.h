@@ -14,6 +14,8 @@ namespace kvsel {
 constexpr int kMaxSegments = 4;
 // Rows of one score / aggregate tile partial when unit_len == 1.
 constexpr int kTokenTile = 256;
+// Keys per LDS tile of the MFMA kernels (4 key blocks of 16).
+constexpr int kMfmaTileKeys = 64;
 // Keys per split of the final attention pass (streaming and tile variants;
 // decode_split_len gives the length a call actually uses).
 constexpr int kDecodeSplit = 512;
@@ -46,6 +48,24 @@ void launch_score_mfma_rot(const void* q, int64_t T, int64_t Hq, const void* k, 
                            float* ms, int natural, int64_t rot_len, const int64_t* delta,
                            int per_instance, double base, int style, hipStream_t s);
 
+// Scored rows of instance b listed by unit: virtual row t is row
+// units[b * n_units + t / unit_len] * unit_len + t % unit_len of the source
+// cache (entries outside [0, n_src) take no part in the softmax).
+struct UnitMap {
+  const int32_t* units;
+  int64_t n_units;
+  int64_t unit_len;
+  int64_t n_src;
+};
+// MFMA scorer over the listed units of `kc` (kc.N is the source length);
+// `delta` (NULL: no rotation) re-positions virtual unit u by delta[u] (or
+// delta[b][u] with per_instance).
+void launch_score_mfma_units(const void* q, int64_t T, int64_t Hq, const void* k,
+                             const kvsel_cache& kc, const UnitMap& map, float scale,
+                             int64_t seg_len, int64_t nseg, float* ms, int natural,
+                             const int64_t* delta, int per_instance, double base, int style,
+                             hipStream_t s);
+
 // Row statistics from segment partials (log2 or natural units as written).
 int launch_rowstats(const float* ms, int64_t rows, int64_t nseg, int natural, float* row_max,
                     float* row_sum, hipStream_t s);
@@ -54,7 +74,7 @@ int launch_rowstats(const float* ms, int64_t rows, int64_t nseg, int natural, fl
 // `ws` holds aggregate_chunk_ws_floats(B, Hq, T, M) floats of row-chunk sums.
 int launch_aggregate_chunks(const float* part, const float* row_max, const float* row_sum,
                             int64_t B, int64_t Hq, int64_t T, int64_t M, int64_t group,
-                            float* unit_score, float* ws, hipStream_t s);
+                            float* unit_score, int accumulate, float* ws, hipStream_t s);
 size_t aggregate_chunk_ws_floats(int64_t B, int64_t Hq, int64_t T, int64_t M);
 
 // Token path: per_token[b][t] = sum_h sum_j alpha (* ||v||), then per unit/group sums.
@@ -68,10 +88,14 @@ void launch_aggregate_mfma(const void* q, int64_t T, int64_t Hq, const void* k, 
                            const kvsel_cache& kc, float scale2, const float* row_max,
                            const float* row_sum, int vnorm, float* per_token, hipStream_t s);
 int launch_unit_sums(const float* per_token, int64_t B, int64_t N, int64_t unit_len,
-                     int64_t group, float* unit_score, hipStream_t s);
+                     int64_t group, float* unit_score, int accumulate, hipStream_t s);
 
 int launch_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,
                 hipStream_t s);
+int launch_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx, int64_t k,
+                int32_t* out, hipStream_t s);
+int launch_order(const float* score, int64_t G, int64_t M, const int32_t* idx, int64_t k,
+                 int descending, int32_t* idx_out, float* val_out, hipStream_t s);
 
 int launch_gather(const void* k_src, const void* v_src, const kvsel_cache& kc, int64_t unit_len,
                   const int32_t* idx, int64_t k, int64_t idx_group, const int64_t* src_start,

@@ -7,6 +7,7 @@
 #pragma once
 
 #include "common.h"
+#include "internal.h"
 
 namespace kvsel {
 
@@ -21,10 +22,8 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Keys per LDS tile of the MFMA kernels (4 key blocks of 16) and the padding
-// of a staged row (16 bytes: the 16 keys one B-fragment read spans land on
-// distinct banks).
-constexpr int kMfmaTileKeys = 64;
+// Padding of a staged row of an LDS key tile (kMfmaTileKeys keys): 16 bytes,
+// so the 16 keys one B-fragment read spans land on distinct banks.
 constexpr int kMfmaPad = 8;
 
 // Row blocks of 16 query rows: how the four waves of a workgroup share them.

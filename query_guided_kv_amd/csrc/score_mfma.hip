@@ -23,17 +23,17 @@
 namespace kvsel {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr int kTileKeys = kMfmaTileKeys;
 constexpr int kPad = kMfmaPad;
 
-// (m, s) merge with the lane holding the same rows in another key column
+// (m, s) of one row merged over the 16 key-column lanes that hold it: the
+// lanes' max, each lane's sum rescaled to it, then the sum over the lanes
+// (DPP, a fixed order; one exp per lane instead of one per merge step)
 __device__ __forceinline__ void merge_cols(float& m, float& s) {
-  merge_ms(m, s, dpp_xor1(m), dpp_xor1(s));
-  merge_ms(m, s, dpp_xor2(m), dpp_xor2(s));
-  merge_ms(m, s, dpp_half_mirror(m), dpp_half_mirror(s));
-  merge_ms(m, s, dpp_mirror(m), dpp_mirror(s));
+  const float mx = group_max<16>(m);
+  const float ref = mx == -INFINITY ? 0.0f : mx;
+  s = group_sum<16>(s * __builtin_amdgcn_exp2f(m - ref));
+  m = mx;
 }
 
 // Re-positioning fused into the staging of K (kvsel_score_reposition): every
@@ -49,20 +49,27 @@ struct ScoreRot {
   bf16_t* kout;              // same layout as k, or NULL
 };
 
-// D: head dim; RBW: row blocks per wave; NWR: waves across row blocks;
+// D: head dim; RBW: row blocks per wave; NWR: waves across row blocks; NW:
+// waves per workgroup (4, or 8 for tall query blocks: fewer rows per wave
+// keeps the registers low enough for two waves per SIMD);
 // ROT: 0 none, 1 half-split pairs, 2 interleaved pairs; WRITE: store K'.
-template <int D, int RBW, int NWR, int ROT, bool WRITE>
-__global__ void __launch_bounds__(kThreads)
+// N is the number of scored (virtual) rows; with map.units set they are the
+// listed units of the source cache, in list order (a unit length that is a
+// multiple of the tile, so every tile reads one source unit).
+template <int D, int RBW, int NWR, int NW, int ROT, bool WRITE>
+__global__ void __launch_bounds__(NW * 64)
 score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int64_t N, int H,
                   int64_t stride_b, int64_t stride_n, int T, int Hq, float scale2,
                   int64_t seg_len, int64_t nseg, int64_t segs_per_block, int64_t groups,
-                  int passes, float* __restrict__ ms, int natural, ScoreRot rot) {
+                  int passes, float* __restrict__ ms, int natural, ScoreRot rot, UnitMap map) {
   constexpr int KS = D / 32;                 // MFMA k-steps
   constexpr int KROW = D + kPad;             // staged row stride (elements)
-  constexpr int NWK = kWaves / NWR;          // waves across key blocks
+  constexpr int kThreads = NW * 64;
+  constexpr int NWK = NW / NWR;              // waves across key blocks
   constexpr int KBW = (kTileKeys / 16) / NWK;  // key blocks per wave and tile
   constexpr int VPT = kTileKeys * D / 8 / kThreads;  // 16-byte vectors per thread and tile
   constexpr int ROWS_PASS = NWR * RBW * 16;
+  static_assert(VPT >= 1 && KBW >= 1, "tile too small for the workgroup");
   __shared__ __align__(16) bf16_t kt[kTileKeys * KROW];
   __shared__ float red[NWK][ROWS_PASS][2];
   __shared__ double2 cs[ROT ? D / 2 : 1];
@@ -106,29 +113,90 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   // partner c + D/16 travel together; else P = 1 and item e is chunk e).
   constexpr int P = ROT == 1 ? 2 : 1;
   constexpr int CPK = D / 8 / P;  // items per key
+  static_assert(VPT % P == 0, "rotation pairs must stay in one thread");
   auto item = [&](int i, int& key, int& ch) {
     const int e = threadIdx.x + (i / P) * kThreads;
     key = e / CPK;
     ch = e % CPK + (i % P) * (D / 16);
   };
-  auto fetch = [&](uint4 (&v)[VPT], int64_t t0) {
+  // Tile cursors.  Every length stepped here (scoring segment, rotation unit,
+  // listed unit) is a multiple of the 64-key tile and t_begin starts a
+  // segment, so each position advances by one tile with an add and a compare:
+  // no integer division inside the loop (64-bit divisions are long scalar
+  // sequences that every wave would repeat).
+  struct Cursor {
+    int64_t u, off, len;
+    __device__ void advance() {
+      off += kTileKeys;
+      if (off >= len) { off = 0; ++u; }
+    }
+  };
+  auto cursor_at = [&](int64_t len) {
+    const int64_t u = t_begin / len;
+    return Cursor{u, t_begin - u * len, len};
+  };
+  // per-thread offsets of the tile's vectors from the tile's first row
+  int64_t voff[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    int key, ch;
+    item(i, key, ch);
+    voff[i] = key * stride_n + ch * 8;
+  }
+  // load the tile whose first virtual row is t0 (cursor c on its listed unit);
+  // returns false when the listed unit is outside the source
+  auto fetch = [&](uint4 (&v)[VPT], int64_t t0, const Cursor& c) -> bool {
+    int64_t r0 = t0;
+    if (map.units != nullptr) {
+      const int64_t su = map.units[b * map.n_units + c.u];
+      r0 = (su >= 0 && su < map.n_src) ? su * map.unit_len + c.off : -1;
+    }
+    const int rem = static_cast<int>(min<int64_t>(t_end - t0, kTileKeys));
+    const bf16_t* base = kb + r0 * stride_n;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       int key, ch;
       item(i, key, ch);
-      v[i] = (t0 + key < t_end)
-                 ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * stride_n + ch * 8)
-                 : make_uint4(0, 0, 0, 0);
+      v[i] = (key < rem && r0 >= 0) ? *reinterpret_cast<const uint4*>(base + voff[i])
+                                     : make_uint4(0, 0, 0, 0);
     }
+    return r0 >= 0;
   };
   const bool write_out = WRITE && pass == 0;
+  // A thread stages the same chunks of every tile, so it always needs the
+  // cos/sin of the same pairs: where these are at most 8 (eight waves), they
+  // are copied to registers once per rotation unit instead of read from LDS
+  // for every tile.
+  constexpr int NCS = ROT == 1 ? (VPT / 2) * 8 : VPT * 4;
+  constexpr bool CS_REG = ROT != 0 && NCS <= 8;
+  double2 creg[CS_REG ? NCS : 1];
+  auto load_cs = [&]() {
+    if constexpr (CS_REG) {
+#pragma unroll
+      for (int i = 0; i < VPT; i += P) {
+        int key, ch;
+        item(i, key, ch);
+        if constexpr (ROT == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) creg[(i / 2) * 8 + e] = cs[ch * 8 + e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) creg[i * 4 + e] = cs[ch * 4 + e];
+        }
+      }
+    }
+  };
   auto stash = [&](uint4 (&v)[VPT], int64_t t0) {
     if constexpr (ROT == 1) {
 #pragma unroll
       for (int i = 0; i < VPT; i += 2) {
         int key, ch;
         item(i, key, ch);
-        rope_rotate16<bf16_t, KVSEL_ROPE_HALF>(v[i], v[i + 1], ch * 8, cs);
+        if constexpr (CS_REG)
+          rope_rotate16_with<bf16_t, KVSEL_ROPE_HALF>(
+              v[i], v[i + 1], [&](int e) { return creg[(i / 2) * 8 + e]; });
+        else
+          rope_rotate16<bf16_t, KVSEL_ROPE_HALF>(v[i], v[i + 1], ch * 8, cs);
       }
     } else if constexpr (ROT == 2) {
 #pragma unroll
@@ -136,17 +204,22 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
         int key, ch;
         item(i, key, ch);
         uint4 unused;
-        rope_rotate16<bf16_t, KVSEL_ROPE_INTERLEAVED>(v[i], unused, ch * 8, cs);
+        if constexpr (CS_REG)
+          rope_rotate16_with<bf16_t, KVSEL_ROPE_INTERLEAVED>(
+              v[i], unused, [&](int e) { return creg[i * 4 + (e >> 1)]; });
+        else
+          rope_rotate16<bf16_t, KVSEL_ROPE_INTERLEAVED>(v[i], unused, ch * 8, cs);
       }
     }
+    const int rem = static_cast<int>(min<int64_t>(t_end - t0, kTileKeys));
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       int key, ch;
       item(i, key, ch);
       *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = v[i];
-      if (write_out && t0 + key < t_end)
-        *reinterpret_cast<uint4*>(rot.kout + b * stride_b + (t0 + key) * stride_n +
-                                  static_cast<int64_t>(g) * D + ch * 8) = v[i];
+      if (write_out && key < rem)
+        *reinterpret_cast<uint4*>(rot.kout + b * stride_b + t0 * stride_n +
+                                  static_cast<int64_t>(g) * D + voff[i]) = v[i];
     }
   };
   int64_t cs_unit = -1;
@@ -157,22 +230,29 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
 #pragma unroll
     for (int v = 0; v < 4; ++v) { m[i][v] = -INFINITY; s[i][v] = 0.0f; }
 
+  Cursor fc = map.units != nullptr ? cursor_at(map.unit_len) : Cursor{0, 0, kTileKeys};
+  Cursor rc = ROT != 0 ? cursor_at(rot.rot_len) : Cursor{0, 0, kTileKeys};
+  int64_t seg = seg0, seg_off = 0;
   uint4 nxt[VPT];
-  if (t_begin < t_end) fetch(nxt, t_begin);
+  bool nxt_ok = true;
+  if (t_begin < t_end) nxt_ok = fetch(nxt, t_begin, fc);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) {
     __syncthreads();               // previous tile fully read
     if constexpr (ROT != 0) {
-      const int64_t u = t0 / rot.rot_len;  // a tile lies inside one unit
-      if (u != cs_unit) {
-        const int64_t delta = rot.delta[b * rot.delta_stride_b + u];
+      if (rc.u != cs_unit) {       // a tile lies inside one unit
+        const int64_t delta = rot.delta[b * rot.delta_stride_b + rc.u];
         for (int i = threadIdx.x; i < D / 2; i += kThreads) cs[i] = rope_cs(delta, i, D, rot.base);
-        cs_unit = u;
+        cs_unit = rc.u;
         __syncthreads();
+        load_cs();
       }
+      rc.advance();
     }
     stash(nxt, t0);
+    const bool tile_ok = nxt_ok;
     __syncthreads();
-    if (t0 + kTileKeys < t_end) fetch(nxt, t0 + kTileKeys);  // in flight during the math
+    fc.advance();
+    if (t0 + kTileKeys < t_end) nxt_ok = fetch(nxt, t0 + kTileKeys, fc);  // in flight during the math
 
     f32x4_t acc[RBW][KBW];
 #pragma unroll
@@ -191,14 +271,22 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
         acc[i][jb] = a;
       }
     }
-    // keys past the end of the cache take no part
+    // keys past the end of the cache, or of a unit outside the source, take
+    // no part (a uniform test: only a range's last tile or an invalid unit
+    // pays for the masking)
+    const int rem = static_cast<int>(min<int64_t>(t_end - t0, kTileKeys));
+    if (!tile_ok || rem < kTileKeys) {
 #pragma unroll
-    for (int jb = 0; jb < KBW; ++jb) {
-      if (t0 + (wk + jb * NWK) * 16 + col >= t_end) {
+      for (int jb = 0; jb < KBW; ++jb) {
+        if (!tile_ok || (wk + jb * NWK) * 16 + col >= rem) {
 #pragma unroll
-        for (int i = 0; i < RBW; ++i) acc[i][jb] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          for (int i = 0; i < RBW; ++i)
+            acc[i][jb] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
       }
     }
+    // online softmax, branch-free: while a row has seen only masked keys its
+    // max stays -inf and the reference 0 keeps every exp at exp2(-inf) = 0
 #pragma unroll
     for (int i = 0; i < RBW; ++i) {
 #pragma unroll
@@ -207,20 +295,19 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
 #pragma unroll
         for (int jb = 1; jb < KBW; ++jb) tmax = fmaxf(tmax, acc[i][jb][v]);
         const float mn = fmaxf(m[i][v], tmax * scale2);
-        if (mn == -INFINITY) continue;
-        float acc_s = s[i][v] * __builtin_amdgcn_exp2f(m[i][v] - mn);
+        const float ref = mn == -INFINITY ? 0.0f : mn;
+        float acc_s = s[i][v] * __builtin_amdgcn_exp2f(m[i][v] - ref);
 #pragma unroll
         for (int jb = 0; jb < KBW; ++jb)
-          acc_s += __builtin_amdgcn_exp2f(fmaf(acc[i][jb][v], scale2, -mn));
+          acc_s += __builtin_amdgcn_exp2f(fmaf(acc[i][jb][v], scale2, -ref));
         s[i][v] = acc_s;
         m[i][v] = mn;
       }
     }
 
     // end of a segment: merge and publish its partials
-    const int64_t t_next = t0 + kTileKeys;
-    if (t_next % seg_len == 0 || t_next >= t_end) {
-      const int64_t seg = (t0 + kTileKeys - 1) / seg_len;
+    seg_off += kTileKeys;
+    if (seg_off == seg_len || t0 + kTileKeys >= t_end) {
 #pragma unroll
       for (int i = 0; i < RBW; ++i)
 #pragma unroll
@@ -251,38 +338,53 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
       for (int i = 0; i < RBW; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) { m[i][v] = -INFINITY; s[i][v] = 0.0f; }
+      ++seg;
+      seg_off = 0;
     }
   }
 }
 
-template <int D, int RBW, int NWR, int ROT, bool WRITE>
+template <int D, int RBW, int NWR, int NW, int ROT, bool WRITE>
 void launch(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
             float scale2, int64_t seg_len, int64_t nseg, int64_t spb, int passes, float* ms,
-            int natural, const ScoreRot& rot, hipStream_t s) {
+            int natural, const ScoreRot& rot, const UnitMap& map, hipStream_t s) {
   const int64_t groups = (nseg + spb - 1) / spb;
   const int64_t blocks = kc.B * kc.H * passes * groups;
-  hipLaunchKernelGGL((score_mfma_kernel<D, RBW, NWR, ROT, WRITE>),
-                     dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((score_mfma_kernel<D, RBW, NWR, NW, ROT, WRITE>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), 0, s,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), kc.N,
                      static_cast<int>(kc.H), kc.stride_b, kc.stride_n, static_cast<int>(T),
                      static_cast<int>(Hq), scale2, seg_len, nseg, spb, groups, passes, ms, natural,
-                     rot);
+                     rot, map);
 }
 
 template <int D, int ROT, bool WRITE>
 void dispatch(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
               float scale2, int64_t seg_len, int64_t nseg, float* ms, int natural,
-              const ScoreRot& rot, hipStream_t s) {
-  const MfmaRowPlan p = mfma_row_plan((Hq / kc.H) * T);
+              const ScoreRot& rot, const UnitMap& map, hipStream_t s) {
+  const int64_t rows = (Hq / kc.H) * T;
+  const int64_t rb = (rows + 15) / 16;
+  // up to 8 row blocks: four waves (mfma_row_plan; a wave's row blocks share
+  // each key fragment it reads from LDS).  Taller blocks, head dim 128: eight
+  // waves of two row blocks, which halves the registers per wave (two waves
+  // per SIMD instead of one).  Measured on MI355X: 224 and 448 rows per kv
+  // head run faster with eight waves, 128 rows slower.
+  MfmaRowPlan p = mfma_row_plan(rows);
+  int nw = 4;
+  if (D == 128 && rb > 8) {
+    nw = 8;
+    p = MfmaRowPlan{2, 8, static_cast<int>((rb + 15) / 16)};
+  }
   // up to 1024 keys per workgroup (segments of 256 go four to a block), fewer
   // when that leaves under ~2048 workgroups for the 256 CUs
   int64_t spb = seg_len >= 1024 ? 1 : 1024 / seg_len;
   while (spb > 1 && kc.B * kc.H * p.passes * ((nseg + spb - 1) / spb) < 2048) spb /= 2;
-#define KVSEL_SM(RBW, NWR)                                                                 \
-  if (p.rbw == RBW && p.nwr == NWR)                                                        \
-    return launch<D, RBW, NWR, ROT, WRITE>(q, T, Hq, k, kc, scale2, seg_len, nseg, spb,    \
-                                           p.passes, ms, natural, rot, s);
-  KVSEL_SM(1, 1) KVSEL_SM(1, 2) KVSEL_SM(1, 4) KVSEL_SM(2, 4) KVSEL_SM(4, 4)
+#define KVSEL_SM(RBW, NWR, NW)                                                             \
+  if (p.rbw == RBW && p.nwr == NWR && nw == NW)                                            \
+    return launch<D, RBW, NWR, NW, ROT, WRITE>(q, T, Hq, k, kc, scale2, seg_len, nseg, spb, \
+                                               p.passes, ms, natural, rot, map, s);
+  KVSEL_SM(1, 1, 4) KVSEL_SM(1, 2, 4) KVSEL_SM(1, 4, 4) KVSEL_SM(2, 4, 4) KVSEL_SM(4, 4, 4)
+  if constexpr (D == 128) { KVSEL_SM(2, 8, 8) }
 #undef KVSEL_SM
 }
 
@@ -300,10 +402,11 @@ void launch_score_mfma(const void* q, int64_t T, int64_t Hq, const void* k,
                        const kvsel_cache& kc, float scale2, int64_t seg_len, int64_t nseg,
                        float* ms, int natural, hipStream_t s) {
   const ScoreRot none{nullptr, 0, 1, 0.0, nullptr};
+  const UnitMap all{nullptr, 0, 1, 0};
   if (kc.D == 128)
-    dispatch<128, 0, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, none, s);
+    dispatch<128, 0, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, none, all, s);
   else
-    dispatch<64, 0, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, none, s);
+    dispatch<64, 0, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, none, all, s);
 }
 
 void launch_score_mfma_rot(const void* q, int64_t T, int64_t Hq, const void* k, void* k_out,
@@ -314,15 +417,37 @@ void launch_score_mfma_rot(const void* q, int64_t T, int64_t Hq, const void* k, 
   const ScoreRot rot{delta, per_instance ? kc.N / rot_len : 0, rot_len, base,
                      static_cast<bf16_t*>(k_out)};
   const bool w = k_out != nullptr;
+  const UnitMap all{nullptr, 0, 1, 0};
 #define KVSEL_SR(D_, ST)                                                                   \
-  if (w) dispatch<D_, ST, true>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, rot, s); \
-  else dispatch<D_, ST, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, rot, s);
+  if (w) dispatch<D_, ST, true>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, rot, all, s); \
+  else dispatch<D_, ST, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, rot, all, s);
   if (kc.D == 128) {
     if (style == KVSEL_ROPE_HALF) { KVSEL_SR(128, 1) } else { KVSEL_SR(128, 2) }
   } else {
     if (style == KVSEL_ROPE_HALF) { KVSEL_SR(64, 1) } else { KVSEL_SR(64, 2) }
   }
 #undef KVSEL_SR
+}
+
+void launch_score_mfma_units(const void* q, int64_t T, int64_t Hq, const void* k,
+                             const kvsel_cache& kc, const UnitMap& map, float scale,
+                             int64_t seg_len, int64_t nseg, float* ms, int natural,
+                             const int64_t* delta, int per_instance, double base, int style,
+                             hipStream_t s) {
+  const float scale2 = scale * kLog2e;
+  kvsel_cache kv = kc;  // N = scored rows; strides stay the source's
+  kv.N = map.n_units * map.unit_len;
+  const ScoreRot rot{delta, per_instance ? map.n_units : 0, map.unit_len, base, nullptr};
+#define KVSEL_SU(D_, ST) \
+  dispatch<D_, ST, false>(q, T, Hq, k, kv, scale2, seg_len, nseg, ms, natural, rot, map, s);
+  if (kc.D == 128) {
+    if (delta == nullptr) { KVSEL_SU(128, 0) }
+    else if (style == KVSEL_ROPE_HALF) { KVSEL_SU(128, 1) } else { KVSEL_SU(128, 2) }
+  } else {
+    if (delta == nullptr) { KVSEL_SU(64, 0) }
+    else if (style == KVSEL_ROPE_HALF) { KVSEL_SU(64, 1) } else { KVSEL_SU(64, 2) }
+  }
+#undef KVSEL_SU
 }
 
 }  // namespace kvsel

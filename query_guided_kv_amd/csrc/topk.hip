@@ -246,7 +246,89 @@ topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* 
   }
 }
 
+// out[g][j] = src[g][idx[g][j]]: composes two index lists, e.g. the
+// positions kept in the current list with the list itself (CacheFocus §2.4:
+// the cache IDs left after a pruning layer).  Indices outside [0, m) give -1.
+constexpr int kTakeThreads = 256;
+
+__global__ void __launch_bounds__(kTakeThreads)
+take_kernel(const int32_t* __restrict__ src, int64_t m, const int32_t* __restrict__ idx,
+            int64_t k, int64_t total, int32_t* __restrict__ out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kTakeThreads + threadIdx.x;
+  if (e >= total) return;
+  const int64_t g = e / k;
+  const int32_t i = idx[e];
+  out[e] = (i >= 0 && i < m) ? src[g * m + i] : -1;
+}
+
+// Lists the k given indices of each row by their scores (CacheFocus §2.5,
+// attention-guided "sort" placement): an entry's rank is the number of
+// entries before it in the order (score descending, index ascending,
+// position in the list ascending), which is a permutation of 0..k-1; rank r
+// goes to slot r (descending) or k-1-r (ascending).  Every thread ranks one
+// entry against all k of its row, read through LDS tiles: O(k^2) compares,
+// exact integer work on the same keys as the top-k.  Indices outside [0, M)
+// rank as the lowest key and get value 0.
+constexpr int kOrderThreads = 256;
+constexpr int kOrderTile = 1024;
+
+__global__ void __launch_bounds__(kOrderThreads)
+order_kernel(const float* __restrict__ score, int64_t M, const int32_t* __restrict__ idx,
+             int64_t k, int64_t jblocks, int descending, int32_t* __restrict__ idx_out,
+             float* __restrict__ val_out) {
+  __shared__ uint32_t skey[kOrderTile];
+  __shared__ int32_t sidx[kOrderTile];
+  const int64_t g = blockIdx.x / jblocks;
+  const int64_t j = (blockIdx.x % jblocks) * kOrderThreads + threadIdx.x;
+  const int32_t* in = idx + g * k;
+  const float* sc = score + g * M;
+  auto key_of = [&](int32_t i) -> uint32_t { return (i >= 0 && i < M) ? order_key(sc[i]) : 0u; };
+  const bool mine = j < k;
+  const int32_t my_i = mine ? in[j] : 0;
+  const uint32_t my_key = mine ? key_of(my_i) : 0u;
+  int64_t rank = 0;
+  for (int64_t t0 = 0; t0 < k; t0 += kOrderTile) {
+    const int n = static_cast<int>(min<int64_t>(kOrderTile, k - t0));
+    __syncthreads();  // previous tile fully read
+    for (int e = threadIdx.x; e < n; e += kOrderThreads) {
+      const int32_t i = in[t0 + e];
+      sidx[e] = i;
+      skey[e] = key_of(i);
+    }
+    __syncthreads();
+    if (mine) {
+      for (int e = 0; e < n; ++e) {
+        const uint32_t ke = skey[e];
+        const int32_t ie = sidx[e];
+        rank += (ke > my_key) || (ke == my_key && (ie < my_i || (ie == my_i && t0 + e < j)));
+      }
+    }
+  }
+  if (mine) {
+    const int64_t pos = g * k + (descending ? rank : k - 1 - rank);
+    idx_out[pos] = my_i;
+    if (val_out) val_out[pos] = (my_i >= 0 && my_i < M) ? sc[my_i] : 0.0f;
+  }
+}
+
 }  // namespace
+
+int launch_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx, int64_t k,
+                int32_t* out, hipStream_t s) {
+  const int64_t total = G * k;
+  const int64_t blocks = (total + kTakeThreads - 1) / kTakeThreads;
+  hipLaunchKernelGGL(take_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kTakeThreads), 0, s,
+                     src, m, idx, k, total, out);
+  return check_launch("kvsel_take");
+}
+
+int launch_order(const float* score, int64_t G, int64_t M, const int32_t* idx, int64_t k,
+                 int descending, int32_t* idx_out, float* val_out, hipStream_t s) {
+  const int64_t jblocks = (k + kOrderThreads - 1) / kOrderThreads;
+  hipLaunchKernelGGL(order_kernel, dim3(static_cast<unsigned>(G * jblocks)), dim3(kOrderThreads),
+                     0, s, score, M, idx, k, jblocks, descending, idx_out, val_out);
+  return check_launch("kvsel_order");
+}
 
 int launch_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,
                 hipStream_t s) {

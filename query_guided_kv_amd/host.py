@@ -28,6 +28,21 @@ def reuse_count(n_docs: int, doc_len: int, window: int) -> int:
     return (n_docs + per_group - 1) // per_group
 
 
+def prune_layers(n_layers: int, every: int) -> list:
+    """Layers (from 0) after which CacheFocus prunes (§2.4, every n-th layer):
+    every-1, 2*every-1, ..."""
+    return list(range(every - 1, n_layers, every)) if every >= 1 else []
+
+
+def keep_schedule(n_docs: int, k_finish: int, n_layers: int, every: int) -> list:
+    """Caches left after each pruning layer (CacheFocus App. C: (k - k_finish)
+    / (L / n) removed per pruning layer).  The p-th of the P pruning layers
+    leaves n_docs - floor(p * (n_docs - k_finish) / P), which is the page's
+    count when it is whole and ends at k_finish in any case."""
+    P = len(prune_layers(n_layers, every))
+    return [n_docs - (p * (n_docs - k_finish)) // P for p in range(1, P + 1)]
+
+
 def chunk_offsets(chunk_lens: Sequence[int]) -> list:
     """Delta_i of InfoFlow KV §4.2 (g(t) = Delta_i + p_i(t)): the global start of
     chunk i in the concatenated order."""

@@ -54,7 +54,12 @@ _SIGNATURES = {
                                               _I32, _D, _I32, _P, _P, _P, _P, _SZ, _P]),
     "kvsel_score_reposition_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, _I32, _I32, _I32]),
     "kvsel_aggregate": (ctypes.c_int, [_P, _I64, _I64, _P, _P, Cache, _F, _P, _P, _P, _I32, _I64,
-                                       _I64, _P, _P, _SZ, _P]),
+                                       _I64, _P, _I32, _P, _SZ, _P]),
+    "kvsel_score_units": (ctypes.c_int, [_P, _I64, _I64, _P, Cache, _F, _I64, _P, _I64, _P, _I32,
+                                         _D, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "kvsel_score_units_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, _I32, _I32]),
+    "kvsel_take": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "kvsel_order": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P]),
     "kvsel_aggregate_workspace": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I32, _I32]),
     "kvsel_topk": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "kvsel_gather": (ctypes.c_int, [_P, _P, Cache, _I64, _P, _I64, _I64, _P, _I64, _D, _I32, _P,
@@ -199,14 +204,46 @@ def score_reposition(q: torch.Tensor, k: torch.Tensor, delta: torch.Tensor, rot_
     return rm, rs, part
 
 
+def score_units(q: torch.Tensor, k: torch.Tensor, units: torch.Tensor, unit_len: int,
+                delta: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                row_stats: bool = True, partials: bool = True, rope_base: float = 10000.0,
+                style: str = "half"):
+    """kvsel_score_units -> (row_max, row_sum, part) of each instance's query
+    block against the listed units of its cache (``units`` int32 [B][n]), unit
+    j re-positioned by ``delta[j]`` (int64 [n] or [B][n]) when given.  ``k``
+    may be a strided view, e.g. one layer of a [R][L][N][H][D] store."""
+    lib = load()
+    B, T, Hq, D = q.shape
+    n = units.shape[1]
+    if units.dtype != torch.int32 or units.dim() != 2 or units.shape[0] != k.shape[0] \
+            or not units.is_contiguous():
+        raise KvselError(-2, "units must be contiguous int32 [B][n_units]")
+    scale = 1.0 / D ** 0.5 if scale is None else scale
+    dev = k.device
+    rm = _empty((B, Hq, T), dev) if row_stats else None
+    rs = _empty((B, Hq, T), dev) if row_stats else None
+    part = _empty((B, Hq, T, n, 2), dev) if partials else None
+    kc = cache_desc(k)
+    need = lib.kvsel_score_units_workspace(T, Hq, kc, unit_len, n, int(row_stats), int(partials))
+    ws = _workspace(need, dev)
+    per = 1 if delta is not None and delta.dim() == 2 else 0
+    _check(lib.kvsel_score_units(_ptr(q), T, Hq, _ptr(k), kc, scale, unit_len, _ptr(units), n,
+                                 _ptr(delta), per, rope_base, ROPE[style], _ptr(rm), _ptr(rs),
+                                 _ptr(part), _ptr(ws), need, _stream(dev)))
+    return rm, rs, part
+
+
 def aggregate(unit_len: int, group: int = 1, signal: str = "mass", *,
               q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
               v: Optional[torch.Tensor] = None, row_max=None, row_sum=None, part=None,
-              scale: Optional[float] = None, cache_shape=None) -> torch.Tensor:
+              scale: Optional[float] = None, cache_shape=None,
+              out: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
     """kvsel_aggregate -> unit_score [B/group][M].
 
     Chunk path: ``part`` (+ optional row stats), with ``cache_shape`` = k's
-    shape or ``k`` given.  Token path: ``q``, ``k`` (``v`` for vnorm) and row stats."""
+    shape or ``k`` given.  Token path: ``q``, ``k`` (``v`` for vnorm) and row stats.
+    ``out``: write into this fp32 [B/group][M] tensor; with ``accumulate`` the
+    result is added to what it holds."""
     lib = load()
     ref = k if k is not None else None
     if ref is not None:
@@ -223,13 +260,19 @@ def aggregate(unit_len: int, group: int = 1, signal: str = "mass", *,
     else:
         _, T, Hq, _ = q.shape
     scale = 1.0 / D ** 0.5 if scale is None else scale
-    out = _empty((B // group, N // unit_len), dev)
+    if out is None:
+        if accumulate:
+            raise KvselError(-1, "accumulate needs out")
+        out = _empty((B // group, N // unit_len), dev)
+    elif (tuple(out.shape) != (B // group, N // unit_len) or out.dtype != torch.float32
+          or not out.is_contiguous()):
+        raise KvselError(-2, "out must be contiguous fp32 [B/group][M]")
     chunk = signal == "mass" and part is not None
     need = lib.kvsel_aggregate_workspace(B, N, Hq, T, unit_len, int(chunk), int(row_max is not None))
     ws = _workspace(need, dev)
     _check(lib.kvsel_aggregate(_ptr(q), T, Hq, _ptr(k), _ptr(v), kc, scale, _ptr(row_max),
                                _ptr(row_sum), _ptr(part), SIGNAL[signal], unit_len, group,
-                               _ptr(out), _ptr(ws), need, _stream(dev)))
+                               _ptr(out), int(accumulate), _ptr(ws), need, _stream(dev)))
     return out
 
 
@@ -241,6 +284,35 @@ def topk(scores: torch.Tensor, k: int, values: bool = False):
     val = _empty((G, k), scores.device) if values else None
     _check(lib.kvsel_topk(_ptr(scores), G, M, k, _ptr(idx), _ptr(val), _stream(scores.device)))
     return (idx, val) if values else idx
+
+
+def take(src: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
+    """kvsel_take -> out[g][j] = src[g][idx[g][j]] (int32; -1 where idx is out of range)."""
+    lib = load()
+    G, m = src.shape
+    kk = idx.shape[1]
+    for t in (src, idx):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise KvselError(-2, "take works on contiguous int32 tensors")
+    out = torch.empty((G, kk), dtype=torch.int32, device=src.device)
+    _check(lib.kvsel_take(_ptr(src), G, m, _ptr(idx), kk, _ptr(out), _stream(src.device)))
+    return out
+
+
+def order(scores: torch.Tensor, idx: torch.Tensor, descending: bool = True,
+          values: bool = False):
+    """kvsel_order -> idx listed by score (most relevant first, or last with
+    ``descending=False``), and the listed scores if asked."""
+    lib = load()
+    G, M = scores.shape
+    kk = idx.shape[1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.shape[0] != G:
+        raise KvselError(-2, "idx must be contiguous int32 [G][k]")
+    out = torch.empty((G, kk), dtype=torch.int32, device=scores.device)
+    val = _empty((G, kk), scores.device) if values else None
+    _check(lib.kvsel_order(_ptr(scores), G, M, _ptr(idx), kk, int(descending), _ptr(out),
+                           _ptr(val), _stream(scores.device)))
+    return (out, val) if values else out
 
 
 def gather(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, unit_len: int,

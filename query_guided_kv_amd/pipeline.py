@@ -183,3 +183,103 @@ class Path:
             out["o"], out["lse"] = o, lse
         out["k_gather"], out["v_gather"] = gk, gv
         return out
+
+
+class PrunePath:
+    """CacheFocus layer-adaptive cache pruning (§2.4) for a batch of requests,
+    then the final re-positioning (§2.4-2.5) and one decode attention pass.
+
+    Caches are a request-major store ``[requests * layers][n_docs * doc_len][H][D]``
+    of document caches at document-local positions; ``q_layers`` is
+    ``[layers][requests][T][Hq][D]``.  Per layer, one call scores every
+    request's current documents in place, each re-positioned to its slot
+    (:func:`kvsel.score_units` on the layer's strided view of the store), and one
+    call adds the document-wise attention to the running totals; after every
+    n-th layer a top-k keeps the scheduled number of documents (with their
+    totals) and a take composes the kept positions with the current IDs.  The
+    survivors are listed in ID order ("align") or by total, most relevant last
+    ("sort"), and a gather re-positions them to consecutive slots for every
+    layer.  Every step is a library call; this class only sequences them.
+    """
+
+    STAGES = ("select", "final_gather", "decode")
+
+    def __init__(self, w, inp: dict):
+        self.w = w
+        R, L, U = w.requests, w.layers, w.unit_len
+        self.k, self.v = inp["k"], inp["v"]
+        dev = self.k.device
+        self.n_docs = w.N // U
+        # one layer's caches of all requests: a strided view of the store
+        self.k_layer = self.k.view(R, L, w.N, w.H, w.D)
+        self.prune_at = dict(zip(host.prune_layers(L, w.prune_every),
+                                 host.keep_schedule(self.n_docs, w.k, L, w.prune_every)))
+        final = list(self.prune_at.values())[-1] if self.prune_at else self.n_docs
+        if final != w.k:
+            raise ValueError(f"the pruning schedule ends at {final} documents, not k={w.k}")
+        lengths = {self.n_docs, *self.prune_at.values()}
+        self.delta = {m: host.delta_tensor(host.reuse_window_starts(m, U, w.window), dev)
+                      for m in lengths}
+        self.ids0 = torch.arange(self.n_docs, dtype=torch.int32, device=dev).repeat(R, 1)
+        self.iota = torch.arange(w.k, dtype=torch.int32, device=dev).repeat(R, 1)
+        last = max(self.prune_at) if self.prune_at else -1
+        # layers after the last pruning layer only change the "sort" order
+        self.n_scored = L if w.allocation == "sort" else last + 1
+        self.stages = self.STAGES if w.decode else self.STAGES[:2]
+
+    def select(self, q_layers: torch.Tensor, trace: list = None):
+        """Run the layer loop; returns (final IDs [R][k] in allocation order,
+        their totals in ID order).  ``trace`` collects (ids, totals) per layer."""
+        w = self.w
+        U = w.unit_len
+        ids, total = self.ids0, None
+        for l in range(self.n_scored):
+            m = ids.shape[1]
+            _, _, part = K.score_units(q_layers[l], self.k_layer[:, l], ids, U,
+                                       delta=self.delta[m], scale=w.scale, row_stats=False,
+                                       partials=True, rope_base=w.rope_base, style=w.rope_style)
+            if total is None:
+                total = torch.empty((ids.shape[0], m), dtype=torch.float32, device=ids.device)
+            K.aggregate(U, 1, "mass", part=part, cache_shape=(ids.shape[0], m * U, w.H, w.D),
+                        q=q_layers[l], out=total, accumulate=l > 0)
+            if trace is not None:
+                trace.append((ids.clone(), total.clone()))
+            keep = self.prune_at.get(l)
+            if keep is not None:
+                pos, total = K.topk(total, keep, values=True)
+                ids = K.take(ids, pos)
+        final = ids
+        if w.allocation == "sort":
+            final = K.take(ids, K.order(total, self.iota, descending=False))
+        return final, total
+
+    def __call__(self, q_layers: torch.Tensor, q_dec: torch.Tensor = None, marks: dict = None,
+                 trace: list = None) -> dict:
+        w = self.w
+        ev = marks or {}
+
+        def mark(stage, i):
+            pair = ev.get(stage)
+            if pair is not None:
+                pair[i].record()
+
+        out = {}
+        mark("select", 0)
+        out["idx"], out["total"] = self.select(q_layers, trace)
+        mark("select", 1)
+        mark("final_gather", 0)
+        out["k_gather"], out["v_gather"] = K.gather(self.k, self.v, out["idx"], w.unit_len,
+                                                    w.layers, align_base=0,
+                                                    rope_base=w.rope_base, style=w.rope_style)
+        mark("final_gather", 1)
+        if w.decode and q_dec is not None:
+            mark("decode", 0)
+            out["o"], out["lse"] = K.decode_attn(q_dec, [(out["k_gather"], out["v_gather"])],
+                                                 w.scale)
+            mark("decode", 1)
+        return out
+
+
+def make_path(w, inp: dict):
+    """The launch sequence of workload ``w``."""
+    return PrunePath(w, inp) if w.recipe == "cachefocus" else Path(w, inp)

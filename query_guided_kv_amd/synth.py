@@ -40,7 +40,8 @@ class Workload:
     """Shape of one workload.  Caches are ``[B][N][H][D]``, queries ``[B][T][Hq][D]``."""
 
     name: str
-    recipe: str          # generator: "tiny", "docs", "bilayer", "infoflow", "serving"
+    recipe: str          # generator: "tiny", "docs", "bilayer", "infoflow", "serving",
+                         # "cachefocus"
     B: int               # independent instances (requests x layers, or layers)
     N: int               # cached rows scored per instance
     Hq: int              # query heads
@@ -62,6 +63,9 @@ class Workload:
     plants: Dict[str, float] = field(default_factory=dict)
     steps: int = 1                # decode steps with fresh queries (serving)
     requests: int = 1             # serving: requests (B = requests * layers)
+    layers: int = 1               # layer-wise pruning: layers per request
+    prune_every: int = 0          # layer-wise pruning: prune after every n-th layer
+    allocation: str = "align"     # layer-wise pruning: final order, "align" or "sort"
 
     @property
     def M(self) -> int:
@@ -120,6 +124,21 @@ WORKLOADS: Dict[str, Workload] = {
         name="serving_16req_8l_128k", recipe="serving", B=128, N=131072, Hq=32, H=8, D=128, T=1,
         dtype="bf16", unit_len=256, k=64, requests=16, steps=128,
         plants={"chunks": 64, "gamma": 1.0, "query_topic": 2.0}),
+    # Layer-adaptive cache pruning on a Qwen2-7B-shaped model: 28 layers, GQA
+    # 28/4, head dim 128, bf16, a 32K positional range.  Per request, 40
+    # retrieved documents x 512 tokens are cached per layer at document-local
+    # positions and a 32-token query block arrives per layer.  Every layer
+    # re-positions the current documents to consecutive slots, scores them and
+    # accumulates document-wise attention; every 4th layer prunes 5 (40 -> 5
+    # over 7 pruning layers).  The 5 survivors are re-positioned to consecutive
+    # slots in order of relevance ("sort") for all 28 layers, and one decode
+    # step (1 query token per layer) attends them.  16 requests (B = 16 x 28
+    # caches); document relevance planted as a ramp of key scales.
+    "cachefocus_qwen2_28l_40docs_x512": Workload(
+        name="cachefocus_qwen2_28l_40docs_x512", recipe="cachefocus", B=16 * 28, N=40 * 512,
+        Hq=28, H=4, D=128, T=32, dtype="bf16", unit_len=512, k=5, reposition="reuse_window",
+        window=32768, requests=16, layers=28, prune_every=4, allocation="sort",
+        plants={"top_scale": 1.6, "scale_step": 0.025}),
 }
 
 
@@ -161,7 +180,8 @@ def generate(w: Workload, seed: int = 0, device="cpu") -> dict:
     when the workload re-positions them.
     """
     gen = {"tiny": _gen_tiny, "docs": _gen_docs, "bilayer": _gen_bilayer,
-           "infoflow": _gen_infoflow, "serving": _gen_serving}[w.recipe]
+           "infoflow": _gen_infoflow, "serving": _gen_serving,
+           "cachefocus": _gen_cachefocus}[w.recipe]
     return gen(w, seed, device)
 
 
@@ -303,3 +323,37 @@ def serving_queries(w: Workload, topic: np.ndarray, seed: int, step: int, device
     per_inst = np.repeat(per_head, layers, axis=0)                              # [B][Hq][D]
     u = torch.from_numpy(per_inst).to(device)[:, None]
     return (z + float(w.plants["query_topic"]) * u).to(td)
+
+
+def _gen_cachefocus(w: Workload, seed: int, device) -> dict:
+    """Per request a random relevance rank of its documents (0 = most
+    relevant); the keys of the document of rank r are scaled by
+    ``top_scale - scale_step * r`` at every layer (raising its expected
+    ``exp`` logit against isotropic queries to ``e^(s^2/2)``; a rotation keeps
+    the scale).  Caches are ``[requests * layers][N][H][D]``, request-major;
+    pre-fill query blocks ``q`` are ``[layers][requests][T][Hq][D]`` (one block
+    per layer and request); ``q_dec`` holds one decode token per cache,
+    ``[requests * layers][1][Hq][D]``.  ``planted`` lists each request's
+    ``k`` documents of best rank."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    g = _device_generator(seed, device)
+    td = _TORCH_DTYPE[w.dtype]
+    R, L, U = w.requests, w.layers, w.unit_len
+    if w.B != R * L:
+        raise ValueError("cachefocus workloads need B = requests * layers")
+    n_docs = w.M
+    q = torch.empty((L, R, w.T, w.Hq, w.D), dtype=td, device=device)
+    q.normal_(generator=g)
+    q_dec = torch.empty((w.B, 1, w.Hq, w.D), dtype=td, device=device)
+    q_dec.normal_(generator=g)
+    rank = np.stack([rng.permutation(n_docs) for _ in range(R)])
+    scale = (w.plants["top_scale"] - w.plants["scale_step"] * rank).astype(np.float32)
+    k = torch.empty((w.B, w.N, w.H, w.D), dtype=td, device=device)
+    v = torch.empty((w.B, w.N, w.H, w.D), dtype=td, device=device)
+    for b in range(w.B):
+        k[b].normal_(generator=g)
+        v[b].normal_(generator=g)
+        s = torch.from_numpy(scale[b // L]).to(device)[:, None, None, None]
+        k[b] = (k[b].float().view(n_docs, U, w.H, w.D) * s).view(w.N, w.H, w.D).to(td)
+    planted = [np.sort(np.flatnonzero(rank[r] < w.k)).astype(np.int64) for r in range(R)]
+    return dict(q=q, q_dec=q_dec, k=k, v=v, planted=planted, rank=rank)

@@ -105,7 +105,7 @@ def test_aggregate_validation(lib):
     call = lambda sig=0, unit=256, group=1, part=FAKE, rm=FAKE, rs=FAKE, out=FAKE, q=FAKE, ws=None, wsb=0: lib.kvsel_aggregate(
         q and ctypes.c_void_p(q), 1, 32, p, p, kc, 0.088, rm and ctypes.c_void_p(rm),
         rs and ctypes.c_void_p(rs), part and ctypes.c_void_p(part), sig, unit, group,
-        out and ctypes.c_void_p(out), ws, wsb, None)
+        out and ctypes.c_void_p(out), 0, ws, wsb, None)
     assert call(sig=3) == SHAPE
     assert call(group=3) == SHAPE                  # 2 % 3 != 0
     assert call(out=0) == NULL
@@ -119,6 +119,73 @@ def test_aggregate_validation(lib):
     assert lib.kvsel_aggregate_workspace(2, 1024, 32, 1, 256, 1, 1) == (1 + 2) * 4 * 4
 
 
+def test_score_units_validation(lib):
+    p = ctypes.c_void_p(FAKE)
+    kc = cache(B=2, N=2048, H=4, D=128)
+    f = ctypes.c_void_p(FAKE)
+
+    def call(q=FAKE, k=FAKE, unit=512, units=FAKE, n=3, delta=FAKE, style=0, base=1e4,
+             rm=FAKE, rs=FAKE, part=FAKE, Hq=28, T=32, ws=None, wsb=0, c=None):
+        v = lambda x: x and ctypes.c_void_p(x)
+        return lib.kvsel_score_units(v(q), T, Hq, v(k), c or kc, 0.088, unit, v(units), n,
+                                     v(delta), 0, base, style, v(rm), v(rs), v(part), ws, wsb,
+                                     None)
+    assert call(q=0) == NULL
+    assert call(q=MISALIGNED) == UNSUP
+    assert call(units=0) == NULL
+    assert call(unit=300) == SHAPE                 # 2048 % 300 != 0
+    assert call(n=0) == SHAPE
+    assert call(n=1 << 22) == SHAPE                # n_units * unit_len >= 2^31
+    assert call(style=5) == SHAPE
+    assert call(base=1.0) == SHAPE
+    # no rotation: the rope arguments are not checked, the next check fails
+    assert call(delta=0, style=5, rm=0, rs=0, part=0) == NULL
+    assert call(Hq=30) == SHAPE                    # not a multiple of H
+    assert call(rm=0) == NULL
+    assert call(rm=0, rs=0, part=0) == NULL        # nothing requested
+    assert call(unit=1, rm=0, rs=0) == SHAPE       # partials need units
+    # matrix-core shape (bf16, 7 * 32 rows per kv head, 512-row units): the
+    # listed units are read in place, so partials alone need no workspace
+    assert lib.kvsel_score_units_workspace(32, 28, kc, 512, 3, 0, 1) == 0
+    # row statistics come from the partials when both are asked for; alone
+    # they need one (m, s) per 256-row segment of the 3 * 512 scored rows
+    assert lib.kvsel_score_units_workspace(32, 28, kc, 512, 3, 1, 1) == 0
+    assert lib.kvsel_score_units_workspace(32, 28, kc, 512, 3, 1, 0) == 2 * 28 * 32 * 6 * 2 * 4
+    # fp32 caches go through a copy of the listed units in the workspace tail
+    k32 = cache(B=2, N=2048, H=4, D=128, dtype=K.FP32)
+    need = lib.kvsel_score_units_workspace(32, 28, k32, 512, 3, 0, 1)
+    assert need == 2 * 3 * 512 * 4 * 128 * 4
+    assert call(c=k32) == WS
+    assert call(c=k32, ws=f, wsb=need - 1) == WS
+    assert lib.kvsel_score_units_workspace(32, 28, kc, 512, 0, 0, 1) == 0   # invalid sizes
+
+
+def test_take_and_order_validation(lib):
+    # every call below fails validation: nothing is launched
+    p = ctypes.c_void_p(FAKE)
+    q = ctypes.c_void_p(FAKE + 4096)
+    inside = ctypes.c_void_p(FAKE + 64)           # within src's 2 x 10 int32
+    assert lib.kvsel_take(p, 2, 10, q, 3, p, None) == SHAPE          # out is src
+    assert lib.kvsel_take(p, 2, 10, q, 3, inside, None) == SHAPE     # out inside src
+    assert lib.kvsel_take(p, 2, 10, q, 3, q, None) == SHAPE          # out is idx
+    assert lib.kvsel_take(None, 2, 10, p, 3, q, None) == NULL
+    assert lib.kvsel_take(p, 0, 10, p, 3, q, None) == SHAPE
+    assert lib.kvsel_take(p, 2, 0, p, 3, q, None) == SHAPE
+    assert lib.kvsel_take(p, 2, 10, p, -1, q, None) == SHAPE
+    assert lib.kvsel_take(p, 1 << 20, 10, q, 1 << 11, ctypes.c_void_p(FAKE << 8), None) == SHAPE
+    assert lib.kvsel_order(p, 1 << 23, 10, q, 3, 1, ctypes.c_void_p(FAKE << 8), None,
+                           None) == SHAPE
+    assert lib.kvsel_take(None, 2, 10, None, 0, None, None) == OK     # k == 0: no-op
+    assert lib.kvsel_order(p, 2, 10, q, 3, 1, q, None, None) == SHAPE  # in place
+    assert lib.kvsel_order(p, 2, 10, q, 3, 1, ctypes.c_void_p(FAKE + 4096 + 16), None,
+                           None) == SHAPE                              # overlaps idx
+    assert lib.kvsel_order(None, 2, 10, p, 3, 1, q, None, None) == NULL
+    assert lib.kvsel_order(p, 2, 10, p, 3, 1, None, None, None) == NULL
+    assert lib.kvsel_order(p, 2, 1 << 31, p, 3, 1, q, None, None) == SHAPE
+    assert lib.kvsel_order(p, 2, 10, p, -2, 1, q, None, None) == SHAPE
+    assert lib.kvsel_order(None, 2, 10, None, 0, 1, None, None, None) == OK
+
+
 def test_topk_validation(lib):
     p = ctypes.c_void_p(FAKE)
     assert lib.kvsel_topk(None, 1, 10, 2, p, None, None) == NULL
@@ -126,6 +193,7 @@ def test_topk_validation(lib):
     assert lib.kvsel_topk(p, 1, 10, -1, p, None, None) == SHAPE
     assert lib.kvsel_topk(p, 0, 10, 1, p, None, None) == SHAPE
     assert lib.kvsel_topk(p, 1, 1 << 31, 1, p, None, None) == SHAPE
+    assert lib.kvsel_topk(p, 1 << 21, 10, 1, p, None, None) == SHAPE   # grid too large
     assert lib.kvsel_topk(p, 1, 10, 0, None, None, None) == OK      # k == 0: no-op
     assert lib.kvsel_topk(p, 1, 10, 3, None, None, None) == NULL
 

@@ -1,0 +1,280 @@
+"""GPU parity of CacheFocus layer-adaptive pruning against the oracle.
+
+Per call: kvsel_score_units (listed units scored in place with re-positioning
+on the matrix-core path, or through a workspace copy elsewhere), the running
+total of kvsel_aggregate, kvsel_take and kvsel_order.  End to end: the pruning
+loop, the final re-positioned cache and the decode pass of PrunePath, at small
+sizes for every request and at the full 16-request workload on sampled
+requests.  Tolerances: scores and totals within relative 2e-3 (fp32
+accumulation against fp64), re-rotated keys within one bf16 ulp (>= 99.9%
+equal), decode outputs within 5e-3 absolute, index lists and copies bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import announce, assert_cache_close, assert_rel, device
+from oracle.pipeline import to64
+from query_guided_kv_amd import kvsel as K
+from query_guided_kv_amd import pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+TD = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def rnd(shape, dtype, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (scale * torch.randn(shape, generator=g)).to(TD[dtype])
+
+
+# --------------------------------------------------------------------------
+# kvsel_score_units
+# --------------------------------------------------------------------------
+SU_CASES = [
+    # name, dtype, B, source units, U, listed, H, Hq, T, D, delta, style
+    ("mfma_shared_delta", "bf16", 2, 6, 128, 4, 2, 8, 8, 128, "shared", "half"),
+    ("mfma_instance_delta_interleaved_d64", "bf16", 3, 5, 64, 5, 2, 4, 16, 64, "inst",
+     "interleaved"),
+    ("mfma_no_delta_repeated_units", "bf16", 2, 4, 256, 6, 4, 28, 4, 128, "none", "half"),
+    ("mfma_two_row_passes", "bf16", 1, 3, 512, 3, 1, 8, 40, 128, "shared", "half"),
+    ("copy_stream_rows4", "bf16", 2, 6, 128, 3, 4, 16, 1, 128, "shared", "half"),
+    ("copy_unit96", "bf16", 2, 5, 96, 4, 2, 8, 8, 128, "inst", "half"),
+    ("copy_fp32", "fp32", 2, 4, 128, 3, 2, 4, 4, 64, "shared", "interleaved"),
+]
+
+
+@pytest.mark.parametrize("case", SU_CASES, ids=[c[0] for c in SU_CASES])
+def test_score_units(case):
+    name, dtype, B, n_src, U, n, H, Hq, T, D, dmode, style = case
+    announce("score_units", case=name)
+    dev = device()
+    N = n_src * U
+    # the source is one layer of a two-layer store: a strided view
+    store = rnd((B, 2, N, H, D), dtype, 11, scale=1.5)
+    k = store[:, 1]
+    q = rnd((B, T, Hq, D), dtype, 12)
+    rng = np.random.default_rng(13)
+    if "repeated" in name:
+        units = rng.integers(0, n_src, size=(B, n))
+    else:
+        units = np.stack([rng.permutation(n_src)[:n] for _ in range(B)])
+    if dmode == "shared":
+        delta = np.arange(n) * U + 3                       # slot starts, shifted
+    elif dmode == "inst":
+        delta = rng.integers(-40000, 40000, size=(B, n))
+    else:
+        delta = None
+    scale = 1.0 / np.sqrt(D)
+    args = dict(delta=None if delta is None else torch.from_numpy(delta).to(dev), scale=scale,
+                style=style)
+    store_d = store.to(dev)
+    units_d = torch.from_numpy(units.astype(np.int32)).to(dev)
+    rm, rs, part = K.score_units(q.to(dev), store_d[:, 1], units_d, U, **args)
+    rm2, rs2, _ = K.score_units(q.to(dev), store_d[:, 1], units_d, U, partials=False, **args)
+    torch.cuda.synchronize()
+    k64 = to64(k)
+    rows = (units[:, :, None] * U + np.arange(U)[None, None, :]).reshape(B, n * U)
+    concat = np.stack([k64[b, rows[b]] for b in range(B)])
+    if delta is not None:
+        p_old = np.tile(np.arange(U), n)
+        d = np.broadcast_to(delta, (B, n))
+        p_new = p_old[None] + np.repeat(d, U, axis=1)
+        concat = O.reposition(concat, np.broadcast_to(p_old, (B, n * U)), p_new, 10000.0,
+                              style, dtype)
+    m, Z, p = O.score(to64(q), concat, scale, U)
+    assert_rel(rm, m, 2e-3, 2e-3, "row_max")
+    assert_rel(rs, Z, 2e-3, 0.0, "row_sum")
+    assert_rel(rm2, m, 2e-3, 2e-3, "row_max (statistics alone)")
+    assert_rel(rs2, Z, 2e-3, 0.0, "row_sum (statistics alone)")
+    assert_rel(part[..., 0], p[..., 0], 2e-3, 2e-3, "m_u")
+    assert_rel(part[..., 1], p[..., 1], 2e-3, 0.0, "S_u")
+
+
+def test_score_units_matches_copy_then_score():
+    # the in-place matrix-core path equals: gather the listed units, re-position
+    # them, score the copy (bit-equal keys, so scores within fp32 ordering noise)
+    announce("score_units_vs_copy")
+    dev = device()
+    B, n_src, U, n, H, Hq, T, D = 2, 6, 128, 4, 2, 8, 8, 128
+    k = rnd((B, n_src * U, H, D), "bf16", 21).to(dev)
+    q = rnd((B, T, Hq, D), "bf16", 22).to(dev)
+    units = torch.tensor([[5, 0, 3, 1], [2, 4, 1, 0]], dtype=torch.int32, device=dev)
+    delta = torch.arange(n, dtype=torch.int64, device=dev) * U
+    _, _, part = K.score_units(q, k, units, U, delta=delta, row_stats=False)
+    gk, _ = K.gather(k, None, units, U)
+    kr = K.reposition(gk, delta, U)
+    _, _, part2 = K.score(q, kr, U, row_stats=False)
+    torch.cuda.synchronize()
+    assert_rel(part[..., 0], to64(part2[..., 0]), 1e-5, 1e-5, "m_u")
+    assert_rel(part[..., 1], to64(part2[..., 1]), 1e-5, 0.0, "S_u")
+
+
+# --------------------------------------------------------------------------
+# running totals, take, order
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["chunk", "token"])
+def test_aggregate_accumulates(path):
+    announce("aggregate_accumulate", path=path)
+    dev = device()
+    B, N, H, Hq, T, D, U = 4, 2048, 2, 8, 8, 128, 256
+    q = rnd((B, T, Hq, D), "bf16", 31).to(dev)
+    k = rnd((B, N, H, D), "bf16", 32).to(dev)
+    prev = torch.rand((B // 2, N // U), device=dev) * 10
+    if path == "chunk":
+        _, _, part = K.score(q, k, U, row_stats=False)
+        kw = dict(part=part, cache_shape=tuple(k.shape), q=q)
+    else:
+        rm, rs, _ = K.score(q, k, U, partials=False)
+        kw = dict(q=q, k=k, row_max=rm, row_sum=rs)
+    fresh = K.aggregate(U, 2, "mass", **kw)
+    acc = prev.clone()
+    K.aggregate(U, 2, "mass", out=acc, accumulate=True, **kw)
+    over = prev.clone()
+    K.aggregate(U, 2, "mass", out=over, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, prev + fresh)          # the call's own sum, then one add
+    assert torch.equal(over, fresh)
+
+
+def test_take():
+    announce("take")
+    dev = device()
+    rng = np.random.default_rng(41)
+    G, m, k = 5, 40, 300
+    src = rng.integers(0, 1 << 30, size=(G, m)).astype(np.int32)
+    idx = rng.integers(-3, m + 3, size=(G, k)).astype(np.int32)       # some out of range
+    out = K.take(torch.from_numpy(src).to(dev), torch.from_numpy(idx).to(dev))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), O.take(src, idx))
+
+
+@pytest.mark.parametrize("G,M,k", [(3, 50, 12), (2, 5000, 3000), (128, 512, 64), (1, 7, 7)])
+def test_order(G, M, k):
+    announce("order", G=G, M=M, k=k)
+    dev = device()
+    rng = np.random.default_rng(G * 1000 + k)
+    s = rng.random((G, M)).astype(np.float32)
+    s[:, ::7] = s[:, 1:2]                                  # ties
+    s[:, 3] = -0.0
+    s[:, 4] = 0.0
+    idx = np.stack([rng.permutation(M)[:k] for _ in range(G)]).astype(np.int32)
+    if k > 4:
+        idx[:, 1] = idx[:, 2]                              # a repeated entry
+        idx[:, 0] = M + 1                                  # out of range
+    sd, idd = torch.from_numpy(s).to(dev), torch.from_numpy(idx).to(dev)
+    for desc in (True, False):
+        out, val = K.order(sd, idd, descending=desc, values=True)
+        torch.cuda.synchronize()
+        want = O.order(s.astype(np.float64), idx, descending=desc)
+        np.testing.assert_array_equal(out.cpu().numpy(), want)
+        ok = (want >= 0) & (want < M)
+        wv = np.where(ok, np.take_along_axis(s, np.clip(want, 0, M - 1), axis=1), 0.0)
+        np.testing.assert_array_equal(val.cpu().numpy(), wv.astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# the pruning path
+# --------------------------------------------------------------------------
+def _oracle_request(w, inp, r, score_after_last):
+    L = w.layers
+    q = to64(inp["q"][:, r])                                   # [L][T][Hq][D]
+    k = to64(inp["k"][r * L:(r + 1) * L])
+    res = O.cf_progressive_prune(q, k, w.unit_len, w.scale, w.prune_every, w.k, w.window,
+                                 w.rope_base, w.rope_style, w.dtype,
+                                 score_after_last_prune=score_after_last)
+    return res, k
+
+
+def _margins_ok(res, w):
+    """Well-separated decisions: at every pruning layer the kept minimum and the
+    dropped maximum differ by > 1e-4 relative (and the final totals too for "sort")."""
+    prune = dict(zip(O.cf_prune_layers(w.layers, w.prune_every),
+                     O.cf_keep_schedule(w.M, w.k, w.layers, w.prune_every)))
+    for l, keep in prune.items():
+        if l >= len(res["total"]):
+            continue
+        t = np.sort(res["total"][l])[::-1]
+        if keep < t.size:
+            assert (t[keep - 1] - t[keep]) / t[keep - 1] > 1e-4, ("near tie at layer", l)
+    if w.allocation == "sort":
+        t = np.sort(res["final_total"])
+        assert np.all(np.diff(t) / t[1:] > 1e-4), "near tie in the final order"
+
+
+def _check_request(w, inp, out, trace, r, check_cache=True):
+    res, k64 = _oracle_request(w, inp, r, w.allocation == "sort")
+    _margins_ok(res, w)
+    L, U = w.layers, w.unit_len
+    assert len(trace) == len(res["ids"])
+    for l, (ids, tot) in enumerate(trace):
+        np.testing.assert_array_equal(ids[r].cpu().numpy(), res["ids"][l], err_msg=f"layer {l}")
+        assert_rel(tot[r], res["total"][l], 2e-3, 0.0, f"running totals, layer {l}")
+    final = res["final_sort"] if w.allocation == "sort" else res["final_align"]
+    np.testing.assert_array_equal(out["idx"][r].cpu().numpy(), final)
+    if not check_cache:
+        return
+    v64 = to64(inp["v"][r * L:(r + 1) * L])
+    Kf, Vf = O.cf_final_cache(k64, v64, final, U, 0, w.rope_base, w.rope_style, w.dtype)
+    assert_cache_close(out["k_gather"][r * L:(r + 1) * L], Kf, w.dtype)
+    np.testing.assert_array_equal(to64(out["v_gather"][r * L:(r + 1) * L]), Vf)
+    if "o" in out:
+        qd = to64(inp["q_dec"][r * L:(r + 1) * L])
+        o, lse = O.decode_attention(qd, [(Kf, Vf)], w.scale)
+        assert_rel(out["o"][r * L:(r + 1) * L], o, 0.0, 5e-3, "decode output")
+        assert_rel(out["lse"][r * L:(r + 1) * L], lse, 0.0, 5e-3, "decode lse")
+
+
+BASE = "cachefocus_qwen2_28l_40docs_x512"
+PRUNE_CASES = [
+    # name, overrides of the full workload
+    ("mfma_sort", dict(requests=2, layers=6, prune_every=2, N=8 * 128, unit_len=128, Hq=8, H=2,
+                       T=8, k=2, window=1 << 15)),
+    ("mfma_align_reused_window", dict(requests=2, layers=4, prune_every=2, N=6 * 128,
+                                      unit_len=128, Hq=8, H=2, T=8, k=2, window=3 * 128,
+                                      allocation="align")),
+    ("mfma_uneven_schedule_d64", dict(requests=3, layers=5, prune_every=2, N=7 * 64, unit_len=64,
+                                      Hq=8, H=2, D=64, T=4, k=2, window=1 << 12)),
+    ("copy_rows4_sort", dict(requests=2, layers=4, prune_every=2, N=6 * 128, unit_len=128,
+                             Hq=8, H=2, T=2, k=2, window=1 << 15)),
+    ("qwen2_shape_one_request", dict(requests=1, layers=8, prune_every=4, N=12 * 512, k=4)),
+]
+
+
+@pytest.mark.parametrize("case", PRUNE_CASES, ids=[c[0] for c in PRUNE_CASES])
+def test_prune_path(case):
+    name, over = case
+    announce("prune_path", case=name)
+    dev = device()
+    w = synth.workload(BASE, **over)
+    w = w.scaled(B=w.requests * w.layers)
+    inp = synth.generate(w, 7, dev)
+    path = pipeline.PrunePath(w, inp)
+    trace = []
+    out = path(inp["q"], inp["q_dec"], trace=trace)
+    torch.cuda.synchronize()
+    for r in range(w.requests):
+        _check_request(w, inp, out, trace, r)
+
+
+def test_prune_path_full_workload_sampled():
+    # the 16-request workload in the configuration the benchmark times;
+    # requests 0 and 15 checked against the oracle (every layer, the final
+    # cache of all 28 layers and the decode pass)
+    w = synth.workload(BASE)
+    announce("prune_path_full", workload=w.name)
+    dev = device()
+    inp = synth.generate(w, 0, dev)
+    path = pipeline.PrunePath(w, inp)
+    trace = []
+    out = path(inp["q"], inp["q_dec"], trace=trace)
+    torch.cuda.synchronize()
+    for r in (0, w.requests - 1):
+        announce("prune_path_full_request", request=r)
+        _check_request(w, inp, out, trace, r)
+    # the planted ramp: every request keeps its most relevant documents
+    hits = [len(set(out["idx"][r].tolist()) & set(inp["planted"][r].tolist()))
+            for r in range(w.requests)]
+    assert min(hits) >= w.k - 1, hits
