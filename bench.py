@@ -77,10 +77,10 @@ def elem_bytes(w) -> int:
 def one_pass_decode(w) -> bool:
     """True where refill and decode attention run as one kernel (the streaming
     decode reads each kept row through the index, writes it to the compact
-    cache and attends to it): bf16, head dim 128, <= 8 kv heads and 1, 2, 4
-    or 8 query rows per kv head."""
+    cache and attends to it): bf16, head dim 128, 1, 2, 4 or 8 kv heads and
+    1 to 8 query rows per kv head."""
     rows = (w.Hq // w.H) * w.T
-    return w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8) and w.H in (1, 2, 4, 8)
+    return w.dtype == "bf16" and w.D == 128 and 1 <= rows <= 8 and w.H in (1, 2, 4, 8)
 
 
 def mfma_shape(w) -> bool:
@@ -164,7 +164,7 @@ def kernel_of(stage: str, w) -> str:
     """Name of the kernel that carries a stage's work for workload w."""
     if w.recipe == "cachefocus":
         return {"select": "score_mfma_kernel" if mfma_shape(w) else "score_stream_kernel",
-                "final_gather": "gather_kernel", "decode": "decode_tile_kernel"}[stage]
+                "final_gather": "gather_kernel", "decode": "decode_stream_kernel"}[stage]
     rows = (w.Hq // w.H) * w.T
     stream = w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
     mfma = mfma_shape(w)
@@ -172,7 +172,8 @@ def kernel_of(stage: str, w) -> str:
                      "score_mfma_kernel" if mfma else "score_tile_kernel",
             "aggregate": "agg_mfma_kernel" if mfma else "agg_token_kernel",
             "topk": "topk_kernel", "gather": "gather_kernel",
-            "decode": "decode_mfma_kernel" if mfma else "decode_stream_kernel",
+            "decode": "decode_mfma_kernel" if mfma else
+                      "decode_stream_kernel" if one_pass_decode(w) else "decode_tile_kernel",
             "gather_decode": "decode_stream_kernel"}[stage]
 
 

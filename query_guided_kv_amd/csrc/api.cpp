@@ -624,7 +624,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
   if (ws == nullptr || ws_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "kvsel_gather_decode: workspace %zu < %zu bytes", ws_bytes,
                 need);
-  if (k > 0 && stream_path_ok(kc.dtype, kc.H, kc.D, (Hq / kc.H) * T)) {
+  if (k > 0 && decode_stream_ok(kc.dtype, kc.H, kc.D, (Hq / kc.H) * T)) {
     // one pass: each kept row is read once, copied to the compact cache and attended
     DecodeSeg ds[kMaxSegments];
     int64_t split = 0;

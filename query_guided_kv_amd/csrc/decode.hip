@@ -57,10 +57,12 @@ __device__ __forceinline__ int find_seg(const SegTable& st, int n_seg, int64_t s
 // ---------------------------------------------------------------------------
 // stream variant
 // ---------------------------------------------------------------------------
+// R: query rows per kv head rounded up to 1, 2, 4 or 8; rows past `rows`
+// (the real count) carry zero queries and are not written.
 template <int D, int H, int R, int UNROLL>
 __global__ void __launch_bounds__(kThreads)
 decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t n_split,
-                     int T, int Hq, float scale2, float* __restrict__ ws_ms,
+                     int T, int Hq, int rows, float scale2, float* __restrict__ ws_ms,
                      float* __restrict__ ws_o) {
   constexpr int LPH = D / 16;
   constexpr int LPT = H * LPH;
@@ -101,8 +103,12 @@ decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = g * G + r / T, j = r % T;
-    const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + c * 16);
-    const uint4 q0 = qp[0], q1 = qp[1];
+    uint4 q0 = make_uint4(0, 0, 0, 0), q1 = q0;
+    if (r < rows) {
+      const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + c * 16);
+      q0 = qp[0];
+      q1 = qp[1];
+    }
     qv[r][0] = q0.x; qv[r][1] = q0.y; qv[r][2] = q0.z; qv[r][3] = q0.w;
     qv[r][4] = q1.x; qv[r][5] = q1.y; qv[r][6] = q1.z; qv[r][7] = q1.w;
   }
@@ -246,6 +252,7 @@ decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64
   for (int i = threadIdx.x; i < ROWS * (D + 2); i += kThreads) {
     const int row = i / (D + 2), e = i % (D + 2);
     const int gg = row / R, r = row % R;
+    if (r >= rows) continue;
     const int h = gg * G + r / T, j = r % T;
     const int64_t orow = (b * Hq + h) * T + j;
     if (e < D) ws_o[(orow * n_split + sp) * D + e] = red_o[row][e];
@@ -601,7 +608,8 @@ void launch_stream(const void* q, const SegTable& st, int n_seg, int64_t n_split
   // shape (<= 4 query rows per kv head); 8 query rows keep 4
   hipLaunchKernelGGL((decode_stream_kernel<D, H, R, (R >= 8 ? 4 : 8)>), dim3(static_cast<unsigned>(B * n_split)),
                      dim3(kThreads), 0, s, static_cast<const bf16_t*>(q), st, n_seg, n_split,
-                     static_cast<int>(T), static_cast<int>(Hq), scale2, ms, o);
+                     static_cast<int>(T), static_cast<int>(Hq), static_cast<int>((Hq / H) * T),
+                     scale2, ms, o);
 }
 
 template <typename T, int D, int TPR>
@@ -630,6 +638,11 @@ void dispatch_tile(const void* q, const SegTable& st, int n_seg, int64_t n_split
 
 }  // namespace
 
+bool decode_stream_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv) {
+  return dtype == KVSEL_BF16 && D == 128 && rows_per_kv >= 1 && rows_per_kv <= 8 &&
+         (H == 1 || H == 2 || H == 4 || H == 8);
+}
+
 int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv) {
   (void)H;
   (void)D;
@@ -647,7 +660,7 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
   st.split_len = decode_split_len(dtype, H, D, (Hq / H) * T);
   if (gather != nullptr) {
     // only the streaming variant gathers on the fly
-    if (!stream_path_ok(dtype, H, D, (Hq / H) * T)) {
+    if (!decode_stream_ok(dtype, H, D, (Hq / H) * T)) {
       set_error("kvsel: fused gather is not available for this shape");
       return KVSEL_ERR_UNSUPPORTED;
     }
@@ -672,9 +685,11 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
   const float scale2 = scale * kLog2e;
   const int64_t R = (Hq / H) * T;
   bool done = false;
-  if (stream_path_ok(dtype, H, D, R)) {
+  if (decode_stream_ok(dtype, H, D, R)) {
+    // rows per kv head padded to 1, 2, 4 or 8
+    const int64_t RP = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8;
 #define KVSEL_DS(H_, R_) \
-  if (!done && H == H_ && R == R_) { launch_stream<128, H_, R_>(q, st, n_seg, n_split, B, T, Hq, scale2, ws_ms, ws_o, s); done = true; }
+  if (!done && H == H_ && RP == R_) { launch_stream<128, H_, R_>(q, st, n_seg, n_split, B, T, Hq, scale2, ws_ms, ws_o, s); done = true; }
     KVSEL_DS(8, 1) KVSEL_DS(8, 2) KVSEL_DS(8, 4) KVSEL_DS(8, 8)
     KVSEL_DS(4, 1) KVSEL_DS(4, 2) KVSEL_DS(4, 4) KVSEL_DS(4, 8)
     KVSEL_DS(2, 1) KVSEL_DS(2, 2) KVSEL_DS(2, 4) KVSEL_DS(2, 8)

@@ -135,5 +135,8 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
 
 // Which score / decode path a shape takes (exposed for tests and docs).
 bool stream_path_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);
+// the streaming decode (and the one-pass refill + decode): bf16, head dim 128,
+// <= 8 kv heads (a power of two), 1 .. 8 query rows per kv head
+bool decode_stream_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);
 
 }  // namespace kvsel

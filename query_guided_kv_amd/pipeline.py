@@ -102,7 +102,7 @@ class Path:
         # refill and attention are one call where one kernel does both (it
         # reads each kept row once); the aligned gather re-positions on the way
         rows = (w.Hq // w.H) * w.T
-        one_pass = (w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
+        one_pass = (w.dtype == "bf16" and w.D == 128 and 1 <= rows <= 8
                     and w.H in (1, 2, 4, 8))
         split = w.decode and (w.align or not one_pass)
         self.split = split

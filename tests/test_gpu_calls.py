@@ -266,6 +266,10 @@ DECODE_CASES = [
     ("stream_R4", "bf16", 3, (1300,), 8, 32, 1, 128),
     ("stream_R4_two_segs", "bf16", 2, (1024, 77), 8, 32, 1, 128),
     ("stream_R2_T2", "bf16", 2, (600,), 4, 4, 2, 128),
+    # rows per kv head padded to the next of 1, 2, 4, 8
+    ("stream_R7_padded", "bf16", 3, (2560,), 4, 28, 1, 128),
+    ("stream_R3_padded_two_segs", "bf16", 2, (700, 33), 8, 24, 1, 128),
+    ("stream_R6_T3_padded", "bf16", 2, (900,), 2, 4, 3, 128),
     ("tile_R16_fp32", "fp32", 1, (256,), 4, 4, 16, 64),
     ("tile_R448_two_segs", "bf16", 1, (700, 600), 4, 28, 64, 128),
     ("tile_R32_bf16", "bf16", 1, (1100,), 4, 4, 32, 128),
@@ -300,6 +304,8 @@ GD_CASES = [
     ("fused_R4_chunks", "bf16", 3, 8, 32, 1, 128, 256, 12, 5, 1, ()),
     ("fused_R2_tokens_group_extra", "bf16", 4, 4, 8, 1, 128, 1, 1000, 300, 2, (77,)),
     ("fused_R8_ragged_two_extra", "bf16", 2, 2, 16, 1, 128, 3, 400, 171, 1, (513, 40)),
+    ("fused_R7_padded", "bf16", 2, 4, 28, 1, 128, 512, 8, 5, 1, ()),
+    ("fused_R5_padded_extra", "bf16", 3, 1, 5, 1, 128, 64, 20, 7, 1, (130,)),
     ("tile_R448_refill_extra", "bf16", 1, 4, 28, 16, 128, 8, 300, 37, 1, (300,)),
     ("tile_fp32_d64", "fp32", 2, 4, 4, 16, 64, 64, 10, 3, 1, ()),
     ("fused_k0_extra_only", "bf16", 2, 8, 32, 1, 128, 256, 4, 0, 1, (600,)),
