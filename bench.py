@@ -322,6 +322,11 @@ def main() -> int:
     work = prune_stage_work(w) if prune else stage_work(w)
     marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for s in path.stages} for _ in range(args.steps)]
+    if prune:   # the scorer's launches inside the layer loop, one pair per scored layer
+        for mk in marks:
+            mk["score_layers"] = [(torch.cuda.Event(enable_timing=True),
+                                   torch.cuda.Event(enable_timing=True))
+                                  for _ in range(path.n_scored)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -340,6 +345,14 @@ def main() -> int:
     dom = max(path.stages, key=lambda s: stage_ms[s])     # the stage that takes longest
     dom_ms = stage_ms[dom]
     bound, quantity, peak, unit = stage_bound(dom, w, work[dom])
+    launches = 1
+    if prune and dom == "select":
+        # the layer loop's bytes are the scorer's: time its launches alone
+        # (the aggregates, top-ks and takes between them are excluded)
+        dom_ms = statistics.mean(sum(a.elapsed_time(b) for a, b in m["score_layers"])
+                                 for m in marks)
+        launches = path.n_scored
+        stage_ms["select_scoring"] = dom_ms
     achieved = quantity / (dom_ms * 1e-3)
     kernel = kernel_of(dom, w)
     traffic = stored_traffic(kernel, w.name)
@@ -370,8 +383,9 @@ def main() -> int:
                            "scored_rows_per_step": rows} if prune else {})),
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "kernel": kernel,
-                     "stage": dom, "algorithmic_bytes_per_launch": work[dom][0],
-                     "algorithmic_flops_per_launch": work[dom][1], "avg_launch_ms": dom_ms},
+                     "stage": dom, "algorithmic_bytes_per_launch": work[dom][0] / launches,
+                     "algorithmic_flops_per_launch": work[dom][1] / launches,
+                     "launches_per_step": launches, "avg_launch_ms": dom_ms / launches},
         "path_hbm": {"algorithmic_bytes_per_step": path_bytes,
                      "achieved_GBps": path_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},

@@ -227,17 +227,23 @@ class PrunePath:
         self.n_scored = L if w.allocation == "sort" else last + 1
         self.stages = self.STAGES if w.decode else self.STAGES[:2]
 
-    def select(self, q_layers: torch.Tensor, trace: list = None):
+    def select(self, q_layers: torch.Tensor, trace: list = None, score_marks: list = None):
         """Run the layer loop; returns (final IDs [R][k] in allocation order,
-        their totals in ID order).  ``trace`` collects (ids, totals) per layer."""
+        their totals in ID order).  ``trace`` collects (ids, totals) per layer;
+        ``score_marks`` holds a (start, end) event pair per scored layer,
+        recorded around its scoring call."""
         w = self.w
         U = w.unit_len
         ids, total = self.ids0, None
         for l in range(self.n_scored):
             m = ids.shape[1]
+            if score_marks is not None:
+                score_marks[l][0].record()
             _, _, part = K.score_units(q_layers[l], self.k_layer[:, l], ids, U,
                                        delta=self.delta[m], scale=w.scale, row_stats=False,
                                        partials=True, rope_base=w.rope_base, style=w.rope_style)
+            if score_marks is not None:
+                score_marks[l][1].record()
             if total is None:
                 total = torch.empty((ids.shape[0], m), dtype=torch.float32, device=ids.device)
             K.aggregate(U, 1, "mass", part=part, cache_shape=(ids.shape[0], m * U, w.H, w.D),
@@ -265,7 +271,7 @@ class PrunePath:
 
         out = {}
         mark("select", 0)
-        out["idx"], out["total"] = self.select(q_layers, trace)
+        out["idx"], out["total"] = self.select(q_layers, trace, ev.get("score_layers"))
         mark("select", 1)
         mark("final_gather", 0)
         out["k_gather"], out["v_gather"] = K.gather(self.k, self.v, out["idx"], w.unit_len,
