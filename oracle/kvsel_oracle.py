@@ -46,7 +46,8 @@ __all__ = [
     "cf_reuse_count", "cf_doc_starts", "cf_k_prune", "cf_prune_layers",
     "cf_keep_schedule", "cf_progressive_prune", "cf_final_cache", "take", "order",
     "if_chunk_offsets",
-    "if_global_positions", "if_budget",
+    "if_global_positions", "if_budget", "if_chunk_fractions", "if_reorder",
+    "if_reordered_offsets", "if_two_stage",
 ]
 
 
@@ -617,6 +618,91 @@ def if_global_positions(chunk_lens: Iterable[int]) -> np.ndarray:
     lens = list(chunk_lens)
     off = if_chunk_offsets(lens)
     return np.concatenate([off[i] + np.arange(n) for i, n in enumerate(lens)]).astype(np.int64)
+
+
+def if_chunk_fractions(sel, chunk_lens: Sequence[int]) -> np.ndarray:
+    """[InfoFlow §4.3]: ``r_i = |S^(1) ∩ C_i| / |C_i|``, the share of chunk i's
+    tokens in the first-stage selection.  Chunks lie back to back in storage
+    (chunk i covers the rows after chunks 0..i-1).  ``sel``: selected row
+    indices ``[G][k]``; returns ``[G][n_chunks]``."""
+    sel = np.asarray(sel, dtype=np.int64)
+    lens = np.asarray(list(chunk_lens), dtype=np.int64)
+    bounds = np.concatenate([[0], np.cumsum(lens)])
+    out = np.zeros((sel.shape[0], lens.size), dtype=np.float64)
+    for g in range(sel.shape[0]):
+        chunk = np.searchsorted(bounds, sel[g], side="right") - 1
+        for c in chunk:
+            out[g, c] += 1.0
+    return out / lens[None, :]
+
+
+def if_reorder(r) -> np.ndarray:
+    """[InfoFlow §4.3, §6.2]: the new chunk order, informative chunks nearest
+    the prompt (which follows the context).  Reading for the order: chunks
+    ranked by (r descending, index ascending), the top-k order, and placed so
+    that rank 0 comes last.  Returns ``order[G][n]``: ``order[g][p]`` is the
+    chunk at position p of the new concatenation."""
+    r = np.asarray(r, dtype=np.float64)
+    out = np.empty(r.shape, dtype=np.int64)
+    idx = np.arange(r.shape[1])
+    for g in range(r.shape[0]):
+        ranked = np.lexsort((idx, -r[g]))            # most informative first
+        out[g] = ranked[::-1]
+    return out
+
+
+def if_reordered_offsets(order, chunk_lens: Sequence[int]) -> np.ndarray:
+    """[InfoFlow §4.3]: GLOBAL positions rebuilt for the new concatenated order
+    (``g(t) = Delta_i + p_i(t)`` with ``Delta_i`` the length of the chunks now
+    before chunk i).  Returns ``Delta[G][n]`` indexed by the original chunk."""
+    order = np.asarray(order, dtype=np.int64)
+    lens = np.asarray(list(chunk_lens), dtype=np.int64)
+    out = np.empty(order.shape, dtype=np.int64)
+    for g in range(order.shape[0]):
+        acc = 0
+        for c in order[g]:
+            out[g, c] = acc
+            acc += lens[c]
+    return out
+
+
+def if_two_stage(q, k, v, chunk_lens: Sequence[int], scale: float, budget: int,
+                 group: int = 1, base: float = 10000.0, style: str = "half",
+                 dtype: str = "bf16", signal: str = "vnorm") -> dict:
+    """Two-stage selection with chunk reordering, [InfoFlow §4.3] and [InfoFlow
+    §5.1]'s choice of geometries.
+
+    1. First stage in the HL-TP geometry: the chunks keep their chunk-local
+       positions (the stored keys, no re-positioning) and the prompt sits at
+       its global position (the query block as given).  Token scores
+       (:func:`aggregate`, summed over ``group`` consecutive instances) and the
+       budget ``budget`` (:func:`topk`) give S^(1).
+    2. ``r_i`` (:func:`if_chunk_fractions`), the new order (:func:`if_reorder`)
+       and the GLOBAL positions of that order (:func:`if_reordered_offsets`).
+    3. Second stage: the keys re-positioned from their local positions to
+       ``Delta_i + p_i(t)`` (:func:`reposition`), scored again, and the same
+       budget selected: S^(2), as row indices of the stored cache.
+
+    ``k``, ``v``: ``[B][N][H][D]`` at chunk-local positions; ``q``: ``[B][T][Hq][D]``.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    lens = list(chunk_lens)
+    s1 = aggregate(q, k, v, scale, signal, 1, group)
+    sel1 = topk(s1, budget)
+    r = if_chunk_fractions(sel1, lens)
+    order = if_reorder(r)
+    delta = if_reordered_offsets(order, lens)
+    local = np.concatenate([np.arange(n) for n in lens]).astype(np.int64)
+    chunk_of = np.repeat(np.arange(len(lens)), lens)
+    B = k.shape[0]
+    G = B // group
+    p_new = np.stack([local + delta[b // group][chunk_of] for b in range(B)])
+    k2 = reposition(k, np.broadcast_to(local, (B, local.size)), p_new, base, style, dtype)
+    s2 = aggregate(q, k2, v, scale, signal, 1, group)
+    sel2 = topk(s2, budget)
+    assert s2.shape[0] == G
+    return {"score1": s1, "sel1": sel1, "r": r, "order": order, "delta": delta,
+            "k_rep": k2, "score2": s2, "sel2": sel2}
 
 
 def if_budget(n_tokens: int, ratio: str = "0.15") -> int:
