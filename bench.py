@@ -148,13 +148,28 @@ def prune_stage_work(w) -> dict:
             "decode": (0, 4 * w.B * w.Hq * 1 * w.k * w.unit_len * w.D)}
 
 
+def reorder_stage_work(w) -> dict:
+    """(bytes, flops) per stage of the two-stage selection: each stage reads
+    the keys once (the second also writes the re-positioned keys, a product it
+    scores from) and the values once for their norms; re-reads are
+    implementation cost."""
+    row = w.H * w.D * elem_bytes(w)
+    rows = w.B * w.N
+    qk = 2 * w.B * w.Hq * w.T * w.N * w.D
+    top = (w.B // w.group) * w.M * 4
+    return {"score1": (rows * row, qk), "aggregate1": (rows * row, 0), "topk1": (top, 0),
+            "reorder": (0, 0),
+            "score2": (2 * rows * row, qk), "aggregate2": (rows * row, 0), "topk2": (top, 0)}
+
+
 def stage_bound(stage: str, w, work) -> tuple:
     """(bound, algorithmic quantity, peak, unit) of a stage: the matrix cores
     where the stage runs on them and its flops per algorithmic byte exceed the
     bf16 ridge of MI355X (2.5 PFLOP/s over 8 TB/s = 312.5), else HBM."""
     nbytes, flops = work
     rows = (w.Hq // w.H) * (1 if (w.recipe == "cachefocus" and stage == "decode") else w.T)
-    on_mfma = w.dtype == "bf16" and rows >= 16 and stage in ("score", "decode", "select")
+    on_mfma = w.dtype == "bf16" and rows >= 16 and stage in ("score", "decode", "select",
+                                                             "score1", "score2")
     if on_mfma and flops > MFMA_RIDGE * max(nbytes, 1):
         return "mfma", flops / 1e12, MFMA_BF16_TFLOPS, "TFLOP/s"
     return "hbm", nbytes / 1e9, HBM_PEAK_GBPS, "GB/s"
@@ -165,6 +180,11 @@ def kernel_of(stage: str, w) -> str:
     if w.recipe == "cachefocus":
         return {"select": "score_mfma_kernel" if mfma_shape(w) else "score_stream_kernel",
                 "final_gather": "gather_kernel", "decode": "decode_stream_kernel"}[stage]
+    if w.reorder and stage not in ("score", "aggregate", "topk"):
+        stage = {"score1": "score", "score2": "score", "aggregate1": "aggregate",
+                 "aggregate2": "aggregate", "topk1": "topk", "topk2": "topk"}.get(stage, stage)
+        if stage == "reorder":
+            return "order_kernel"
     rows = (w.Hq // w.H) * w.T
     stream = w.dtype == "bf16" and w.D == 128 and rows in (1, 2, 4, 8)
     mfma = mfma_shape(w)
@@ -225,6 +245,28 @@ def cpu_baseline_prune(w, inp, layers: int = 8) -> dict:
     return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
             "sample": f"request 0, layers 0-{L - 1} of the pruning loop ({rows} scored "
                       f"token-rows; fp64 numpy, 1 thread), {elapsed:.1f} s"}
+
+
+def cpu_baseline_reorder(w, inp) -> dict:
+    """The fp64 oracle's two-stage selection on one layer's share (instance 0
+    as a selection of its own, same budget), single-threaded; rate in scored
+    token-rows per second (two passes over the cache)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import kvsel_oracle as O
+    from oracle import pipeline as OP
+
+    sub = {key: OP.to64(inp[key][0:1]) for key in ("q", "k", "v")}
+    lens = [int(w.plants["chunk_len"])] * (w.N // int(w.plants["chunk_len"]))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.if_two_stage(sub["q"], sub["k"], sub["v"], lens, w.scale, w.k, 1, w.rope_base,
+                       w.rope_style, w.dtype, w.signal)
+        elapsed = time.perf_counter() - t0
+    rows = 2 * w.N
+    log(f"cpu oracle: two-stage selection of instance 0 in {elapsed:.1f} s")
+    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"instance 0 of {w.B} as its own selection (2 x {w.N} scored token-rows; "
+                      f"fp64 numpy, 1 thread), {elapsed:.1f} s"}
 
 
 def cpu_baseline(w, inp, budget_s: float = 12.0, max_instances: int = 8) -> dict:
@@ -319,7 +361,8 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"{args.warmup} warm-up steps done")
 
-    work = prune_stage_work(w) if prune else stage_work(w)
+    work = (prune_stage_work(w) if prune else reorder_stage_work(w) if w.reorder
+            else stage_work(w))
     marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for s in path.stages} for _ in range(args.steps)]
     if prune:   # the scorer's launches inside the layer loop, one pair per scored layer
@@ -358,7 +401,8 @@ def main() -> int:
     traffic = stored_traffic(kernel, w.name)
     # token-rows scored per step: every cached row once, or for the pruning
     # loop the rows of the documents present at each scored layer
-    rows = w.requests * prune_scored_units(w) * w.unit_len if prune else w.B * w.N
+    rows = (w.requests * prune_scored_units(w) * w.unit_len if prune
+            else 2 * w.B * w.N if w.reorder else w.B * w.N)
     path_bytes = sum(b for b, _ in work.values())
 
     result = {
@@ -393,7 +437,9 @@ def main() -> int:
     }
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline_prune(w, inp) if prune else cpu_baseline(w, inp)
+        result["cpu_baseline"] = (cpu_baseline_prune(w, inp) if prune
+                                  else cpu_baseline_reorder(w, inp) if w.reorder
+                                  else cpu_baseline(w, inp))
     print(json.dumps(result), flush=True)
     return 0
 

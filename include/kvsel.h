@@ -15,7 +15,8 @@
  * kvsel_gather_decode).  Three more serve CacheFocus's layer-wise pruning
  * (§2.4-2.5): kvsel_score_units scores a list of units of a cache, re-positioned
  * to their slots, without copying them; kvsel_take composes index lists;
- * kvsel_order lists a kept set by score.
+ * kvsel_order lists a kept set by score.  Two serve InfoFlow's chunk reordering
+ * (§4.3): kvsel_unit_fractions and kvsel_slot_starts.
  *
  * Conventions for every call
  * --------------------------
@@ -298,6 +299,39 @@ int kvsel_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx,
 int kvsel_order(const float* score, int64_t G, int64_t M, const int32_t* idx,
                 int64_t k, int32_t descending, int32_t* idx_out,
                 float* val_out, hipStream_t stream);
+
+/*
+ * kvsel_unit_fractions -- r[g][u] = |sel_g ∩ unit u| / unit_len: the share of
+ * unit u's rows (unit u = rows [u*unit_len, (u+1)*unit_len)) in the index set
+ * sel_g ([InfoFlow §4.3], r_i = |S^(1) ∩ C_i| / |C_i| for equal chunks).
+ *   sel   int32 [G][k], ascending within each row (kvsel_topk's order);
+ *         another order gives unspecified fractions (no fault).
+ *   r     fp32 [G][M]; count / unit_len with one rounding, so equal counts
+ *         give equal values and larger counts larger ones.
+ *   G * M < 2^31, unit_len * M < 2^31.  k may be 0 (all fractions 0).
+ */
+int kvsel_unit_fractions(const int32_t* sel, int64_t G, int64_t k,
+                         int64_t unit_len, int64_t M, float* r,
+                         hipStream_t stream);
+
+/*
+ * kvsel_slot_starts -- the start position of every unit once the units are
+ * concatenated in a new order ([InfoFlow §4.3]: GLOBAL positions
+ * reconstructed for the reordered chunks, g(t) = Delta_i + p_i(t)):
+ *   delta[g*rep + i][order[g][p]] = base + p * unit_len,   i < rep.
+ * With units stored at unit-local positions, delta is the rotation each unit
+ * needs (kvsel_reposition / kvsel_score_reposition with
+ * delta_per_instance = 1; rep = the instances that share a selection row,
+ * e.g. layers).
+ *   order  int32 [G][M], a permutation of 0..M-1 per row (kvsel_order's
+ *          output); entries outside [0, M) are skipped, and units they leave
+ *          out keep what delta held.
+ *   delta  int64 [G*rep][M], not overlapping order.
+ *   G * M < 2^31, 1 <= rep <= 65536, 0 <= base, base + unit_len * M < 2^31.
+ */
+int kvsel_slot_starts(const int32_t* order, int64_t G, int64_t M,
+                      int64_t unit_len, int64_t base, int64_t rep,
+                      int64_t* delta, hipStream_t stream);
 
 /*
  * kvsel_gather -- copy the kept units into a compact cache ("refill",

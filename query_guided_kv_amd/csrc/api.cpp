@@ -464,6 +464,35 @@ int kvsel_order(const float* score, int64_t G, int64_t M, const int32_t* idx, in
   return launch_order(score, G, M, idx, k, descending != 0, idx_out, val_out, stream);
 }
 
+int kvsel_unit_fractions(const int32_t* sel, int64_t G, int64_t k, int64_t unit_len,
+                         int64_t M, float* r, hipStream_t stream) {
+  // one work-item per (row, unit): G * M must fit the dispatch's 32-bit size
+  if (G < 1 || k < 0 || k >= (int64_t{1} << 31) || unit_len < 1 || M < 1 ||
+      M >= (int64_t{1} << 31) || G >= (int64_t{1} << 31) || G * M >= (int64_t{1} << 31) ||
+      unit_len * M >= (int64_t{1} << 31))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_unit_fractions: G=%lld k=%lld unit_len=%lld M=%lld out of range",
+                (long long)G, (long long)k, (long long)unit_len, (long long)M);
+  if (r == nullptr) return fail(KVSEL_ERR_NULL, "r is NULL");
+  if (k > 0 && sel == nullptr) return fail(KVSEL_ERR_NULL, "sel is NULL");
+  if (k > 0 && overlap(r, G * M * 4, sel, G * k * 4))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_unit_fractions: r must not overlap sel");
+  return launch_unit_fractions(sel, G, k, unit_len, M, r, stream);
+}
+
+int kvsel_slot_starts(const int32_t* order, int64_t G, int64_t M, int64_t unit_len, int64_t base,
+                      int64_t rep, int64_t* delta, hipStream_t stream) {
+  if (G < 1 || M < 1 || M >= (int64_t{1} << 31) || unit_len < 1 || rep < 1 || rep > 65536 ||
+      G >= (int64_t{1} << 31) || G * M >= (int64_t{1} << 31) || base < 0 ||
+      base + unit_len * M >= (int64_t{1} << 31))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_slot_starts: G=%lld M=%lld unit_len=%lld rep=%lld base=%lld out of range",
+                (long long)G, (long long)M, (long long)unit_len, (long long)rep, (long long)base);
+  if (order == nullptr || delta == nullptr)
+    return fail(KVSEL_ERR_NULL, "kvsel_slot_starts: order and delta must be set");
+  if (overlap(delta, G * rep * M * 8, order, G * M * 4))
+    return fail(KVSEL_ERR_SHAPE, "kvsel_slot_starts: delta must not overlap order");
+  return launch_slot_starts(order, G, M, unit_len, base, rep, delta, stream);
+}
+
 int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc, int64_t unit_len,
                  const int32_t* idx, int64_t k, int64_t idx_group, const int64_t* src_start,
                  int64_t align_base, double rope_base, int32_t rope_style,

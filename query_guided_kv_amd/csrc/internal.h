@@ -96,6 +96,10 @@ int launch_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx, in
                 int32_t* out, hipStream_t s);
 int launch_order(const float* score, int64_t G, int64_t M, const int32_t* idx, int64_t k,
                  int descending, int32_t* idx_out, float* val_out, hipStream_t s);
+int launch_unit_fractions(const int32_t* sel, int64_t G, int64_t k, int64_t unit_len, int64_t M,
+                          float* r, hipStream_t s);
+int launch_slot_starts(const int32_t* order, int64_t G, int64_t M, int64_t unit_len, int64_t base,
+                       int64_t rep, int64_t* delta, hipStream_t s);
 
 int launch_gather(const void* k_src, const void* v_src, const kvsel_cache& kc, int64_t unit_len,
                   const int32_t* idx, int64_t k, int64_t idx_group, const int64_t* src_start,

@@ -311,7 +311,63 @@ order_kernel(const float* __restrict__ score, int64_t M, const int32_t* __restri
   }
 }
 
+// r[g][u] = |sel_g ∩ unit u| / unit_len (InfoFlow §4.3, the share of chunk
+// u's tokens in a selection): one work-item per (row, unit) counts the
+// ascending index list between the unit's bounds with two binary searches.
+constexpr int kFracThreads = 256;
+
+__device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, int64_t x) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kFracThreads)
+unit_fractions_kernel(const int32_t* __restrict__ sel, int64_t k, int64_t unit_len, int64_t M,
+                      int64_t total, float* __restrict__ r) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kFracThreads + threadIdx.x;
+  if (e >= total) return;
+  const int64_t g = e / M, u = e % M;
+  const int32_t* s = sel + g * k;
+  const int64_t n = lower_bound_i32(s, k, (u + 1) * unit_len) - lower_bound_i32(s, k, u * unit_len);
+  r[e] = static_cast<float>(n) / static_cast<float>(unit_len);
+}
+
+// delta[g * rep + i][order[g][p]] = base + p * unit_len for i < rep: the start
+// of each unit once the units are concatenated in `order` (InfoFlow §4.3,
+// GLOBAL positions rebuilt for the new order).  Entries outside [0, M) are
+// skipped.
+__global__ void __launch_bounds__(kFracThreads)
+slot_starts_kernel(const int32_t* __restrict__ order, int64_t M, int64_t unit_len, int64_t base,
+                   int64_t rep, int64_t total, int64_t* __restrict__ delta) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kFracThreads + threadIdx.x;
+  if (e >= total) return;
+  const int64_t g = e / M, p = e % M;
+  const int32_t c = order[e];
+  if (c < 0 || c >= M) return;
+  for (int64_t i = 0; i < rep; ++i) delta[(g * rep + i) * M + c] = base + p * unit_len;
+}
+
 }  // namespace
+
+int launch_unit_fractions(const int32_t* sel, int64_t G, int64_t k, int64_t unit_len, int64_t M,
+                          float* r, hipStream_t s) {
+  const int64_t total = G * M;
+  hipLaunchKernelGGL(unit_fractions_kernel, dim3(static_cast<unsigned>((total + kFracThreads - 1) / kFracThreads)),
+                     dim3(kFracThreads), 0, s, sel, k, unit_len, M, total, r);
+  return check_launch("kvsel_unit_fractions");
+}
+
+int launch_slot_starts(const int32_t* order, int64_t G, int64_t M, int64_t unit_len, int64_t base,
+                       int64_t rep, int64_t* delta, hipStream_t s) {
+  const int64_t total = G * M;
+  hipLaunchKernelGGL(slot_starts_kernel, dim3(static_cast<unsigned>((total + kFracThreads - 1) / kFracThreads)),
+                     dim3(kFracThreads), 0, s, order, M, unit_len, base, rep, total, delta);
+  return check_launch("kvsel_slot_starts");
+}
 
 int launch_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx, int64_t k,
                 int32_t* out, hipStream_t s) {

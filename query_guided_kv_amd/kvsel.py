@@ -60,6 +60,8 @@ _SIGNATURES = {
     "kvsel_score_units_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, _I32, _I32]),
     "kvsel_take": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "kvsel_order": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P]),
+    "kvsel_unit_fractions": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
+    "kvsel_slot_starts": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "kvsel_aggregate_workspace": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I32, _I32]),
     "kvsel_topk": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "kvsel_gather": (ctypes.c_int, [_P, _P, Cache, _I64, _P, _I64, _I64, _P, _I64, _D, _I32, _P,
@@ -313,6 +315,32 @@ def order(scores: torch.Tensor, idx: torch.Tensor, descending: bool = True,
     _check(lib.kvsel_order(_ptr(scores), G, M, _ptr(idx), kk, int(descending), _ptr(out),
                            _ptr(val), _stream(scores.device)))
     return (out, val) if values else out
+
+
+def unit_fractions(sel: torch.Tensor, unit_len: int, n_units: int) -> torch.Tensor:
+    """kvsel_unit_fractions -> r fp32 [G][n_units]: the share of each unit's
+    rows in the ascending index lists ``sel`` (int32 [G][k])."""
+    lib = load()
+    if sel.dtype != torch.int32 or sel.dim() != 2 or not sel.is_contiguous():
+        raise KvselError(-2, "sel must be contiguous int32 [G][k]")
+    G, kk = sel.shape
+    r = _empty((G, n_units), sel.device)
+    _check(lib.kvsel_unit_fractions(_ptr(sel), G, kk, unit_len, n_units, _ptr(r),
+                                    _stream(sel.device)))
+    return r
+
+
+def slot_starts(order: torch.Tensor, unit_len: int, rep: int = 1, base: int = 0) -> torch.Tensor:
+    """kvsel_slot_starts -> delta int64 [G*rep][M]: each unit's start once the
+    units are concatenated in ``order`` (int32 [G][M], a permutation per row)."""
+    lib = load()
+    if order.dtype != torch.int32 or order.dim() != 2 or not order.is_contiguous():
+        raise KvselError(-2, "order must be contiguous int32 [G][M]")
+    G, M = order.shape
+    delta = torch.empty((G * rep, M), dtype=torch.int64, device=order.device)
+    _check(lib.kvsel_slot_starts(_ptr(order), G, M, unit_len, base, rep, _ptr(delta),
+                                 _stream(order.device)))
+    return delta
 
 
 def gather(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, unit_len: int,

@@ -286,6 +286,82 @@ class PrunePath:
         return out
 
 
+class ReorderPath:
+    """InfoFlow two-stage selection with chunk reordering (§4.3, with the
+    geometries of §5.1), as library calls:
+
+    1. first stage on the stored chunk-local keys (HL-TP: the query block as
+       given, at the prompt's global position): score, token scores summed
+       over the layers of a selection, top-k;
+    2. the share r_i of each chunk's tokens in that selection
+       (:func:`kvsel.unit_fractions`), the chunks listed with the most
+       informative last (:func:`kvsel.order`), and each chunk's start in that
+       order (:func:`kvsel.slot_starts`);
+    3. second stage with the keys re-positioned to those GLOBAL starts (fused
+       into scoring; the re-positioned keys are kept for the token scores),
+       and the same budget selected again.
+    """
+
+    STAGES = ("score1", "aggregate1", "topk1", "reorder", "score2", "aggregate2", "topk2")
+
+    def __init__(self, w, inp: dict):
+        self.w = w
+        self.k, self.v = inp["k"], inp["v"]
+        dev = self.k.device
+        self.chunk_len = int(w.plants["chunk_len"])
+        self.n_chunks = w.N // self.chunk_len
+        G = w.B // w.group
+        self.iota = torch.arange(self.n_chunks, dtype=torch.int32, device=dev).repeat(G, 1)
+        self.k_rep = torch.empty_like(self.k)
+        self.stages = self.STAGES
+
+    def __call__(self, q: torch.Tensor, marks: dict = None) -> dict:
+        w = self.w
+        ev = marks or {}
+
+        def mark(stage, i):
+            pair = ev.get(stage)
+            if pair is not None:
+                pair[i].record()
+
+        def select(k, tag, delta=None):
+            mark("score" + tag, 0)
+            if delta is None:
+                rm, rs, _ = K.score(q, k, 1, w.scale, row_stats=True, partials=False)
+                kk = k
+            else:
+                rm, rs, _ = K.score_reposition(q, k, delta, self.chunk_len, 1, k_out=self.k_rep,
+                                               scale=w.scale, row_stats=True, partials=False,
+                                               rope_base=w.rope_base, style=w.rope_style)
+                kk = self.k_rep
+            mark("score" + tag, 1)
+            mark("aggregate" + tag, 0)
+            s = K.aggregate(1, w.group, w.signal, q=q, k=kk, v=self.v, row_max=rm, row_sum=rs,
+                            scale=w.scale)
+            mark("aggregate" + tag, 1)
+            mark("topk" + tag, 0)
+            idx = K.topk(s, w.k)
+            mark("topk" + tag, 1)
+            return s, idx
+
+        out = {}
+        out["score1"], out["sel1"] = select(self.k, "1")
+        mark("reorder", 0)
+        out["r"] = K.unit_fractions(out["sel1"], self.chunk_len, self.n_chunks)
+        out["order"] = K.order(out["r"], self.iota, descending=False)
+        out["delta"] = K.slot_starts(out["order"], self.chunk_len, rep=w.group)
+        mark("reorder", 1)
+        out["score2"], out["sel2"] = select(self.k, "2", out["delta"])
+        out["k_rep"] = self.k_rep
+        # the product of the path: the final selection and the chunk layout
+        out["idx"], out["unit_score"] = out["sel2"], out["score2"]
+        return out
+
+
 def make_path(w, inp: dict):
     """The launch sequence of workload ``w``."""
-    return PrunePath(w, inp) if w.recipe == "cachefocus" else Path(w, inp)
+    if w.recipe == "cachefocus":
+        return PrunePath(w, inp)
+    if w.reorder:
+        return ReorderPath(w, inp)
+    return Path(w, inp)

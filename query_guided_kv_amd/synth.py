@@ -66,6 +66,7 @@ class Workload:
     layers: int = 1               # layer-wise pruning: layers per request
     prune_every: int = 0          # layer-wise pruning: prune after every n-th layer
     allocation: str = "align"     # layer-wise pruning: final order, "align" or "sort"
+    reorder: bool = False         # two-stage selection with chunk reordering
 
     @property
     def M(self) -> int:
@@ -114,6 +115,17 @@ WORKLOADS: Dict[str, Workload] = {
         name="infoflow_32l_64x1024", recipe="infoflow", B=32, N=65536, Hq=32, H=8, D=128, T=32,
         dtype="bf16", unit_len=1, k=9830, group=32, signal="vnorm",
         reposition="global", decode=False,
+        plants={"chunk_len": 1024, "chunks": 6, "chunk_scale": 1.5,
+                "tokens": 3686, "token_scale": 1.3}),
+    # The same caches with chunk reordering: a first selection on the stored
+    # chunk-local keys (the prompt at its global position), the share r_i of
+    # each chunk's tokens in it, the chunks reordered with the most informative
+    # nearest the prompt, GLOBAL positions rebuilt for that order, and the
+    # same 15% budget selected again.
+    "infoflow_reorder_32l_64x1024": Workload(
+        name="infoflow_reorder_32l_64x1024", recipe="infoflow", B=32, N=65536, Hq=32, H=8,
+        D=128, T=32, dtype="bf16", unit_len=1, k=9830, group=32, signal="vnorm",
+        reposition="global", decode=False, reorder=True,
         plants={"chunk_len": 1024, "chunks": 6, "chunk_scale": 1.5,
                 "tokens": 3686, "token_scale": 1.3}),
     # Batched serving: 16 requests x 8 layers, 131072 cached tokens each, GQA

@@ -186,6 +186,24 @@ def test_take_and_order_validation(lib):
     assert lib.kvsel_order(None, 2, 10, None, 0, 1, None, None, None) == OK
 
 
+def test_unit_fractions_and_slot_starts_validation(lib):
+    # every call below fails validation: nothing is launched
+    p = ctypes.c_void_p(FAKE)
+    q = ctypes.c_void_p(FAKE + 4096)
+    assert lib.kvsel_unit_fractions(p, 1, 10, 1024, 64, None, None) == NULL
+    assert lib.kvsel_unit_fractions(None, 1, 10, 1024, 64, q, None) == NULL
+    assert lib.kvsel_unit_fractions(p, 0, 10, 1024, 64, q, None) == SHAPE
+    assert lib.kvsel_unit_fractions(p, 1, 10, 0, 64, q, None) == SHAPE
+    assert lib.kvsel_unit_fractions(p, 1, 10, 1 << 20, 1 << 12, q, None) == SHAPE   # rows >= 2^31
+    assert lib.kvsel_unit_fractions(p, 1, 10, 1024, 64, ctypes.c_void_p(FAKE + 8), None) == SHAPE
+    assert lib.kvsel_slot_starts(None, 1, 64, 1024, 0, 32, q, None) == NULL
+    assert lib.kvsel_slot_starts(p, 1, 64, 1024, 0, 32, None, None) == NULL
+    assert lib.kvsel_slot_starts(p, 1, 64, 1024, 0, 0, q, None) == SHAPE            # rep < 1
+    assert lib.kvsel_slot_starts(p, 1, 64, 1024, -1, 1, q, None) == SHAPE           # base < 0
+    assert lib.kvsel_slot_starts(p, 1, 64, 1 << 25, 0, 1, q, None) == SHAPE         # positions >= 2^31
+    assert lib.kvsel_slot_starts(p, 1, 64, 1024, 0, 2, ctypes.c_void_p(FAKE + 128), None) == SHAPE
+
+
 def test_topk_validation(lib):
     p = ctypes.c_void_p(FAKE)
     assert lib.kvsel_topk(None, 1, 10, 2, p, None, None) == NULL
