@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak, vendor figure
+HOST_LINK_GBPS = 64.0           # PCIe 5.0 x16, one direction (MI355X's host link)
 MFMA_RIDGE = MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop per byte
 DEFAULT_WORKLOAD = "serving_16req_8l_128k"
 PROFILES = os.path.join(ROOT, "profiles")
@@ -167,6 +168,10 @@ def stage_bound(stage: str, w, work) -> tuple:
     where the stage runs on them and its flops per algorithmic byte exceed the
     bf16 ridge of MI355X (2.5 PFLOP/s over 8 TB/s = 312.5), else HBM."""
     nbytes, flops = work
+    if w.l2_host and stage == "gather":
+        # the kept L2 rows cross the host link once (half of the gather's
+        # algorithmic bytes: they are then written to HBM)
+        return "host_link", nbytes / 2 / 1e9, HOST_LINK_GBPS, "GB/s"
     rows = (w.Hq // w.H) * (1 if (w.recipe == "cachefocus" and stage == "decode") else w.T)
     on_mfma = w.dtype == "bf16" and rows >= 16 and stage in ("score", "decode", "select",
                                                              "score1", "score2")
@@ -344,6 +349,24 @@ def main() -> int:
         del src, dst
         log("copy probe: 3 x (1 GiB read + 1 GiB written) done")
 
+    host_link = None
+    if w.l2_host:
+        # the host link's DMA rate: 1 GiB pinned host -> device, timed on the GPU clock
+        src = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
+        dst = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(2):
+            dst.copy_(src, non_blocking=True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        host_link = {"dma_copy_GBps": 5 * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9,
+                     "peak_GBps": HOST_LINK_GBPS}
+        del src, dst
+        log(f"host link: pinned -> device copy at {host_link['dma_copy_GBps']:.1f} GB/s")
+
     t0 = time.perf_counter()
     inp = synth.generate(w, args.seed, dev)
     torch.cuda.synchronize()
@@ -435,6 +458,8 @@ def main() -> int:
                      "frac": path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "stages_ms": stage_ms,
     }
+    if host_link is not None:
+        result["host_link"] = host_link
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = (cpu_baseline_prune(w, inp) if prune

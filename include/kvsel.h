@@ -358,6 +358,13 @@ int kvsel_slot_starts(const int32_t* order, int64_t G, int64_t M,
  * are copied unchanged.  Not available in nested mode.
  *
  *   v_src / v_dst (and v_proxy) may be NULL to gather keys only.
+ *
+ * Host-resident source ([ACRE §2.2, §2.4]: the L2 cache offloaded to CPU
+ * memory, the L1 cache kept on the GPU): k_src / v_src may be pinned host
+ * memory (hipHostMalloc).  The same kernel then reads only the kept rows,
+ * over the host link, through the device address the runtime maps them to.
+ * Pageable host memory is refused with KVSEL_ERR_UNSUPPORTED before anything
+ * is enqueued.  Every other pointer is device memory.
  */
 int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc,
                  int64_t unit_len, const int32_t* idx, int64_t k,
@@ -396,13 +403,14 @@ size_t kvsel_decode_workspace(int64_t T, int64_t Hq, const kvsel_segment* segs,
  * Same result as kvsel_gather in the compact layout (no re-positioning, no
  * proxy cache) into (k_dst, v_dst), followed by kvsel_decode_attn over the
  * segments extra[0 .. n_extra) plus that compact cache.  Where the shape
- * allows it (bf16, head dim 128, H in {1,2,4,8} and (Hq / H) * T in
- * {1,2,4,8}) one kernel reads every kept row once, writes it to the compact
- * cache and attends to it from registers; otherwise the kernels of the two
- * separate calls run back to back.
+ * allows it (bf16, head dim 128, H in {1,2,4,8} and 1 <= (Hq / H) * T <= 8)
+ * one kernel reads every kept row once, writes it to the compact cache and
+ * attends to it from registers; otherwise the kernels of the two separate
+ * calls run back to back.
  *
  *   q, T, Hq, scale   as in kvsel_decode_attn.
- *   k_src, v_src, kc, unit_len, idx, k, idx_group   as in kvsel_gather.  Every
+ *   k_src, v_src, kc, unit_len, idx, k, idx_group   as in kvsel_gather
+ *                     (pinned host memory allowed for k_src / v_src).  Every
  *                     index must lie in [0, M); a slot outside that range is
  *                     never read from or written to, and the output is then
  *                     unspecified.

@@ -40,6 +40,37 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Where the rows of a gather source live.  Device (and managed) memory is read
+// directly; pinned host memory through the device address the runtime maps it
+// to, over the host link; anything else, pageable host memory in particular,
+// is refused here, before a kernel could touch it.
+int resolve_rows(const void* p, const void** out, const char* name) {
+  hipPointerAttribute_t a{};
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // leave no sticky error for the next launch check
+    return fail(KVSEL_ERR_UNSUPPORTED,
+                "%s: neither device memory nor pinned host memory (%s)", name, hipGetErrorString(e));
+  }
+  switch (a.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      *out = p;
+      return KVSEL_OK;
+    case hipMemoryTypeHost:
+      if (a.devicePointer == nullptr)
+        return fail(KVSEL_ERR_UNSUPPORTED, "%s: pinned host memory without a device mapping", name);
+      if ((reinterpret_cast<uintptr_t>(a.devicePointer) & 15u) != 0)
+        return fail(KVSEL_ERR_UNSUPPORTED, "%s: mapped host address is not 16-byte aligned", name);
+      *out = a.devicePointer;
+      return KVSEL_OK;
+    default:
+      return fail(KVSEL_ERR_UNSUPPORTED,
+                  "%s: pageable host memory; allocate it pinned (hipHostMalloc)", name);
+  }
+}
+
 // do the byte ranges [a, a + na) and [b, b + nb) share a byte?
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -537,10 +568,16 @@ int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc, int64_t u
       return fail(KVSEL_ERR_UNSUPPORTED, "kvsel_gather: re-positioning is not available in nested mode");
     dst_rows += proxy->N;
   }
-  if (k > 0)
-    KVSEL_TRY(launch_gather(k_src, v_src, kc, unit_len, idx, k, idx_group, src_start, align_base,
+  if (k > 0) {
+    // the kept rows may live in pinned host memory (a host-resident cache)
+    const void* ks = nullptr;
+    const void* vs = nullptr;
+    KVSEL_TRY(resolve_rows(k_src, &ks, "k_src"));
+    if (v_src != nullptr) KVSEL_TRY(resolve_rows(v_src, &vs, "v_src"));
+    KVSEL_TRY(launch_gather(ks, vs, kc, unit_len, idx, k, idx_group, src_start, align_base,
                             rope_base, rope_style, proxy != nullptr, dst_rows, k_dst, v_dst,
                             stream));
+  }
   if (proxy != nullptr)
     return launch_proxy_copy(k_proxy, v_proxy, *proxy, unit_len, idx, k, idx_group, dst_rows,
                              k_dst, v_dst, stream);
@@ -653,6 +690,10 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
   if (ws == nullptr || ws_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "kvsel_gather_decode: workspace %zu < %zu bytes", ws_bytes,
                 need);
+  if (k > 0) {  // the kept rows may live in pinned host memory
+    KVSEL_TRY(resolve_rows(k_src, &k_src, "k_src"));
+    KVSEL_TRY(resolve_rows(v_src, &v_src, "v_src"));
+  }
   if (k > 0 && decode_stream_ok(kc.dtype, kc.H, kc.D, (Hq / kc.H) * T)) {
     // one pass: each kept row is read once, copied to the compact cache and attended
     DecodeSeg ds[kMaxSegments];

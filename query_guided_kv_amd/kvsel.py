@@ -347,17 +347,20 @@ def gather(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, unit_l
            idx_group: int = 1, src_start: Optional[torch.Tensor] = None, align_base: int = -1,
            rope_base: float = 10000.0, style: str = "half",
            proxy_k: Optional[torch.Tensor] = None, proxy_v: Optional[torch.Tensor] = None):
-    """kvsel_gather -> (k_dst, v_dst): compact, or nested with a proxy cache."""
+    """kvsel_gather -> (k_dst, v_dst): compact, or nested with a proxy cache.
+    ``k`` / ``v`` may be pinned host tensors (a host-resident cache); the
+    outputs are on the device of ``idx``."""
     lib = load()
     B, N, H, D = k.shape
     kk = idx.shape[1]
+    dev = idx.device
     rows = kk * unit_len + (proxy_k.shape[1] if proxy_k is not None else 0)
-    kd = torch.empty((B, rows, H, D), dtype=k.dtype, device=k.device)
+    kd = torch.empty((B, rows, H, D), dtype=k.dtype, device=dev)
     vd = torch.empty_like(kd) if v is not None else None
     pdesc = ctypes.pointer(cache_desc(proxy_k)) if proxy_k is not None else None
     _check(lib.kvsel_gather(_ptr(k), _ptr(v), cache_desc(k), unit_len, _ptr(idx), kk, idx_group,
                             _ptr(src_start), align_base, rope_base, ROPE[style], _ptr(proxy_k),
-                            _ptr(proxy_v), pdesc, _ptr(kd), _ptr(vd), _stream(k.device)))
+                            _ptr(proxy_v), pdesc, _ptr(kd), _ptr(vd), _stream(dev)))
     return kd, vd
 
 
@@ -389,7 +392,7 @@ def gather_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     _, N, H, _ = k.shape
     kk = idx.shape[1]
     scale = 1.0 / D ** 0.5 if scale is None else scale
-    kd = torch.empty((B, kk * unit_len, H, D), dtype=k.dtype, device=k.device)
+    kd = torch.empty((B, kk * unit_len, H, D), dtype=k.dtype, device=q.device)
     vd = torch.empty_like(kd)
     n_extra = len(extra)
     segs = (Segment * max(1, n_extra))(*[Segment(a.data_ptr(), b.data_ptr(), cache_desc(a))

@@ -67,6 +67,7 @@ class Workload:
     prune_every: int = 0          # layer-wise pruning: prune after every n-th layer
     allocation: str = "align"     # layer-wise pruning: final order, "align" or "sort"
     reorder: bool = False         # two-stage selection with chunk reordering
+    l2_host: bool = False         # bi-layer refill: L2 cache in pinned host memory
 
     @property
     def M(self) -> int:
@@ -106,6 +107,13 @@ WORKLOADS: Dict[str, Workload] = {
     "acre_bilayer_l1_16k_l2_128k": Workload(
         name="acre_bilayer_l1_16k_l2_128k", recipe="bilayer", B=1, N=16384, Hq=28, H=4, D=128, T=64,
         dtype="bf16", unit_len=1, k=2048, refill_interval=8,
+        plants={"planted": 2048, "gamma": 1.0, "l1_noise_std": 0.1}),
+    # The same bi-layer cache with L2 offloaded to (pinned) host memory and L1
+    # kept on the GPU: the refill reads only the kept L2 blocks over the host
+    # link.
+    "acre_bilayer_host_l2_l1_16k_l2_128k": Workload(
+        name="acre_bilayer_host_l2_l1_16k_l2_128k", recipe="bilayer", B=1, N=16384, Hq=28,
+        H=4, D=128, T=64, dtype="bf16", unit_len=1, k=2048, refill_interval=8, l2_host=True,
         plants={"planted": 2048, "gamma": 1.0, "l1_noise_std": 0.1}),
     # Token-level recompute selection: 32 layers, GQA 32/8, head dim 128, bf16;
     # 64 chunks x 1024 tokens at chunk-local positions; re-rotated to global
@@ -252,9 +260,13 @@ def _gen_bilayer(w: Workload, seed: int, device) -> dict:
     v1 = v2t.float().numpy().reshape(w.B, w.N, l, w.H, w.D).mean(axis=2)
     k1 = k1 + std * rng.standard_normal(k1.shape, dtype=np.float32)
     v1 = v1 + std * rng.standard_normal(v1.shape, dtype=np.float32)
+    if w.l2_host:   # a fresh pinned (page-locked) host allocation the GPU can read
+        l2_k, l2_v = k2t.pin_memory(), v2t.pin_memory()
+    else:
+        l2_k, l2_v = k2t.to(device), v2t.to(device)
     return dict(q=_to_cache(q, w.dtype, device),
                 k=_to_cache(k1, w.dtype, device), v=_to_cache(v1, w.dtype, device),
-                l2_k=k2t.to(device), l2_v=v2t.to(device),
+                l2_k=l2_k, l2_v=l2_v,
                 planted=[chosen.astype(np.int64)] * (w.B // w.group))
 
 
