@@ -42,7 +42,7 @@ __all__ = [
     "round_bf16", "round_to", "rope_theta", "rope_pairs", "rope_rotate",
     "reposition", "logits", "attention_weights", "score", "combine_partials",
     "aggregate", "acre_mean_pool", "topk", "gather", "gather_aligned",
-    "refill_nested", "decode_attention", "acre_k", "cf_group_size",
+    "refill_nested", "decode_attention", "index_causal_attention", "acre_k", "cf_group_size",
     "cf_reuse_count", "cf_doc_starts", "cf_k_prune", "cf_prune_layers",
     "cf_keep_schedule", "cf_progressive_prune", "cf_final_cache", "take", "order",
     "if_chunk_offsets",
@@ -407,6 +407,43 @@ def decode_attention(q, segments: Sequence, scale: float):
         for h in range(Hq):
             o[b, :, h, :] = A[b, h] @ V[b, :, _kv_head(h, Hq, H), :]
     return o, m + np.log(Z)
+
+
+def index_causal_attention(q, k, v, pos, scale: float):
+    """Attention of selected tokens to the context under a causal constraint
+    ([InfoFlow §4.2] KV recomputation: a selected token is run at its global
+    position, so it attends to every context row up to and including its own;
+    [InfoFlow §8]: an index-based causal pattern, neither dense nor strictly
+    causal).
+
+    ``q``: ``[B][S][Hq][D]``, the queries of the S selected tokens;
+    ``pos``: ``[B][S]``, their positions in the context; ``k``, ``v``:
+    ``[B][N][H][D]``.  Row (b, i, h) attends to keys ``0 .. pos[b][i]``
+    (clipped to N - 1); a negative position attends to nothing and gives a
+    zero row and lse = -inf.  Returns ``(o [B][S][Hq][D], lse [B][Hq][S])``
+    with lse the natural log of the row's sum of exp(logit).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    B, S, Hq, D = q.shape
+    N, H = k.shape[1], k.shape[2]
+    o = np.zeros((B, S, Hq, v.shape[-1]), dtype=np.float64)
+    lse = np.full((B, Hq, S), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for i in range(S):
+            n = min(int(pos[b, i]), N - 1) + 1
+            if n <= 0:
+                continue
+            for h in range(Hq):
+                g = _kv_head(h, Hq, H)
+                lg = scale * (k[b, :n, g, :] @ q[b, i, h, :])
+                m = lg.max()
+                e = np.exp(lg - m)
+                o[b, i, h] = (e @ v[b, :n, g, :]) / e.sum()
+                lse[b, h, i] = m + np.log(e.sum())
+    return o, lse
 
 
 # ---------------------------------------------------------------------------
