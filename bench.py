@@ -163,6 +163,17 @@ def reorder_stage_work(w) -> dict:
             "score2": (2 * rows * row, qk), "aggregate2": (rows * row, 0), "topk2": (top, 0)}
 
 
+def recompute_stage_work(w, pos) -> dict:
+    """(bytes, flops) of the recomputation attention: every selected row reads
+    keys 0 .. pos (2 flops per multiply-add of q.k and of p.v); the context's K
+    and V are read once (re-reads by other row blocks are implementation cost)."""
+    import numpy as np
+    p = np.minimum(np.asarray(pos.cpu(), np.int64), w.N - 1) + 1
+    keys = int(np.clip(p, 0, None).sum())                 # over instances and rows
+    row = w.H * w.D * elem_bytes(w)
+    return {"recompute": (2 * w.B * w.N * row, 4 * w.Hq * w.D * keys)}
+
+
 def stage_bound(stage: str, w, work) -> tuple:
     """(bound, algorithmic quantity, peak, unit) of a stage: the matrix cores
     where the stage runs on them and its flops per algorithmic byte exceed the
@@ -174,7 +185,7 @@ def stage_bound(stage: str, w, work) -> tuple:
         return "host_link", nbytes / 2 / 1e9, HOST_LINK_GBPS, "GB/s"
     rows = (w.Hq // w.H) * (1 if (w.recipe == "cachefocus" and stage == "decode") else w.T)
     on_mfma = w.dtype == "bf16" and rows >= 16 and stage in ("score", "decode", "select",
-                                                             "score1", "score2")
+                                                             "score1", "score2", "recompute")
     if on_mfma and flops > MFMA_RIDGE * max(nbytes, 1):
         return "mfma", flops / 1e12, MFMA_BF16_TFLOPS, "TFLOP/s"
     return "hbm", nbytes / 1e9, HBM_PEAK_GBPS, "GB/s"
@@ -185,6 +196,8 @@ def kernel_of(stage: str, w) -> str:
     if w.recipe == "cachefocus":
         return {"select": "score_mfma_kernel" if mfma_shape(w) else "score_stream_kernel",
                 "final_gather": "gather_kernel", "decode": "decode_stream_kernel"}[stage]
+    if stage == "recompute":
+        return "index_attn_kernel"
     if w.reorder and stage not in ("score", "aggregate", "topk"):
         stage = {"score1": "score", "score2": "score", "aggregate1": "aggregate",
                  "aggregate2": "aggregate", "topk1": "topk", "topk2": "topk"}.get(stage, stage)
@@ -272,6 +285,31 @@ def cpu_baseline_reorder(w, inp) -> dict:
     return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
             "sample": f"instance 0 of {w.B} as its own selection (2 x {w.N} scored token-rows; "
                       f"fp64 numpy, 1 thread), {elapsed:.1f} s"}
+
+
+def cpu_baseline_recompute(w, inp, rows: int = 64) -> dict:
+    """The fp64 oracle on a sample of the recomputation: ``rows`` selected
+    tokens of layer 0 (every head), single-threaded; rate in attended
+    (row, key) pairs per second, the unit the GPU line reports."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import kvsel_oracle as O
+    from oracle import pipeline as OP
+
+    S = inp["pos"].shape[1]
+    pick = np.linspace(0, S - 1, rows).astype(np.int64)
+    q = OP.to64(inp["q_sel"][0:1])[:, pick]
+    pos = inp["pos"][0:1].cpu().numpy()[:, pick]
+    k, v = OP.to64(inp["k"][0:1]), OP.to64(inp["v"][0:1])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.index_causal_attention(q, k, v, pos, w.scale)
+        elapsed = time.perf_counter() - t0
+    pairs = int((np.minimum(pos, w.N - 1) + 1).sum())
+    log(f"cpu oracle: {rows} recomputed rows in {elapsed:.1f} s")
+    return {"value": pairs / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {S} selected tokens of layer 0, every head ({pairs} attended "
+                      f"context rows; fp64 numpy, 1 thread), {elapsed:.1f} s"}
 
 
 def cpu_baseline(w, inp, budget_s: float = 12.0, max_instances: int = 8) -> dict:
@@ -375,6 +413,8 @@ def main() -> int:
     path = pipeline.make_path(w, inp)
     if prune:
         step = lambda i, m=None: path(inp["q"], inp["q_dec"], m)
+    elif w.recompute:
+        step = lambda i, m=None: path(inp["q_sel"], m)
     else:
         queries = make_queries(w, inp, args.warmup + args.steps, args.seed, dev)
         step = lambda i, m=None: path(queries[i], m)
@@ -385,7 +425,7 @@ def main() -> int:
     log(f"{args.warmup} warm-up steps done")
 
     work = (prune_stage_work(w) if prune else reorder_stage_work(w) if w.reorder
-            else stage_work(w))
+            else recompute_stage_work(w, inp["pos"]) if w.recompute else stage_work(w))
     marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for s in path.stages} for _ in range(args.steps)]
     if prune:   # the scorer's launches inside the layer loop, one pair per scored layer
@@ -425,7 +465,8 @@ def main() -> int:
     # token-rows scored per step: every cached row once, or for the pruning
     # loop the rows of the documents present at each scored layer
     rows = (w.requests * prune_scored_units(w) * w.unit_len if prune
-            else 2 * w.B * w.N if w.reorder else w.B * w.N)
+            else 2 * w.B * w.N if w.reorder
+            else work["recompute"][1] // (4 * w.Hq * w.D) if w.recompute else w.B * w.N)
     path_bytes = sum(b for b, _ in work.values())
 
     result = {
@@ -464,6 +505,7 @@ def main() -> int:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = (cpu_baseline_prune(w, inp) if prune
                                   else cpu_baseline_reorder(w, inp) if w.reorder
+                                  else cpu_baseline_recompute(w, inp) if w.recompute
                                   else cpu_baseline(w, inp))
     print(json.dumps(result), flush=True)
     return 0

@@ -16,7 +16,8 @@
  * (§2.4-2.5): kvsel_score_units scores a list of units of a cache, re-positioned
  * to their slots, without copying them; kvsel_take composes index lists;
  * kvsel_order lists a kept set by score.  Two serve InfoFlow's chunk reordering
- * (§4.3): kvsel_unit_fractions and kvsel_slot_starts.
+ * (§4.3): kvsel_unit_fractions and kvsel_slot_starts.  kvsel_index_attn
+ * attends selected tokens causally to the context (InfoFlow's recomputation).
  *
  * Conventions for every call
  * --------------------------
@@ -299,6 +300,31 @@ int kvsel_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx,
 int kvsel_order(const float* score, int64_t G, int64_t M, const int32_t* idx,
                 int64_t k, int32_t descending, int32_t* idx_out,
                 float* val_out, hipStream_t stream);
+
+/*
+ * kvsel_index_attn -- attention of selected tokens to the context under a
+ * causal constraint: the recomputation of selected tokens at their global
+ * positions ([InfoFlow §4.2] KV recomputation; [InfoFlow §8] the index-based
+ * causal pattern, neither dense nor strictly causal).
+ *
+ * Selected token j of instance b sits at context position pos[b][j]; its query
+ * row for head h attends to keys 0 .. min(pos[b][j], N - 1), its own row
+ * included:
+ *   out[b,j,h,:] = sum_{t <= pos} softmax_t(scale * q[b,j,h,:] . k[b,t,kv(h),:]) v[b,t,kv(h),:]
+ *   lse[b,h,j]   = natural log of sum_{t <= pos} exp(scale * q . k_t)
+ * A negative position attends to nothing: a zero row and lse = -inf.
+ *
+ *   q      [B][S][Hq][D] bf16, the selected tokens' queries.
+ *   pos    int32 [B][S], device; any order (ascending keeps a workgroup's
+ *          rows close together and is fastest).
+ *   k, v   the context, cache `kc` (bf16 only: the matrix-core kernel).
+ *   out    fp32 [B][S][Hq][D];  lse fp32 [B][Hq][S] or NULL.
+ *   S * Hq < 2^31.  No workspace: every row's output is written once.
+ */
+int kvsel_index_attn(const void* q, int64_t S, int64_t Hq, float scale,
+                     const void* k, const void* v, kvsel_cache kc,
+                     const int32_t* pos, float* out, float* lse,
+                     hipStream_t stream);
 
 /*
  * kvsel_unit_fractions -- r[g][u] = |sel_g ∩ unit u| / unit_len: the share of

@@ -495,6 +495,26 @@ int kvsel_order(const float* score, int64_t G, int64_t M, const int32_t* idx, in
   return launch_order(score, G, M, idx, k, descending != 0, idx_out, val_out, stream);
 }
 
+int kvsel_index_attn(const void* q, int64_t S, int64_t Hq, float scale, const void* k,
+                     const void* v, kvsel_cache kc, const int32_t* pos, float* out, float* lse,
+                     hipStream_t stream) {
+  const char* what = "kvsel_index_attn";
+  KVSEL_TRY(check_ptr(q, "q"));
+  KVSEL_TRY(check_ptr(k, "k"));
+  KVSEL_TRY(check_ptr(v, "v"));
+  if (pos == nullptr) return fail(KVSEL_ERR_NULL, "pos is NULL");
+  if (out == nullptr) return fail(KVSEL_ERR_NULL, "out is NULL");
+  KVSEL_TRY(check_cache(kc, what));
+  if (kc.dtype != KVSEL_BF16)
+    return fail(KVSEL_ERR_UNSUPPORTED, "%s: bf16 caches only (matrix cores)", what);
+  if (S < 1 || Hq < 1 || Hq % kc.H != 0 || Hq > 4096 || S >= (int64_t{1} << 31) / Hq)
+    return fail(KVSEL_ERR_SHAPE, "%s: need S >= 1, Hq a multiple of H, S * Hq < 2^31", what);
+  // 512 work-items per workgroup: the dispatch counts work-items in 32 bits
+  if (index_attn_blocks(kc, S, Hq) >= (int64_t{1} << 23))
+    return fail(KVSEL_ERR_SHAPE, "%s: too many rows for one launch", what);
+  return launch_index_attn(q, S, Hq, scale, k, v, kc, pos, out, lse, stream);
+}
+
 int kvsel_unit_fractions(const int32_t* sel, int64_t G, int64_t k, int64_t unit_len,
                          int64_t M, float* r, hipStream_t stream) {
   // one work-item per (row, unit): G * M must fit the dispatch's 32-bit size

@@ -96,6 +96,12 @@ int launch_take(const int32_t* src, int64_t G, int64_t m, const int32_t* idx, in
                 int32_t* out, hipStream_t s);
 int launch_order(const float* score, int64_t G, int64_t M, const int32_t* idx, int64_t k,
                  int descending, int32_t* idx_out, float* val_out, hipStream_t s);
+// index-based causal attention (index_attn.hip): workgroups of the launch,
+// and the launch
+int64_t index_attn_blocks(const kvsel_cache& kc, int64_t S, int64_t Hq);
+int launch_index_attn(const void* q, int64_t S, int64_t Hq, float scale, const void* k,
+                      const void* v, const kvsel_cache& kc, const int32_t* pos, float* out,
+                      float* lse, hipStream_t s);
 int launch_unit_fractions(const int32_t* sel, int64_t G, int64_t k, int64_t unit_len, int64_t M,
                           float* r, hipStream_t s);
 int launch_slot_starts(const int32_t* order, int64_t G, int64_t M, int64_t unit_len, int64_t base,

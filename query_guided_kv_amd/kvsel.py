@@ -60,6 +60,7 @@ _SIGNATURES = {
     "kvsel_score_units_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, _I32, _I32]),
     "kvsel_take": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "kvsel_order": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P]),
+    "kvsel_index_attn": (ctypes.c_int, [_P, _I64, _I64, _F, _P, _P, Cache, _P, _P, _P, _P]),
     "kvsel_unit_fractions": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
     "kvsel_slot_starts": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "kvsel_aggregate_workspace": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I32, _I32]),
@@ -315,6 +316,24 @@ def order(scores: torch.Tensor, idx: torch.Tensor, descending: bool = True,
     _check(lib.kvsel_order(_ptr(scores), G, M, _ptr(idx), kk, int(descending), _ptr(out),
                            _ptr(val), _stream(scores.device)))
     return (out, val) if values else out
+
+
+def index_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor,
+               scale: Optional[float] = None, want_lse: bool = True):
+    """kvsel_index_attn -> (o fp32 [B][S][Hq][D], lse [B][Hq][S] or None): the
+    selected tokens' queries ``q`` [B][S][Hq][D] attend to keys 0 .. pos[b][j]."""
+    lib = load()
+    B, S, Hq, D = q.shape
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B, S) or not pos.is_contiguous():
+        raise KvselError(-2, "pos must be contiguous int32 [B][S]")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise KvselError(-2, "k and v must share shape and strides")
+    scale = 1.0 / D ** 0.5 if scale is None else scale
+    out = _empty((B, S, Hq, D), q.device)
+    lse = _empty((B, Hq, S), q.device) if want_lse else None
+    _check(lib.kvsel_index_attn(_ptr(q), S, Hq, scale, _ptr(k), _ptr(v), cache_desc(k), _ptr(pos),
+                                _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
 
 
 def unit_fractions(sel: torch.Tensor, unit_len: int, n_units: int) -> torch.Tensor:

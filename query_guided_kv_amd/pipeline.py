@@ -358,10 +358,35 @@ class ReorderPath:
         return out
 
 
+class RecomputePath:
+    """The recomputation attention of the selected tokens ([InfoFlow §4.2]):
+    every selected token's query attends to the context rows up to its own
+    position (:func:`kvsel.index_attn`), for every layer."""
+
+    STAGES = ("recompute",)
+
+    def __init__(self, w, inp: dict):
+        self.w = w
+        self.k, self.v, self.pos = inp["k"], inp["v"], inp["pos"]
+        self.stages = self.STAGES
+
+    def __call__(self, q_sel: torch.Tensor, marks: dict = None) -> dict:
+        ev = marks or {}
+        pair = ev.get("recompute")
+        if pair is not None:
+            pair[0].record()
+        o, lse = K.index_attn(q_sel, self.k, self.v, self.pos, self.w.scale)
+        if pair is not None:
+            pair[1].record()
+        return {"o": o, "lse": lse}
+
+
 def make_path(w, inp: dict):
     """The launch sequence of workload ``w``."""
     if w.recipe == "cachefocus":
         return PrunePath(w, inp)
     if w.reorder:
         return ReorderPath(w, inp)
+    if w.recompute:
+        return RecomputePath(w, inp)
     return Path(w, inp)

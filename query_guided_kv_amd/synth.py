@@ -68,6 +68,7 @@ class Workload:
     allocation: str = "align"     # layer-wise pruning: final order, "align" or "sort"
     reorder: bool = False         # two-stage selection with chunk reordering
     l2_host: bool = False         # bi-layer refill: L2 cache in pinned host memory
+    recompute: bool = False       # attention of the selected tokens to the context
 
     @property
     def M(self) -> int:
@@ -134,6 +135,15 @@ WORKLOADS: Dict[str, Workload] = {
         name="infoflow_reorder_32l_64x1024", recipe="infoflow", B=32, N=65536, Hq=32, H=8,
         D=128, T=32, dtype="bf16", unit_len=1, k=9830, group=32, signal="vnorm",
         reposition="global", decode=False, reorder=True,
+        plants={"chunk_len": 1024, "chunks": 6, "chunk_scale": 1.5,
+                "tokens": 3686, "token_scale": 1.3}),
+    # Recomputation of the selected tokens on the same caches: the 9830 selected
+    # tokens (the planted 15%) of every layer attend causally to the context
+    # up to their own positions, with fresh queries.
+    "infoflow_recompute_32l_64x1024": Workload(
+        name="infoflow_recompute_32l_64x1024", recipe="infoflow", B=32, N=65536, Hq=32, H=8,
+        D=128, T=32, dtype="bf16", unit_len=1, k=9830, group=32, signal="vnorm",
+        reposition="global", decode=False, recompute=True,
         plants={"chunk_len": 1024, "chunks": 6, "chunk_scale": 1.5,
                 "tokens": 3686, "token_scale": 1.3}),
     # Batched serving: 16 requests x 8 layers, 131072 cached tokens each, GQA
@@ -304,8 +314,16 @@ def _gen_infoflow(w: Workload, seed: int, device) -> dict:
     for b in range(w.B):
         k[b] = (k[b].float() * scale).to(td)
     planted = np.sort(np.concatenate([np.flatnonzero(in_chunk), tokens])).astype(np.int64)
-    return dict(q=q, k=k, v=v, planted=[planted] * (w.B // w.group),
-                planted_chunks=chunks.astype(np.int64), planted_tokens=tokens)
+    out = dict(q=q, k=k, v=v, planted=[planted] * (w.B // w.group),
+               planted_chunks=chunks.astype(np.int64), planted_tokens=tokens)
+    if w.recompute:
+        # queries of the selected tokens, one block per layer, and their positions
+        S = planted.size
+        qs = torch.empty((w.B, S, w.Hq, w.D), dtype=td, device=device)
+        qs.normal_(generator=g)
+        out["q_sel"] = qs
+        out["pos"] = torch.from_numpy(np.tile(planted.astype(np.int32), (w.B, 1))).to(device)
+    return out
 
 
 def _gen_serving(w: Workload, seed: int, device) -> dict:
