@@ -56,6 +56,8 @@ KERNEL_SOURCES = {
     "gather_kernel": [_C + "gather.hip", _C + "common.h"],
     "decode_stream_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
     "decode_mfma_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
+    "index_attn_kernel": [_C + "index_attn.hip", _C + "mfma.h", _C + "common.h"],
+    "order_kernel": [_C + "topk.hip", _C + "common.h"],
 }
 
 
