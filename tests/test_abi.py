@@ -186,6 +186,25 @@ def test_take_and_order_validation(lib):
     assert lib.kvsel_order(None, 2, 10, None, 0, 1, None, None, None) == OK
 
 
+def test_index_attn_validation(lib):
+    # every call below fails validation: nothing is launched
+    p = ctypes.c_void_p(FAKE)
+    kc = cache(B=2, N=4096, H=8, D=128)
+
+    def call(q=FAKE, S=100, Hq=32, k=FAKE, v=FAKE, c=None, pos=FAKE, out=FAKE):
+        z = lambda x: x and ctypes.c_void_p(x)
+        return lib.kvsel_index_attn(z(q), S, Hq, 0.088, z(k), z(v), c or kc, z(pos), z(out),
+                                    None, None)
+    assert call(q=0) == NULL
+    assert call(q=MISALIGNED) == UNSUP
+    assert call(pos=0) == NULL
+    assert call(out=0) == NULL
+    assert call(c=cache(B=2, N=4096, H=8, D=128, dtype=K.FP32)) == UNSUP   # bf16 only
+    assert call(S=0) == SHAPE
+    assert call(Hq=30) == SHAPE                   # not a multiple of H
+    assert call(S=1 << 27) == SHAPE               # S * Hq >= 2^31
+
+
 def test_unit_fractions_and_slot_starts_validation(lib):
     # every call below fails validation: nothing is launched
     p = ctypes.c_void_p(FAKE)
