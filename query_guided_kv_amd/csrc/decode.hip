@@ -361,9 +361,9 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
 //                 B = the lane's own probabilities, rounded to bf16): the 32
 //                 keys of two key blocks, in the order the lane holds them.
 // The running max, sum and output of a query row all live in the lanes with
-// l%16 == row, so rescaling is lane-local; the max and the final sum are
-// reduced across the four lane quads.  Waves split the query rows; blocks with
-// fewer than four row blocks launch fewer waves, taller ones run in passes.
+// l%16 == row, so rescaling is lane-local (and lazy: attn_softmax in mfma.h);
+// the max and the final sum are reduced across the four lane quads.  Waves
+// split the query rows, RBW row blocks each; taller blocks run in passes.
 template <int D, int RBW, int NW>
 __global__ void __launch_bounds__(64 * NW)
 decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t n_split, int H,
@@ -379,6 +379,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   constexpr int KV = TK * (D / 8) / NT;    // K vectors per thread and tile
   constexpr int VITEMS = KG * (D / 8);     // V items (4 keys x 8 dims) per tile
   constexpr int VI = (VITEMS + NT - 1) / NT;
+  static_assert(KV >= 1 && NT % KG == 0, "tile staging");
   __shared__ __align__(16) bf16_t kt[TK * KROW];
   __shared__ __align__(16) bf16_t vt[D * VROW];
 
@@ -427,59 +428,70 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     for (int c = 0; c < CB; ++c) o[i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // the next tile's K and V rows are in flight while this tile computes
+  // the next tile's K and V rows are in flight while this tile computes; in a
+  // split's last, partial tile the rows past its end are clamped to its last
+  // row and masked below
   uint4 kn[KV], vn4[VI][4];
+  const int64_t koff = (threadIdx.x / (D / 8)) * sn + (threadIdx.x % (D / 8)) * 8;
+  const int64_t voff = (threadIdx.x % KG) * 4 * sn + (threadIdx.x / KG) * 8;
+  const int64_t kstep = (NT / (D / 8)) * sn;
+  constexpr int VSTEP = (NT / KG) * 8;   // dims between a thread's V items
   auto fetch = [&](int64_t t0) {
+    if (t0 + TK <= t_end) {   // uniform
+      const bf16_t* kt0 = kb + t0 * sn;
+      const bf16_t* vt0 = vb + t0 * sn;
 #pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int key = e / (D / 8), ch = e % (D / 8);
-      kn[i] = (t0 + key < t_end) ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * sn + ch * 8)
-                                 : make_uint4(0, 0, 0, 0);
-    }
+      for (int i = 0; i < KV; ++i) {
+        const uint4 x = *reinterpret_cast<const uint4*>(kt0 + koff + i * kstep);
+        kn[i] = x;
+      }
 #pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int kg = e % KG, ch = e / KG;
+      for (int i = 0; i < VI; ++i) {
+        if (threadIdx.x + i * NT < VITEMS) {   // the other threads stage no V
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t t = t0 + kg * 4 + j;
-        vn4[i][j] = (e < VITEMS && t < t_end) ? *reinterpret_cast<const uint4*>(vb + t * sn + ch * 8)
-                                              : make_uint4(0, 0, 0, 0);
+          for (int j = 0; j < 4; ++j) {
+            const uint4 y = *reinterpret_cast<const uint4*>(vt0 + voff + i * VSTEP + j * sn);
+            vn4[i][j] = y;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const int e = threadIdx.x + i * NT;
+        const int64_t t = min<int64_t>(t0 + e / (D / 8), t_end - 1);
+        const uint4 x = *reinterpret_cast<const uint4*>(kb + t * sn + (e % (D / 8)) * 8);
+        kn[i] = x;
+      }
+#pragma unroll
+      for (int i = 0; i < VI; ++i) {
+        const int e = threadIdx.x + i * NT;
+        if (e < VITEMS) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t t = min<int64_t>(t0 + (e % KG) * 4 + j, t_end - 1);
+            const uint4 y = *reinterpret_cast<const uint4*>(vb + t * sn + (e / KG) * 8);
+            vn4[i][j] = y;
+          }
+        }
       }
     }
   };
   if (t_begin < t_end) fetch(t_begin);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TK) {
     __syncthreads();
-    // K row-major: item (key, 16-byte chunk); rows past the end are zero
+    // K row-major: item (key, 16-byte chunk)
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
       const int e = threadIdx.x + i * NT;
       const int key = e / (D / 8), ch = e % (D / 8);
       *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
     }
-    // V transposed: item (4 consecutive keys, 8-dim chunk) -> eight 8-byte runs
+    // V transposed: item (4 consecutive keys, 8-dim chunk)
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int e = threadIdx.x + i * NT;
-      if (e >= VITEMS) break;
-      const int kg = e % KG, ch = e / KG;
-      uint32_t w[4][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[j][0] = vn4[i][j].x; w[j][1] = vn4[i][j].y; w[j][2] = vn4[i][j].z; w[j][3] = vn4[i][j].w;
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        // dims ch*8 + 2p (low halves) and ch*8 + 2p + 1 (high halves)
-        const uint2 lo = make_uint2((w[0][p] & 0xffffu) | (w[1][p] << 16),
-                                    (w[2][p] & 0xffffu) | (w[3][p] << 16));
-        const uint2 hi = make_uint2((w[0][p] >> 16) | (w[1][p] & 0xffff0000u),
-                                    (w[2][p] >> 16) | (w[3][p] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&vt[(ch * 8 + 2 * p) * VROW + kg * 4]) = lo;
-        *reinterpret_cast<uint2*>(&vt[(ch * 8 + 2 * p + 1) * VROW + kg * 4]) = hi;
-      }
+      if (e < VITEMS) stage_vt<VROW>(vt, vn4[i], e % KG, e / KG);
     }
     __syncthreads();
     if (t0 + TK < t_end) fetch(t0 + TK);
@@ -497,53 +509,27 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
         f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) a = mfma16x16x32(ka[s2], qb[i][s2], a);
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv)
-          if (t0 + kb4 * 16 + quad * 4 + vv >= t_end) a[vv] = -INFINITY;
         sv[i][kb4] = a;
       }
     }
-    // online softmax per row block; probabilities packed to bf16 pairs
+    if (t0 + TK > t_end) {   // the split's last, partial tile (uniform)
+#pragma unroll
+      for (int i = 0; i < RBW; ++i)
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv)
+            if (t0 + kb4 * 16 + quad * 4 + vv >= t_end) sv[i][kb4][vv] = -INFINITY;
+    }
     uint32_t pk[RBW][4][2];
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      float tmax = sv[i][0][0];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) tmax = fmaxf(tmax, sv[i][kb4][vv]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m[i], tmax * scale2);
-      // a fully masked tile only happens past a row's last key: nothing to add
-      const bool live = mn != -INFINITY;
-      const float alpha = live ? __builtin_amdgcn_exp2f(m[i] - mn) : 1.0f;
-      float ps = 0.0f;
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
-        float p[4];
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          p[vv] = live ? __builtin_amdgcn_exp2f(fmaf(sv[i][kb4][vv], scale2, -mn)) : 0.0f;
-          ps += p[vv];
-        }
-        pk[i][kb4][0] = pack2_bf16(p[0], p[1]);
-        pk[i][kb4][1] = pack2_bf16(p[2], p[3]);
-      }
-      if (live) m[i] = mn;
-      s[i] = s[i] * alpha + ps;
-#pragma unroll
-      for (int c = 0; c < CB; ++c) o[i][c] *= alpha;
-    }
+    for (int i = 0; i < RBW; ++i) attn_softmax<CB>(sv[i], scale2, m[i], s[i], o[i], pk[i]);
     // O^T += V^T P^T: one V^T fragment serves every row block
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const bf16_t* vr = &vt[(c * 16 + col) * VROW + pr * 32 + quad * 4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        const uint4 va = load_vt<VROW>(vt, c, pr, col, quad);
 #pragma unroll
         for (int i = 0; i < RBW; ++i) {
           const uint4 pb = make_uint4(pk[i][2 * pr][0], pk[i][2 * pr][1], pk[i][2 * pr + 1][0],
@@ -697,18 +683,24 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
 #undef KVSEL_DS
   }
   if (!done && dtype == KVSEL_BF16 && R >= 16) {
-    // one row block per wave; two waves for up to two row blocks, eight for
-    // 16 or more, else four; taller query blocks run in passes
+    // Tall query blocks (12 row blocks or more): eight waves of two row blocks,
+    // so every staged K and V fragment feeds two products; 256 rows a pass.
+    // Otherwise one row block per wave: two waves for up to two row blocks,
+    // else four.
     const int64_t rbs = (R + 15) / 16;
-    const int nwaves = rbs <= 2 ? 2 : (rbs >= 16 ? 8 : 4);
-    const int passes = static_cast<int>((rbs + nwaves - 1) / nwaves);
+    const int rbw = rbs >= 12 ? 2 : 1;
+    const int nwaves = rbs >= 12 ? 8 : rbs <= 2 ? 2 : 4;
+    const int passes = static_cast<int>((rbs + rbw * nwaves - 1) / (rbw * nwaves));
     const dim3 grid(static_cast<unsigned>(B * H * passes * n_split)), block(64 * nwaves);
-#define KVSEL_DM(D_, NW_) \
-    hipLaunchKernelGGL((decode_mfma_kernel<D_, 1, NW_>), grid, block, 0, s, static_cast<const bf16_t*>(q), st, \
+#define KVSEL_DM(D_, RBW_, NW_) \
+    hipLaunchKernelGGL((decode_mfma_kernel<D_, RBW_, NW_>), grid, block, 0, s, static_cast<const bf16_t*>(q), st, \
                        n_seg, n_split, static_cast<int>(H), static_cast<int>(T), static_cast<int>(Hq), scale2, \
                        passes, ws_ms, ws_o)
-    if (D == 128) { if (nwaves == 2) KVSEL_DM(128, 2); else if (nwaves == 8) KVSEL_DM(128, 8); else KVSEL_DM(128, 4); }
-    else { if (nwaves == 2) KVSEL_DM(64, 2); else if (nwaves == 8) KVSEL_DM(64, 8); else KVSEL_DM(64, 4); }
+    if (D == 128) {
+      if (rbw == 2) KVSEL_DM(128, 2, 8); else if (nwaves == 2) KVSEL_DM(128, 1, 2); else KVSEL_DM(128, 1, 4);
+    } else {
+      if (rbw == 2) KVSEL_DM(64, 2, 8); else if (nwaves == 2) KVSEL_DM(64, 1, 2); else KVSEL_DM(64, 1, 4);
+    }
 #undef KVSEL_DM
     done = true;
   }

@@ -40,6 +40,7 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   constexpr int VITEMS = KG * (D / 8);     // V items (4 keys x 8 dims) per tile
   constexpr int VI = (VITEMS + NT - 1) / NT;
   static_assert(KV >= 1, "tile too small for the workgroup");
+  static_assert(VI == 1, "one V item per thread at most");
   __shared__ __align__(16) bf16_t kt[TK * KROW];
   __shared__ __align__(16) bf16_t vt[D * VROW];
   __shared__ int wave_lim[NW];
@@ -101,26 +102,47 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int c = 0; c < CB; ++c) o[i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // the next tile's K and V rows are in flight while this tile computes
+  // the next tile's K and V rows are in flight while this tile computes.  Keys
+  // from t_end on lie beyond every row's limit and get zero weight from the
+  // mask, so a tile is loaded whole; only rows past the cache's end are
+  // clamped to its last row.
   uint4 kn[KV], vn4[VI][4];
+  // a thread's rows within a tile: K rows key0 + i * (NT / (D / 8)), V rows
+  // 4 * (thread % KG) + j
+  const int64_t koff = (threadIdx.x / (D / 8)) * stride_n + (threadIdx.x % (D / 8)) * 8;
+  const int64_t voff = (threadIdx.x % KG) * 4 * stride_n + (threadIdx.x / KG) * 8;
+  const int64_t kstep = (NT / (D / 8)) * stride_n;
   auto fetch = [&](int64_t t0) {
+    if (t0 + TK <= N) {   // uniform
+      const bf16_t* kt0 = kb + t0 * stride_n;
+      const bf16_t* vt0 = vb + t0 * stride_n;
 #pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int key = e / (D / 8), ch = e % (D / 8);
-      kn[i] = (t0 + key < t_end) ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * stride_n + ch * 8)
-                                 : make_uint4(0, 0, 0, 0);
-    }
+      for (int i = 0; i < KV; ++i) {
+        const uint4 x = *reinterpret_cast<const uint4*>(kt0 + koff + i * kstep);
+        kn[i] = x;
+      }
+      if (threadIdx.x < VITEMS) {   // the other threads stage no V
 #pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int kg = e % KG, ch = e / KG;
+        for (int j = 0; j < 4; ++j) {
+          const uint4 y = *reinterpret_cast<const uint4*>(vt0 + voff + j * stride_n);
+          vn4[0][j] = y;
+        }
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t t = t0 + kg * 4 + j;
-        vn4[i][j] = (e < VITEMS && t < t_end)
-                        ? *reinterpret_cast<const uint4*>(vb + t * stride_n + ch * 8)
-                        : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < KV; ++i) {
+        const int e = threadIdx.x + i * NT;
+        const int64_t t = min<int64_t>(t0 + e / (D / 8), N - 1);
+        const uint4 x = *reinterpret_cast<const uint4*>(kb + t * stride_n + (e % (D / 8)) * 8);
+        kn[i] = x;
+      }
+      if (threadIdx.x < VITEMS) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t t = min<int64_t>(t0 + (threadIdx.x % KG) * 4 + j, N - 1);
+          const uint4 y = *reinterpret_cast<const uint4*>(vb + t * stride_n + (threadIdx.x / KG) * 8);
+          vn4[0][j] = y;
+        }
       }
     }
   };
@@ -138,20 +160,7 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const int e = threadIdx.x + i * NT;
       if (e >= VITEMS) break;
       const int kg = e % KG, ch = e / KG;
-      uint32_t w[4][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[j][0] = vn4[i][j].x; w[j][1] = vn4[i][j].y; w[j][2] = vn4[i][j].z; w[j][3] = vn4[i][j].w;
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint2 lo = make_uint2((w[0][p] & 0xffffu) | (w[1][p] << 16),
-                                    (w[2][p] & 0xffffu) | (w[3][p] << 16));
-        const uint2 hi = make_uint2((w[0][p] >> 16) | (w[1][p] & 0xffff0000u),
-                                    (w[2][p] >> 16) | (w[3][p] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&vt[(ch * 8 + 2 * p) * VROW + kg * 4]) = lo;
-        *reinterpret_cast<uint2*>(&vt[(ch * 8 + 2 * p + 1) * VROW + kg * 4]) = hi;
-      }
+      stage_vt<VROW>(vt, vn4[i], kg, ch);
     }
     __syncthreads();
     if (t0 + TK < t_end) fetch(t0 + TK);
@@ -186,43 +195,13 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     // online softmax per row (the lane's column); probabilities as bf16 pairs
     uint32_t pk[RBW][4][2];
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      float tmax = sv[i][0][0];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) tmax = fmaxf(tmax, sv[i][kb4][vv]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m[i], tmax * scale2);
-      const float ref = mn == -INFINITY ? 0.0f : mn;   // nothing seen yet: every p is 0
-      const float alpha = __builtin_amdgcn_exp2f(m[i] - ref);
-      float ps = 0.0f;
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
-        float p[4];
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          p[vv] = __builtin_amdgcn_exp2f(fmaf(sv[i][kb4][vv], scale2, -ref));
-          ps += p[vv];
-        }
-        pk[i][kb4][0] = pack2_bf16(p[0], p[1]);
-        pk[i][kb4][1] = pack2_bf16(p[2], p[3]);
-      }
-      m[i] = mn;
-      s[i] = s[i] * alpha + ps;
-#pragma unroll
-      for (int c = 0; c < CB; ++c) o[i][c] *= alpha;
-    }
+    for (int i = 0; i < RBW; ++i) attn_softmax<CB>(sv[i], scale2, m[i], s[i], o[i], pk[i]);
     // O^T += V^T P^T: one V^T fragment serves every row block
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const bf16_t* vr = &vt[(c * 16 + col) * VROW + pr * 32 + quad * 4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        const uint4 va = load_vt<VROW>(vt, c, pr, col, quad);
 #pragma unroll
         for (int i = 0; i < RBW; ++i) {
           const uint4 pb = make_uint4(pk[i][2 * pr][0], pk[i][2 * pr][1], pk[i][2 * pr + 1][0],
