@@ -56,9 +56,15 @@ KERNEL_SOURCES = {
     "gather_kernel": [_C + "gather.hip", _C + "common.h"],
     "decode_stream_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
     "decode_mfma_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
+    "decode_tile_kernel": [_C + "decode.hip", _C + "common.h"],
     "index_attn_kernel": [_C + "index_attn.hip", _C + "mfma.h", _C + "common.h"],
     "order_kernel": [_C + "topk.hip", _C + "common.h"],
+    "decode_merge_kernel": [_C + "decode.hip"],
 }
+
+# The decode calls run split-K: a pass over the keys, then the merge of the
+# splits.  Their stage is timed as one call, so its roofline names both kernels.
+MERGE = "+decode_merge_kernel"
 
 
 def log(msg: str) -> None:
@@ -66,8 +72,12 @@ def log(msg: str) -> None:
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the sources of a kernel, or of every kernel of an 'a+b' call."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kernel]:
+    rels = []
+    for k in kernel.split("+"):
+        rels += [r for r in KERNEL_SOURCES[k] if r not in rels]
+    for rel in rels:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -197,7 +207,10 @@ def kernel_of(stage: str, w) -> str:
     """Name of the kernel that carries a stage's work for workload w."""
     if w.recipe == "cachefocus":
         return {"select": "score_mfma_kernel" if mfma_shape(w) else "score_stream_kernel",
-                "final_gather": "gather_kernel", "decode": "decode_stream_kernel"}[stage]
+                "final_gather": "gather_kernel",
+                "decode": ("decode_mfma_kernel" if mfma_shape(w) else
+                           "decode_stream_kernel" if one_pass_decode(w) else
+                           "decode_tile_kernel") + MERGE}[stage]
     if stage == "recompute":
         return "index_attn_kernel"
     if w.reorder and stage not in ("score", "aggregate", "topk"):
@@ -212,9 +225,9 @@ def kernel_of(stage: str, w) -> str:
                      "score_mfma_kernel" if mfma else "score_tile_kernel",
             "aggregate": "agg_mfma_kernel" if mfma else "agg_token_kernel",
             "topk": "topk_kernel", "gather": "gather_kernel",
-            "decode": "decode_mfma_kernel" if mfma else
-                      "decode_stream_kernel" if one_pass_decode(w) else "decode_tile_kernel",
-            "gather_decode": "decode_stream_kernel"}[stage]
+            "decode": ("decode_mfma_kernel" if mfma else
+                       "decode_stream_kernel" if one_pass_decode(w) else "decode_tile_kernel") + MERGE,
+            "gather_decode": "decode_stream_kernel" + MERGE}[stage]
 
 
 def stored_traffic(kernel: str, workload: str):
