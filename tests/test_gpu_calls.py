@@ -278,6 +278,9 @@ DECODE_CASES = [
     ("mfma_R16_d64_two_segs", "bf16", 2, (700, 77), 2, 4, 8, 64),
     ("mfma_R128_ragged", "bf16", 1, (1300,), 4, 16, 32, 128),
     ("mfma_R300_d64_three_passes", "bf16", 1, (530, 40), 1, 10, 30, 64),
+    # two row blocks per wave: one pass with idle waves, a segment shorter than a tile
+    ("mfma_R224_one_pass_short_seg", "bf16", 2, (1030, 5), 4, 28, 32, 128),
+    ("mfma_R200_d64_one_pass", "bf16", 1, (2100,), 2, 10, 40, 64),
 ]
 
 

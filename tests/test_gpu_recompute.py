@@ -27,6 +27,7 @@ CASES = [
     ("two_row_blocks_per_wave", 1, 1100, 3000, 2, 8, 128, "sorted"),
     ("d64_unsorted_edges", 2, 50, 700, 1, 4, 64, "edges"),
     ("gqa7_one_key_tiles", 1, 20, 130, 4, 28, 128, "sorted"),
+    ("context_shorter_than_a_tile", 1, 9, 40, 2, 8, 64, "edges"),
 ]
 
 
