@@ -38,9 +38,12 @@ def hipcc() -> str:
 
 def compile_flags() -> list:
     # packed fp32 VALU ops are disabled on purpose: the compiler would form
-    # v_pk_{add,mul,fma}_f32 from plain float code otherwise.
+    # v_pk_{add,mul,fma}_f32 from plain float code otherwise.  No kernel makes
+    # or tests a NaN (masked logits are -inf), so device code is built with
+    # -fno-honor-nans: fmaxf then skips the quieting of its operands.  Host
+    # code keeps IEEE comparisons (argument checks reject NaN).
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Xarch_device", "-fno-honor-nans",
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -186,7 +186,8 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
       }
     }
   };
-  auto stash = [&](uint4 (&v)[VPT], int64_t t0) {
+  // rotation of a staged tile in registers (cs / creg hold its unit)
+  auto rotate_tile = [&](uint4 (&v)[VPT]) {
     if constexpr (ROT == 1) {
 #pragma unroll
       for (int i = 0; i < VPT; i += 2) {
@@ -211,6 +212,8 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
           rope_rotate16<bf16_t, KVSEL_ROPE_INTERLEAVED>(v[i], unused, ch * 8, cs);
       }
     }
+  };
+  auto store = [&](uint4 (&v)[VPT], int64_t t0) {
     const int rem = static_cast<int>(min<int64_t>(t_end - t0, kTileKeys));
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -233,26 +236,57 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   Cursor fc = map.units != nullptr ? cursor_at(map.unit_len) : Cursor{0, 0, kTileKeys};
   Cursor rc = ROT != 0 ? cursor_at(rot.rot_len) : Cursor{0, 0, kTileKeys};
   int64_t seg = seg0, seg_off = 0;
-  uint4 nxt[VPT];
-  bool nxt_ok = true;
-  if (t_begin < t_end) nxt_ok = fetch(nxt, t_begin, fc);
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) {
-    __syncthreads();               // previous tile fully read
+  // cos/sin of the rotation unit rc.u (a uniform test; the table is rebuilt
+  // only at a unit change, between barriers that every rotation lies outside)
+  auto unit_cs = [&]() {
     if constexpr (ROT != 0) {
-      if (rc.u != cs_unit) {       // a tile lies inside one unit
+      if (rc.u != cs_unit) {
         const int64_t delta = rot.delta[b * rot.delta_stride_b + rc.u];
         for (int i = threadIdx.x; i < D / 2; i += kThreads) cs[i] = rope_cs(delta, i, D, rot.base);
         cs_unit = rc.u;
         __syncthreads();
         load_cs();
       }
+    }
+  };
+  // Staging pipeline.  A tile's loads are issued one tile ahead into the
+  // buffer just stored, and a rotated tile is rotated right before it is
+  // stored.  With eight waves (registers to spare) the rotation is pipelined:
+  // loads run two tiles ahead and tile t + 1 is rotated in registers while
+  // tile t's products run on the matrix cores; tiles alternate between two
+  // buffers (a tile's buffer is free once stored, and takes tile t + 2).
+  constexpr bool PIPE = ROT != 0 && NW == 8;
+  uint4 bufA[VPT], bufB[VPT];
+  bool okA = true, okB = true;
+  if (t_begin < t_end) {
+    okA = fetch(bufA, t_begin, fc);
+    fc.advance();
+    if constexpr (PIPE) {
+      unit_cs();
+      rotate_tile(bufA);
+      rc.advance();
+      if (t_begin + kTileKeys < t_end) {
+        okB = fetch(bufB, t_begin + kTileKeys, fc);
+        fc.advance();
+      }
+    }
+  }
+  // one tile: sb holds it (rotated), rb the next tile's raw rows
+  auto body = [&](uint4 (&sb)[VPT], bool& sb_ok, uint4 (&rb)[VPT], int64_t t0) {
+    __syncthreads();               // previous tile fully read
+    if constexpr (ROT != 0 && !PIPE) {
+      unit_cs();
+      rotate_tile(sb);
       rc.advance();
     }
-    stash(nxt, t0);
-    const bool tile_ok = nxt_ok;
+    store(sb, t0);
+    const bool tile_ok = sb_ok;
     __syncthreads();
-    fc.advance();
-    if (t0 + kTileKeys < t_end) nxt_ok = fetch(nxt, t0 + kTileKeys, fc);  // in flight during the math
+    constexpr int64_t ahead = PIPE ? 2 * kTileKeys : kTileKeys;
+    if (t0 + ahead < t_end) {      // in flight during the math
+      sb_ok = fetch(sb, t0 + ahead, fc);
+      fc.advance();
+    }
 
     f32x4_t acc[RBW][KBW];
 #pragma unroll
@@ -269,6 +303,13 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
         for (int st = 0; st < KS; ++st)
           a = mfma16x16x32(qa[i][st], bk[st], a);
         acc[i][jb] = a;
+      }
+    }
+    if constexpr (PIPE) {
+      if (t0 + kTileKeys < t_end) {   // tile t + 1, while the products run
+        unit_cs();
+        rotate_tile(rb);
+        rc.advance();
       }
     }
     // keys past the end of the cache, or of a unit outside the source, take
@@ -341,6 +382,14 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
       ++seg;
       seg_off = 0;
     }
+  };
+  if constexpr (PIPE) {
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kTileKeys) {
+      body(bufA, okA, bufB, t0);
+      if (t0 + kTileKeys < t_end) body(bufB, okB, bufA, t0 + kTileKeys);
+    }
+  } else {
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) body(bufA, okA, bufA, t0);
   }
 }
 
