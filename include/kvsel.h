@@ -241,7 +241,10 @@ size_t kvsel_score_units_workspace(int64_t T, int64_t Hq, kvsel_cache kc,
  *    kvsel_score; q, k, v are not read and may be NULL; row_max/row_sum may be
  *    NULL (then derived from part).
  *  - token path (otherwise): re-reads q and k (and v for VNORM) and needs
- *    row_max/row_sum from kvsel_score; works for any unit_len >= 1.
+ *    row_max/row_sum from kvsel_score; works for any unit_len >= 1.  Its
+ *    workspace holds per-token sums: B*N floats, or 16*B*N when B*N < 2^19
+ *    (small caches split the kv heads over groups of workgroups, each with
+ *    its own partial sums, added in a fixed order).
  *   ws           kvsel_aggregate_workspace(...) bytes (both paths need one).
  */
 int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k,

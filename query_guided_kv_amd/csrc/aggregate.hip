@@ -155,15 +155,18 @@ agg_token_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 // unit_score[g][u] = sum_{b in g} sum_{t in u} per_token[b][t], fixed order
 // (added to unit_score[g][u] with `accumulate`).
 __global__ void __launch_bounds__(kThreads)
-unit_sum_kernel(const float* __restrict__ per_token, int64_t N, int64_t unit_len, int64_t M,
-                int64_t group, int64_t mblocks, int accumulate, float* __restrict__ out) {
+unit_sum_kernel(const float* __restrict__ per_token, int64_t parts, int64_t part_stride,
+                int64_t N, int64_t unit_len, int64_t M, int64_t group, int64_t mblocks,
+                int accumulate, float* __restrict__ out) {
   const int64_t gi = blockIdx.x / mblocks;
   const int64_t u = (blockIdx.x % mblocks) * kThreads + threadIdx.x;
   if (u >= M) return;
   float acc = 0.0f;
-  for (int64_t bi = 0; bi < group; ++bi) {
-    const float* pt = per_token + (gi * group + bi) * N + u * unit_len;
-    for (int64_t t = 0; t < unit_len; ++t) acc += pt[t];
+  for (int64_t p = 0; p < parts; ++p) {
+    for (int64_t bi = 0; bi < group; ++bi) {
+      const float* pt = per_token + p * part_stride + (gi * group + bi) * N + u * unit_len;
+      for (int64_t t = 0; t < unit_len; ++t) acc += pt[t];
+    }
   }
   out[gi * M + u] = accumulate ? out[gi * M + u] + acc : acc;
 }
@@ -234,13 +237,19 @@ int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k,
   return check_launch("kvsel_aggregate (token path)");
 }
 
-int launch_unit_sums(const float* per_token, int64_t B, int64_t N, int64_t unit_len,
-                     int64_t group, float* unit_score, int accumulate, hipStream_t s) {
+int64_t aggregate_token_parts(const kvsel_cache& kc, int64_t Hq, int64_t T) {
+  const int64_t rows = (Hq / kc.H) * T;
+  return aggregate_mfma_ok(kc.dtype, rows) ? aggregate_mfma_parts(kc, rows) : 1;
+}
+
+int launch_unit_sums(const float* per_token, int64_t parts, int64_t B, int64_t N,
+                     int64_t unit_len, int64_t group, float* unit_score, int accumulate,
+                     hipStream_t s) {
   const int64_t M = N / unit_len;
   const int64_t mblocks = (M + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(unit_sum_kernel, dim3(static_cast<unsigned>((B / group) * mblocks)),
-                     dim3(kThreads), 0, s, per_token, N, unit_len, M, group, mblocks, accumulate,
-                     unit_score);
+                     dim3(kThreads), 0, s, per_token, parts, B * N, N, unit_len, M, group, mblocks,
+                     accumulate, unit_score);
   return check_launch("kvsel_aggregate (unit sums)");
 }
 

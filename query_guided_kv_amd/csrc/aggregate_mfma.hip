@@ -7,13 +7,17 @@
 // value norm).
 //
 // A workgroup owns a range of cached rows of one instance and loops over the kv
-// heads (and row passes for very tall query blocks).  For every 64-key tile of
+// heads (and row passes for very tall query blocks); for small caches the
+// (kv head, row pass) items are split over groups of workgroups, each group
+// writing its own per-token partials.  For every 64-key tile of
 // K staged in LDS it recomputes the logits with v_mfma_f32_16x16x32_bf16 (the
 // same operand layout as score_mfma.hip), forms alpha with one exp per logit,
 // sums it over the lane's rows, over the four lane quads (shuffles) and over
 // the waves that split the rows (LDS), then scales by the value norm of the
 // head.  The per-token totals stay in LDS across heads and are written once:
 // a fixed summation order, no atomics.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -26,6 +30,8 @@ constexpr int kWaves = 4;
 constexpr int kTileKeys = kMfmaTileKeys;
 constexpr int kPad = kMfmaPad;
 constexpr int kMaxRange = 1024;   // cached rows per workgroup
+constexpr int kSmallRange = 512;  // cached rows per workgroup for small caches
+constexpr int kTargetBlocks = 256;
 
 template <int D, int RBW, int NWR, bool VNORM>
 __global__ void __launch_bounds__(kThreads)
@@ -33,20 +39,21 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, int64_t N, int H, int64_t stride_b,
                 int64_t stride_n, int T, int Hq, float scale2, const float* __restrict__ row_max,
                 const float* __restrict__ row_sum, int64_t range, int64_t ranges, int passes,
-                float* __restrict__ per_token) {
+                int64_t parts, int hp_per_block, int64_t nb, float* __restrict__ per_token) {
   constexpr int KS = D / 32;
   constexpr int KROW = D + kPad;
   constexpr int NWK = kWaves / NWR;
   constexpr int KBW = (kTileKeys / 16) / NWK;
   constexpr int VPT = kTileKeys * D / 8 / kThreads;
-  constexpr int ROWS_PASS = NWR * RBW * 16;
   __shared__ __align__(16) bf16_t kt[kTileKeys * KROW];
   __shared__ float vn[kTileKeys];
   __shared__ float part[kWaves][kTileKeys];
   __shared__ float tot[kMaxRange];
 
-  const int64_t b = blockIdx.x / ranges;
-  const int64_t t_begin = (blockIdx.x % ranges) * range;
+  int64_t x = blockIdx.x;
+  const int64_t grp = x % parts; x /= parts;
+  const int64_t b = x / ranges;
+  const int64_t t_begin = (x % ranges) * range;
   const int64_t t_end = min(N, t_begin + range);
   const int G = Hq / H;
   const int R = G * T;
@@ -54,18 +61,23 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int wave = threadIdx.x >> 6;
   const int wr = wave % NWR, wk = wave / NWR;
   const int col = lane & 15, quad = lane >> 4;
+  // this group's (kv head, row pass) items: hp = g * passes + pass
+  const int hp0 = static_cast<int>(grp) * hp_per_block;
+  const int hp1 = min(H * passes, hp0 + hp_per_block);
 
   for (int i = threadIdx.x; i < range; i += kThreads) tot[i] = 0.0f;
 
-  // one flat sequence of (kv head, row pass, 64-key tile) items; the next
-  // item's K slice (and V slice for the norms) is in flight during the math
+  // items (hp, tile) in order; the next item's K slice (and V slice for the
+  // norms) is in flight during the math.  The fetch cursor advances by one
+  // tile with an add and a compare.
   constexpr int VV = D / 32;  // 16-byte vectors of V per thread (4 lanes per key)
   const int64_t n_tiles = (t_end - t_begin + kTileKeys - 1) / kTileKeys;
-  const int64_t n_items = static_cast<int64_t>(H) * passes * n_tiles;
   uint4 kn[VPT], vr[VNORM ? VV : 1];
-  auto fetch = [&](int64_t it) {
-    const int g = static_cast<int>(it / (passes * n_tiles));
-    const int64_t t0 = t_begin + (it % n_tiles) * kTileKeys;
+  int f_hp = hp0;
+  int64_t f_ti = 0;
+  auto fetch = [&]() {
+    const int g = f_hp / passes;
+    const int64_t t0 = t_begin + f_ti * kTileKeys;
     const bf16_t* kb = k + b * stride_b + static_cast<int64_t>(g) * D;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -83,125 +95,158 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                     ? *reinterpret_cast<const uint4*>(vb + (t0 + key) * stride_n + qd * (D / 4) + i * 8)
                     : make_uint4(0, 0, 0, 0);
     }
+    if (++f_ti == n_tiles) {
+      f_ti = 0;
+      ++f_hp;
+    }
   };
 
   uint4 qa[RBW][KS];
   float m2[RBW][4], iz[RBW][4];
-  if (n_items > 0) fetch(0);
-  for (int64_t it = 0; it < n_items; ++it) {
-    const int g = static_cast<int>(it / (passes * n_tiles));
-    const int pass = static_cast<int>((it / n_tiles) % passes);
-    const int64_t t0 = t_begin + (it % n_tiles) * kTileKeys;
-    if (it % n_tiles == 0) {
-      // query fragments and row statistics of this wave's row blocks; rows
-      // past R get zero weight
+  if (hp0 < hp1 && n_tiles > 0) fetch();
+  for (int hp = hp0; hp < hp1; ++hp) {
+    const int g = hp / passes, pass = hp % passes;
+    // query fragments and row statistics of this wave's row blocks; rows past
+    // R get zero weight
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) {
-        const int rb = pass * NWR * RBW + wr + i * NWR;
-        const int r = rb * 16 + col;
-        if (r < R) {
-          const int h = g * G + r / T, j = r % T;
-          const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + quad * 8);
+    for (int i = 0; i < RBW; ++i) {
+      const int rb = pass * NWR * RBW + wr + i * NWR;
+      const int r = rb * 16 + col;
+      if (r < R) {
+        const int h = g * G + r / T, j = r % T;
+        const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + quad * 8);
 #pragma unroll
-          for (int s2 = 0; s2 < KS; ++s2) qa[i][s2] = qp[s2 * 4];
+        for (int s2 = 0; s2 < KS; ++s2) qa[i][s2] = qp[s2 * 4];
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) qa[i][s2] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const int rr = rb * 16 + quad * 4 + vv;
+        if (rr < R) {
+          const int h = g * G + rr / T, j = rr % T;
+          const int64_t row = (b * Hq + h) * T + j;
+          m2[i][vv] = row_max[row] * kLog2e;
+          iz[i][vv] = 1.0f / row_sum[row];
         } else {
-#pragma unroll
-          for (int s2 = 0; s2 < KS; ++s2) qa[i][s2] = make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          const int rr = rb * 16 + quad * 4 + vv;
-          if (rr < R) {
-            const int h = g * G + rr / T, j = rr % T;
-            const int64_t row = (b * Hq + h) * T + j;
-            m2[i][vv] = row_max[row] * kLog2e;
-            iz[i][vv] = 1.0f / row_sum[row];
-          } else {
-            m2[i][vv] = 0.0f;
-            iz[i][vv] = 0.0f;
-          }
+          m2[i][vv] = 0.0f;
+          iz[i][vv] = 0.0f;
         }
       }
     }
-
-    __syncthreads();  // previous tile's kt / vn / part fully used
+    for (int64_t ti = 0; ti < n_tiles; ++ti) {
+      const int64_t t0 = t_begin + ti * kTileKeys;
+      __syncthreads();  // previous tile's kt / vn / part fully used
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int key = e / (D / 8), ch = e % (D / 8);
-      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
-    }
-    if constexpr (VNORM) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int i = 0; i < VV; ++i) {
-        float f[8];
-        unpack16<bf16_t>(vr[i], f);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) ss = fmaf(f[d], f[d], ss);
+      for (int i = 0; i < VPT; ++i) {
+        const int e = threadIdx.x + i * kThreads;
+        const int key = e / (D / 8), ch = e % (D / 8);
+        *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
       }
-      ss = group_sum<4>(ss);
-      if ((threadIdx.x & 3) == 0) vn[threadIdx.x >> 2] = sqrtf(ss);
-    }
-    __syncthreads();
-    if (it + 1 < n_items) fetch(it + 1);
-
-    float c[KBW];
+      if constexpr (VNORM) {
+        float ss = 0.0f;
 #pragma unroll
-    for (int jb = 0; jb < KBW; ++jb) {
-      const int key = (wk + jb * NWK) * 16 + col;
-      uint4 bk[KS];
+        for (int i = 0; i < VV; ++i) {
+          float f[8];
+          unpack16<bf16_t>(vr[i], f);
 #pragma unroll
-      for (int st = 0; st < KS; ++st)
-        bk[st] = *reinterpret_cast<const uint4*>(&kt[key * KROW + st * 32 + quad * 8]);
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < RBW; ++i) {
-        f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int st = 0; st < KS; ++st) a = mfma16x16x32(qa[i][st], bk[st], a);
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv)
-          sum = fmaf(__builtin_amdgcn_exp2f(fmaf(a[vv], scale2, -m2[i][vv])), iz[i][vv], sum);
+          for (int d = 0; d < 8; ++d) ss = fmaf(f[d], f[d], ss);
+        }
+        ss = group_sum<4>(ss);
+        if ((threadIdx.x & 3) == 0) vn[threadIdx.x >> 2] = sqrtf(ss);
       }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      c[jb] = sum;
-    }
-    if (quad == 0) {
+      __syncthreads();
+      if (f_hp < hp1) fetch();
+
+      float c[KBW];
 #pragma unroll
-      for (int jb = 0; jb < KBW; ++jb) part[wave][(wk + jb * NWK) * 16 + col] = c[jb];
-    }
-    __syncthreads();
-    if (threadIdx.x < kTileKeys) {
-      const int key = threadIdx.x;
-      const int owner = (key / 16) % NWK;  // the waves (wr, owner) computed this key
-      float s2 = 0.0f;
+      for (int jb = 0; jb < KBW; ++jb) {
+        const int key = (wk + jb * NWK) * 16 + col;
+        uint4 bk[KS];
 #pragma unroll
-      for (int w = 0; w < NWR; ++w) s2 += part[w + owner * NWR][key];
-      if (VNORM) s2 *= vn[key];
-      if (t0 + key < t_end) tot[t0 - t_begin + key] += s2;
+        for (int st = 0; st < KS; ++st)
+          bk[st] = *reinterpret_cast<const uint4*>(&kt[key * KROW + st * 32 + quad * 8]);
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int st = 0; st < KS; ++st) a = mfma16x16x32(qa[i][st], bk[st], a);
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv)
+            sum = fmaf(__builtin_amdgcn_exp2f(fmaf(a[vv], scale2, -m2[i][vv])), iz[i][vv], sum);
+        }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        c[jb] = sum;
+      }
+      if (quad == 0) {
+#pragma unroll
+        for (int jb = 0; jb < KBW; ++jb) part[wave][(wk + jb * NWK) * 16 + col] = c[jb];
+      }
+      __syncthreads();
+      if (threadIdx.x < kTileKeys) {
+        const int key = threadIdx.x;
+        const int owner = (key / 16) % NWK;  // the waves (wr, owner) computed this key
+        float s2 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWR; ++w) s2 += part[w + owner * NWR][key];
+        if (VNORM) s2 *= vn[key];
+        if (t0 + key < t_end) tot[t0 - t_begin + key] += s2;
+      }
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < t_end - t_begin; i += kThreads) per_token[b * N + t_begin + i] = tot[i];
+  float* out = per_token + (grp * nb + b) * N;   // this group's partials
+  for (int i = threadIdx.x; i < t_end - t_begin; i += kThreads) out[t_begin + i] = tot[i];
+}
+
+// Workgroup plan: cached rows per workgroup, and how the (kv head, row pass)
+// items split over groups.  Large caches: one group, ranges sized to fill the
+// chip.  Small caches (B * N < kAggSplitRows): ranges of kSmallRange rows and
+// up to kAggMaxParts groups, so each workgroup keeps its query fragments for
+// several tiles instead of reloading them for every tile.
+struct AggPlan {
+  int64_t range, ranges, parts;
+  int hp_per_block, passes, rbw, nwr;
+};
+
+AggPlan agg_plan(const kvsel_cache& kc, int64_t rows_per_kv) {
+  const MfmaRowPlan p = mfma_row_plan(rows_per_kv);
+  AggPlan a{};
+  a.passes = p.passes;
+  a.rbw = p.rbw;
+  a.nwr = p.nwr;
+  const int64_t hp_total = kc.H * p.passes;
+  if (kc.B * kc.N < kAggSplitRows) {
+    a.range = std::min<int64_t>(kSmallRange, (kc.N + kTileKeys - 1) / kTileKeys * kTileKeys);
+    a.ranges = (kc.N + a.range - 1) / a.range;
+    int64_t want = (kTargetBlocks + kc.B * a.ranges - 1) / (kc.B * a.ranges);
+    want = std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(kAggMaxParts, hp_total)));
+    a.hp_per_block = static_cast<int>((hp_total + want - 1) / want);
+    a.parts = (hp_total + a.hp_per_block - 1) / a.hp_per_block;
+  } else {
+    int64_t range = (kc.B * kc.N / 1024) / kTileKeys * kTileKeys;
+    a.range = range < kTileKeys ? kTileKeys : (range > kMaxRange ? kMaxRange : range);
+    a.ranges = (kc.N + a.range - 1) / a.range;
+    a.hp_per_block = static_cast<int>(hp_total);
+    a.parts = 1;
+  }
+  return a;
 }
 
 template <int D, int RBW, int NWR>
 void launch(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
             const kvsel_cache& kc, float scale2, const float* rm, const float* rs, int vnorm,
-            int passes, float* per_token, hipStream_t s) {
-  // enough workgroups to fill the chip: the range shrinks for small caches
-  int64_t range = (kc.B * kc.N / 1024) / kTileKeys * kTileKeys;
-  range = range < kTileKeys ? kTileKeys : (range > kMaxRange ? kMaxRange : range);
-  const int64_t ranges = (kc.N + range - 1) / range;
-  const dim3 grid(static_cast<unsigned>(kc.B * ranges));
+            const AggPlan& a, float* per_token, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(kc.B * a.ranges * a.parts));
 #define KVSEL_AM(VN)                                                                         \
   hipLaunchKernelGGL((agg_mfma_kernel<D, RBW, NWR, VN>), grid, dim3(kThreads), 0, s,          \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),            \
                      static_cast<const bf16_t*>(v), kc.N, static_cast<int>(kc.H), kc.stride_b, \
                      kc.stride_n, static_cast<int>(T), static_cast<int>(Hq), scale2, rm, rs,   \
-                     range, ranges, passes, per_token)
+                     a.range, a.ranges, a.passes, a.parts, a.hp_per_block, kc.B, per_token)
   if (vnorm) KVSEL_AM(true); else KVSEL_AM(false);
 #undef KVSEL_AM
 }
@@ -210,15 +255,19 @@ template <int D>
 void dispatch(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
               const kvsel_cache& kc, float scale2, const float* rm, const float* rs, int vnorm,
               float* per_token, hipStream_t s) {
-  const MfmaRowPlan p = mfma_row_plan((Hq / kc.H) * T);
+  const AggPlan a = agg_plan(kc, (Hq / kc.H) * T);
 #define KVSEL_AD(RBW, NWR) \
-  if (p.rbw == RBW && p.nwr == NWR) \
-    return launch<D, RBW, NWR>(q, T, Hq, k, v, kc, scale2, rm, rs, vnorm, p.passes, per_token, s);
+  if (a.rbw == RBW && a.nwr == NWR) \
+    return launch<D, RBW, NWR>(q, T, Hq, k, v, kc, scale2, rm, rs, vnorm, a, per_token, s);
   KVSEL_AD(1, 1) KVSEL_AD(1, 2) KVSEL_AD(1, 4) KVSEL_AD(2, 4) KVSEL_AD(4, 4)
 #undef KVSEL_AD
 }
 
 }  // namespace
+
+int64_t aggregate_mfma_parts(const kvsel_cache& kc, int64_t rows_per_kv) {
+  return agg_plan(kc, rows_per_kv).parts;
+}
 
 bool aggregate_mfma_ok(int dtype, int64_t rows_per_kv) {
   return dtype == KVSEL_BF16 && rows_per_kv >= 16;

@@ -136,7 +136,8 @@ size_t aggregate_ws(int64_t B, int64_t N, int64_t Hq, int64_t T, int64_t unit_le
   if (chunk)
     return (static_cast<size_t>(have_stats ? 0 : 2 * B * Hq * T) +
             aggregate_chunk_ws_floats(B, Hq, T, N / unit_len)) * sizeof(float);
-  return static_cast<size_t>(B * N) * sizeof(float);
+  // token path: per-token sums, in up to kAggMaxParts partial arrays for small caches
+  return static_cast<size_t>(B * N * (B * N < kAggSplitRows ? kAggMaxParts : 1)) * sizeof(float);
 }
 
 int64_t decode_splits(const kvsel_segment* segs, int n_seg, int64_t split_len) {
@@ -444,10 +445,11 @@ int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const v
   if (!stats)
     return fail(KVSEL_ERR_NULL, "kvsel_aggregate: the token path needs row_max and row_sum");
   float* per_token = static_cast<float*>(ws);
+  const int64_t parts = aggregate_token_parts(kc, Hq, T);
   KVSEL_TRY(launch_aggregate_tokens(q, T, Hq, k, v, kc, scale, row_max, row_sum,
                                     signal == KVSEL_SIG_VNORM, per_token, stream));
-  return launch_unit_sums(per_token, kc.B, kc.N, unit_len, group, unit_score, accumulate != 0,
-                          stream);
+  return launch_unit_sums(per_token, parts, kc.B, kc.N, unit_len, group, unit_score,
+                          accumulate != 0, stream);
 }
 
 int kvsel_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,

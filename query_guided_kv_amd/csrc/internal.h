@@ -78,17 +78,27 @@ int launch_aggregate_chunks(const float* part, const float* row_max, const float
 size_t aggregate_chunk_ws_floats(int64_t B, int64_t Hq, int64_t T, int64_t M);
 
 // Token path: per_token[b][t] = sum_h sum_j alpha (* ||v||), then per unit/group sums.
+// Small caches split the (kv head, row pass) items of the matrix-core variant
+// over aggregate_token_parts() workgroup groups; each group writes its own
+// per-token partials (parts arrays of B * N floats, summed by the unit sums in
+// a fixed order).  Parts stay 1 unless B * N < kAggSplitRows, and never exceed
+// kAggMaxParts.
+constexpr int64_t kAggSplitRows = int64_t{1} << 19;
+constexpr int64_t kAggMaxParts = 16;
+int64_t aggregate_token_parts(const kvsel_cache& kc, int64_t Hq, int64_t T);
 int launch_aggregate_tokens(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
                             const kvsel_cache& kc, float scale, const float* row_max,
                             const float* row_sum, int vnorm, float* per_token, hipStream_t s);
 // Matrix-core variant of launch_aggregate_tokens (bf16, >= 16 query rows per
 // kv head); aggregate_mfma_ok tells whether it applies.
 bool aggregate_mfma_ok(int dtype, int64_t rows_per_kv);
+int64_t aggregate_mfma_parts(const kvsel_cache& kc, int64_t rows_per_kv);
 void launch_aggregate_mfma(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
                            const kvsel_cache& kc, float scale2, const float* row_max,
                            const float* row_sum, int vnorm, float* per_token, hipStream_t s);
-int launch_unit_sums(const float* per_token, int64_t B, int64_t N, int64_t unit_len,
-                     int64_t group, float* unit_score, int accumulate, hipStream_t s);
+int launch_unit_sums(const float* per_token, int64_t parts, int64_t B, int64_t N,
+                     int64_t unit_len, int64_t group, float* unit_score, int accumulate,
+                     hipStream_t s);
 
 int launch_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* idx, float* val,
                 hipStream_t s);

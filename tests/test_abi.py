@@ -113,7 +113,9 @@ def test_aggregate_validation(lib):
     assert call(rm=0, rs=0) == WS                  # derives row stats: needs workspace
     assert call(part=0, rm=0, rs=0, ws=ctypes.c_void_p(FAKE), wsb=1 << 30) == NULL  # token path needs stats
     assert call(part=0, q=0, ws=ctypes.c_void_p(FAKE), wsb=1 << 30) == NULL
-    assert lib.kvsel_aggregate_workspace(2, 1024, 32, 1, 1, 0, 1) == 2 * 1024 * 4
+    # token path: per-token sums, 16 partial arrays for a small cache (B*N < 2^19)
+    assert lib.kvsel_aggregate_workspace(2, 1024, 32, 1, 1, 0, 1) == 16 * 2 * 1024 * 4
+    assert lib.kvsel_aggregate_workspace(8, 65536, 32, 1, 1, 0, 1) == 8 * 65536 * 4
     # chunk path: derived row stats (2 x B*Hq*T) + row-chunk sums ((ceil(B*Hq*T/64) + B) x M)
     assert lib.kvsel_aggregate_workspace(2, 1024, 32, 1, 256, 1, 0) == (2 * 2 * 32 + (1 + 2) * 4) * 4
     assert lib.kvsel_aggregate_workspace(2, 1024, 32, 1, 256, 1, 1) == (1 + 2) * 4 * 4
