@@ -570,15 +570,20 @@ __global__ void decode_merge_kernel(const float* __restrict__ ws_ms, const float
                                     float* __restrict__ out, float* __restrict__ lse) {
   const int64_t row = blockIdx.x;  // (b*Hq + h)*T + j
   const int d = threadIdx.x;
+  const float* ms = ws_ms + row * n_split * 2;   // (m_i, s_i) pairs
+  const float* po = ws_o + row * n_split * D + d;
   float m = -INFINITY;
-  for (int64_t i = 0; i < n_split; ++i) m = fmaxf(m, ws_ms[(row * n_split + i) * 2]);
+#pragma unroll 8
+  for (int64_t i = 0; i < n_split; ++i) m = fmaxf(m, ms[2 * i]);
+  // a split with no keys (m_i = -inf) weighs 0; the loads of several splits
+  // are in flight together
+  const float ref = m == -INFINITY ? 0.0f : m;
   float s = 0.0f, acc = 0.0f;
+#pragma unroll 8
   for (int64_t i = 0; i < n_split; ++i) {
-    const float mi = ws_ms[(row * n_split + i) * 2];
-    if (mi == -INFINITY) continue;
-    const float a = exp2f(mi - m);
-    s += ws_ms[(row * n_split + i) * 2 + 1] * a;
-    acc += ws_o[(row * n_split + i) * D + d] * a;
+    const float a = __builtin_amdgcn_exp2f(ms[2 * i] - ref);
+    s = fmaf(ms[2 * i + 1], a, s);
+    acc = fmaf(po[i * D], a, acc);
   }
   const int64_t j = row % T_;
   const int64_t h = (row / T_) % Hq;
