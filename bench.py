@@ -359,6 +359,37 @@ def cpu_baseline(w, inp, budget_s: float = 12.0, max_instances: int = 8) -> dict
                       f"fp64 numpy, 1 thread), {elapsed:.1f} s"}
 
 
+def time_graph(step, w, args, rows: int) -> dict:
+    """The step captured once as a HIP graph (torch.cuda.graph) and replayed
+    ``args.steps`` times between events: what a serving loop that launches the
+    whole path at once would see.  Only for steps whose inputs stay the same
+    (every workload but the serving one, which takes fresh queries per step)."""
+    import torch
+    if w.recipe == "serving":
+        return {"skipped": "the step's queries change every step"}
+    side = torch.cuda.Stream()                     # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(0)
+    for _ in range(max(args.warmup, 1)):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    log(f"{args.steps} graph replays: {ms:.4f} ms per step")
+    return {"ms_per_step": ms, "value": rows / (ms * 1e-3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +400,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB streaming kernel (counter scale reference)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured as one HIP graph and replayed "
+                         "(workloads whose step inputs do not change between steps)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -516,6 +550,8 @@ def main() -> int:
     }
     if host_link is not None:
         result["host_link"] = host_link
+    if args.graph:
+        result["graph"] = time_graph(step, w, args, rows)
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = (cpu_baseline_prune(w, inp) if prune
