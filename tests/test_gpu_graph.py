@@ -89,3 +89,25 @@ def test_graph_replay_prune_path():
     inp = synth.generate(w, 7, dev)
     path = pipeline.PrunePath(w, inp)
     _capture_and_check(lambda: path(inp["q"], inp["q_dec"]), _tensors(inp))
+
+
+def test_graph_replay_reorder_path():
+    w = synth.workload("infoflow_reorder_32l_64x1024", B=4, N=8 * 256, group=4, k=612,
+                       plants={"chunk_len": 256, "chunks": 2, "chunk_scale": 1.5,
+                               "tokens": 100, "token_scale": 1.3})
+    announce("graph_replay", case="reorder")
+    dev = device()
+    inp = synth.generate(w, 5, dev)
+    path = pipeline.ReorderPath(w, inp)
+    _capture_and_check(lambda: path(inp["q"]), _tensors(inp))
+
+
+def test_graph_replay_recompute_path():
+    w = synth.workload("infoflow_recompute_32l_64x1024", B=2, N=4096, group=2, k=600,
+                       plants={"chunk_len": 1024, "chunks": 1, "chunk_scale": 1.5,
+                               "tokens": 300, "token_scale": 1.3})
+    announce("graph_replay", case="recompute")
+    dev = device()
+    inp = synth.generate(w, 6, dev)
+    path = pipeline.RecomputePath(w, inp)
+    _capture_and_check(lambda: path(inp["q_sel"]), _tensors(inp))
