@@ -97,8 +97,18 @@ def one_pass_decode(w) -> bool:
 
 
 def mfma_shape(w) -> bool:
-    """Shapes whose scoring and decode run on the matrix cores."""
+    """Shapes whose scoring runs on the matrix cores."""
     return w.dtype == "bf16" and (w.Hq // w.H) * w.T >= 16
+
+
+def decode_kernel(w, rows: int) -> str:
+    """The kernel of a plain (not gathering) decode pass with `rows` query rows
+    per kv head: the matrix cores from 5 rows (bf16), the streaming kernel
+    below that where it applies, else the tile kernel."""
+    stream = w.dtype == "bf16" and w.D == 128 and 1 <= rows <= 8 and w.H in (1, 2, 4, 8)
+    if w.dtype == "bf16" and rows >= 5:
+        return "decode_mfma_kernel"
+    return "decode_stream_kernel" if stream else "decode_tile_kernel"
 
 
 def stage_work(w) -> dict:
@@ -208,9 +218,7 @@ def kernel_of(stage: str, w) -> str:
     if w.recipe == "cachefocus":
         return {"select": "score_mfma_kernel" if mfma_shape(w) else "score_stream_kernel",
                 "final_gather": "gather_kernel",
-                "decode": ("decode_mfma_kernel" if mfma_shape(w) else
-                           "decode_stream_kernel" if one_pass_decode(w) else
-                           "decode_tile_kernel") + MERGE}[stage]
+                "decode": decode_kernel(w, w.Hq // w.H) + MERGE}[stage]   # one decode token
     if stage == "recompute":
         return "index_attn_kernel"
     if w.reorder and stage not in ("score", "aggregate", "topk"):
@@ -225,8 +233,7 @@ def kernel_of(stage: str, w) -> str:
                      "score_mfma_kernel" if mfma else "score_tile_kernel",
             "aggregate": "agg_mfma_kernel" if mfma else "agg_token_kernel",
             "topk": "topk_kernel", "gather": "gather_kernel",
-            "decode": ("decode_mfma_kernel" if mfma else
-                       "decode_stream_kernel" if one_pass_decode(w) else "decode_tile_kernel") + MERGE,
+            "decode": decode_kernel(w, rows) + MERGE,
             "gather_decode": "decode_stream_kernel" + MERGE}[stage]
 
 

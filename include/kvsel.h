@@ -411,10 +411,10 @@ int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc,
  * over the concatenation of the n_seg segments (a HOST array; all share B, H,
  * D and dtype with the query), no mask.  Output fp32 [B][T][Hq][D]; lse (fp32
  * [B][Hq][T], natural log of sum_t exp(l)) or NULL.  1 <= n_seg <= 4; every
- * segment has N >= 1.  For bf16 query blocks with >= 16 rows per kv head the
- * pass runs on the matrix cores and the attention weights exp(l - max) are
- * rounded to bf16 before they multiply V (the sum that normalises them is
- * fp32).
+ * segment has N >= 1.  For bf16 query blocks with >= 5 rows per kv head the
+ * pass runs on the matrix cores (5 to 15 rows padded to one 16-row block) and
+ * the attention weights exp(l - ref) are rounded to bf16 before they multiply
+ * V; the sum that normalises them adds the same rounded weights, in fp32.
  *   ws  kvsel_decode_workspace(...) bytes (returns 0 for invalid arguments).
  */
 int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale,

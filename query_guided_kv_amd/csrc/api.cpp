@@ -146,8 +146,18 @@ int64_t decode_splits(const kvsel_segment* segs, int n_seg, int64_t split_len) {
   return n;
 }
 
-int64_t split_len_of(int64_t T, int64_t Hq, const kvsel_cache& c) {
-  return decode_split_len(c.dtype, c.H, c.D, c.H > 0 ? (Hq / c.H) * T : 1);
+int64_t split_len_of(int64_t T, int64_t Hq, const kvsel_cache& c, bool gathered) {
+  return decode_split_len(c.dtype, c.H, c.D, c.H > 0 ? (Hq / c.H) * T : 1, gathered);
+}
+
+// (m, s, o) partials of every split of the segments; `gathered` when the last
+// segment is gathered on the fly (the split length depends on the kernel)
+size_t decode_ws(int64_t T, int64_t Hq, const kvsel_segment* segs, int n_seg, bool gathered) {
+  if (segs == nullptr || n_seg < 1 || n_seg > kMaxSegments || T < 1 || Hq < 1) return 0;
+  for (int i = 0; i < n_seg; ++i)
+    if (segs[i].kc.N < 1 || segs[i].kc.B < 1 || segs[i].kc.D < 1) return 0;
+  const int64_t n_split = decode_splits(segs, n_seg, split_len_of(T, Hq, segs[0].kc, gathered));
+  return static_cast<size_t>(segs[0].kc.B * Hq * T * n_split * (2 + segs[0].kc.D)) * sizeof(float);
 }
 
 }  // namespace
@@ -607,11 +617,7 @@ int kvsel_gather(const void* k_src, const void* v_src, kvsel_cache kc, int64_t u
 }
 
 size_t kvsel_decode_workspace(int64_t T, int64_t Hq, const kvsel_segment* segs, int32_t n_seg) {
-  if (segs == nullptr || n_seg < 1 || n_seg > kMaxSegments || T < 1 || Hq < 1) return 0;
-  for (int i = 0; i < n_seg; ++i)
-    if (segs[i].kc.N < 1 || segs[i].kc.B < 1 || segs[i].kc.D < 1) return 0;
-  const int64_t n_split = decode_splits(segs, n_seg, split_len_of(T, Hq, segs[0].kc));
-  return static_cast<size_t>(segs[0].kc.B * Hq * T * n_split * (2 + segs[0].kc.D)) * sizeof(float);
+  return decode_ws(T, Hq, segs, n_seg, false);
 }
 
 int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const kvsel_segment* segs,
@@ -633,7 +639,7 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const k
     if (c.B != c0.B || c.H != c0.H || c.D != c0.D || c.dtype != c0.dtype)
       return fail(KVSEL_ERR_SHAPE, "kvsel_decode_attn: segments must share B, H, D and dtype");
     ds[i] = DecodeSeg{segs[i].k, segs[i].v, c.N, c.stride_b, c.stride_n, split};
-    split += (c.N + split_len_of(T, Hq, c0) - 1) / split_len_of(T, Hq, c0);
+    split += (c.N + split_len_of(T, Hq, c0, false) - 1) / split_len_of(T, Hq, c0, false);
   }
   KVSEL_TRY(check_heads(T, Hq, c0, "kvsel_decode_attn"));
   const size_t need = kvsel_decode_workspace(T, Hq, segs, n_seg);
@@ -660,7 +666,8 @@ size_t kvsel_gather_decode_workspace(int64_t T, int64_t Hq, kvsel_cache kc, int6
                                           kc.H * kc.D, kc.dtype}};
   }
   if (n == 0) return 0;
-  return kvsel_decode_workspace(T, Hq, segs, n);
+  const bool fused = k > 0 && kc.H > 0 && decode_stream_ok(kc.dtype, kc.H, kc.D, (Hq / kc.H) * T);
+  return decode_ws(T, Hq, segs, n, fused);
 }
 
 int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const void* k_src,
@@ -708,7 +715,10 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
     if (c.B != kc.B || c.H != kc.H || c.D != kc.D || c.dtype != kc.dtype)
       return fail(KVSEL_ERR_SHAPE, "kvsel_gather_decode: segments must share B, H, D and dtype");
   }
-  const size_t need = kvsel_decode_workspace(T, Hq, segs, n);
+  // one pass (each kept row read once, copied to the compact cache and
+  // attended) where the streaming kernel applies; else a copy then a decode
+  const bool fused = k > 0 && decode_stream_ok(kc.dtype, kc.H, kc.D, (Hq / kc.H) * T);
+  const size_t need = decode_ws(T, Hq, segs, n, fused);
   if (ws == nullptr || ws_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "kvsel_gather_decode: workspace %zu < %zu bytes", ws_bytes,
                 need);
@@ -716,8 +726,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
     KVSEL_TRY(resolve_rows(k_src, &k_src, "k_src"));
     KVSEL_TRY(resolve_rows(v_src, &v_src, "v_src"));
   }
-  if (k > 0 && decode_stream_ok(kc.dtype, kc.H, kc.D, (Hq / kc.H) * T)) {
-    // one pass: each kept row is read once, copied to the compact cache and attended
+  if (fused) {
     DecodeSeg ds[kMaxSegments];
     int64_t split = 0;
     for (int i = 0; i < n; ++i) {
@@ -725,7 +734,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
       ds[i] = DecodeSeg{g ? k_src : segs[i].k, g ? v_src : segs[i].v, segs[i].kc.N,
                         g ? kc.stride_b : segs[i].kc.stride_b,
                         g ? kc.stride_n : segs[i].kc.stride_n, split};
-      split += (segs[i].kc.N + split_len_of(T, Hq, kc) - 1) / split_len_of(T, Hq, kc);
+      split += (segs[i].kc.N + split_len_of(T, Hq, kc, true) - 1) / split_len_of(T, Hq, kc, true);
     }
     const DecodeGather gather{n - 1, idx, unit_len, k, idx_group, M, k_dst, v_dst};
     float* ws_ms = static_cast<float*>(ws);

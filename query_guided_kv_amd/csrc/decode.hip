@@ -634,12 +634,18 @@ bool decode_stream_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv) {
          (H == 1 || H == 2 || H == 4 || H == 8);
 }
 
-int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv) {
-  (void)H;
-  (void)D;
-  // the matrix-core variant runs tall query blocks: longer splits leave fewer
-  // (m, s, o) partials to write and merge
-  return dtype == KVSEL_BF16 && rows_per_kv >= 16 ? 1024 : kDecodeSplit;
+bool decode_uses_stream(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered) {
+  // the streaming kernel is the only one that gathers on the fly (up to 8
+  // rows); a plain pass with 5 or more rows runs faster on the matrix cores
+  // (one 16-row block, padded), which read K and V through LDS tiles
+  return decode_stream_ok(dtype, H, D, rows_per_kv) && (gathered || rows_per_kv < kDecodeMfmaRows);
+}
+
+int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered) {
+  if (decode_uses_stream(dtype, H, D, rows_per_kv, gathered)) return kDecodeSplit;
+  // the matrix-core variant: longer splits leave fewer (m, s, o) partials to
+  // write and merge
+  return dtype == KVSEL_BF16 && rows_per_kv >= kDecodeMfmaRows ? 1024 : kDecodeSplit;
 }
 
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
@@ -648,7 +654,7 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
                   const DecodeGather* gather) {
   SegTable st{};
   st.gather_seg = -1;
-  st.split_len = decode_split_len(dtype, H, D, (Hq / H) * T);
+  st.split_len = decode_split_len(dtype, H, D, (Hq / H) * T, gather != nullptr);
   if (gather != nullptr) {
     // only the streaming variant gathers on the fly
     if (!decode_stream_ok(dtype, H, D, (Hq / H) * T)) {
@@ -676,7 +682,7 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
   const float scale2 = scale * kLog2e;
   const int64_t R = (Hq / H) * T;
   bool done = false;
-  if (decode_stream_ok(dtype, H, D, R)) {
+  if (decode_uses_stream(dtype, H, D, R, gather != nullptr)) {
     // rows per kv head padded to 1, 2, 4 or 8
     const int64_t RP = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8;
 #define KVSEL_DS(H_, R_) \
@@ -687,7 +693,7 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
     KVSEL_DS(1, 1) KVSEL_DS(1, 2) KVSEL_DS(1, 4) KVSEL_DS(1, 8)
 #undef KVSEL_DS
   }
-  if (!done && dtype == KVSEL_BF16 && R >= 16) {
+  if (!done && dtype == KVSEL_BF16 && R >= kDecodeMfmaRows) {
     // Tall query blocks (12 row blocks or more): eight waves of two row blocks,
     // so every staged K and V fragment feeds two products; 256 rows a pass.
     // Otherwise one row block per wave: two waves for up to two row blocks,

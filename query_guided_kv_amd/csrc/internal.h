@@ -147,7 +147,7 @@ struct DecodeGather {
   void* k_dst;
   void* v_dst;
 };
-int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);
+int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered);
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
                   int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
                   float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s,
@@ -158,5 +158,8 @@ bool stream_path_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);
 // the streaming decode (and the one-pass refill + decode): bf16, head dim 128,
 // <= 8 kv heads (a power of two), 1 .. 8 query rows per kv head
 bool decode_stream_ok(int dtype, int64_t H, int64_t D, int64_t rows_per_kv);
+// Rows per kv head from which a plain (not gathering) pass runs on the matrix cores.
+constexpr int64_t kDecodeMfmaRows = 5;
+bool decode_uses_stream(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered);
 
 }  // namespace kvsel

@@ -266,10 +266,12 @@ DECODE_CASES = [
     ("stream_R4", "bf16", 3, (1300,), 8, 32, 1, 128),
     ("stream_R4_two_segs", "bf16", 2, (1024, 77), 8, 32, 1, 128),
     ("stream_R2_T2", "bf16", 2, (600,), 4, 4, 2, 128),
-    # rows per kv head padded to the next of 1, 2, 4, 8
-    ("stream_R7_padded", "bf16", 3, (2560,), 4, 28, 1, 128),
+    # rows per kv head padded to the next of 1, 2, 4
     ("stream_R3_padded_two_segs", "bf16", 2, (700, 33), 8, 24, 1, 128),
-    ("stream_R6_T3_padded", "bf16", 2, (900,), 2, 4, 3, 128),
+    # 5 to 15 rows: the matrix cores, one 16-row block
+    ("mfma_R7_one_block", "bf16", 3, (2560,), 4, 28, 1, 128),
+    ("mfma_R6_T3_one_block", "bf16", 2, (900,), 2, 4, 3, 128),
+    ("mfma_R5_d64_two_segs", "bf16", 2, (300, 70), 2, 10, 1, 64),
     ("tile_R16_fp32", "fp32", 1, (256,), 4, 4, 16, 64),
     ("tile_R448_two_segs", "bf16", 1, (700, 600), 4, 28, 64, 128),
     ("tile_R32_bf16", "bf16", 1, (1100,), 4, 4, 32, 128),
@@ -338,11 +340,14 @@ def test_gather_decode(case):
     wo, wl = O.decode_attention(to64(q), segs, 1.0 / np.sqrt(D))
     assert_rel(o, wo, 0.0, 5e-3, "o")
     assert_rel(lse, wl, 0.0, 2e-3, "lse")
-    # the separate calls give the same output
+    # the separate calls give the same output (the same kernel where the plain
+    # decode also streams; from 5 rows per kv head it runs on the matrix cores
+    # with bf16 weights, so the two agree to the parity tolerance)
     segs_d = [(a.to(dev), b.to(dev)) for a, b in extra] + ([(kd, vd)] if kept else [])
     o2, lse2 = K.decode_attn(q.to(dev), segs_d)
     torch.cuda.synchronize()
-    assert_rel(o2, to64(o), 0.0, 1e-5, "o vs separate calls")
+    same_kernel = not (dtype == "bf16" and (Hq // H) * T >= 5)
+    assert_rel(o2, to64(o), 0.0, 1e-5 if same_kernel else 5e-3, "o vs separate calls")
 
 
 # --------------------------------------------------------------------------
