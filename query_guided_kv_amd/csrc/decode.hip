@@ -1,17 +1,19 @@
 // Final attention pass over the compact cache (ACRE §2.1 Eq. 4; decoding on
 // the refilled cache, ACRE §2.4).
 //
-// Split-K: the keys of every segment are cut into splits of kDecodeSplit rows;
-// one workgroup computes, for its split, each row's running max m, sum s and
-// unnormalised output o (online softmax in the log2 domain).  A merge kernel
-// combines the splits of a row with the usual rescaling and writes
+// Split-K: the keys of every segment are cut into splits (decode_split_len
+// rows); one workgroup computes, for its split, each row's reference m, sum s
+// and unnormalised output o (online softmax in the log2 domain).  A merge
+// kernel combines the splits of a row with the usual rescaling and writes
 // o / s and lse = (m + log2 s) * ln 2.
 //
-// stream variant: bf16, few rows per kv head (decode).  Lanes own 32 bytes of
-// a key row and the matching 32 bytes of the value row; logits use packed bf16
-// dots and an 8-lane DPP reduction; the four waves' partials are merged
-// through LDS one wave at a time.
-// tile variant: any shape; keys and values staged through LDS as fp32.
+// stream variant: bf16, head dim 128, 1 to 4 rows per kv head (up to 8 when it
+// gathers the kept rows on the fly).  Lanes own 32 bytes of a key row and the
+// matching 32 bytes of the value row; logits use packed bf16 dots and an
+// 8-lane DPP reduction; the four waves' partials are merged through LDS one
+// wave at a time.
+// matrix-core variant: bf16, 5 or more rows per kv head (below).
+// tile variant: any other shape; keys and values staged through LDS as fp32.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
