@@ -374,7 +374,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   constexpr int TK = kMfmaTileKeys;
   constexpr int KS = D / 32;
   constexpr int KROW = D + kMfmaPad;
-  constexpr int VROW = TK + 8;          // transposed V: dims x keys (+16 bytes)
+  constexpr int VROW = TK + kMfmaPad;   // transposed V: dims x keys (+32 bytes)
   constexpr int CB = D / 16;            // output column blocks
   constexpr int KG = TK / 4;            // groups of 4 keys
   constexpr int NT = 64 * NW;

@@ -22,9 +22,12 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Padding of a staged row of an LDS key tile (kMfmaTileKeys keys): 16 bytes,
-// so the 16 keys one B-fragment read spans land on distinct banks.
-constexpr int kMfmaPad = 8;
+// Padding of a staged row of an LDS tile (keys of the K tile, dims of the
+// transposed V tile): 32 bytes, so that the row stride is 8 dwords past a
+// multiple of 16.  Measured on gfx950 for the 16-byte fragment reads of these
+// kernels: strides of 68, 76, 36 or 44 dwords conflict (up to 44% of the LDS
+// cycles), 72 and 40 do not.
+constexpr int kMfmaPad = 16;
 
 // Row blocks of 16 query rows: how the four waves of a workgroup share them.
 // NWR waves split the row blocks (RBW per wave), 4 / NWR split the key blocks.
