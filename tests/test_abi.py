@@ -323,3 +323,28 @@ def test_score_reposition_validation(lib):
     # matrix-core shape (32 rows per kv head): fused, no extra room
     assert lib.kvsel_score_reposition_workspace(32, 32, kc, 256, 256, 1, 1, 0) == \
         lib.kvsel_score_workspace(2, 1024, 32, 32, 256, 1, 1)
+
+
+def test_decode_split_by_path(lib):
+    """The workspace of a decode call follows the kernel it runs: the
+    streaming kernel splits the keys by 512; a plain pass with 5 or more bf16
+    rows per kv head runs on the matrix cores and splits them by 1024; the
+    fused refill keeps the streaming kernel (512) up to 8 rows."""
+    N, D = 3000, 128
+    seven = (K.Segment * 1)(K.Segment(FAKE, FAKE, cache(B=2, N=N, H=4, D=D)))
+    # 28 / 4 heads x 1 token = 7 rows per kv head: matrix cores, ceil(3000 / 1024) = 3 splits
+    assert lib.kvsel_decode_workspace(1, 28, seven, 1) == 2 * 28 * 1 * 3 * (2 + D) * 4
+    # 4 rows per kv head: streaming, ceil(3000 / 512) = 6 splits
+    assert lib.kvsel_decode_workspace(1, 16, seven, 1) == 2 * 16 * 1 * 6 * (2 + D) * 4
+    # fp32 keys: the tile kernel, 512-key splits
+    f32 = (K.Segment * 1)(K.Segment(FAKE, FAKE, cache(B=2, N=N, H=4, D=D, dtype=1)))
+    assert lib.kvsel_decode_workspace(1, 28, f32, 1) == 2 * 28 * 1 * 6 * (2 + D) * 4
+    # the fused refill with 7 rows: streaming, the kept rows split by 512
+    kc = cache(B=2, N=8 * 512, H=4, D=D)
+    rows = 5 * 512
+    need = lib.kvsel_gather_decode_workspace(1, 28, kc, 512, 5, None, 0)
+    assert need == 2 * 28 * 1 * ((rows + 511) // 512) * (2 + D) * 4
+    # with 16 rows per kv head (no streaming kernel) the copy and the plain pass
+    # run separately: 1024-key splits
+    need16 = lib.kvsel_gather_decode_workspace(4, 16, kc, 512, 5, None, 0)
+    assert need16 == 2 * 16 * 4 * ((rows + 1023) // 1024) * (2 + D) * 4
