@@ -90,7 +90,8 @@ template <int D, int H, int R, int U>
 __global__ void __launch_bounds__(kThreads)
 score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int64_t N,
                     int64_t stride_b, int64_t stride_n, int T, int Hq, float scale2,
-                    int64_t seg_len, int64_t nseg, float* __restrict__ ms, int natural) {
+                    int64_t seg_len, int64_t nseg, int64_t spb, float* __restrict__ ms,
+                    int natural) {
   constexpr int LPH = D / 16;
   constexpr int LPT = H * LPH;
   constexpr int TPW = 64 / LPT;
@@ -106,8 +107,12 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   const int slot = lane / LPT;
   const int g = (lane % LPT) / LPH;
   const int c = lane % LPH;
-  const int64_t b = blockIdx.x / nseg;
-  const int64_t seg = blockIdx.x % nseg;
+  // a workgroup scores spb consecutive segments (one partial each): the
+  // query slices are loaded once and the per-segment fixed cost is shared
+  const int64_t groups = (nseg + spb - 1) / spb;
+  const int64_t b = blockIdx.x / groups;
+  const int64_t seg0 = (blockIdx.x % groups) * spb;
+  const int64_t seg1 = min(nseg, seg0 + spb);
   const int G = Hq / H;
   // the block of (row, key) pairs this lane owns after the scatter
   const int j = ((c >> 2) & 1) * 4 + (c & 1) * 2 + ((c >> 1) & 1);
@@ -125,12 +130,12 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     qv[r][4] = q1.x; qv[r][5] = q1.y; qv[r][6] = q1.z; qv[r][7] = q1.w;
   }
 
-  float m = -INFINITY, s = 0.0f;  // softmax partial of row own_r over this lane's keys
-
-  const int64_t t_begin = seg * seg_len;
-  const int64_t t_end = min(N, t_begin + seg_len);
   const bf16_t* kb = k + b * stride_b + g * D + c * 16;
   constexpr int STEP = kWaves * TPW;
+  for (int64_t seg = seg0; seg < seg1; ++seg) {
+  float m = -INFINITY, s = 0.0f;  // softmax partial of row own_r over this lane's keys
+  const int64_t t_begin = seg * seg_len;
+  const int64_t t_end = min(N, t_begin + seg_len);
 
   // logits of U rows (t0 + u*STEP) from their loaded slices; rows with
   // u >= n_valid are masked out
@@ -209,6 +214,7 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     merge_ms(m, s, m2, s2);
   }
   // one lane per (head, row) publishes: the owner of the row's first keys
+  if (seg > seg0) __syncthreads();   // the previous segment's partials fully read
   if (slot == 0 && own_u == 0) {
     red[wave][g * R + own_r][0] = m;
     red[wave][g * R + own_r][1] = s;
@@ -223,6 +229,7 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     float* o = ms + (((b * Hq + h) * T + jj) * nseg + seg) * 2;
     o[0] = natural ? mm * kLn2 : mm;
     o[1] = ss;
+  }
   }
 }
 
@@ -346,16 +353,22 @@ rowstat_kernel(const float* __restrict__ ms, int64_t rows, int64_t nseg, int nat
 // buffering the loads in registers and 8 rows per step measured the same on
 // MI355X: the stream runs at the memory system's rate either way.)
 template <int R> constexpr int stream_unroll() { return R >= 2 ? 4 : 8; }
+constexpr int64_t kStreamSegsPerBlock = 2;
 
 template <int D, int H, int R>
 void launch_stream(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
                    float scale2, int64_t seg_len, int64_t nseg, float* ms, int natural,
                    hipStream_t s) {
+  // segments per workgroup: up to kStreamSegsPerBlock while the grid keeps
+  // at least 8192 workgroups
+  int64_t spb = kStreamSegsPerBlock;
+  while (spb > 1 && kc.B * ((nseg + spb - 1) / spb) < 8192) spb /= 2;
+  const int64_t groups = (nseg + spb - 1) / spb;
   hipLaunchKernelGGL((score_stream_kernel<D, H, R, stream_unroll<R>()>),
-                     dim3(static_cast<unsigned>(kc.B * nseg)),
+                     dim3(static_cast<unsigned>(kc.B * groups)),
                      dim3(kThreads), 0, s, static_cast<const bf16_t*>(q),
                      static_cast<const bf16_t*>(k), kc.N, kc.stride_b, kc.stride_n,
-                     static_cast<int>(T), static_cast<int>(Hq), scale2, seg_len, nseg, ms,
+                     static_cast<int>(T), static_cast<int>(Hq), scale2, seg_len, nseg, spb, ms,
                      natural);
 }
 
