@@ -323,6 +323,9 @@ int kvsel_order(const float* score, int64_t G, int64_t M, const int32_t* idx,
  *   k, v   the context, cache `kc` (bf16 only: the matrix-core kernel).
  *   out    fp32 [B][S][Hq][D];  lse fp32 [B][Hq][S] or NULL.
  *   S * Hq < 2^31.  No workspace: every row's output is written once.
+ * As in kvsel_decode_attn's matrix-core pass, the weights exp(l - ref) are
+ * rounded to bf16 before they multiply V, and the sum that normalises them
+ * adds the same rounded weights, in fp32.
  */
 int kvsel_index_attn(const void* q, int64_t S, int64_t Hq, float scale,
                      const void* k, const void* v, kvsel_cache kc,
