@@ -334,7 +334,7 @@ def cpu_baseline_recompute(w, inp, rows: int = 64) -> dict:
                       f"context rows; fp64 numpy, 1 thread), {elapsed:.1f} s"}
 
 
-def cpu_baseline(w, inp, budget_s: float = 12.0, max_instances: int = 8) -> dict:
+def cpu_baseline(w, inp, budget_s: float = 15.0, max_instances: int = 24) -> dict:
     """Time the fp64 oracle on whole instances of the workload (inputs copied to
     host memory first, outside the timed region), single-threaded."""
     import numpy as np
