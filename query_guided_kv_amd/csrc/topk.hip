@@ -3,12 +3,20 @@
 // Order: score descending, ties by smaller index.  Scores become 32-bit keys
 // whose unsigned order is the float order (-0 folded onto +0), so selection
 // is exact integer work.  One workgroup per row:
-//  1. radix select, 4 passes of 8 bits with an LDS histogram, finds the k-th
-//     largest key K* and how many keys equal to K* are kept (need_eq);
+//  1. the k-th largest key K*, and how many keys equal to K* are kept
+//     (need_eq), from histograms over the row's own key range [lo, hi]:
+//     2048 bins, bin = (key - base) >> shift (monotone in the key); each pass
+//     narrows the range to the bin that holds the k-th largest key, until
+//     that bin holds at most 256 keys (then ranked exactly against each
+//     other) or a single key value.  At most three passes.
 //  2. each thread counts keys > K* and == K* over a contiguous slice of
 //     indices; a block-wide exclusive scan of both counts gives every kept
 //     index its output slot, so the kept set is written in ascending index
 //     order with no sort.
+// Rows of up to 16 * 1024 scores keep each thread's slice in registers and
+// read the scores once; longer rows read them again for every pass (coalesced
+// reads of a row the L2 holds), since their slices would not fit in the
+// registers of a 1024-thread workgroup.
 #include "common.h"
 #include "internal.h"
 
@@ -17,6 +25,12 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kFastBits = 11;
+constexpr int kFastBins = 1 << kFastBits;
+constexpr int kFastCand = 256;
+constexpr int kRegKeys = 16;   // keys per thread held in registers, at most
+static_assert(kFastBins == 2 * kThreads, "two bins per thread in the bin scan");
+static_assert(kFastCand <= kThreads, "one candidate per thread in the ranking");
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -24,9 +38,20 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of (a, b) over the block; returns the prefix of this thread.
+struct TopkShared {
+  uint32_t hist[kFastBins];
+  uint32_t scan_a[kWaves], scan_b[kWaves];
+  uint32_t lo[kWaves], hi[kWaves];
+  uint32_t bin, rank, count, ncand, kstar, need;
+  uint32_t tot[2];
+  uint32_t cand[kFastCand];
+};
+
+// Exclusive scan of (a, b) over the block; returns the prefix of this thread
+// (and, where tot is given, the block totals in tot[0], tot[1]).
 __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t& pa,
-                                                      uint32_t& pb, uint32_t* sa, uint32_t* sb) {
+                                                      uint32_t& pb, uint32_t* sa, uint32_t* sb,
+                                                      uint32_t* tot = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   uint32_t ia = a, ib = b;  // inclusive within the wave
@@ -45,179 +70,180 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
       sa[w] = ca; sb[w] = cb;
       ca += xa; cb += xb;
     }
+    if (tot != nullptr) { tot[0] = ca; tot[1] = cb; }
   }
   __syncthreads();
   pa = sa[wave] + ia - a;
   pb = sb[wave] + ib - b;
 }
 
-// Pick the digit of the k-th largest key from a 256-bin histogram (one wave,
-// threadIdx.x < 64): lane l owns bins 255-4l .. 252-4l (high to low); an
-// exclusive scan of the lanes' counts gives the number of keys in higher bins,
-// and the one bin with above < rank <= above + count publishes the new prefix
-// and the rank left inside that bin.
-__device__ __forceinline__ void select_bin(const uint32_t* h, uint32_t rank, uint32_t prefix,
-                                           int shift, uint32_t* sh_prefix, uint32_t* sh_rank) {
-  const int lane = threadIdx.x;
-  uint32_t c[4], tot = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    c[j] = h[255 - 4 * lane - j];
-    tot += c[j];
-  }
-  uint32_t incl = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
-  }
-  uint32_t above = incl - tot;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (above < rank && rank <= above + c[j]) {
-      *sh_prefix = prefix | (static_cast<uint32_t>(255 - 4 * lane - j) << shift);
-      *sh_rank = rank - above;
-    }
-    above += c[j];
-  }
-}
-
-// Count `bin` into this wave's histogram.  Scores of one row share most of
-// their leading bits, so the lanes of a wave mostly hit the same bin: the
-// lanes with the first active lane's bin add their count once (ballot +
-// popcount), the rest add one by one.  Integer counts: exact in any order.
-__device__ __forceinline__ void count_bin(uint32_t* hist, uint32_t bin, bool active) {
-  const uint64_t act = __ballot(active);
-  if (act == 0) return;
-  const int first = __builtin_ctzll(act);
-  const uint32_t lead = __shfl(bin, first, 64);
-  const bool same = active && bin == lead;
-  const uint64_t grp = __ballot(same);
-  const int lane = threadIdx.x & 63;
-  if (lane == first) atomicAdd(&hist[lead], static_cast<uint32_t>(__popcll(grp)));
-  if (active && !same) atomicAdd(&hist[bin], 1u);
-}
-
-__global__ void __launch_bounds__(kThreads)
-topk_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* __restrict__ idx,
-            float* __restrict__ val) {
-  __shared__ uint32_t hist[kWaves][256];
-  __shared__ uint32_t sh_prefix, sh_rank;
-  __shared__ uint32_t scan_a[kWaves], scan_b[kWaves];
-  const float* s = score + static_cast<int64_t>(blockIdx.x) * M;
-  int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
-  float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
-  const int wave = threadIdx.x >> 6;
-
-  // 1. radix select of the k-th largest key, 8 bits per pass, one histogram
-  //    per wave merged in a fixed order
-  uint32_t prefix = 0, mask = 0, rank = static_cast<uint32_t>(k);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    const int64_t rounds = (M + kThreads - 1) / kThreads;
-    for (int64_t rd = 0; rd < rounds; ++rd) {
-      const int64_t i = rd * kThreads + threadIdx.x;
-      uint32_t key = 0;
-      bool act = false;
-      if (i < M) {
-        key = order_key(s[i]);
-        act = (key & mask) == prefix;
-      }
-      count_bin(hist[wave], (key >> shift) & 255u, act);
-    }
-    __syncthreads();
-    if (threadIdx.x < 256) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) t += hist[w][threadIdx.x];
-      hist[0][threadIdx.x] = t;   // each thread reads and writes its own bin only
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) select_bin(hist[0], rank, prefix, shift, &sh_prefix, &sh_rank);
-    __syncthreads();
-    rank = sh_rank;
-    prefix = sh_prefix;
-    mask |= 255u << shift;
-  }
-  const uint32_t kstar = prefix;
-  const uint32_t need_eq = rank;  // keys equal to K* that are kept
-
-  // 2. ordered compaction over contiguous index slices
-  const int64_t per = (M + kThreads - 1) / kThreads;
-  const int64_t i0 = min(M, threadIdx.x * per);
-  const int64_t i1 = min(M, i0 + per);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int64_t i = i0; i < i1; ++i) {
-    const uint32_t key = order_key(s[i]);
-    n_gt += key > kstar;
-    n_eq += key == kstar;
-  }
-  uint32_t gt_before, eq_before;
-  block_exclusive_scan2(n_gt, n_eq, gt_before, eq_before, scan_a, scan_b);
-  for (int64_t i = i0; i < i1; ++i) {
-    const float x = s[i];
-    const uint32_t key = order_key(x);
-    if (key > kstar) {
-      const uint32_t pos = gt_before + min(eq_before, need_eq);
-      out_i[pos] = static_cast<int32_t>(i);
-      if (out_v) out_v[pos] = x;
-      ++gt_before;
-    } else if (key == kstar) {
-      if (eq_before < need_eq) {
-        const uint32_t pos = gt_before + eq_before;
-        out_i[pos] = static_cast<int32_t>(i);
-        if (out_v) out_v[pos] = x;
-      }
-      ++eq_before;
-    }
-  }
-}
-
-// Rows of up to 64 * 1024 scores: each thread keeps its contiguous slice of
-// KPT keys in registers, so the four radix passes and the ordered compaction
-// read the scores once.
+// Keys of a row held in registers: indices i0 .. i0 + KPT - 1 of this thread.
 template <int KPT>
-__global__ void __launch_bounds__(kThreads)
-topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* __restrict__ idx,
-                float* __restrict__ val) {
-  __shared__ uint32_t hist[kWaves][256];
-  __shared__ uint32_t sh_prefix, sh_rank;
-  __shared__ uint32_t scan_a[kWaves], scan_b[kWaves];
-  const float* s = score + static_cast<int64_t>(blockIdx.x) * M;
-  int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
-  float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
-  const int wave = threadIdx.x >> 6;
-  const int64_t i0 = static_cast<int64_t>(threadIdx.x) * KPT;
-
+struct RegKeys {
   uint32_t key[KPT];
+  int64_t i0, M;
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const {
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) key[e] = i0 + e < M ? order_key(s[i0 + e]) : 0u;
+    for (int e = 0; e < KPT; ++e) f(i0 + e < M, key[e]);
+  }
+};
 
-  uint32_t prefix = 0, mask = 0, rank = static_cast<uint32_t>(k);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
+// Loads issued together before their keys are used: a thread's reads are
+// independent, so kBatch of them are in flight instead of one.
+constexpr int kBatch = 16;
+
+// Keys of a row read for every pass: indices threadIdx.x + r * kThreads.
+struct StreamKeys {
+  const float* s;
+  int64_t M;
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const {
+    for (int64_t i0 = threadIdx.x; i0 < M; i0 += kBatch * kThreads) {
+      uint32_t key[kBatch];
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
-      count_bin(hist[wave], (key[e] >> shift) & 255u, i0 + e < M && (key[e] & mask) == prefix);
-    __syncthreads();
-    if (threadIdx.x < 256) {
-      uint32_t t = 0;
+      for (int b = 0; b < kBatch; ++b) {
+        const int64_t i = i0 + static_cast<int64_t>(b) * kThreads;
+        key[b] = i < M ? order_key(s[i]) : 0u;
+      }
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) t += hist[w][threadIdx.x];
-      hist[0][threadIdx.x] = t;
+      for (int b = 0; b < kBatch; ++b) f(i0 + static_cast<int64_t>(b) * kThreads < M, key[b]);
+    }
+  }
+};
+
+// Step 1: K* and need_eq of the k-th largest key (1 <= k <= M).  Every
+// thread of the block calls it and gets the same two values.
+template <typename Keys>
+__device__ __forceinline__ void range_select(const Keys& keys, uint32_t k, TopkShared& sm,
+                                             uint32_t& kstar, uint32_t& need_eq) {
+  const int wave = threadIdx.x >> 6;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  keys.each([&](bool valid, uint32_t key) {
+    if (valid) {
+      lo = min(lo, key);
+      hi = max(hi, key);
+    }
+  });
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off, 64)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off, 64)));
+  }
+  if ((threadIdx.x & 63) == 0) { sm.lo[wave] = lo; sm.hi[wave] = hi; }
+  if (threadIdx.x == 0) sm.ncand = 0;
+  __syncthreads();
+  lo = sm.lo[0];
+  hi = sm.hi[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    lo = min(lo, sm.lo[w]);
+    hi = max(hi, sm.hi[w]);
+  }
+  // The current range holds the keys with base <= key and key - base < span
+  // (span = 2^bits, then the previous pass's bin width); its bins are
+  // (key - base) >> sh, kFastBins of them at most.
+  const uint32_t range = hi - lo;
+  const int bits = range == 0u ? 0 : 32 - __clz(static_cast<int>(range));
+  uint32_t base = lo;
+  uint64_t span = uint64_t{1} << bits;
+  int sh = bits > kFastBits ? bits - kFastBits : 0;
+  uint32_t rank = k, fbin = 0, fcount = 0;
+  for (;;) {
+    for (int i = threadIdx.x; i < kFastBins; i += kThreads) sm.hist[i] = 0;
+    __syncthreads();
+    keys.each([&](bool valid, uint32_t key) {
+      const uint32_t d = key - base;
+      if (valid && key >= base && d < span) atomicAdd(&sm.hist[d >> sh], 1u);
+    });
+    __syncthreads();
+    // bins from the top: thread t owns bins 2047 - 2t and 2046 - 2t; exactly
+    // one bin b has above(b) < rank <= above(b) + count(b), since the range
+    // holds at least `rank` keys
+    const uint32_t c0 = sm.hist[kFastBins - 1 - 2 * threadIdx.x];
+    const uint32_t c1 = sm.hist[kFastBins - 2 - 2 * threadIdx.x];
+    uint32_t above, unused;
+    block_exclusive_scan2(c0 + c1, 0u, above, unused, sm.scan_a, sm.scan_b);
+    if (above < rank && rank <= above + c0) {
+      sm.bin = kFastBins - 1 - 2 * threadIdx.x;
+      sm.rank = rank - above;
+      sm.count = c0;
+    } else if (above + c0 < rank && rank <= above + c0 + c1) {
+      sm.bin = kFastBins - 2 - 2 * threadIdx.x;
+      sm.rank = rank - above - c0;
+      sm.count = c1;
     }
     __syncthreads();
-    if (threadIdx.x < 64) select_bin(hist[0], rank, prefix, shift, &sh_prefix, &sh_rank);
-    __syncthreads();
-    rank = sh_rank;
-    prefix = sh_prefix;
-    mask |= 255u << shift;
+    fbin = sm.bin;
+    rank = sm.rank;
+    fcount = sm.count;
+    if (fcount <= kFastCand || sh == 0) break;
+    base += fbin << sh;
+    span = uint64_t{1} << sh;
+    sh = sh > kFastBits ? sh - kFastBits : 0;
+    __syncthreads();               // every thread has read hist and sm.* before they change
   }
-  const uint32_t kstar = prefix;
-  const uint32_t need_eq = rank;
+  if (sh == 0) {
+    // the bin is one key value
+    kstar = base + fbin;
+    need_eq = rank;
+    return;
+  }
+  // at most kFastCand keys: each one's exact rank among them; K* is the key
+  // with (# greater) < rank <= (# greater or equal)
+  keys.each([&](bool valid, uint32_t key) {
+    const uint32_t d = key - base;
+    if (valid && key >= base && d < span && (d >> sh) == fbin)
+      sm.cand[atomicAdd(&sm.ncand, 1u)] = key;
+  });
+  __syncthreads();
+  if (threadIdx.x < fcount) {
+    const uint32_t x = sm.cand[threadIdx.x];
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < fcount; ++j) {
+      const uint32_t y = sm.cand[j];
+      gt += y > x;
+      ge += y >= x;
+    }
+    // keys equal to K* all write the same two values
+    if (gt < rank && rank <= ge) { sm.kstar = x; sm.need = rank - gt; }
+  }
+  __syncthreads();
+  kstar = sm.kstar;
+  need_eq = sm.need;
+}
 
+// KPT consecutive keys of indices i0 .. i0 + KPT - 1 (those past M read as 0).
+template <int KPT>
+__device__ __forceinline__ void load_slice(const float* s, int64_t i0, int64_t M,
+                                           uint32_t (&key)[KPT]) {
+  if (KPT % 4 == 0 && i0 + KPT <= M && (reinterpret_cast<uintptr_t>(s + i0) & 15u) == 0) {
+    // a whole 16-byte aligned slice: vector loads (a quarter of the requests)
+#pragma unroll
+    for (int e = 0; e < KPT; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(s + i0 + e);
+      key[e] = order_key(v.x);
+      if constexpr (KPT % 4 == 0) {
+        key[e + 1] = order_key(v.y);
+        key[e + 2] = order_key(v.z);
+        key[e + 3] = order_key(v.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) key[e] = i0 + e < M ? order_key(s[i0 + e]) : 0u;
+  }
+}
+
+// Step 2 for one tile of kThreads * KPT indices starting at tile0: thread t
+// owns the slice tile0 + t * KPT .. + KPT - 1.  gt_run / eq_run count the kept
+// keys (> K*, == K*) of earlier tiles and are advanced past this one.
+template <int KPT>
+__device__ __forceinline__ void write_tile(const uint32_t (&key)[KPT], int64_t tile0, int64_t M,
+                                           uint32_t kstar, uint32_t need_eq, uint32_t& gt_run,
+                                           uint32_t& eq_run, TopkShared& sm, const float* s,
+                                           int32_t* out_i, float* out_v) {
+  const int64_t i0 = tile0 + static_cast<int64_t>(threadIdx.x) * KPT;
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
@@ -226,7 +252,10 @@ topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* 
     n_eq += in && key[e] == kstar;
   }
   uint32_t gt_before, eq_before;
-  block_exclusive_scan2(n_gt, n_eq, gt_before, eq_before, scan_a, scan_b);
+  block_exclusive_scan2(n_gt, n_eq, gt_before, eq_before, sm.scan_a, sm.scan_b, sm.tot);
+  const uint32_t tile_gt = sm.tot[0], tile_eq = sm.tot[1];
+  gt_before += gt_run;
+  eq_before += eq_run;
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
     if (i0 + e >= M) break;
@@ -243,6 +272,50 @@ topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* 
       }
       ++eq_before;
     }
+  }
+  gt_run += tile_gt;
+  eq_run += tile_eq;
+  __syncthreads();                 // scan_a/b and tot are free for the next tile
+}
+
+// Rows of up to KPT * 1024 scores (KPT <= kRegKeys): each thread keeps its
+// contiguous slice of KPT keys in registers, so the scores are read once.
+template <int KPT>
+__global__ void __launch_bounds__(kThreads)
+topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* __restrict__ idx,
+                float* __restrict__ val) {
+  __shared__ TopkShared sm;
+  const float* s = score + static_cast<int64_t>(blockIdx.x) * M;
+  int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
+  float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
+  RegKeys<KPT> keys;
+  keys.i0 = static_cast<int64_t>(threadIdx.x) * KPT;
+  keys.M = M;
+  load_slice<KPT>(s, keys.i0, M, keys.key);
+  uint32_t kstar, need_eq;
+  range_select(keys, static_cast<uint32_t>(k), sm, kstar, need_eq);
+  uint32_t gt_run = 0, eq_run = 0;
+  write_tile<KPT>(keys.key, 0, M, kstar, need_eq, gt_run, eq_run, sm, s, out_i, out_v);
+}
+
+// Longer rows: the selection reads the row again for every pass; the
+// compaction walks tiles of kThreads * kRegKeys scores, each read once.
+__global__ void __launch_bounds__(kThreads)
+topk_stream_kernel(const float* __restrict__ score, int64_t M, int64_t k,
+                   int32_t* __restrict__ idx, float* __restrict__ val) {
+  __shared__ TopkShared sm;
+  const float* s = score + static_cast<int64_t>(blockIdx.x) * M;
+  int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
+  float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
+  uint32_t kstar, need_eq;
+  range_select(StreamKeys{s, M}, static_cast<uint32_t>(k), sm, kstar, need_eq);
+
+  // tiles of kThreads * kRegKeys indices, in ascending order
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int64_t tile0 = 0; tile0 < M; tile0 += static_cast<int64_t>(kThreads) * kRegKeys) {
+    uint32_t key[kRegKeys];
+    load_slice<kRegKeys>(s, tile0 + static_cast<int64_t>(threadIdx.x) * kRegKeys, M, key);
+    write_tile<kRegKeys>(key, tile0, M, kstar, need_eq, gt_run, eq_run, sm, s, out_i, out_v);
   }
 }
 
@@ -392,9 +465,10 @@ int launch_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* id
   const int64_t per = (M + kThreads - 1) / kThreads;
 #define KVSEL_TK(KPT) \
   if (per <= KPT) { hipLaunchKernelGGL(topk_reg_kernel<KPT>, grid, block, 0, s, score, M, k, idx, val); return check_launch("kvsel_topk"); }
-  KVSEL_TK(1) KVSEL_TK(2) KVSEL_TK(4) KVSEL_TK(8) KVSEL_TK(16) KVSEL_TK(32) KVSEL_TK(64)
+  KVSEL_TK(1) KVSEL_TK(2) KVSEL_TK(4) KVSEL_TK(8) KVSEL_TK(16)
 #undef KVSEL_TK
-  hipLaunchKernelGGL(topk_kernel, grid, block, 0, s, score, M, k, idx, val);
+  static_assert(kRegKeys == 16, "the register variants above end at kRegKeys");
+  hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, s, score, M, k, idx, val);
   return check_launch("kvsel_topk");
 }
 

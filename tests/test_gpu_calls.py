@@ -167,6 +167,9 @@ TOPK_CASES = [
     (3, 512, 64, "float"), (2, 1, 1, "float"), (4, 7, 3, "ties"), (2, 1000, 999, "ties"),
     (1, 65536, 9830, "float"), (1, 65539, 2048, "ties"), (5, 4096, 4096, "float"),
     (2, 16384, 2048, "ties_few"), (3, 2500, 1, "zeros"),
+    # ~200 copies of each value: the last histogram bin holds one value, ranked
+    # against itself; scores packed into a 1e-4 band; both signs
+    (2, 20000, 300, "ties100"), (1, 16384, 2048, "cluster"), (3, 4096, 1000, "signed"),
 ]
 
 
@@ -181,6 +184,12 @@ def test_topk(G, M, k, kind):
         s = rng.integers(0, 50, size=(G, M)).astype(np.float32)
     elif kind == "ties_few":
         s = rng.integers(0, 3, size=(G, M)).astype(np.float32) * 0.25
+    elif kind == "ties100":
+        s = rng.integers(0, 100, size=(G, M)).astype(np.float32)
+    elif kind == "cluster":
+        s = (1.0 + 1e-4 * rng.standard_normal((G, M))).astype(np.float32)
+    elif kind == "signed":
+        s = rng.standard_normal((G, M)).astype(np.float32)
     else:
         s = np.where(rng.random((G, M)) < 0.5, 0.0, -0.0).astype(np.float32)
         s[:, M // 2] = 1.0
