@@ -52,7 +52,8 @@ KERNEL_SOURCES = {
     "score_mfma_kernel": [_C + "score_mfma.hip", _C + "mfma.h", _C + "common.h"],
     "agg_mfma_kernel": [_C + "aggregate_mfma.hip", _C + "mfma.h", _C + "common.h"],
     "agg_token_kernel": [_C + "aggregate.hip", _C + "common.h"],
-    "topk_kernel": [_C + "topk.hip", _C + "common.h"],
+    "topk_reg_kernel": [_C + "topk.hip", _C + "common.h"],
+    "topk_stream_kernel": [_C + "topk.hip", _C + "common.h"],
     "gather_kernel": [_C + "gather.hip", _C + "common.h"],
     "decode_stream_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
     "decode_mfma_kernel": [_C + "decode.hip", _C + "mfma.h", _C + "common.h"],
@@ -232,7 +233,8 @@ def kernel_of(stage: str, w) -> str:
     return {"score": "score_stream_kernel" if stream else
                      "score_mfma_kernel" if mfma else "score_tile_kernel",
             "aggregate": "agg_mfma_kernel" if mfma else "agg_token_kernel",
-            "topk": "topk_kernel", "gather": "gather_kernel",
+            "topk": "topk_reg_kernel" if w.N // w.unit_len <= 16384 else "topk_stream_kernel",
+            "gather": "gather_kernel",
             "decode": decode_kernel(w, rows) + MERGE,
             "gather_decode": "decode_stream_kernel" + MERGE}[stage]
 
