@@ -146,8 +146,14 @@ int64_t decode_splits(const kvsel_segment* segs, int n_seg, int64_t split_len) {
   return n;
 }
 
-int64_t split_len_of(int64_t T, int64_t Hq, const kvsel_cache& c, bool gathered) {
-  return decode_split_len(c.dtype, c.H, c.D, c.H > 0 ? (Hq / c.H) * T : 1, gathered);
+int64_t total_keys(const kvsel_segment* segs, int n_seg) {
+  int64_t n = 0;
+  for (int i = 0; i < n_seg; ++i) n += segs[i].kc.N;
+  return n;
+}
+
+int64_t split_len_of(int64_t T, int64_t Hq, const kvsel_cache& c, bool gathered, int64_t n_keys) {
+  return decode_split_len(c.dtype, c.H, c.D, c.H > 0 ? (Hq / c.H) * T : 1, gathered, c.B, n_keys);
 }
 
 // (m, s, o) partials of every split of the segments; `gathered` when the last
@@ -156,7 +162,8 @@ size_t decode_ws(int64_t T, int64_t Hq, const kvsel_segment* segs, int n_seg, bo
   if (segs == nullptr || n_seg < 1 || n_seg > kMaxSegments || T < 1 || Hq < 1) return 0;
   for (int i = 0; i < n_seg; ++i)
     if (segs[i].kc.N < 1 || segs[i].kc.B < 1 || segs[i].kc.D < 1) return 0;
-  const int64_t n_split = decode_splits(segs, n_seg, split_len_of(T, Hq, segs[0].kc, gathered));
+  const int64_t n_split =
+      decode_splits(segs, n_seg, split_len_of(T, Hq, segs[0].kc, gathered, total_keys(segs, n_seg)));
   return static_cast<size_t>(segs[0].kc.B * Hq * T * n_split * (2 + segs[0].kc.D)) * sizeof(float);
 }
 
@@ -638,10 +645,15 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const k
     KVSEL_TRY(check_ptr(segs[i].v, "segment v"));
     if (c.B != c0.B || c.H != c0.H || c.D != c0.D || c.dtype != c0.dtype)
       return fail(KVSEL_ERR_SHAPE, "kvsel_decode_attn: segments must share B, H, D and dtype");
-    ds[i] = DecodeSeg{segs[i].k, segs[i].v, c.N, c.stride_b, c.stride_n, split};
-    split += (c.N + split_len_of(T, Hq, c0, false) - 1) / split_len_of(T, Hq, c0, false);
+    ds[i] = DecodeSeg{segs[i].k, segs[i].v, c.N, c.stride_b, c.stride_n, 0};
   }
   KVSEL_TRY(check_heads(T, Hq, c0, "kvsel_decode_attn"));
+  // splits of every segment, numbered across the segments (sizes validated)
+  const int64_t split_len = split_len_of(T, Hq, c0, false, total_keys(segs, n_seg));
+  for (int i = 0; i < n_seg; ++i) {
+    ds[i].split_begin = split;
+    split += (segs[i].kc.N + split_len - 1) / split_len;
+  }
   const size_t need = kvsel_decode_workspace(T, Hq, segs, n_seg);
   if (ws == nullptr || ws_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "kvsel_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
@@ -729,12 +741,13 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
   if (fused) {
     DecodeSeg ds[kMaxSegments];
     int64_t split = 0;
+    const int64_t split_len = split_len_of(T, Hq, kc, true, total_keys(segs, n));
     for (int i = 0; i < n; ++i) {
       const bool g = i == n - 1;
       ds[i] = DecodeSeg{g ? k_src : segs[i].k, g ? v_src : segs[i].v, segs[i].kc.N,
                         g ? kc.stride_b : segs[i].kc.stride_b,
                         g ? kc.stride_n : segs[i].kc.stride_n, split};
-      split += (segs[i].kc.N + split_len_of(T, Hq, kc, true) - 1) / split_len_of(T, Hq, kc, true);
+      split += (segs[i].kc.N + split_len - 1) / split_len;
     }
     const DecodeGather gather{n - 1, idx, unit_len, k, idx_group, M, k_dst, v_dst};
     float* ws_ms = static_cast<float*>(ws);

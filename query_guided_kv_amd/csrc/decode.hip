@@ -643,11 +643,36 @@ bool decode_uses_stream(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bo
   return decode_stream_ok(dtype, H, D, rows_per_kv) && (gathered || rows_per_kv < kDecodeMfmaRows);
 }
 
-int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered) {
+namespace {
+// Matrix-core plan for R query rows per kv head.  Tall query blocks (12 row
+// blocks or more): eight waves of two row blocks, so every staged K and V
+// fragment feeds two products; 256 rows a pass.  Otherwise one row block per
+// wave: two waves for up to two row blocks, else four.
+struct DecodeMfmaPlan {
+  int rbw, nwaves, passes;
+};
+DecodeMfmaPlan decode_mfma_plan(int64_t R) {
+  const int64_t rbs = (R + 15) / 16;
+  const int rbw = rbs >= 12 ? 2 : 1;
+  const int nwaves = rbs >= 12 ? 8 : rbs <= 2 ? 2 : 4;
+  return {rbw, nwaves, static_cast<int>((rbs + rbw * nwaves - 1) / (rbw * nwaves))};
+}
+// waves a matrix-core decode launch should hold at least (8 per CU)
+constexpr int64_t kDecodeFillWaves = 2048;
+}  // namespace
+
+int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered,
+                         int64_t B, int64_t n_keys) {
   if (decode_uses_stream(dtype, H, D, rows_per_kv, gathered)) return kDecodeSplit;
-  // the matrix-core variant: longer splits leave fewer (m, s, o) partials to
-  // write and merge
-  return dtype == KVSEL_BF16 && rows_per_kv >= kDecodeMfmaRows ? 1024 : kDecodeSplit;
+  if (!(dtype == KVSEL_BF16 && rows_per_kv >= kDecodeMfmaRows)) return kDecodeSplit;
+  // the matrix-core variant: splits of 1024 keys leave fewer (m, s, o)
+  // partials to write and merge; they are halved, down to 256, while the
+  // launch would hold fewer than kDecodeFillWaves waves
+  const DecodeMfmaPlan p = decode_mfma_plan(rows_per_kv);
+  int64_t len = 1024;
+  while (len > 256 && B * H * p.passes * ((n_keys + len - 1) / len) * p.nwaves < kDecodeFillWaves)
+    len /= 2;
+  return len;
 }
 
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
@@ -656,7 +681,9 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
                   const DecodeGather* gather) {
   SegTable st{};
   st.gather_seg = -1;
-  st.split_len = decode_split_len(dtype, H, D, (Hq / H) * T, gather != nullptr);
+  int64_t n_keys = 0;
+  for (int i = 0; i < n_seg; ++i) n_keys += segs[i].N;
+  st.split_len = decode_split_len(dtype, H, D, (Hq / H) * T, gather != nullptr, B, n_keys);
   if (gather != nullptr) {
     // only the streaming variant gathers on the fly
     if (!decode_stream_ok(dtype, H, D, (Hq / H) * T)) {
@@ -696,14 +723,8 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
 #undef KVSEL_DS
   }
   if (!done && dtype == KVSEL_BF16 && R >= kDecodeMfmaRows) {
-    // Tall query blocks (12 row blocks or more): eight waves of two row blocks,
-    // so every staged K and V fragment feeds two products; 256 rows a pass.
-    // Otherwise one row block per wave: two waves for up to two row blocks,
-    // else four.
-    const int64_t rbs = (R + 15) / 16;
-    const int rbw = rbs >= 12 ? 2 : 1;
-    const int nwaves = rbs >= 12 ? 8 : rbs <= 2 ? 2 : 4;
-    const int passes = static_cast<int>((rbs + rbw * nwaves - 1) / (rbw * nwaves));
+    const DecodeMfmaPlan p = decode_mfma_plan(R);
+    const int rbw = p.rbw, nwaves = p.nwaves, passes = p.passes;
     const dim3 grid(static_cast<unsigned>(B * H * passes * n_split)), block(64 * nwaves);
 #define KVSEL_DM(D_, RBW_, NW_) \
     hipLaunchKernelGGL((decode_mfma_kernel<D_, RBW_, NW_>), grid, block, 0, s, static_cast<const bf16_t*>(q), st, \

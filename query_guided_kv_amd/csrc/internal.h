@@ -147,7 +147,10 @@ struct DecodeGather {
   void* k_dst;
   void* v_dst;
 };
-int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered);
+// Keys per split of a decode launch over n_keys keys (all segments) of B
+// instances; the workspace query and the launch use the same value.
+int64_t decode_split_len(int dtype, int64_t H, int64_t D, int64_t rows_per_kv, bool gathered,
+                         int64_t B, int64_t n_keys);
 int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const DecodeSeg* segs,
                   int n_seg, int64_t B, int64_t H, int64_t D, int dtype, int64_t n_split,
                   float* out, float* lse, float* ws_ms, float* ws_o, hipStream_t s,

@@ -325,15 +325,40 @@ def test_score_reposition_validation(lib):
         lib.kvsel_score_workspace(2, 1024, 32, 32, 256, 1, 1)
 
 
+def mfma_decode_splits(B, H, rows, n_keys):
+    """Splits of a matrix-core decode: 1024 keys, halved down to 256 while the
+    launch holds fewer than 2048 waves (row blocks of 16; up to 2 blocks run
+    as 2 waves, up to 11 as 4 waves, 12 or more as 8 waves of 2 blocks a pass)."""
+    rbs = -(-rows // 16)
+    rbw, nwaves = (2, 8) if rbs >= 12 else (1, 2 if rbs <= 2 else 4)
+    passes = -(-rbs // (rbw * nwaves))
+    length = 1024
+    while length > 256 and B * H * passes * -(-n_keys // length) * nwaves < 2048:
+        length //= 2
+    return length
+
+
+def test_decode_split_rule():
+    # small launches take shorter splits; launches that fill the chip keep 1024
+    assert mfma_decode_splits(2, 4, 7, 3000) == 256
+    assert mfma_decode_splits(1, 32, 32, 4096) == 256           # 32 docs x 512, 32 kv heads
+    assert mfma_decode_splits(1, 4, 448, 32768) == 1024         # 448 rows: 8 waves, 2 passes
+    assert mfma_decode_splits(448, 4, 7, 2560) == 1024
+    assert mfma_decode_splits(1, 8, 16, 65536) == 512
+
+
 def test_decode_split_by_path(lib):
     """The workspace of a decode call follows the kernel it runs: the
     streaming kernel splits the keys by 512; a plain pass with 5 or more bf16
-    rows per kv head runs on the matrix cores and splits them by 1024; the
-    fused refill keeps the streaming kernel (512) up to 8 rows."""
+    rows per kv head runs on the matrix cores, whose split length follows
+    mfma_decode_splits; the fused refill keeps the streaming kernel (512) up
+    to 8 rows."""
     N, D = 3000, 128
     seven = (K.Segment * 1)(K.Segment(FAKE, FAKE, cache(B=2, N=N, H=4, D=D)))
-    # 28 / 4 heads x 1 token = 7 rows per kv head: matrix cores, ceil(3000 / 1024) = 3 splits
-    assert lib.kvsel_decode_workspace(1, 28, seven, 1) == 2 * 28 * 1 * 3 * (2 + D) * 4
+    # 28 / 4 heads x 1 token = 7 rows per kv head: matrix cores, a small launch
+    n7 = -(-N // mfma_decode_splits(2, 4, 7, N))
+    assert n7 == 12
+    assert lib.kvsel_decode_workspace(1, 28, seven, 1) == 2 * 28 * 1 * n7 * (2 + D) * 4
     # 4 rows per kv head: streaming, ceil(3000 / 512) = 6 splits
     assert lib.kvsel_decode_workspace(1, 16, seven, 1) == 2 * 16 * 1 * 6 * (2 + D) * 4
     # fp32 keys: the tile kernel, 512-key splits
@@ -345,6 +370,7 @@ def test_decode_split_by_path(lib):
     need = lib.kvsel_gather_decode_workspace(1, 28, kc, 512, 5, None, 0)
     assert need == 2 * 28 * 1 * ((rows + 511) // 512) * (2 + D) * 4
     # with 16 rows per kv head (no streaming kernel) the copy and the plain pass
-    # run separately: 1024-key splits
+    # run separately: matrix-core splits
     need16 = lib.kvsel_gather_decode_workspace(4, 16, kc, 512, 5, None, 0)
-    assert need16 == 2 * 16 * 4 * ((rows + 1023) // 1024) * (2 + D) * 4
+    L16 = mfma_decode_splits(2, 4, 16, rows)
+    assert need16 == 2 * 16 * 4 * -(-rows // L16) * (2 + D) * 4
