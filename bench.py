@@ -63,6 +63,10 @@ KERNEL_SOURCES = {
     "decode_merge_kernel": [_C + "decode.hip"],
 }
 
+# Stages of the selection proper (the rest of a step refills and attends).
+SELECTION_STAGES = ("score", "aggregate", "topk", "score1", "aggregate1", "topk1", "reorder",
+                    "score2", "aggregate2", "topk2", "select")
+
 # The decode calls run split-K: a pass over the keys, then the merge of the
 # splits.  Their stage is timed as one call, so its roofline names both kernels.
 MERGE = "+decode_merge_kernel"
@@ -445,6 +449,21 @@ def main() -> int:
         del src, dst
         log("copy probe: 3 x (1 GiB read + 1 GiB written) done")
 
+    # the device's own copy rate on this machine: 1 GiB read + 1 GiB written per
+    # copy, timed on the GPU clock (the path's HBM rate is also given against it)
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_GBps = 5 * 2 * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    log(f"device copy: {copy_GBps:.0f} GB/s (read + written)")
+
     host_link = None
     if w.l2_host:
         # the host link's DMA rate: 1 GiB pinned host -> device, timed on the GPU clock
@@ -554,9 +573,22 @@ def main() -> int:
                      "launches_per_step": launches, "avg_launch_ms": dom_ms / launches},
         "path_hbm": {"algorithmic_bytes_per_step": path_bytes,
                      "achieved_GBps": path_bytes / (ms_step * 1e-3) / 1e9,
-                     "frac": path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                     "frac": path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "device_copy_GBps": copy_GBps,
+                     "frac_of_device_copy": path_bytes / (ms_step * 1e-3) / 1e9 / copy_GBps},
         "stages_ms": stage_ms,
     }
+    # selection alone (re-position, score, aggregate, top-k; both stages and the
+    # reordering of a two-stage selection; the pruning loop), beside the full path
+    sel = [s for s in path.stages if s in SELECTION_STAGES]
+    if sel:
+        sel_ms = sum(stage_ms[s] for s in sel)
+        result["selection"] = {"stages": sel, "ms_per_step": sel_ms,
+                               "value": rows / (sel_ms * 1e-3), "unit": "token-rows/s"}
+    if w.refill_interval:
+        # every kept L1 entry stands for refill_interval L2 tokens
+        result["covered"] = {"value": w.B * w.N * w.refill_interval / (ms_step * 1e-3),
+                             "unit": "L2 token-rows/s", "l2_tokens_per_l1_entry": w.refill_interval}
     if host_link is not None:
         result["host_link"] = host_link
     if args.graph:
