@@ -340,6 +340,21 @@ def cpu_baseline_recompute(w, inp, rows: int = 64) -> dict:
                       f"context rows; fp64 numpy, 1 thread), {elapsed:.1f} s"}
 
 
+def host_cpu() -> dict:
+    """The host the oracle ran on: CPU model, logical CPUs, CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, inp, budget_s: float = 15.0, max_instances: int = 24) -> dict:
     """Time the fp64 oracle on whole instances of the workload (inputs copied to
     host memory first, outside the timed region), single-threaded."""
@@ -599,6 +614,7 @@ def main() -> int:
                                   else cpu_baseline_reorder(w, inp) if w.reorder
                                   else cpu_baseline_recompute(w, inp) if w.recompute
                                   else cpu_baseline(w, inp))
+        result["cpu_baseline"]["host"] = host_cpu()
     print(json.dumps(result), flush=True)
     return 0
 
