@@ -170,6 +170,8 @@ TOPK_CASES = [
     # ~200 copies of each value: the last histogram bin holds one value, ranked
     # against itself; scores packed into a 1e-4 band; both signs
     (2, 20000, 300, "ties100"), (1, 16384, 2048, "cluster"), (3, 4096, 1000, "signed"),
+    # rows re-read per pass: 19 compaction tiles with a ragged tail; several rows
+    (1, 300007, 12345, "cluster"), (2, 40000, 5000, "signed"), (1, 100000, 99999, "ties100"),
 ]
 
 
