@@ -2,8 +2,11 @@
 // token is recomputed at its global position, attending to every context row
 // up to its own; InfoFlow §8: the pattern is neither dense nor strictly causal).
 //
-// Row r of kv head g is query head h = g*G + r / S of selected token j = r % S;
+// Row r of kv head g is query head h = g*G + r % G of selected token j = r / G;
 // it attends to keys 0 .. lim, lim = min(pos[b][j], N - 1) (none when pos < 0).
+// A workgroup's rows are consecutive selected tokens (all G heads of each), so
+// with positions listed in ascending order its rows' limits are close; passes
+// run from the last rows to the first, so the longest workgroups start first.
 //
 // Matrix cores, bf16 (lane layout in mfma.h), as the MFMA decode:
 //   S^T = K Q^T  (A = 16 keys x 32 dims from the LDS K tile, B = 32 dims x 16
@@ -46,7 +49,7 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ int wave_lim[NW];
 
   int64_t x = blockIdx.x;
-  const int pass = static_cast<int>(x % passes); x /= passes;
+  const int pass = passes - 1 - static_cast<int>(x % passes); x /= passes;
   const int g = static_cast<int>(x % H);
   const int64_t b = x / H;
   const int G = Hq / H;
@@ -67,7 +70,7 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int r = rb[i] * 16 + col;
     lim[i] = -1;
     if (r < R) {
-      const int h = g * G + r / S, j = r % S;
+      const int h = g * G + r % G, j = r / G;
       const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * S + j) * Hq + h) * D + quad * 8);
 #pragma unroll
       for (int s2 = 0; s2 < KS; ++s2) qb[i][s2] = qp[s2 * 4];
@@ -220,7 +223,7 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     tot += __shfl_xor(tot, 32, 64);
     const int r = rb[i] * 16 + col;
     if (r >= R) continue;
-    const int h = g * G + r / S, j = r % S;
+    const int h = g * G + r % G, j = r / G;
     const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
     float* wo = out + ((b * S + j) * Hq + h) * D;
 #pragma unroll
