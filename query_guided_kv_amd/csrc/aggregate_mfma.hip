@@ -25,16 +25,14 @@
 namespace kvsel {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr int kTileKeys = kMfmaTileKeys;
 constexpr int kPad = kMfmaPad;
 constexpr int kMaxRange = 1024;   // cached rows per workgroup
 constexpr int kSmallRange = 512;  // cached rows per workgroup for small caches
 constexpr int kTargetBlocks = 256;
 
-template <int D, int RBW, int NWR, bool VNORM>
-__global__ void __launch_bounds__(kThreads)
+template <int D, int RBW, int NWR, int NW, bool VNORM>
+__global__ void __launch_bounds__(64 * NW)
 agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, int64_t N, int H, int64_t stride_b,
                 int64_t stride_n, int T, int Hq, float scale2, const float* __restrict__ row_max,
@@ -42,12 +40,14 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 int64_t parts, int hp_per_block, int64_t nb, float* __restrict__ per_token) {
   constexpr int KS = D / 32;
   constexpr int KROW = D + kPad;
-  constexpr int NWK = kWaves / NWR;
+  constexpr int NT = 64 * NW;
+  static_assert(!VNORM || NW == 4, "the value norms are staged by 4 lanes per key of 256 threads");
+  constexpr int NWK = NW / NWR;
   constexpr int KBW = (kTileKeys / 16) / NWK;
-  constexpr int VPT = kTileKeys * D / 8 / kThreads;
+  constexpr int VPT = kTileKeys * D / 8 / NT;
   __shared__ __align__(16) bf16_t kt[kTileKeys * KROW];
   __shared__ float vn[kTileKeys];
-  __shared__ float part[kWaves][kTileKeys];
+  __shared__ float part[NW][kTileKeys];
   __shared__ float tot[kMaxRange];
 
   int64_t x = blockIdx.x;
@@ -65,7 +65,7 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int hp0 = static_cast<int>(grp) * hp_per_block;
   const int hp1 = min(H * passes, hp0 + hp_per_block);
 
-  for (int i = threadIdx.x; i < range; i += kThreads) tot[i] = 0.0f;
+  for (int i = threadIdx.x; i < range; i += NT) tot[i] = 0.0f;
 
   // items (hp, tile) in order; the next item's K slice (and V slice for the
   // norms) is in flight during the math.  The fetch cursor advances by one
@@ -81,7 +81,7 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* kb = k + b * stride_b + static_cast<int64_t>(g) * D;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int e = threadIdx.x + i * kThreads;
+      const int e = threadIdx.x + i * NT;
       const int key = e / (D / 8), ch = e % (D / 8);
       kn[i] = (t0 + key < t_end) ? *reinterpret_cast<const uint4*>(kb + (t0 + key) * stride_n + ch * 8)
                                  : make_uint4(0, 0, 0, 0);
@@ -140,7 +140,7 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       __syncthreads();  // previous tile's kt / vn / part fully used
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        const int e = threadIdx.x + i * kThreads;
+        const int e = threadIdx.x + i * NT;
         const int key = e / (D / 8), ch = e % (D / 8);
         *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
       }
@@ -199,7 +199,7 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
   __syncthreads();
   float* out = per_token + (grp * nb + b) * N;   // this group's partials
-  for (int i = threadIdx.x; i < t_end - t_begin; i += kThreads) out[t_begin + i] = tot[i];
+  for (int i = threadIdx.x; i < t_end - t_begin; i += NT) out[t_begin + i] = tot[i];
 }
 
 // Workgroup plan: cached rows per workgroup, and how the (kv head, row pass)
@@ -209,15 +209,24 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 // several tiles instead of reloading them for every tile.
 struct AggPlan {
   int64_t range, ranges, parts;
-  int hp_per_block, passes, rbw, nwr;
+  int hp_per_block, passes, rbw, nwr, nw;
 };
 
-AggPlan agg_plan(const kvsel_cache& kc, int64_t rows_per_kv) {
+AggPlan agg_plan(const kvsel_cache& kc, int64_t rows_per_kv, bool vnorm) {
   const MfmaRowPlan p = mfma_row_plan(rows_per_kv);
   AggPlan a{};
   a.passes = p.passes;
   a.rbw = p.rbw;
   a.nwr = p.nwr;
+  a.nw = 4;
+  if (!vnorm && kc.D == 128 && p.rbw == 4) {
+    // tall query blocks: eight waves of two row blocks (half the registers
+    // per wave, two waves per SIMD), 16 row blocks a pass as with four waves
+    // of four, so the passes and the partials are the same
+    a.rbw = 2;
+    a.nwr = 8;
+    a.nw = 8;
+  }
   const int64_t hp_total = kc.H * p.passes;
   if (kc.B * kc.N < kAggSplitRows) {
     a.range = std::min<int64_t>(kSmallRange, (kc.N + kTileKeys - 1) / kTileKeys * kTileKeys);
@@ -236,18 +245,22 @@ AggPlan agg_plan(const kvsel_cache& kc, int64_t rows_per_kv) {
   return a;
 }
 
-template <int D, int RBW, int NWR>
+template <int D, int RBW, int NWR, int NW>
 void launch(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
             const kvsel_cache& kc, float scale2, const float* rm, const float* rs, int vnorm,
             const AggPlan& a, float* per_token, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(kc.B * a.ranges * a.parts));
 #define KVSEL_AM(VN)                                                                         \
-  hipLaunchKernelGGL((agg_mfma_kernel<D, RBW, NWR, VN>), grid, dim3(kThreads), 0, s,          \
+  hipLaunchKernelGGL((agg_mfma_kernel<D, RBW, NWR, NW, VN>), grid, dim3(64 * NW), 0, s,       \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),            \
                      static_cast<const bf16_t*>(v), kc.N, static_cast<int>(kc.H), kc.stride_b, \
                      kc.stride_n, static_cast<int>(T), static_cast<int>(Hq), scale2, rm, rs,   \
                      a.range, a.ranges, a.passes, a.parts, a.hp_per_block, kc.B, per_token)
-  if (vnorm) KVSEL_AM(true); else KVSEL_AM(false);
+  if constexpr (NW == 4) {
+    if (vnorm) KVSEL_AM(true); else KVSEL_AM(false);
+  } else {
+    KVSEL_AM(false);
+  }
 #undef KVSEL_AM
 }
 
@@ -255,18 +268,20 @@ template <int D>
 void dispatch(const void* q, int64_t T, int64_t Hq, const void* k, const void* v,
               const kvsel_cache& kc, float scale2, const float* rm, const float* rs, int vnorm,
               float* per_token, hipStream_t s) {
-  const AggPlan a = agg_plan(kc, (Hq / kc.H) * T);
-#define KVSEL_AD(RBW, NWR) \
-  if (a.rbw == RBW && a.nwr == NWR) \
-    return launch<D, RBW, NWR>(q, T, Hq, k, v, kc, scale2, rm, rs, vnorm, a, per_token, s);
-  KVSEL_AD(1, 1) KVSEL_AD(1, 2) KVSEL_AD(1, 4) KVSEL_AD(2, 4) KVSEL_AD(4, 4)
+  const AggPlan a = agg_plan(kc, (Hq / kc.H) * T, vnorm != 0);
+#define KVSEL_AD(RBW, NWR, NW) \
+  if (a.rbw == RBW && a.nwr == NWR && a.nw == NW) \
+    return launch<D, RBW, NWR, NW>(q, T, Hq, k, v, kc, scale2, rm, rs, vnorm, a, per_token, s);
+  KVSEL_AD(1, 1, 4) KVSEL_AD(1, 2, 4) KVSEL_AD(1, 4, 4) KVSEL_AD(2, 4, 4) KVSEL_AD(4, 4, 4)
+  if constexpr (D == 128) { KVSEL_AD(2, 8, 8) }
 #undef KVSEL_AD
 }
 
 }  // namespace
 
 int64_t aggregate_mfma_parts(const kvsel_cache& kc, int64_t rows_per_kv) {
-  return agg_plan(kc, rows_per_kv).parts;
+  // the same for either signal: both plans cover 16 row blocks a pass
+  return agg_plan(kc, rows_per_kv, true).parts;
 }
 
 bool aggregate_mfma_ok(int dtype, int64_t rows_per_kv) {
