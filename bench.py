@@ -540,6 +540,8 @@ def main() -> int:
 
     stage_ms = {s: statistics.mean(m[s][0].elapsed_time(m[s][1]) for m in marks)
                 for s in path.stages}
+    # per-step times from the first stage's start to the last stage's end
+    step_ms = [m[path.stages[0]][0].elapsed_time(m[path.stages[-1]][1]) for m in marks]
     dom = max(path.stages, key=lambda s: stage_ms[s])     # the stage that takes longest
     dom_ms = stage_ms[dom]
     bound, quantity, peak, unit = stage_bound(dom, w, work[dom])
@@ -569,6 +571,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": statistics.median(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
