@@ -39,13 +39,15 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   constexpr int CB = D / 16;            // output column blocks
   constexpr int KG = TK / 4;            // groups of 4 keys
   constexpr int NT = 64 * NW;
-  constexpr int KV = TK * (D / 8) / NT;    // K vectors per thread and tile
+  constexpr int NL = NT / 2;               // lead threads: they load and stage the tiles
+  constexpr int KV = TK * (D / 8) / NL;    // K vectors per lead thread and tile
   constexpr int VITEMS = KG * (D / 8);     // V items (4 keys x 8 dims) per tile
   constexpr int VI = (VITEMS + NT - 1) / NT;
   static_assert(KV >= 1, "tile too small for the workgroup");
   static_assert(VI == 1, "one V item per thread at most");
+  static_assert(VITEMS <= NL, "V is staged by the lead threads");
   __shared__ __align__(16) bf16_t kt[TK * KROW];
-  __shared__ __align__(16) bf16_t vt[D * VROW];
+  __shared__ __align__(16) bf16_t vt2[2][D * VROW];   // V of tiles t (t / TK even, odd)
   __shared__ int wave_lim[NW];
 
   int64_t x = blockIdx.x;
@@ -110,11 +112,11 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // mask, so a tile is loaded whole; only rows past the cache's end are
   // clamped to its last row.
   uint4 kn[KV], vn4[VI][4];
-  // a thread's rows within a tile: K rows key0 + i * (NT / (D / 8)), V rows
+  // a lead thread's rows within a tile: K rows key0 + i * (NL / (D / 8)), V rows
   // 4 * (thread % KG) + j
   const int64_t koff = (threadIdx.x / (D / 8)) * stride_n + (threadIdx.x % (D / 8)) * 8;
   const int64_t voff = (threadIdx.x % KG) * 4 * stride_n + (threadIdx.x / KG) * 8;
-  const int64_t kstep = (NT / (D / 8)) * stride_n;
+  const int64_t kstep = (NL / (D / 8)) * stride_n;
   auto fetch = [&](int64_t t0) {
     if (t0 + TK <= N) {   // uniform
       const bf16_t* kt0 = kb + t0 * stride_n;
@@ -134,7 +136,7 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     } else {
 #pragma unroll
       for (int i = 0; i < KV; ++i) {
-        const int e = threadIdx.x + i * NT;
+        const int e = threadIdx.x + i * NL;
         const int64_t t = min<int64_t>(t0 + e / (D / 8), N - 1);
         const uint4 x = *reinterpret_cast<const uint4*>(kb + t * stride_n + (e % (D / 8)) * 8);
         kn[i] = x;
@@ -149,28 +151,9 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       }
     }
   };
-  if (t_end > 0) fetch(0);
-  for (int64_t t0 = 0; t0 < t_end; t0 += TK) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int key = e / (D / 8), ch = e % (D / 8);
-      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int e = threadIdx.x + i * NT;
-      if (e >= VITEMS) break;
-      const int kg = e % KG, ch = e / KG;
-      stage_vt<VROW>(vt, vn4[i], kg, ch);
-    }
-    __syncthreads();
-    if (t0 + TK < t_end) fetch(t0 + TK);
-    if (t0 > wmax) continue;           // this wave's rows are complete (uniform)
-
-    // S^T blocks: key block outer, so one K fragment serves every row block
-    f32x4_t sv[RBW][4];
+  // S^T blocks of the staged K tile: key block outer, so one K fragment
+  // serves every row block
+  auto scores = [&](f32x4_t (&sv)[RBW][4]) {
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4) {
       uint4 ka[KS];
@@ -185,15 +168,19 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         sv[i][kb4] = a;
       }
     }
+  };
+  // the causal limit, softmax and value products of the tile at tt (its V
+  // staged in vtt)
+  auto apply = [&](f32x4_t (&sv)[RBW][4], int64_t tt, const bf16_t* vtt) {
     // the causal limit, only in tiles that reach past some row's limit
-    if (t0 + TK - 1 > wmin) {
+    if (tt + TK - 1 > wmin) {
 #pragma unroll
       for (int i = 0; i < RBW; ++i)
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
           for (int vv = 0; vv < 4; ++vv)
-            if (t0 + kb4 * 16 + quad * 4 + vv > lim[i]) sv[i][kb4][vv] = -INFINITY;
+            if (tt + kb4 * 16 + quad * 4 + vv > lim[i]) sv[i][kb4][vv] = -INFINITY;
     }
     // online softmax per row (the lane's column); probabilities as bf16 pairs
     uint32_t pk[RBW][4][2];
@@ -204,7 +191,7 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const uint4 va = load_vt<VROW>(vt, c, pr, col, quad);
+        const uint4 va = load_vt<VROW>(vtt, c, pr, col, quad);
 #pragma unroll
         for (int i = 0; i < RBW; ++i) {
           const uint4 pb = make_uint4(pk[i][2 * pr][0], pk[i][2 * pr][1], pk[i][2 * pr + 1][0],
@@ -212,6 +199,50 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           o[i][c] = mfma16x16x32(va, pb, o[i][c]);
         }
       }
+    }
+  };
+  // Waves NW/2 .. NW-1 (one per SIMD beside a lead wave) run one tile behind
+  // the lead waves, so that on each SIMD one wave's products overlap the
+  // other's softmax; V is staged in two buffers for them.  The lead waves load
+  // and stage every tile.  Both loops meet the same two barriers per tile.
+  if (wave < NW / 2) {
+    if (t_end > 0) fetch(0);
+    for (int64_t t0 = 0; t0 < t_end; t0 += TK) {
+      __syncthreads();               // every wave is done with the buffers restaged here
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const int e = threadIdx.x + i * NL;
+        const int key = e / (D / 8), ch = e % (D / 8);
+        *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
+      }
+      bf16_t* vt = vt2[(t0 / TK) & 1];
+      if (threadIdx.x < VITEMS) {
+        const int kg = threadIdx.x % KG, ch = threadIdx.x / KG;
+        stage_vt<VROW>(vt, vn4[0], kg, ch);
+      }
+      __syncthreads();
+      if (t0 + TK < t_end) fetch(t0 + TK);
+      if (t0 > wmax) continue;       // this wave's rows are complete (uniform)
+      f32x4_t sv[RBW][4];
+      scores(sv);
+      apply(sv, t0, vt);
+    }
+  } else {
+    // the previous tile's softmax and value products (its V is still staged)
+    // first, then this tile's scores: vector work while the lead wave on this
+    // SIMD runs its score products
+    f32x4_t svp[RBW][4];
+    bool have_prev = false;
+    for (int64_t t0 = 0; t0 < t_end; t0 += TK) {
+      __syncthreads();
+      __syncthreads();               // the tile at t0 is staged
+      if (have_prev) apply(svp, t0 - TK, vt2[((t0 - TK) / TK) & 1]);
+      have_prev = t0 <= wmax;
+      if (have_prev) scores(svp);
+    }
+    if (have_prev) {
+      const int64_t last = (t_end - 1) / TK * TK;
+      apply(svp, last, vt2[(last / TK) & 1]);
     }
   }
 
