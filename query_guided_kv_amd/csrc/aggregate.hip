@@ -29,11 +29,17 @@ constexpr int kAggUnits = 64;
 constexpr int kAggRowLanes = kThreads / kAggUnits;
 constexpr int kAggChunkRows = 64;
 
+// DERIVE: no row statistics are given; the workgroup derives (row_max,
+// row_sum) of its 64 rows from their partials first (4 lanes per row, merged
+// in a fixed order), in the log2 domain.
+template <bool DERIVE>
 __global__ void __launch_bounds__(kThreads)
 agg_chunk_kernel(const float* __restrict__ part, const float* __restrict__ row_max,
                  const float* __restrict__ row_sum, int64_t rows_per_g, int64_t M, int64_t n_rc,
                  int64_t n_uc, int accumulate, float* __restrict__ dst) {
+  static_assert(kThreads == 4 * kAggChunkRows, "4 lanes per row derive its statistics");
   __shared__ float red[kAggRowLanes][kAggUnits];
+  __shared__ float s_m[DERIVE ? kAggChunkRows : 1], s_iz[DERIVE ? kAggChunkRows : 1];
   const int64_t uc = blockIdx.x % n_uc;
   const int64_t rc = (blockIdx.x / n_uc) % n_rc;
   const int64_t gi = blockIdx.x / (n_uc * n_rc);
@@ -41,12 +47,30 @@ agg_chunk_kernel(const float* __restrict__ part, const float* __restrict__ row_m
   const int64_t u = uc * kAggUnits + ul;
   const int64_t r0 = rc * kAggChunkRows;
   const int64_t r1 = min(rows_per_g, r0 + kAggChunkRows);
+  if constexpr (DERIVE) {
+    const int sr = threadIdx.x / 4, sq = threadIdx.x % 4;
+    float m = -INFINITY, z = 0.0f;
+    if (r0 + sr < r1) {
+      const float* pr = part + (gi * rows_per_g + r0 + sr) * M * 2;
+      for (int64_t uu = sq; uu < M; uu += 4) {
+        const float2 pu = *reinterpret_cast<const float2*>(pr + uu * 2);
+        merge_ms(m, z, pu.x * kLog2e, pu.y);
+      }
+    }
+    merge_ms(m, z, __shfl_xor(m, 1, 64), __shfl_xor(z, 1, 64));
+    merge_ms(m, z, __shfl_xor(m, 2, 64), __shfl_xor(z, 2, 64));
+    if (sq == 0) { s_m[sr] = m; s_iz[sr] = z > 0.0f ? 1.0f / z : 0.0f; }
+    __syncthreads();
+  }
   float acc = 0.0f;
   if (u < M) {
     for (int64_t r = r0 + rl; r < r1; r += kAggRowLanes) {
       const int64_t row = gi * rows_per_g + r;
       const float2 pu = *reinterpret_cast<const float2*>(part + (row * M + u) * 2);
-      acc += pu.y * exp2f((pu.x - row_max[row]) * kLog2e) / row_sum[row];
+      if constexpr (DERIVE)
+        acc += pu.y * exp2f(pu.x * kLog2e - s_m[r - r0]) * s_iz[r - r0];
+      else
+        acc += pu.y * exp2f((pu.x - row_max[row]) * kLog2e) / row_sum[row];
     }
   }
   red[rl][ul] = acc;
@@ -202,9 +226,14 @@ int launch_aggregate_chunks(const float* part, const float* row_max, const float
   const int64_t n_rc = (rows_per_g + kAggChunkRows - 1) / kAggChunkRows;
   const int64_t n_uc = (M + kAggUnits - 1) / kAggUnits;
   float* dst = n_rc == 1 ? unit_score : ws;
-  hipLaunchKernelGGL(agg_chunk_kernel, dim3(static_cast<unsigned>(G * n_rc * n_uc)),
-                     dim3(kThreads), 0, s, part, row_max, row_sum, rows_per_g, M, n_rc, n_uc,
-                     n_rc == 1 ? accumulate : 0, dst);
+  if (row_max == nullptr)
+    hipLaunchKernelGGL(agg_chunk_kernel<true>, dim3(static_cast<unsigned>(G * n_rc * n_uc)),
+                       dim3(kThreads), 0, s, part, row_max, row_sum, rows_per_g, M, n_rc, n_uc,
+                       n_rc == 1 ? accumulate : 0, dst);
+  else
+    hipLaunchKernelGGL(agg_chunk_kernel<false>, dim3(static_cast<unsigned>(G * n_rc * n_uc)),
+                       dim3(kThreads), 0, s, part, row_max, row_sum, rows_per_g, M, n_rc, n_uc,
+                       n_rc == 1 ? accumulate : 0, dst);
   if (n_rc > 1) {
     const int rc = check_launch("kvsel_aggregate");
     if (rc != KVSEL_OK) return rc;
@@ -212,6 +241,11 @@ int launch_aggregate_chunks(const float* part, const float* row_max, const float
                        dim3(kThreads), 0, s, ws, G, M, n_rc, accumulate, unit_score);
   }
   return check_launch("kvsel_aggregate");
+}
+
+bool aggregate_chunks_derive(int64_t M) {
+  // each unit chunk's workgroups derive the statistics again: at most two
+  return (M + kAggUnits - 1) / kAggUnits <= 2;
 }
 
 size_t aggregate_chunk_ws_floats(int64_t B, int64_t Hq, int64_t T, int64_t M) {

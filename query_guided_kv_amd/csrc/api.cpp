@@ -447,7 +447,10 @@ int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const v
     const float* rm = row_max;
     const float* rs = row_sum;
     float* w = static_cast<float*>(ws);
-    if (!stats) {
+    if (!stats && aggregate_chunks_derive(M)) {
+      rm = rs = nullptr;             // derived inside the aggregation launch
+      w += 2 * rows;
+    } else if (!stats) {
       KVSEL_TRY(launch_rowstats(part, rows, M, 1, w, w + rows, stream));
       rm = w;
       rs = w + rows;

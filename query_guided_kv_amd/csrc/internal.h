@@ -72,6 +72,9 @@ int launch_rowstats(const float* ms, int64_t rows, int64_t nseg, int natural, fl
 
 // Chunk path: unit_score[g][u] from natural-unit partials and row stats.
 // `ws` holds aggregate_chunk_ws_floats(B, Hq, T, M) floats of row-chunk sums.
+// True where the chunk path derives the row statistics inside its own
+// launch (row_max = row_sum = NULL to launch_aggregate_chunks).
+bool aggregate_chunks_derive(int64_t M);
 int launch_aggregate_chunks(const float* part, const float* row_max, const float* row_sum,
                             int64_t B, int64_t Hq, int64_t T, int64_t M, int64_t group,
                             float* unit_score, int accumulate, float* ws, hipStream_t s);
