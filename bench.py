@@ -464,7 +464,7 @@ def main() -> int:
         del src, dst
         log("copy probe: 3 x (1 GiB read + 1 GiB written) done")
 
-    # the device's own copy rate on this machine: 1 GiB read + 1 GiB written per
+    # the device's own copy rate: 1 GiB read + 1 GiB written per
     # copy, timed on the GPU clock (the path's HBM rate is also given against it)
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
