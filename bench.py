@@ -27,6 +27,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -270,10 +271,10 @@ def make_queries(w, inp, n: int, seed: int, device):
     return [inp["q"]] * n
 
 
-def cpu_baseline_prune(w, inp, layers: int = 8) -> dict:
+def cpu_baseline_prune(w, inp, threads: int, layers: int = 8) -> dict:
     """The fp64 oracle's layer loop on request 0, first ``layers`` layers
-    (two pruning layers at n = 4), single-threaded; rate in scored token-rows
-    per second."""
+    (two pruning layers at n = 4) with ``threads`` BLAS threads; rate in scored
+    token-rows per second."""
     from threadpoolctl import threadpool_limits
     from oracle import kvsel_oracle as O
     from oracle import pipeline as OP
@@ -281,44 +282,44 @@ def cpu_baseline_prune(w, inp, layers: int = 8) -> dict:
     L = min(layers, w.layers)
     q = OP.to64(inp["q"][:L, 0])
     k = OP.to64(inp["k"][:L])
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
         res = O.cf_progressive_prune(q, k, w.unit_len, w.scale, w.prune_every, w.k, w.window,
                                      w.rope_base, w.rope_style, w.dtype)
         elapsed = time.perf_counter() - t0
     rows = sum(ids.size for ids in res["ids"]) * w.unit_len
-    log(f"cpu oracle: {L} layers of request 0 in {elapsed:.1f} s")
-    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+    log(f"cpu oracle ({threads} threads): {L} layers of request 0 in {elapsed:.1f} s")
+    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": threads, "kind": "oracle",
             "sample": f"request 0, layers 0-{L - 1} of the pruning loop ({rows} scored "
-                      f"token-rows; fp64 numpy, 1 thread), {elapsed:.1f} s"}
+                      f"token-rows; fp64 numpy, {threads} BLAS threads), {elapsed:.1f} s"}
 
 
-def cpu_baseline_reorder(w, inp) -> dict:
+def cpu_baseline_reorder(w, inp, threads: int) -> dict:
     """The fp64 oracle's two-stage selection on one layer's share (instance 0
-    as a selection of its own, same budget), single-threaded; rate in scored
-    token-rows per second (two passes over the cache)."""
+    as a selection of its own, same budget); rate in scored token-rows per
+    second (two passes over the cache)."""
     from threadpoolctl import threadpool_limits
     from oracle import kvsel_oracle as O
     from oracle import pipeline as OP
 
     sub = {key: OP.to64(inp[key][0:1]) for key in ("q", "k", "v")}
     lens = [int(w.plants["chunk_len"])] * (w.N // int(w.plants["chunk_len"]))
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
         O.if_two_stage(sub["q"], sub["k"], sub["v"], lens, w.scale, w.k, 1, w.rope_base,
                        w.rope_style, w.dtype, w.signal)
         elapsed = time.perf_counter() - t0
     rows = 2 * w.N
-    log(f"cpu oracle: two-stage selection of instance 0 in {elapsed:.1f} s")
-    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+    log(f"cpu oracle ({threads} threads): two-stage selection of instance 0 in {elapsed:.1f} s")
+    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": threads, "kind": "oracle",
             "sample": f"instance 0 of {w.B} as its own selection (2 x {w.N} scored token-rows; "
-                      f"fp64 numpy, 1 thread), {elapsed:.1f} s"}
+                      f"fp64 numpy, {threads} BLAS threads), {elapsed:.1f} s"}
 
 
-def cpu_baseline_recompute(w, inp, rows: int = 64) -> dict:
+def cpu_baseline_recompute(w, inp, threads: int, rows: int = 64) -> dict:
     """The fp64 oracle on a sample of the recomputation: ``rows`` selected
-    tokens of layer 0 (every head), single-threaded; rate in attended
-    (row, key) pairs per second, the unit the GPU line reports."""
+    tokens of layer 0 (every head); rate in attended (row, key) pairs per
+    second, the unit the GPU line reports."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import kvsel_oracle as O
@@ -329,15 +330,15 @@ def cpu_baseline_recompute(w, inp, rows: int = 64) -> dict:
     q = OP.to64(inp["q_sel"][0:1])[:, pick]
     pos = inp["pos"][0:1].cpu().numpy()[:, pick]
     k, v = OP.to64(inp["k"][0:1]), OP.to64(inp["v"][0:1])
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
         O.index_causal_attention(q, k, v, pos, w.scale)
         elapsed = time.perf_counter() - t0
     pairs = int((np.minimum(pos, w.N - 1) + 1).sum())
-    log(f"cpu oracle: {rows} recomputed rows in {elapsed:.1f} s")
-    return {"value": pairs / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+    log(f"cpu oracle ({threads} threads): {rows} recomputed rows in {elapsed:.1f} s")
+    return {"value": pairs / elapsed, "unit": "token-rows/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {S} selected tokens of layer 0, every head ({pairs} attended "
-                      f"context rows; fp64 numpy, 1 thread), {elapsed:.1f} s"}
+                      f"context rows; fp64 numpy, {threads} BLAS threads), {elapsed:.1f} s"}
 
 
 def host_cpu() -> dict:
@@ -355,10 +356,10 @@ def host_cpu() -> dict:
             "affinity": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(w, inp, budget_s: float = 15.0, max_instances: int = 24) -> dict:
+def cpu_baseline(w, inp, threads: int, budget_s: float = 8.0, max_instances: int = 16) -> dict:
     """Time the fp64 oracle on whole instances of the workload (inputs copied to
-    host memory first, outside the timed region), single-threaded."""
-    import numpy as np
+    host memory first, outside the timed region) with ``threads`` BLAS
+    threads, until ``budget_s`` seconds or ``max_instances`` instances."""
     from threadpoolctl import threadpool_limits
     from oracle import pipeline as OP
 
@@ -369,7 +370,7 @@ def cpu_baseline(w, inp, budget_s: float = 15.0, max_instances: int = 24) -> dic
     else:
         wi = w.scaled(B=1, requests=1)
     done, elapsed = 0, 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while done < min(max_instances, w.B) and elapsed < budget_s:
             b = done
             sub = {key: OP.to64(inp[key][b:b + 1]) for key in ("q", "k", "v")}
@@ -380,42 +381,81 @@ def cpu_baseline(w, inp, budget_s: float = 15.0, max_instances: int = 24) -> dic
             OP.run(wi, sub)
             elapsed += time.perf_counter() - t0
             done += 1
-            log(f"cpu oracle: instance {b} done, {elapsed:.1f} s so far")
+            log(f"cpu oracle ({threads} threads): instance {b} done, {elapsed:.1f} s so far")
     rows = done * w.N
-    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": 1, "kind": "oracle",
+    return {"value": rows / elapsed, "unit": "token-rows/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {w.B} instances ({w.N} cached rows each, whole path, "
-                      f"fp64 numpy, 1 thread), {elapsed:.1f} s"}
+                      f"fp64 numpy, {threads} BLAS threads), {elapsed:.1f} s"}
 
 
-def time_graph(step, w, args, rows: int) -> dict:
+def cpu_baselines(w, inp, prune: bool) -> dict:
+    """The oracle with BLAS threads set to the CPUs this process may use, and
+    single-threaded beside it (numpy's elementwise work runs on one thread
+    either way)."""
+    threads = len(os.sched_getaffinity(0))
+    leg = (lambda t: cpu_baseline_prune(w, inp, t)) if prune else \
+        (lambda t: cpu_baseline_reorder(w, inp, t)) if w.reorder else \
+        (lambda t: cpu_baseline_recompute(w, inp, t)) if w.recompute else \
+        (lambda t: cpu_baseline(w, inp, t))
+    res = leg(threads)
+    res["single_thread"] = leg(1) if threads > 1 else dict(res)
+    res["host"] = host_cpu()
+    return res
+
+
+def step_timeline(start, stop, marks, first: str, last: str, step_ms: list,
+                  host_ms: list) -> dict:
+    """Where the GPU clock of the timed region went outside the steps' own
+    spans: from the region's start event to step 0's first stage (lead),
+    between one step's last stage and the next step's first (gaps), and after
+    the last step (tail); with the spread of the step spans and the host time
+    each step's launches took (a host slower than the GPU leaves gaps)."""
+    gaps = [marks[i][last][1].elapsed_time(marks[i + 1][first][0])
+            for i in range(len(marks) - 1)]
+    spans = sorted(step_ms)
+    p90 = spans[min(len(spans) - 1, int(round(0.9 * (len(spans) - 1))))]
+    return {"lead_ms": start.elapsed_time(marks[0][first][0]),
+            "gap_ms_total": sum(gaps), "gap_ms_max": max(gaps, default=0.0),
+            "tail_ms": marks[-1][last][1].elapsed_time(stop),
+            "step_span_ms": {"mean": statistics.mean(spans), "median": statistics.median(spans),
+                             "p90": p90, "max": spans[-1]},
+            "host_launch_ms": {"mean": statistics.mean(host_ms), "max": max(host_ms)}}
+
+
+def time_graph(step, feed, args, rows: int) -> dict:
     """The step captured once as a HIP graph (torch.cuda.graph) and replayed
     ``args.steps`` times between events: what a serving loop that launches the
-    whole path at once would see.  Only for steps whose inputs stay the same
-    (every workload but the serving one, which takes fresh queries per step)."""
+    whole path at once would see.  ``step()`` runs the path on its static
+    inputs; ``feed(i)`` (or None) copies step i's fresh inputs into them (the
+    serving workload's new queries), on the same stream, inside the timed
+    region."""
     import torch
-    if w.recipe == "serving":
-        return {"skipped": "the step's queries change every step"}
     side = torch.cuda.Stream()                     # default priority
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        step(0)
+        step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step(0)
-    for _ in range(max(args.warmup, 1)):
+        step()
+    for i in range(max(args.warmup, 1)):
+        if feed is not None:
+            feed(i)
         graph.replay()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if feed is not None:
+            feed(args.warmup + i)
         graph.replay()
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
     log(f"{args.steps} graph replays: {ms:.4f} ms per step")
-    return {"ms_per_step": ms, "value": rows / (ms * 1e-3)}
+    return {"ms_per_step": ms, "value": rows / (ms * 1e-3),
+            "inputs_copied_per_step": feed is not None}
 
 
 def main() -> int:
@@ -511,6 +551,11 @@ def main() -> int:
         queries = make_queries(w, inp, args.warmup + args.steps, args.seed, dev)
         step = lambda i, m=None: path(queries[i], m)
 
+    # no garbage collection inside the warm-up and timed regions: a collection
+    # pauses the host for tens of ms, and one that falls before the first
+    # timed launches leaves the GPU idle (the queue is still empty)
+    gc.collect()
+    gc.disable()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -526,14 +571,27 @@ def main() -> int:
                                    torch.cuda.Event(enable_timing=True))
                                   for _ in range(path.n_scored)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # create every event now (torch makes the HIP event on its first record),
+    # so that the timed region only records them
+    for mk in marks:
+        for pairs in mk.values():
+            for pair in (pairs if isinstance(pairs, list) else [pairs]):
+                for e in pair:
+                    e.record()
+    start.record()
+    stop.record()
     torch.cuda.synchronize()
+    host_ms = []
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
+        h0 = time.perf_counter()
         step(args.warmup + i, marks[i])
+        host_ms.append((time.perf_counter() - h0) * 1e3)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
     log(f"{args.steps} timed steps: {total_ms:.2f} ms on the GPU clock, {wall * 1e3:.2f} ms wall")
@@ -541,7 +599,13 @@ def main() -> int:
     stage_ms = {s: statistics.mean(m[s][0].elapsed_time(m[s][1]) for m in marks)
                 for s in path.stages}
     # per-step times from the first stage's start to the last stage's end
-    step_ms = [m[path.stages[0]][0].elapsed_time(m[path.stages[-1]][1]) for m in marks]
+    first, last = path.stages[0], path.stages[-1]
+    step_ms = [m[first][0].elapsed_time(m[last][1]) for m in marks]
+    timeline = step_timeline(start, stop, marks, first, last, step_ms, host_ms)
+    log(f"timeline: lead {timeline['lead_ms']:.3f} ms, gaps {timeline['gap_ms_total']:.3f} ms "
+        f"(max {timeline['gap_ms_max']:.3f}), tail {timeline['tail_ms']:.3f} ms, "
+        f"host launch {timeline['host_launch_ms']['mean']:.3f} ms/step "
+        f"(max {timeline['host_launch_ms']['max']:.3f})")
     dom = max(path.stages, key=lambda s: stage_ms[s])     # the stage that takes longest
     dom_ms = stage_ms[dom]
     bound, quantity, peak, unit = stage_bound(dom, w, work[dom])
@@ -595,6 +659,7 @@ def main() -> int:
                      "device_copy_GBps": copy_GBps,
                      "frac_of_device_copy": path_bytes / (ms_step * 1e-3) / 1e9 / copy_GBps},
         "stages_ms": stage_ms,
+        "timeline": timeline,
     }
     # selection alone (re-position, score, aggregate, top-k; both stages and the
     # reordering of a two-stage selection; the pruning loop), beside the full path
@@ -610,14 +675,22 @@ def main() -> int:
     if host_link is not None:
         result["host_link"] = host_link
     if args.graph:
-        result["graph"] = time_graph(step, w, args, rows)
+        if prune:
+            result["graph"] = time_graph(lambda: path(inp["q"], inp["q_dec"]), None, args, rows)
+        elif w.recompute:
+            result["graph"] = time_graph(lambda: path(inp["q_sel"]), None, args, rows)
+        elif w.recipe != "serving":
+            result["graph"] = time_graph(lambda: path(inp["q"]), None, args, rows)
+        else:
+            # the captured step reads a static query block; each replay is
+            # preceded by a copy of that step's fresh queries into it
+            static_q = queries[0].clone()
+            result["graph"] = time_graph(lambda: path(static_q),
+                                         lambda i: static_q.copy_(queries[i % len(queries)]),
+                                         args, rows)
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = (cpu_baseline_prune(w, inp) if prune
-                                  else cpu_baseline_reorder(w, inp) if w.reorder
-                                  else cpu_baseline_recompute(w, inp) if w.recompute
-                                  else cpu_baseline(w, inp))
-        result["cpu_baseline"]["host"] = host_cpu()
+        result["cpu_baseline"] = cpu_baselines(w, inp, prune)
     print(json.dumps(result), flush=True)
     return 0
 

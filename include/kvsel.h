@@ -45,6 +45,10 @@
  * - A "unit" is unit_len consecutive cached rows: a chunk, a document, an L1
  *   entry's L2 block, or a single token (unit_len = 1).  N must be a multiple
  *   of unit_len; M = N / unit_len.
+ * - `scale` (the logit scale, usually 1/sqrt(D)) must be finite and > 0 in
+ *   every call that takes it, else KVSEL_ERR_SHAPE: the kernels take the
+ *   maximum of the unscaled dot products, which is the maximum logit only for
+ *   a positive scale.
  */
 #ifndef KVSEL_H
 #define KVSEL_H

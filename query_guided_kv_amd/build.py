@@ -72,6 +72,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """The compiler's AddressSanitizer runtime (to preload into a process that
+    loads the sanitizer build)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime of hipcc was not found")
+    return path
+
+
+def build_asan(out_dir: str) -> str:
+    """The same library with its HOST code built under AddressSanitizer
+    (device code as in build(); sanitizers are not used on the GPU), into
+    out_dir; returns the library path.  Load it in a process that preloads
+    asan_runtime()."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in compile_flags() if f != "-O3"] + \
+        "-O1 -g -Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+    def one(src: str) -> str:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        r = subprocess.run([hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libkvsel_asan.so")
+    r = subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", lib] + objs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

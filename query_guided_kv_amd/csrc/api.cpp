@@ -1,6 +1,7 @@
 // C ABI of libkvsel: argument validation, workspace sizing and dispatch.
 // Every check runs on the host before anything is enqueued; no call allocates
 // device memory.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -106,6 +107,15 @@ int check_heads(int64_t T, int64_t Hq, const kvsel_cache& kc, const char* what) 
                 what, (long long)T, (long long)Hq, (long long)kc.H);
   if (Hq > 4096 || T > 65536 || (Hq / kc.H) * T > (int64_t{1} << 20))
     return fail(KVSEL_ERR_SHAPE, "%s: query block too large", what);
+  return KVSEL_OK;
+}
+
+// The matrix-core kernels take the maximum of the raw dot products and scale
+// it afterwards, which is the maximum scaled logit only for a positive scale;
+// a scale that is not finite would turn every logit into inf or NaN.
+int check_scale(float scale, const char* what) {
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(KVSEL_ERR_SHAPE, "%s: scale %g must be finite and > 0", what, static_cast<double>(scale));
   return KVSEL_OK;
 }
 
@@ -268,6 +278,7 @@ int score_impl(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_
   KVSEL_TRY(check_cache(kc, what));
   KVSEL_TRY(check_heads(T, Hq, kc, what));
   KVSEL_TRY(check_units(kc, unit_len, what));
+  KVSEL_TRY(check_scale(scale, what));
   if ((row_max == nullptr) != (row_sum == nullptr))
     return fail(KVSEL_ERR_NULL, "%s: row_max and row_sum must both be set or both NULL", what);
   const bool stats = row_max != nullptr;
@@ -368,6 +379,7 @@ int kvsel_score_units(const void* q, int64_t T, int64_t Hq, const void* k, kvsel
   KVSEL_TRY(check_cache(kc, what));
   KVSEL_TRY(check_heads(T, Hq, kc, what));
   KVSEL_TRY(check_units(kc, unit_len, what));
+  KVSEL_TRY(check_scale(scale, what));
   if (n_units < 1 || n_units * unit_len >= (int64_t{1} << 31))
     return fail(KVSEL_ERR_SHAPE, "%s: n_units=%lld out of range", what, (long long)n_units);
   if (delta != nullptr) {
@@ -427,6 +439,7 @@ int kvsel_aggregate(const void* q, int64_t T, int64_t Hq, const void* k, const v
   KVSEL_TRY(check_cache(kc, "kvsel_aggregate"));
   KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_aggregate"));
   KVSEL_TRY(check_units(kc, unit_len, "kvsel_aggregate"));
+  KVSEL_TRY(check_scale(scale, "kvsel_aggregate"));
   if (signal != KVSEL_SIG_MASS && signal != KVSEL_SIG_VNORM)
     return fail(KVSEL_ERR_SHAPE, "kvsel_aggregate: unknown signal %d", signal);
   if (group < 1 || kc.B % group != 0)
@@ -527,6 +540,7 @@ int kvsel_index_attn(const void* q, int64_t S, int64_t Hq, float scale, const vo
   if (pos == nullptr) return fail(KVSEL_ERR_NULL, "pos is NULL");
   if (out == nullptr) return fail(KVSEL_ERR_NULL, "out is NULL");
   KVSEL_TRY(check_cache(kc, what));
+  KVSEL_TRY(check_scale(scale, what));
   if (kc.dtype != KVSEL_BF16)
     return fail(KVSEL_ERR_UNSUPPORTED, "%s: bf16 caches only (matrix cores)", what);
   if (S < 1 || Hq < 1 || Hq % kc.H != 0 || Hq > 4096 || S >= (int64_t{1} << 31) / Hq)
@@ -651,6 +665,7 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const k
     ds[i] = DecodeSeg{segs[i].k, segs[i].v, c.N, c.stride_b, c.stride_n, 0};
   }
   KVSEL_TRY(check_heads(T, Hq, c0, "kvsel_decode_attn"));
+  KVSEL_TRY(check_scale(scale, "kvsel_decode_attn"));
   // splits of every segment, numbered across the segments (sizes validated)
   const int64_t split_len = split_len_of(T, Hq, c0, false, total_keys(segs, n_seg));
   for (int i = 0; i < n_seg; ++i) {
@@ -701,6 +716,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
   KVSEL_TRY(check_cache(kc, "kvsel_gather_decode"));
   KVSEL_TRY(check_units(kc, unit_len, "kvsel_gather_decode"));
   KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_gather_decode"));
+  KVSEL_TRY(check_scale(scale, "kvsel_gather_decode"));
   const int64_t M = kc.N / unit_len;
   if (k < 0 || k > M)
     return fail(KVSEL_ERR_SHAPE, "kvsel_gather_decode: k=%lld not in [0, M=%lld]", (long long)k,

@@ -1,103 +1,34 @@
 """Python binding of libkvsel (ctypes).  Argument marshalling only.
 
 Each function mirrors one C entry point of ``include/kvsel.h``: it takes torch
-tensors that live on the GPU, allocates outputs and workspace with torch's
-caching allocator, passes raw device pointers and the current HIP stream, and
-raises :class:`KvselError` on a negative status.  All computation happens in
-the library's kernels; there is no fallback.
+tensors that live on the GPU, checks that they have the shapes, dtypes,
+layouts and devices the entry point reads, allocates the outputs and
+workspace it is not given (torch's caching allocator), passes raw device
+pointers and the current HIP stream, and raises :class:`KvselError` on a
+negative status.  A tensor that does not fit is refused here, before any
+pointer reaches the library.  All computation happens in the library's
+kernels; there is no fallback.
+
+Every output (and the workspace, a uint8 tensor) may be passed in instead of
+allocated, so that a loop of calls allocates nothing per step and can be
+captured as a HIP graph.
 """
 
 from __future__ import annotations
 
 import ctypes
-import os
 from typing import Optional, Sequence, Tuple
 
 import torch
 
-_HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvsel.so")
-
-BF16, FP32 = 0, 1
-ROPE = {"half": 0, "interleaved": 1}
-SIGNAL = {"mass": 0, "vnorm": 1}
+from .abi import (BF16, FP32, LIB_PATH, ROPE, SIGNAL, Cache, Segment, load,  # noqa: F401
+                  ERR_DTYPE, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE)
 
 
 class KvselError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"kvsel status {status}: {msg}")
         self.status = status
-
-
-class Cache(ctypes.Structure):
-    _fields_ = [("B", ctypes.c_int64), ("N", ctypes.c_int64), ("H", ctypes.c_int64),
-                ("D", ctypes.c_int64), ("stride_b", ctypes.c_int64),
-                ("stride_n", ctypes.c_int64), ("dtype", ctypes.c_int32)]
-
-
-class Segment(ctypes.Structure):
-    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("kc", Cache)]
-
-
-_P = ctypes.c_void_p
-_I64 = ctypes.c_int64
-_I32 = ctypes.c_int32
-_F = ctypes.c_float
-_D = ctypes.c_double
-_SZ = ctypes.c_size_t
-
-_SIGNATURES = {
-    "kvsel_reposition": (ctypes.c_int, [_P, _P, Cache, _I64, _P, _I32, _D, _I32, _P]),
-    "kvsel_score": (ctypes.c_int, [_P, _I64, _I64, _P, Cache, _F, _I64, _P, _P, _P, _P, _SZ, _P]),
-    "kvsel_score_workspace": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I32, _I32]),
-    "kvsel_score_reposition": (ctypes.c_int, [_P, _I64, _I64, _P, _P, Cache, _F, _I64, _I64, _P,
-                                              _I32, _D, _I32, _P, _P, _P, _P, _SZ, _P]),
-    "kvsel_score_reposition_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, _I32, _I32, _I32]),
-    "kvsel_aggregate": (ctypes.c_int, [_P, _I64, _I64, _P, _P, Cache, _F, _P, _P, _P, _I32, _I64,
-                                       _I64, _P, _I32, _P, _SZ, _P]),
-    "kvsel_score_units": (ctypes.c_int, [_P, _I64, _I64, _P, Cache, _F, _I64, _P, _I64, _P, _I32,
-                                         _D, _I32, _P, _P, _P, _P, _SZ, _P]),
-    "kvsel_score_units_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, _I32, _I32]),
-    "kvsel_take": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
-    "kvsel_order": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P]),
-    "kvsel_index_attn": (ctypes.c_int, [_P, _I64, _I64, _F, _P, _P, Cache, _P, _P, _P, _P]),
-    "kvsel_unit_fractions": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
-    "kvsel_slot_starts": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
-    "kvsel_aggregate_workspace": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I32, _I32]),
-    "kvsel_topk": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
-    "kvsel_gather": (ctypes.c_int, [_P, _P, Cache, _I64, _P, _I64, _I64, _P, _I64, _D, _I32, _P,
-                                    _P, ctypes.POINTER(Cache), _P, _P, _P]),
-    "kvsel_decode_attn": (ctypes.c_int, [_P, _I64, _I64, _F, ctypes.POINTER(Segment), _I32, _P,
-                                         _P, _P, _SZ, _P]),
-    "kvsel_decode_workspace": (_SZ, [_I64, _I64, ctypes.POINTER(Segment), _I32]),
-    "kvsel_gather_decode": (ctypes.c_int, [_P, _I64, _I64, _F, _P, _P, Cache, _I64, _P, _I64, _I64,
-                                           _P, _P, ctypes.POINTER(Segment), _I32, _P, _P, _P, _SZ,
-                                           _P]),
-    "kvsel_gather_decode_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, ctypes.POINTER(Segment),
-                                            _I32]),
-    "kvsel_status_str": (ctypes.c_char_p, [ctypes.c_int]),
-    "kvsel_last_error": (ctypes.c_char_p, []),
-    "kvsel_version": (ctypes.c_int, []),
-}
-
-_lib: Optional[ctypes.CDLL] = None
-
-
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libkvsel.so (built in-tree by ``query_guided_kv_amd.build``)."""
-    global _lib
-    if _lib is not None and path == LIB_PATH:
-        return _lib
-    if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python -m query_guided_kv_amd.build`")
-    lib = ctypes.CDLL(path)
-    for name, (res, args) in _SIGNATURES.items():
-        fn = getattr(lib, name)
-        fn.restype = res
-        fn.argtypes = args
-    if path == LIB_PATH:
-        _lib = lib
-    return lib
 
 
 def _check(rc: int) -> None:
@@ -119,25 +50,151 @@ def dtype_code(t: torch.Tensor) -> int:
         return BF16
     if t.dtype == torch.float32:
         return FP32
-    raise KvselError(-3, f"unsupported dtype {t.dtype}")
+    raise KvselError(ERR_DTYPE, f"unsupported dtype {t.dtype}")
 
 
 def cache_desc(t: torch.Tensor) -> Cache:
     """Descriptor of a [B][N][H][D] tensor whose [H][D] block is contiguous."""
     if t.dim() != 4:
-        raise KvselError(-2, f"cache must be [B][N][H][D], got {tuple(t.shape)}")
+        raise KvselError(ERR_SHAPE, f"cache must be [B][N][H][D], got {tuple(t.shape)}")
     B, N, H, D = t.shape
     if t.stride(3) != 1 or t.stride(2) != D:
-        raise KvselError(-4, "cache rows must hold contiguous [H][D]")
+        raise KvselError(ERR_UNSUPPORTED, "cache rows must hold contiguous [H][D]")
     return Cache(B, N, H, D, t.stride(0), t.stride(1), dtype_code(t))
 
 
-def _empty(shape, dev, dtype=torch.float32):
-    return torch.empty(shape, dtype=dtype, device=dev)
+# ---------------------------------------------------------------------------
+# argument checks (all raise KvselError before anything is launched)
+# ---------------------------------------------------------------------------
+
+def _gpu(**tensors) -> None:
+    """Checked after every shape and dtype check: the named tensors are GPU
+    memory (a CPU tensor never reaches the library)."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise KvselError(ERR_UNSUPPORTED, f"{name} must be GPU memory, got {t.device}")
 
 
-def _workspace(nbytes: int, dev) -> Optional[torch.Tensor]:
+def _same_device(t: torch.Tensor, dev: torch.device, name: str) -> None:
+    if t.device != dev:
+        raise KvselError(ERR_UNSUPPORTED, f"{name} is on {t.device}, expected {dev}")
+
+
+def _source_device(t: torch.Tensor, dev: torch.device, name: str) -> None:
+    """Gather sources may also be pinned host memory (a host-resident cache)."""
+    if t.device != dev and not (t.device.type == "cpu" and t.is_pinned()):
+        raise KvselError(ERR_UNSUPPORTED,
+                         f"{name} must be on {dev} or in pinned host memory, got {t.device}")
+
+
+def _check_query(q: torch.Tensor, ref: torch.Tensor, name: str = "q",
+                 same_device: bool = True) -> Tuple[int, int]:
+    """q is a contiguous [B][T][Hq][D] block in ref's dtype (and on its device
+    unless the cache may be host memory), for a cache ref [B][N][H][D] (Hq a
+    multiple of H); returns (T, Hq)."""
+    if q.dim() != 4:
+        raise KvselError(ERR_SHAPE, f"{name} must be [B][T][Hq][D], got {tuple(q.shape)}")
+    B, _, H, D = ref.shape
+    if q.shape[0] != B or q.shape[3] != D or q.shape[1] < 1 or q.shape[2] < 1 \
+            or q.shape[2] % H != 0:
+        raise KvselError(ERR_SHAPE, f"{name} {tuple(q.shape)} does not fit cache {tuple(ref.shape)} "
+                                    "(same B and D, Hq a multiple of H)")
+    if q.dtype != ref.dtype:
+        raise KvselError(ERR_DTYPE, f"{name} is {q.dtype}, the cache {ref.dtype}")
+    if same_device and q.device != ref.device:
+        raise KvselError(ERR_UNSUPPORTED, f"{name} is on {q.device}, the cache on {ref.device}")
+    if not q.is_contiguous():
+        raise KvselError(ERR_UNSUPPORTED, f"{name} must be contiguous")
+    return q.shape[1], q.shape[2]
+
+
+def _check_like(t: torch.Tensor, ref: torch.Tensor, name: str, ref_name: str = "k") -> None:
+    """t has ref's shape, strides, dtype and device (a value cache beside its keys)."""
+    if tuple(t.shape) != tuple(ref.shape) or t.stride() != ref.stride():
+        raise KvselError(ERR_SHAPE, f"{name} must match {ref_name} in shape and strides")
+    if t.dtype != ref.dtype:
+        raise KvselError(ERR_DTYPE, f"{name} is {t.dtype}, {ref_name} is {ref.dtype}")
+    if t.device != ref.device:
+        raise KvselError(ERR_UNSUPPORTED, f"{name} is on {t.device}, {ref_name} on {ref.device}")
+
+
+def _check_tensor(t: torch.Tensor, shape, dtype, dev: torch.device, name: str) -> None:
+    """A contiguous tensor of exactly this shape and dtype on dev."""
+    if t.dtype != dtype:
+        raise KvselError(ERR_DTYPE, f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise KvselError(ERR_SHAPE, f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise KvselError(ERR_UNSUPPORTED, f"{name} must be contiguous")
+    _same_device(t, dev, name)
+
+
+def _check_delta(delta: torch.Tensor, B: int, M: int, dev: torch.device) -> int:
+    """int64 [M] (shared) or [B][M] (per instance); returns the per-instance flag."""
+    if delta.dim() == 1:
+        _check_tensor(delta, (M,), torch.int64, dev, "delta")
+        return 0
+    _check_tensor(delta, (B, M), torch.int64, dev, "delta")
+    return 1
+
+
+def _check_idx(idx: torch.Tensor, B: int, idx_group: int, dev: torch.device) -> int:
+    """int32 [B/idx_group][k]; returns k."""
+    if idx_group < 1 or B % idx_group != 0:
+        raise KvselError(ERR_SHAPE, f"idx_group {idx_group} must divide B={B}")
+    if idx.dim() != 2:
+        raise KvselError(ERR_SHAPE, f"idx must be [B/idx_group][k], got {tuple(idx.shape)}")
+    _check_tensor(idx, (B // idx_group, idx.shape[1]), torch.int32, dev, "idx")
+    return idx.shape[1]
+
+
+def _out(t: Optional[torch.Tensor], shape, dtype, dev, name: str) -> torch.Tensor:
+    """The caller's output tensor, checked, or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _check_tensor(t, shape, dtype, dev, name)
+    return t
+
+
+class Workspace:
+    """A workspace kept across calls: allocated by the first call that needs
+    it and grown only when a call needs more, so that a loop of identical
+    calls allocates once (and a HIP graph captured after the first call
+    allocates nothing)."""
+
+    def __init__(self):
+        self.tensor: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int, dev) -> Optional[torch.Tensor]:
+        if nbytes == 0:
+            return None
+        t = self.tensor
+        if t is None or t.numel() < nbytes or t.device != dev:
+            t = torch.empty((nbytes + 255) // 256 * 256, dtype=torch.uint8, device=dev)
+            self.tensor = t
+        return t
+
+
+def _workspace(nbytes: int, dev, ws=None) -> Optional[torch.Tensor]:
+    """The caller's uint8 workspace (at least nbytes; a tensor or a
+    :class:`Workspace`), or a new one."""
+    if isinstance(ws, Workspace):
+        return ws.get(nbytes, dev)
+    if ws is not None:
+        if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.numel() < nbytes:
+            raise KvselError(ERR_WORKSPACE, f"workspace must be contiguous uint8 of at least "
+                                            f"{nbytes} bytes")
+        _same_device(ws, dev, "workspace")
+        return ws
     return torch.empty(max(1, (nbytes + 255) // 256 * 256), dtype=torch.uint8, device=dev) if nbytes else None
+
+
+def _nbytes(ws: Optional[torch.Tensor]) -> int:
+    return 0 if ws is None else ws.numel()
+
+
+def _scale(scale: Optional[float], D: int) -> float:
+    return 1.0 / D ** 0.5 if scale is None else scale
 
 
 # ---------------------------------------------------------------------------
@@ -150,89 +207,108 @@ def reposition(k: torch.Tensor, delta: torch.Tensor, unit_len: int,
     """kvsel_reposition: rotate every row of unit u by delta[u] positions.
     ``delta``: int64 [M] or [B][M] on the device.  ``out`` may be ``k`` (in place)."""
     lib = load()
-    out = torch.empty_like(k) if out is None else out
-    if out.shape != k.shape or out.stride() != k.stride():
-        raise KvselError(-2, "out must match k in shape and strides")
-    per = 1 if delta.dim() == 2 else 0
-    _check(lib.kvsel_reposition(_ptr(k), _ptr(out), cache_desc(k), unit_len, _ptr(delta), per,
-                                rope_base, ROPE[style], _stream(k.device)))
+    kc = cache_desc(k)
+    dev = k.device
+    if unit_len < 1 or k.shape[1] % unit_len:
+        raise KvselError(ERR_SHAPE, f"unit_len {unit_len} must divide N={k.shape[1]}")
+    per = _check_delta(delta, k.shape[0], k.shape[1] // unit_len, dev)
+    if out is None:
+        out = torch.empty_like(k)
+    else:
+        _check_like(out, k, "out")
+    _gpu(k=k, delta=delta, out=out)
+    _check(lib.kvsel_reposition(_ptr(k), _ptr(out), kc, unit_len, _ptr(delta), per,
+                                rope_base, ROPE[style], _stream(dev)))
     return out
 
 
+def _stat_outs(B, Hq, T, M, dev, row_stats, partials, rm, rs, part):
+    rm = _out(rm, (B, Hq, T), torch.float32, dev, "row_max") if row_stats else None
+    rs = _out(rs, (B, Hq, T), torch.float32, dev, "row_sum") if row_stats else None
+    part = _out(part, (B, Hq, T, M, 2), torch.float32, dev, "part") if partials else None
+    return rm, rs, part
+
+
 def score(q: torch.Tensor, k: torch.Tensor, unit_len: int, scale: Optional[float] = None,
-          row_stats: bool = True, partials: bool = True):
+          row_stats: bool = True, partials: bool = True, *, rm_out=None, rs_out=None,
+          part_out=None, ws=None):
     """kvsel_score -> (row_max, row_sum, part); entries not requested are None."""
     lib = load()
-    B, T, Hq, D = q.shape
-    N = k.shape[1]
-    scale = 1.0 / D ** 0.5 if scale is None else scale
+    kc = cache_desc(k)
     dev = k.device
-    rm = _empty((B, Hq, T), dev) if row_stats else None
-    rs = _empty((B, Hq, T), dev) if row_stats else None
-    part = _empty((B, Hq, T, N // unit_len, 2), dev) if partials else None
+    T, Hq = _check_query(q, k)
+    B, N, _, D = k.shape
+    if unit_len < 1 or N % unit_len:
+        raise KvselError(ERR_SHAPE, f"unit_len {unit_len} must divide N={N}")
+    rm, rs, part = _stat_outs(B, Hq, T, N // unit_len, dev, row_stats, partials, rm_out, rs_out,
+                              part_out)
     need = lib.kvsel_score_workspace(B, N, Hq, T, unit_len, int(row_stats), int(partials))
-    ws = _workspace(need, dev)
-    _check(lib.kvsel_score(_ptr(q), T, Hq, _ptr(k), cache_desc(k), scale, unit_len, _ptr(rm),
-                           _ptr(rs), _ptr(part), _ptr(ws), need, _stream(dev)))
+    ws = _workspace(need, dev, ws)
+    _gpu(q=q, k=k)
+    _check(lib.kvsel_score(_ptr(q), T, Hq, _ptr(k), kc, _scale(scale, D), unit_len, _ptr(rm),
+                           _ptr(rs), _ptr(part), _ptr(ws), _nbytes(ws), _stream(dev)))
     return rm, rs, part
 
 
 def score_reposition(q: torch.Tensor, k: torch.Tensor, delta: torch.Tensor, rot_unit_len: int,
                      unit_len: int, k_out: Optional[torch.Tensor] = None,
                      scale: Optional[float] = None, row_stats: bool = True,
-                     partials: bool = True, rope_base: float = 10000.0, style: str = "half"):
+                     partials: bool = True, rope_base: float = 10000.0, style: str = "half",
+                     *, rm_out=None, rs_out=None, part_out=None, ws=None):
     """kvsel_score_reposition -> (row_max, row_sum, part) of the keys rotated by
     delta[u] per unit of ``rot_unit_len`` rows; ``k_out`` (same shape and strides
     as ``k``) receives the re-positioned keys when given."""
     lib = load()
-    B, T, Hq, D = q.shape
-    N = k.shape[1]
-    scale = 1.0 / D ** 0.5 if scale is None else scale
-    dev = k.device
-    if k_out is not None and (k_out.shape != k.shape or k_out.stride() != k.stride()):
-        raise KvselError(-2, "k_out must match k in shape and strides")
-    rm = _empty((B, Hq, T), dev) if row_stats else None
-    rs = _empty((B, Hq, T), dev) if row_stats else None
-    part = _empty((B, Hq, T, N // unit_len, 2), dev) if partials else None
     kc = cache_desc(k)
+    dev = k.device
+    T, Hq = _check_query(q, k)
+    B, N, _, D = k.shape
+    if unit_len < 1 or N % unit_len or rot_unit_len < 1 or N % rot_unit_len:
+        raise KvselError(ERR_SHAPE, f"unit_len {unit_len} and rot_unit_len {rot_unit_len} "
+                                    f"must divide N={N}")
+    per = _check_delta(delta, B, N // rot_unit_len, dev)
+    if k_out is not None:
+        _check_like(k_out, k, "k_out")
+    rm, rs, part = _stat_outs(B, Hq, T, N // unit_len, dev, row_stats, partials, rm_out, rs_out,
+                              part_out)
     need = lib.kvsel_score_reposition_workspace(T, Hq, kc, unit_len, rot_unit_len,
                                                 int(row_stats), int(partials),
                                                 int(k_out is not None))
-    ws = _workspace(need, dev)
-    per = 1 if delta.dim() == 2 else 0
-    _check(lib.kvsel_score_reposition(_ptr(q), T, Hq, _ptr(k), _ptr(k_out), kc, scale, unit_len,
-                                      rot_unit_len, _ptr(delta), per, rope_base, ROPE[style],
-                                      _ptr(rm), _ptr(rs), _ptr(part), _ptr(ws), need,
-                                      _stream(dev)))
+    ws = _workspace(need, dev, ws)
+    _gpu(q=q, k=k)
+    _check(lib.kvsel_score_reposition(_ptr(q), T, Hq, _ptr(k), _ptr(k_out), kc, _scale(scale, D),
+                                      unit_len, rot_unit_len, _ptr(delta), per, rope_base,
+                                      ROPE[style], _ptr(rm), _ptr(rs), _ptr(part), _ptr(ws),
+                                      _nbytes(ws), _stream(dev)))
     return rm, rs, part
 
 
 def score_units(q: torch.Tensor, k: torch.Tensor, units: torch.Tensor, unit_len: int,
                 delta: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                 row_stats: bool = True, partials: bool = True, rope_base: float = 10000.0,
-                style: str = "half"):
+                style: str = "half", *, rm_out=None, rs_out=None, part_out=None, ws=None):
     """kvsel_score_units -> (row_max, row_sum, part) of each instance's query
     block against the listed units of its cache (``units`` int32 [B][n]), unit
     j re-positioned by ``delta[j]`` (int64 [n] or [B][n]) when given.  ``k``
     may be a strided view, e.g. one layer of a [R][L][N][H][D] store."""
     lib = load()
-    B, T, Hq, D = q.shape
-    n = units.shape[1]
-    if units.dtype != torch.int32 or units.dim() != 2 or units.shape[0] != k.shape[0] \
-            or not units.is_contiguous():
-        raise KvselError(-2, "units must be contiguous int32 [B][n_units]")
-    scale = 1.0 / D ** 0.5 if scale is None else scale
-    dev = k.device
-    rm = _empty((B, Hq, T), dev) if row_stats else None
-    rs = _empty((B, Hq, T), dev) if row_stats else None
-    part = _empty((B, Hq, T, n, 2), dev) if partials else None
     kc = cache_desc(k)
+    dev = k.device
+    T, Hq = _check_query(q, k)
+    B, _, _, D = k.shape
+    if units.dim() != 2:
+        raise KvselError(ERR_SHAPE, "units must be contiguous int32 [B][n_units]")
+    n = units.shape[1]
+    _check_tensor(units, (B, n), torch.int32, dev, "units")
+    per = 0 if delta is None else _check_delta(delta, B, n, dev)
+    rm, rs, part = _stat_outs(B, Hq, T, n, dev, row_stats, partials, rm_out, rs_out, part_out)
     need = lib.kvsel_score_units_workspace(T, Hq, kc, unit_len, n, int(row_stats), int(partials))
-    ws = _workspace(need, dev)
-    per = 1 if delta is not None and delta.dim() == 2 else 0
-    _check(lib.kvsel_score_units(_ptr(q), T, Hq, _ptr(k), kc, scale, unit_len, _ptr(units), n,
-                                 _ptr(delta), per, rope_base, ROPE[style], _ptr(rm), _ptr(rs),
-                                 _ptr(part), _ptr(ws), need, _stream(dev)))
+    ws = _workspace(need, dev, ws)
+    _gpu(q=q, k=k)
+    _check(lib.kvsel_score_units(_ptr(q), T, Hq, _ptr(k), kc, _scale(scale, D), unit_len,
+                                 _ptr(units), n, _ptr(delta), per, rope_base, ROPE[style],
+                                 _ptr(rm), _ptr(rs), _ptr(part), _ptr(ws), _nbytes(ws),
+                                 _stream(dev)))
     return rm, rs, part
 
 
@@ -240,7 +316,8 @@ def aggregate(unit_len: int, group: int = 1, signal: str = "mass", *,
               q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
               v: Optional[torch.Tensor] = None, row_max=None, row_sum=None, part=None,
               scale: Optional[float] = None, cache_shape=None,
-              out: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+              out: Optional[torch.Tensor] = None, accumulate: bool = False,
+              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """kvsel_aggregate -> unit_score [B/group][M].
 
     Chunk path: ``part`` (+ optional row stats), with ``cache_shape`` = k's
@@ -248,57 +325,87 @@ def aggregate(unit_len: int, group: int = 1, signal: str = "mass", *,
     ``out``: write into this fp32 [B/group][M] tensor; with ``accumulate`` the
     result is added to what it holds."""
     lib = load()
-    ref = k if k is not None else None
-    if ref is not None:
-        kc = cache_desc(ref)
-        B, N, H, D = ref.shape
-        dev = ref.device
+    chunk = signal == "mass" and part is not None
+    if k is not None:
+        kc = cache_desc(k)
+        B, N, H, D = k.shape
+        dev = k.device
     else:
+        if not chunk or cache_shape is None:
+            raise KvselError(ERR_NULL, "the token path needs k (and q, row statistics)")
         B, N, H, D = cache_shape
         dtype = BF16 if q is None or q.dtype == torch.bfloat16 else FP32
         kc = Cache(B, N, H, D, N * H * D, H * D, dtype)
         dev = part.device
-    if part is not None:
-        _, Hq, T = part.shape[:3]
+    if unit_len < 1 or N % unit_len:
+        raise KvselError(ERR_SHAPE, f"unit_len {unit_len} must divide N={N}")
+    if group < 1 or B % group:
+        raise KvselError(ERR_SHAPE, f"group {group} must divide B={B}")
+    M = N // unit_len
+    if chunk:
+        if part.dim() != 5:
+            raise KvselError(ERR_SHAPE, "part must be [B][Hq][T][M][2]")
+        Hq, T = part.shape[1], part.shape[2]
+        _check_tensor(part, (B, Hq, T, M, 2), torch.float32, dev, "part")
     else:
-        _, T, Hq, _ = q.shape
-    scale = 1.0 / D ** 0.5 if scale is None else scale
-    if out is None:
-        if accumulate:
-            raise KvselError(-1, "accumulate needs out")
-        out = _empty((B // group, N // unit_len), dev)
-    elif (tuple(out.shape) != (B // group, N // unit_len) or out.dtype != torch.float32
-          or not out.is_contiguous()):
-        raise KvselError(-2, "out must be contiguous fp32 [B/group][M]")
-    chunk = signal == "mass" and part is not None
+        if q is None or row_max is None or row_sum is None:
+            raise KvselError(ERR_NULL, "the token path needs q, k and the row statistics")
+        T, Hq = _check_query(q, k)
+        if signal == "vnorm":
+            if v is None:
+                raise KvselError(ERR_NULL, "the vnorm signal needs v")
+            _check_like(v, k, "v")
+    if (row_max is None) != (row_sum is None):
+        raise KvselError(ERR_NULL, "row_max and row_sum must both be given or both omitted")
+    if row_max is not None:
+        _check_tensor(row_max, (B, Hq, T), torch.float32, dev, "row_max")
+        _check_tensor(row_sum, (B, Hq, T), torch.float32, dev, "row_sum")
+    if out is None and accumulate:
+        raise KvselError(ERR_NULL, "accumulate needs out")
+    out = _out(out, (B // group, M), torch.float32, dev, "out")
     need = lib.kvsel_aggregate_workspace(B, N, Hq, T, unit_len, int(chunk), int(row_max is not None))
-    ws = _workspace(need, dev)
-    _check(lib.kvsel_aggregate(_ptr(q), T, Hq, _ptr(k), _ptr(v), kc, scale, _ptr(row_max),
-                               _ptr(row_sum), _ptr(part), SIGNAL[signal], unit_len, group,
-                               _ptr(out), int(accumulate), _ptr(ws), need, _stream(dev)))
+    ws = _workspace(need, dev, ws)
+    _gpu(out=out, part=part, k=k)
+    _check(lib.kvsel_aggregate(_ptr(q), T, Hq, _ptr(k), _ptr(v), kc, _scale(scale, D),
+                               _ptr(row_max), _ptr(row_sum), _ptr(part), SIGNAL[signal], unit_len,
+                               group, _ptr(out), int(accumulate), _ptr(ws), _nbytes(ws),
+                               _stream(dev)))
     return out
 
 
-def topk(scores: torch.Tensor, k: int, values: bool = False):
+def _check_scores(scores: torch.Tensor, name: str = "scores") -> Tuple[int, int]:
+    dev = scores.device
+    if scores.dim() != 2:
+        raise KvselError(ERR_SHAPE, f"{name} must be fp32 [G][M], got {tuple(scores.shape)}")
+    _check_tensor(scores, scores.shape, torch.float32, dev, name)
+    return scores.shape
+
+
+def topk(scores: torch.Tensor, k: int, values: bool = False, *, idx_out=None, val_out=None):
     """kvsel_topk -> idx int32 [G][k] ascending (and the kept scores if asked)."""
     lib = load()
-    G, M = scores.shape
-    idx = torch.empty((G, k), dtype=torch.int32, device=scores.device)
-    val = _empty((G, k), scores.device) if values else None
-    _check(lib.kvsel_topk(_ptr(scores), G, M, k, _ptr(idx), _ptr(val), _stream(scores.device)))
+    G, M = _check_scores(scores)
+    dev = scores.device
+    idx = _out(idx_out, (G, k), torch.int32, dev, "idx")
+    val = _out(val_out, (G, k), torch.float32, dev, "val") if values else None
+    _gpu(scores=scores)
+    _check(lib.kvsel_topk(_ptr(scores), G, M, k, _ptr(idx), _ptr(val), _stream(dev)))
     return (idx, val) if values else idx
 
 
 def take(src: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
     """kvsel_take -> out[g][j] = src[g][idx[g][j]] (int32; -1 where idx is out of range)."""
     lib = load()
+    dev = src.device
+    if src.dim() != 2 or idx.dim() != 2 or idx.shape[0] != src.shape[0]:
+        raise KvselError(ERR_SHAPE, "take works on int32 [G][m] and [G][k]")
+    _check_tensor(src, src.shape, torch.int32, dev, "src")
+    _check_tensor(idx, idx.shape, torch.int32, dev, "idx")
     G, m = src.shape
     kk = idx.shape[1]
-    for t in (src, idx):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise KvselError(-2, "take works on contiguous int32 tensors")
-    out = torch.empty((G, kk), dtype=torch.int32, device=src.device)
-    _check(lib.kvsel_take(_ptr(src), G, m, _ptr(idx), kk, _ptr(out), _stream(src.device)))
+    out = torch.empty((G, kk), dtype=torch.int32, device=dev)
+    _gpu(src=src)
+    _check(lib.kvsel_take(_ptr(src), G, m, _ptr(idx), kk, _ptr(out), _stream(dev)))
     return out
 
 
@@ -307,14 +414,17 @@ def order(scores: torch.Tensor, idx: torch.Tensor, descending: bool = True,
     """kvsel_order -> idx listed by score (most relevant first, or last with
     ``descending=False``), and the listed scores if asked."""
     lib = load()
-    G, M = scores.shape
+    G, M = _check_scores(scores)
+    dev = scores.device
+    if idx.dim() != 2:
+        raise KvselError(ERR_SHAPE, "idx must be contiguous int32 [G][k]")
     kk = idx.shape[1]
-    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.shape[0] != G:
-        raise KvselError(-2, "idx must be contiguous int32 [G][k]")
-    out = torch.empty((G, kk), dtype=torch.int32, device=scores.device)
-    val = _empty((G, kk), scores.device) if values else None
+    _check_tensor(idx, (G, kk), torch.int32, dev, "idx")
+    out = torch.empty((G, kk), dtype=torch.int32, device=dev)
+    val = torch.empty((G, kk), dtype=torch.float32, device=dev) if values else None
+    _gpu(scores=scores)
     _check(lib.kvsel_order(_ptr(scores), G, M, _ptr(idx), kk, int(descending), _ptr(out),
-                           _ptr(val), _stream(scores.device)))
+                           _ptr(val), _stream(dev)))
     return (out, val) if values else out
 
 
@@ -323,16 +433,17 @@ def index_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Ten
     """kvsel_index_attn -> (o fp32 [B][S][Hq][D], lse [B][Hq][S] or None): the
     selected tokens' queries ``q`` [B][S][Hq][D] attend to keys 0 .. pos[b][j]."""
     lib = load()
-    B, S, Hq, D = q.shape
-    if pos.dtype != torch.int32 or tuple(pos.shape) != (B, S) or not pos.is_contiguous():
-        raise KvselError(-2, "pos must be contiguous int32 [B][S]")
-    if k.shape != v.shape or k.stride() != v.stride():
-        raise KvselError(-2, "k and v must share shape and strides")
-    scale = 1.0 / D ** 0.5 if scale is None else scale
-    out = _empty((B, S, Hq, D), q.device)
-    lse = _empty((B, Hq, S), q.device) if want_lse else None
-    _check(lib.kvsel_index_attn(_ptr(q), S, Hq, scale, _ptr(k), _ptr(v), cache_desc(k), _ptr(pos),
-                                _ptr(out), _ptr(lse), _stream(q.device)))
+    kc = cache_desc(k)
+    dev = k.device
+    _check_like(v, k, "v")
+    S, Hq = _check_query(q, k)
+    B, _, _, D = k.shape
+    _check_tensor(pos, (B, S), torch.int32, dev, "pos")
+    out = torch.empty((B, S, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if want_lse else None
+    _gpu(q=q, k=k)
+    _check(lib.kvsel_index_attn(_ptr(q), S, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc, _ptr(pos),
+                                _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
 
 
@@ -340,12 +451,14 @@ def unit_fractions(sel: torch.Tensor, unit_len: int, n_units: int) -> torch.Tens
     """kvsel_unit_fractions -> r fp32 [G][n_units]: the share of each unit's
     rows in the ascending index lists ``sel`` (int32 [G][k])."""
     lib = load()
-    if sel.dtype != torch.int32 or sel.dim() != 2 or not sel.is_contiguous():
-        raise KvselError(-2, "sel must be contiguous int32 [G][k]")
+    dev = sel.device
+    if sel.dim() != 2:
+        raise KvselError(ERR_SHAPE, "sel must be contiguous int32 [G][k]")
+    _check_tensor(sel, sel.shape, torch.int32, dev, "sel")
     G, kk = sel.shape
-    r = _empty((G, n_units), sel.device)
-    _check(lib.kvsel_unit_fractions(_ptr(sel), G, kk, unit_len, n_units, _ptr(r),
-                                    _stream(sel.device)))
+    r = torch.empty((G, n_units), dtype=torch.float32, device=dev)
+    _gpu(sel=sel)
+    _check(lib.kvsel_unit_fractions(_ptr(sel), G, kk, unit_len, n_units, _ptr(r), _stream(dev)))
     return r
 
 
@@ -353,75 +466,126 @@ def slot_starts(order: torch.Tensor, unit_len: int, rep: int = 1, base: int = 0)
     """kvsel_slot_starts -> delta int64 [G*rep][M]: each unit's start once the
     units are concatenated in ``order`` (int32 [G][M], a permutation per row)."""
     lib = load()
-    if order.dtype != torch.int32 or order.dim() != 2 or not order.is_contiguous():
-        raise KvselError(-2, "order must be contiguous int32 [G][M]")
+    dev = order.device
+    if order.dim() != 2:
+        raise KvselError(ERR_SHAPE, "order must be contiguous int32 [G][M]")
+    _check_tensor(order, order.shape, torch.int32, dev, "order")
     G, M = order.shape
-    delta = torch.empty((G * rep, M), dtype=torch.int64, device=order.device)
+    delta = torch.empty((G * rep, M), dtype=torch.int64, device=dev)
+    _gpu(order=order)
     _check(lib.kvsel_slot_starts(_ptr(order), G, M, unit_len, base, rep, _ptr(delta),
-                                 _stream(order.device)))
+                                 _stream(dev)))
     return delta
 
 
 def gather(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, unit_len: int,
            idx_group: int = 1, src_start: Optional[torch.Tensor] = None, align_base: int = -1,
            rope_base: float = 10000.0, style: str = "half",
-           proxy_k: Optional[torch.Tensor] = None, proxy_v: Optional[torch.Tensor] = None):
+           proxy_k: Optional[torch.Tensor] = None, proxy_v: Optional[torch.Tensor] = None,
+           *, k_out=None, v_out=None):
     """kvsel_gather -> (k_dst, v_dst): compact, or nested with a proxy cache.
     ``k`` / ``v`` may be pinned host tensors (a host-resident cache); the
     outputs are on the device of ``idx``."""
     lib = load()
-    B, N, H, D = k.shape
-    kk = idx.shape[1]
+    kc = cache_desc(k)
     dev = idx.device
+    _source_device(k, dev, "k")
+    if v is not None:
+        _check_like(v, k, "v")
+    B, N, H, D = k.shape
+    if unit_len < 1 or N % unit_len:
+        raise KvselError(ERR_SHAPE, f"unit_len {unit_len} must divide N={N}")
+    kk = _check_idx(idx, B, idx_group, dev)
+    if src_start is not None:
+        _check_tensor(src_start, (N // unit_len,), torch.int64, dev, "src_start")
+    pdesc = None
+    if proxy_k is not None:
+        pdesc = ctypes.pointer(cache_desc(proxy_k))
+        _same_device(proxy_k, dev, "proxy_k")
+        if (proxy_v is None) != (v is None):
+            raise KvselError(ERR_NULL, "proxy_v must be given exactly when v is")
+        if proxy_v is not None:
+            _check_like(proxy_v, proxy_k, "proxy_v", "proxy_k")
     rows = kk * unit_len + (proxy_k.shape[1] if proxy_k is not None else 0)
-    kd = torch.empty((B, rows, H, D), dtype=k.dtype, device=dev)
-    vd = torch.empty_like(kd) if v is not None else None
-    pdesc = ctypes.pointer(cache_desc(proxy_k)) if proxy_k is not None else None
-    _check(lib.kvsel_gather(_ptr(k), _ptr(v), cache_desc(k), unit_len, _ptr(idx), kk, idx_group,
+    kd = _out(k_out, (B, rows, H, D), k.dtype, dev, "k_out")
+    vd = _out(v_out, (B, rows, H, D), k.dtype, dev, "v_out") if v is not None else None
+    _gpu(idx=idx)
+    _check(lib.kvsel_gather(_ptr(k), _ptr(v), kc, unit_len, _ptr(idx), kk, idx_group,
                             _ptr(src_start), align_base, rope_base, ROPE[style], _ptr(proxy_k),
                             _ptr(proxy_v), pdesc, _ptr(kd), _ptr(vd), _stream(dev)))
     return kd, vd
 
 
+def _segments(q: torch.Tensor, pairs: Sequence[Tuple[torch.Tensor, torch.Tensor]], name: str):
+    """ctypes segment array of (k, v) pairs that the query block q attends."""
+    for i, (kk, vv) in enumerate(pairs):
+        cache_desc(kk)
+        k0 = pairs[0][0]
+        if (kk.shape[0], kk.shape[2], kk.shape[3], kk.dtype) != \
+                (k0.shape[0], k0.shape[2], k0.shape[3], k0.dtype):
+            raise KvselError(ERR_SHAPE, f"{name}: segments must share B, H, D and dtype")
+        _check_like(vv, kk, f"{name}[{i}] v", f"{name}[{i}] k")
+        _same_device(kk, q.device, f"{name}[{i}] k")
+        _check_query(q, kk)
+    return (Segment * max(1, len(pairs)))(*[Segment(kk.data_ptr(), vv.data_ptr(), cache_desc(kk))
+                                            for kk, vv in pairs])
+
+
 def decode_attn(q: torch.Tensor, segments: Sequence[Tuple[torch.Tensor, torch.Tensor]],
-                scale: Optional[float] = None, want_lse: bool = True):
+                scale: Optional[float] = None, want_lse: bool = True, *, out=None, lse_out=None,
+                ws=None):
     """kvsel_decode_attn -> (o fp32 [B][T][Hq][D], lse [B][Hq][T] or None)."""
     lib = load()
+    if not segments:
+        raise KvselError(ERR_SHAPE, "decode_attn needs at least one segment")
+    segs = _segments(q, segments, "segments")
     B, T, Hq, D = q.shape
-    scale = 1.0 / D ** 0.5 if scale is None else scale
-    segs = (Segment * len(segments))(*[Segment(kk.data_ptr(), vv.data_ptr(), cache_desc(kk))
-                                       for kk, vv in segments])
+    dev = q.device
     need = lib.kvsel_decode_workspace(T, Hq, segs, len(segments))
-    ws = _workspace(need, q.device)
-    out = _empty((B, T, Hq, D), q.device)
-    lse = _empty((B, Hq, T), q.device) if want_lse else None
-    _check(lib.kvsel_decode_attn(_ptr(q), T, Hq, scale, segs, len(segments), _ptr(out), _ptr(lse),
-                                 _ptr(ws), need, _stream(q.device)))
-    return out, lse
+    ws = _workspace(need, dev, ws)
+    o = _out(out, (B, T, Hq, D), torch.float32, dev, "out")
+    lse = _out(lse_out, (B, Hq, T), torch.float32, dev, "lse") if want_lse else None
+    _gpu(q=q)
+    _check(lib.kvsel_decode_attn(_ptr(q), T, Hq, _scale(scale, D), segs, len(segments), _ptr(o),
+                                 _ptr(lse), _ptr(ws), _nbytes(ws), _stream(dev)))
+    return o, lse
 
 
 def gather_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                   unit_len: int, idx_group: int = 1,
                   extra: Sequence[Tuple[torch.Tensor, torch.Tensor]] = (),
-                  scale: Optional[float] = None, want_lse: bool = True):
+                  scale: Optional[float] = None, want_lse: bool = True, *, k_out=None,
+                  v_out=None, out=None, lse_out=None, ws=None):
     """kvsel_gather_decode -> (k_dst, v_dst, o, lse): the compact cache of the
     kept units and one attention pass over ``extra`` segments plus that cache."""
     lib = load()
+    kc = cache_desc(k)
+    dev = q.device
+    _source_device(k, dev, "k")
+    _check_like(v, k, "v")
+    _check_query(q, k, same_device=False)
     B, T, Hq, D = q.shape
     _, N, H, _ = k.shape
-    kk = idx.shape[1]
-    scale = 1.0 / D ** 0.5 if scale is None else scale
-    kd = torch.empty((B, kk * unit_len, H, D), dtype=k.dtype, device=q.device)
-    vd = torch.empty_like(kd)
+    if unit_len < 1 or N % unit_len:
+        raise KvselError(ERR_SHAPE, f"unit_len {unit_len} must divide N={N}")
+    kk = _check_idx(idx, B, idx_group, dev)
     n_extra = len(extra)
-    segs = (Segment * max(1, n_extra))(*[Segment(a.data_ptr(), b.data_ptr(), cache_desc(a))
-                                         for a, b in extra])
-    kc = cache_desc(k)
+    segs = _segments(q, extra, "extra")
+    kd = _out(k_out, (B, kk * unit_len, H, D), k.dtype, dev, "k_out")
+    vd = _out(v_out, (B, kk * unit_len, H, D), k.dtype, dev, "v_out")
     need = lib.kvsel_gather_decode_workspace(T, Hq, kc, unit_len, kk, segs, n_extra)
-    ws = _workspace(need, q.device)
-    out = _empty((B, T, Hq, D), q.device)
-    lse = _empty((B, Hq, T), q.device) if want_lse else None
-    _check(lib.kvsel_gather_decode(_ptr(q), T, Hq, scale, _ptr(k), _ptr(v), kc, unit_len,
-                                   _ptr(idx), kk, idx_group, _ptr(kd), _ptr(vd), segs, n_extra,
-                                   _ptr(out), _ptr(lse), _ptr(ws), need, _stream(q.device)))
-    return kd, vd, out, lse
+    ws = _workspace(need, dev, ws)
+    o = _out(out, (B, T, Hq, D), torch.float32, dev, "out")
+    lse = _out(lse_out, (B, Hq, T), torch.float32, dev, "lse") if want_lse else None
+    _gpu(q=q)
+    _check(lib.kvsel_gather_decode(_ptr(q), T, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc,
+                                   unit_len, _ptr(idx), kk, idx_group, _ptr(kd), _ptr(vd), segs,
+                                   n_extra, _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                   _stream(dev)))
+    return kd, vd, o, lse
+
+
+def workspace_bytes(call: str, *args) -> int:
+    """The library's workspace query of a call (e.g. ``"gather_decode"``), for
+    callers that allocate a workspace once and pass it to every step."""
+    return int(getattr(load(), f"kvsel_{call}_workspace")(*args))

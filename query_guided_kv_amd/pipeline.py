@@ -84,6 +84,12 @@ class Path:
     partials, row statistics derived inside the aggregate call).  ``marks``
     maps a stage name to a (start, end) pair of torch.cuda.Event recorded on
     the launch stream around that stage.
+
+    Outputs and workspaces are allocated by the first call and reused by every
+    later one: a step allocates nothing after the first, so a loop of steps
+    makes no allocator calls and a step captured as a HIP graph replays into
+    the same buffers.  The returned tensors are those buffers: the next call
+    overwrites them (clone what must outlive it).
     """
 
     STAGES = ("score", "aggregate", "topk", "gather", "decode", "gather_decode")
@@ -109,10 +115,19 @@ class Path:
         self.stages = tuple(s for s in self.STAGES
                             if (s not in ("gather", "decode") or split)
                             and (s != "gather_decode" or (w.decode and not split)))
+        self.buf = {}                                   # outputs kept across calls
+        self.ws = {s: K.Workspace() for s in ("score", "aggregate", "decode")}
+
+    def _keep(self, *pairs):
+        """Record the outputs a call allocated (first call) or filled."""
+        for name, t in pairs:
+            if t is not None:
+                self.buf[name] = t
 
     def __call__(self, q: torch.Tensor, marks: dict = None) -> dict:
         w = self.w
         ev = marks or {}
+        b = self.buf
 
         def mark(stage, i):
             pair = ev.get(stage)
@@ -123,13 +138,19 @@ class Path:
         k_score = self.k if self.k_rep is None else self.k_rep
 
         def score(stats: bool, partials: bool):
+            outs = dict(rm_out=b.get("row_max"), rs_out=b.get("row_sum"),
+                        part_out=b.get("part"), ws=self.ws["score"])
             # re-positioning happens inside the scoring call (one read of K)
             if self.delta is None:
-                return K.score(q, self.k, w.unit_len, w.scale, row_stats=stats, partials=partials)
-            return K.score_reposition(q, self.k, self.delta, self.delta_len, w.unit_len,
-                                      k_out=self.k_rep, scale=w.scale, row_stats=stats,
-                                      partials=partials, rope_base=w.rope_base,
-                                      style=w.rope_style)
+                res = K.score(q, self.k, w.unit_len, w.scale, row_stats=stats,
+                              partials=partials, **outs)
+            else:
+                res = K.score_reposition(q, self.k, self.delta, self.delta_len, w.unit_len,
+                                         k_out=self.k_rep, scale=w.scale, row_stats=stats,
+                                         partials=partials, rope_base=w.rope_base,
+                                         style=w.rope_style, **outs)
+            self._keep(*zip(("row_max", "row_sum", "part"), res))
+            return res
 
         if self.k_rep is not None:
             out["k_rep"] = self.k_rep
@@ -139,7 +160,8 @@ class Path:
             mark("score", 1)
             mark("aggregate", 0)
             out["unit_score"] = K.aggregate(w.unit_len, w.group, "mass", part=part,
-                                            cache_shape=tuple(k_score.shape), q=q)
+                                            cache_shape=tuple(k_score.shape), q=q,
+                                            out=b.get("unit_score"), ws=self.ws["aggregate"])
             mark("aggregate", 1)
         else:
             mark("score", 0)
@@ -147,27 +169,32 @@ class Path:
             mark("score", 1)
             mark("aggregate", 0)
             out["unit_score"] = K.aggregate(w.unit_len, w.group, w.signal, q=q, k=k_score,
-                                            v=self.v, row_max=rm, row_sum=rs, scale=w.scale)
+                                            v=self.v, row_max=rm, row_sum=rs, scale=w.scale,
+                                            out=b.get("unit_score"), ws=self.ws["aggregate"])
             mark("aggregate", 1)
         mark("topk", 0)
-        out["idx"] = K.topk(out["unit_score"], w.k)
+        out["idx"] = K.topk(out["unit_score"], w.k, idx_out=b.get("idx"))
         mark("topk", 1)
+        self._keep(("unit_score", out["unit_score"]), ("idx", out["idx"]))
         if not w.decode:
             return out
+        gouts = dict(k_out=b.get("k_gather"), v_out=b.get("v_gather"))
+        douts = dict(out=b.get("o"), lse_out=b.get("lse"), ws=self.ws["decode"])
         if self.split:
             # the copy (re-positioned for "align"), then attention over it
             mark("gather", 0)
             if w.align:
                 gk, gv = K.gather(self.k, self.v, out["idx"], w.unit_len, w.group, align_base=0,
-                                  rope_base=w.rope_base, style=w.rope_style)
+                                  rope_base=w.rope_base, style=w.rope_style, **gouts)
             elif w.refill_interval:     # ACRE: L1 entry j -> its L2 block
-                gk, gv = K.gather(self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group)
+                gk, gv = K.gather(self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group,
+                                  **gouts)
             else:
-                gk, gv = K.gather(k_score, self.v, out["idx"], w.unit_len, w.group)
+                gk, gv = K.gather(k_score, self.v, out["idx"], w.unit_len, w.group, **gouts)
             mark("gather", 1)
             mark("decode", 0)
             segs = [(self.k, self.v), (gk, gv)] if w.refill_interval else [(gk, gv)]
-            out["o"], out["lse"] = K.decode_attn(q, segs, w.scale)
+            out["o"], out["lse"] = K.decode_attn(q, segs, w.scale, **douts)
             mark("decode", 1)
         else:
             # refill and attention in one pass over the kept rows
@@ -175,13 +202,15 @@ class Path:
             if w.refill_interval:       # ACRE: L1 entry j -> its L2 block, L1 kept as a segment
                 gk, gv, o, lse = K.gather_decode(q, self.l2[0], self.l2[1], out["idx"],
                                                  w.refill_interval, w.group,
-                                                 extra=[(self.k, self.v)], scale=w.scale)
+                                                 extra=[(self.k, self.v)], scale=w.scale,
+                                                 **gouts, **douts)
             else:
                 gk, gv, o, lse = K.gather_decode(q, k_score, self.v, out["idx"], w.unit_len,
-                                                 w.group, scale=w.scale)
+                                                 w.group, scale=w.scale, **gouts, **douts)
             mark("gather_decode", 1)
             out["o"], out["lse"] = o, lse
         out["k_gather"], out["v_gather"] = gk, gv
+        self._keep(("k_gather", gk), ("v_gather", gv), ("o", out["o"]), ("lse", out["lse"]))
         return out
 
 

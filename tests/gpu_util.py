@@ -7,7 +7,12 @@ import sys
 import numpy as np
 import torch
 
+from oracle import pipeline as OP
 from oracle.pipeline import to64
+
+# relative gap the oracle must show at a top-k cut before index sets are
+# compared bit for bit (a smaller one makes the case invalid, not passed)
+MARGIN = 1e-2
 
 
 def device() -> torch.device:
@@ -49,3 +54,25 @@ def assert_rel(got, want, rel: float, atol: float = 0.0, what: str = ""):
     bound = rel * np.abs(w) + atol
     bad = err > bound
     assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside rel {rel} (worst {float(np.max(err - bound)):.3g})"
+
+
+def check_against_oracle(w, got: dict, want: dict, planted=None):
+    for g, m in enumerate(want["margin"]):
+        assert m >= MARGIN, f"oracle margin {m:.3g} at the cut of group {g}: invalid case"
+    if planted is not None:
+        for g in range(len(planted)):
+            assert np.array_equal(want["idx"][g], planted[g]), "oracle misses the planted set"
+    idx = got["idx"].cpu().numpy().astype(np.int64)
+    assert np.array_equal(idx, want["idx"]), "kept index sets differ"
+    assert_rel(got["unit_score"], want["unit_score"], 2e-3, 0.0, "unit_score")
+    if "k_rep" in got:   # kept where later steps read them
+        assert_cache_close(got["k_rep"], want["k_rep"], w.dtype)
+    if not w.decode:
+        return
+    if w.align:
+        assert_cache_close(got["k_gather"], want["k_gather"], w.dtype)
+    else:
+        assert np.array_equal(OP.to64(got["k_gather"]), want["k_gather"]), "gathered keys"
+    assert np.array_equal(OP.to64(got["v_gather"]), want["v_gather"]), "gathered values"
+    assert_rel(got["o"], want["o"], 0.0, 5e-3, "decode output")
+    assert_rel(got["lse"], want["lse"], 0.0, 2e-3, "lse")

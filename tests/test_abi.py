@@ -10,7 +10,7 @@ import re
 
 import pytest
 
-from query_guided_kv_amd import kvsel as K
+from query_guided_kv_amd import abi as K
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvsel.h")
@@ -22,6 +22,11 @@ MISALIGNED = 0x10008
 
 @pytest.fixture(scope="module")
 def lib():
+    # KVSEL_TEST_LIB: another build of the same sources (the host-sanitizer
+    # build runs this file against its own library)
+    path = os.environ.get("KVSEL_TEST_LIB")
+    if path:
+        return K.load(path)
     if not os.path.exists(K.LIB_PATH):
         from query_guided_kv_amd import build
         build.build()
@@ -374,3 +379,23 @@ def test_decode_split_by_path(lib):
     need16 = lib.kvsel_gather_decode_workspace(4, 16, kc, 512, 5, None, 0)
     L16 = mfma_decode_splits(2, 4, 16, rows)
     assert need16 == 2 * 16 * 4 * -(-rows // L16) * (2 + D) * 4
+
+
+def test_scale_must_be_finite_and_positive(lib):
+    # every call below fails validation on its scale alone: nothing is launched
+    p = ctypes.c_void_p(FAKE)
+    kc = cache(B=2, N=1024, H=8, D=128)
+    one = (K.Segment * 1)(K.Segment(FAKE, FAKE, kc))
+    for bad in (0.0, -0.088, float("inf"), float("nan")):
+        assert lib.kvsel_score(p, 1, 32, p, kc, bad, 256, p, p, p, p, 1 << 40, None) == SHAPE
+        assert lib.kvsel_score_reposition(p, 1, 32, p, None, kc, bad, 256, 256, p, 0, 1e4, 0,
+                                          p, p, p, p, 1 << 40, None) == SHAPE
+        assert lib.kvsel_score_units(p, 32, 28, p, cache(B=2, N=2048, H=4), bad, 512, p, 3, None,
+                                     0, 1e4, 0, p, p, p, p, 1 << 40, None) == SHAPE
+        assert lib.kvsel_aggregate(p, 1, 32, p, p, kc, bad, p, p, p, 0, 256, 1, p, 0, p, 1 << 40,
+                                   None) == SHAPE
+        assert lib.kvsel_index_attn(p, 100, 32, bad, p, p, kc, p, p, None, None) == SHAPE
+        assert lib.kvsel_decode_attn(p, 1, 32, bad, one, 1, p, None, p, 1 << 40, None) == SHAPE
+        assert lib.kvsel_gather_decode(p, 1, 32, bad, p, p, kc, 256, p, 4, 1, p, p, None, 0, p,
+                                       None, p, 1 << 40, None) == SHAPE
+        assert b"scale" in lib.kvsel_last_error()

@@ -188,9 +188,14 @@ def _oracle_request(w, inp, r, score_after_last):
     return res, k
 
 
+MARGIN = 1e-2
+
+
 def _margins_ok(res, w):
     """Well-separated decisions: at every pruning layer the kept minimum and the
-    dropped maximum differ by > 1e-4 relative (and the final totals too for "sort")."""
+    dropped maximum differ by >= 1e-2 relative (and the final totals too for
+    "sort"), five times the 2e-3 score tolerance; a smaller gap makes the case
+    invalid, not passed."""
     prune = dict(zip(O.cf_prune_layers(w.layers, w.prune_every),
                      O.cf_keep_schedule(w.M, w.k, w.layers, w.prune_every)))
     for l, keep in prune.items():
@@ -198,10 +203,12 @@ def _margins_ok(res, w):
             continue
         t = np.sort(res["total"][l])[::-1]
         if keep < t.size:
-            assert (t[keep - 1] - t[keep]) / t[keep - 1] > 1e-4, ("near tie at layer", l)
+            m = (t[keep - 1] - t[keep]) / t[keep - 1]
+            assert m >= MARGIN, f"oracle margin {m:.3g} at pruning layer {l}: invalid case"
     if w.allocation == "sort":
         t = np.sort(res["final_total"])
-        assert np.all(np.diff(t) / t[1:] > 1e-4), "near tie in the final order"
+        m = np.min(np.diff(t) / t[1:])
+        assert m >= MARGIN, f"oracle margin {m:.3g} in the final order: invalid case"
 
 
 def _check_request(w, inp, out, trace, r, check_cache=True):
@@ -228,18 +235,24 @@ def _check_request(w, inp, out, trace, r, check_cache=True):
 
 
 BASE = "cachefocus_qwen2_28l_40docs_x512"
+# With a handful of documents of 64-128 rows and 8-32 query rows per kv head,
+# each layer's document mass sums few terms, so the cases plant a steeper
+# relevance ramp (key scale 1.6 - 0.1 * rank) than the full workload's: the
+# decisions then clear the 1e-2 margin (checked on the CPU over 12 seeds).
+STEEP = {"top_scale": 1.6, "scale_step": 0.1}
 PRUNE_CASES = [
     # name, overrides of the full workload
     ("mfma_sort", dict(requests=2, layers=6, prune_every=2, N=8 * 128, unit_len=128, Hq=8, H=2,
-                       T=8, k=2, window=1 << 15)),
+                       T=8, k=2, window=1 << 15, plants=STEEP)),
     ("mfma_align_reused_window", dict(requests=2, layers=4, prune_every=2, N=6 * 128,
                                       unit_len=128, Hq=8, H=2, T=8, k=2, window=3 * 128,
-                                      allocation="align")),
+                                      allocation="align", plants=STEEP)),
     ("mfma_uneven_schedule_d64", dict(requests=3, layers=5, prune_every=2, N=7 * 64, unit_len=64,
-                                      Hq=8, H=2, D=64, T=4, k=2, window=1 << 12)),
+                                      Hq=8, H=2, D=64, T=4, k=2, window=1 << 12, plants=STEEP)),
     ("copy_rows4_sort", dict(requests=2, layers=4, prune_every=2, N=6 * 128, unit_len=128,
-                             Hq=8, H=2, T=2, k=2, window=1 << 15)),
-    ("qwen2_shape_one_request", dict(requests=1, layers=8, prune_every=4, N=12 * 512, k=4)),
+                             Hq=8, H=2, T=2, k=2, window=1 << 15, plants=STEEP)),
+    ("qwen2_shape_one_request", dict(requests=1, layers=8, prune_every=4, N=12 * 512, k=4,
+                                     plants=STEEP)),
 ]
 
 

@@ -13,23 +13,21 @@ same seeded inputs:
 * gathered caches bit-exact (aligned keys: as re-positioned keys);
 * decode outputs within 5e-3 absolute.
 
-Small sizes are checked in full.  The full-size workloads are checked on
-sampled instances (or layers) that the oracle computes one at a time, plus
-properties that hold at any size.
+Small sizes are checked in full here; the full-size InfoFlow-shaped and
+serving workloads are checked on every layer and instance in
+test_gpu_full_infoflow.py and test_gpu_full_serving.py.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import announce, assert_cache_close, assert_rel, device
+from gpu_util import announce, assert_rel, check_against_oracle, device
 from oracle import pipeline as OP
-from query_guided_kv_amd import kvsel as K
 from query_guided_kv_amd import pipeline, synth
 
 pytestmark = pytest.mark.gpu
 
-MARGIN = 1e-2
 
 SMALL = {
     "tiny": lambda: synth.workload("tiny_mha4_d64_fp32_8x128"),
@@ -47,28 +45,6 @@ SMALL = {
         "serving_16req_8l_128k", B=4, requests=2, N=16384, k=8,
         plants={"chunks": 8, "gamma": 1.0, "query_topic": 2.0}),
 }
-
-
-def check_against_oracle(w, got: dict, want: dict, planted=None):
-    for g, m in enumerate(want["margin"]):
-        assert m >= MARGIN, f"oracle margin {m:.3g} at the cut of group {g}: invalid case"
-    if planted is not None:
-        for g in range(len(planted)):
-            assert np.array_equal(want["idx"][g], planted[g]), "oracle misses the planted set"
-    idx = got["idx"].cpu().numpy().astype(np.int64)
-    assert np.array_equal(idx, want["idx"]), "kept index sets differ"
-    assert_rel(got["unit_score"], want["unit_score"], 2e-3, 0.0, "unit_score")
-    if "k_rep" in got:   # kept where later steps read them
-        assert_cache_close(got["k_rep"], want["k_rep"], w.dtype)
-    if not w.decode:
-        return
-    if w.align:
-        assert_cache_close(got["k_gather"], want["k_gather"], w.dtype)
-    else:
-        assert np.array_equal(OP.to64(got["k_gather"]), want["k_gather"]), "gathered keys"
-    assert np.array_equal(OP.to64(got["v_gather"]), want["v_gather"]), "gathered values"
-    assert_rel(got["o"], want["o"], 0.0, 5e-3, "decode output")
-    assert_rel(got["lse"], want["lse"], 0.0, 2e-3, "lse")
 
 
 @pytest.mark.parametrize("name,seed", [("tiny", s) for s in range(5)] +
@@ -232,65 +208,6 @@ def test_full_literal_band(name, plants):
     n_diff = check_band(w, got, want)
     print(f"[literal] {name}: oracle margin {min(want['margin']):.2e}, {n_diff} units differ",
           flush=True)
-
-
-def test_full_infoflow_sampled_layers():
-    """32 layers x 65,536 tokens.  The selection sums all layers; the oracle
-    computes two sampled layers in full, and the summed scores are checked
-    against the per-layer GPU scores (any-size property) and the plants."""
-    w = synth.workload("infoflow_32l_64x1024")
-    announce("full", workload=w.name, seed=0)
-    dev = device()
-    inp = synth.generate(w, 0, dev)
-    path = pipeline.Path(w, inp)
-    got = path(inp["q"])
-    torch.cuda.synchronize()
-    # the selection is the planted set, an exact top-k of the GPU's own scores
-    idx = got["idx"].cpu().numpy().astype(np.int64)[0]
-    assert np.array_equal(idx, inp["planted"][0])
-    s = got["unit_score"].cpu().numpy()[0].astype(np.float64)
-    kept = np.zeros(w.N, bool)
-    kept[idx] = True
-    assert s[kept].min() > s[~kept].max() * (1 + MARGIN)
-    # per-layer scores of the GPU (same kernels, group 1) sum to the selection scores
-    rm, rs, _ = K.score(inp["q"], got["k_rep"], 1, w.scale, row_stats=True, partials=False)
-    per_layer = K.aggregate(1, 1, "vnorm", q=inp["q"], k=got["k_rep"], v=inp["v"],
-                            row_max=rm, row_sum=rs, scale=w.scale)
-    torch.cuda.synchronize()
-    assert_rel(per_layer.double().sum(0, keepdim=True).cpu().numpy(), s[None], 1e-4, 0.0,
-               "sum over layers")
-    # two sampled layers against the oracle, in full
-    wl = w.scaled(B=1, group=1)
-    for layer in (0, 23):
-        sub = {key: inp[key][layer:layer + 1] for key in ("q", "k", "v")}
-        want = OP.run(wl, sub)
-        assert_cache_close(got["k_rep"][layer:layer + 1], want["k_rep"], w.dtype)
-        assert_rel(rm[layer:layer + 1], want["row_max"], 2e-3, 2e-3, "row_max")
-        assert_rel(rs[layer:layer + 1], want["row_sum"], 2e-3, 0.0, "row_sum")
-        assert_rel(per_layer[layer:layer + 1], want["unit_score"], 2e-3, 0.0, "layer scores")
-
-
-def test_full_serving_sampled_instances():
-    """16 requests x 8 layers x 131,072 tokens (68.7 GB), the benchmark's
-    launch configuration; the oracle checks sampled instances in full."""
-    w = synth.workload("serving_16req_8l_128k")
-    announce("full", workload=w.name, seed=0)
-    dev = device()
-    inp = synth.generate(w, 0, dev)
-    path = pipeline.Path(w, inp)
-    q = synth.serving_queries(w, inp["topic"], 0, 5, dev)
-    got = path(q)
-    torch.cuda.synchronize()
-    idx = got["idx"].cpu().numpy().astype(np.int64)
-    for b in range(w.B):
-        assert np.array_equal(idx[b], inp["planted"][b]), f"instance {b}"
-    wi = w.scaled(B=1, requests=1)
-    for b in (0, 77, 127):
-        sub = {"q": q[b:b + 1], "k": inp["k"][b:b + 1], "v": inp["v"][b:b + 1]}
-        want = OP.run(wi, sub)
-        one = {key: got[key][b:b + 1] for key in ("idx", "unit_score", "k_gather", "v_gather",
-                                                   "o", "lse")}
-        check_against_oracle(wi, one, want, [inp["planted"][b]])
 
 
 # ---------------------------------------------------------------------------
