@@ -422,7 +422,7 @@ def step_timeline(start, stop, marks, first: str, last: str, step_ms: list,
             "host_launch_ms": {"mean": statistics.mean(host_ms), "max": max(host_ms)}}
 
 
-def time_graph(step, feed, args, rows: int) -> dict:
+def time_graph(step, feed, steps: int, warmup: int, rows: int) -> dict:
     """The step captured once as a HIP graph (torch.cuda.graph) and replayed
     ``args.steps`` times between events: what a serving loop that launches the
     whole path at once would see.  ``step()`` runs the path on its static
@@ -439,73 +439,29 @@ def time_graph(step, feed, args, rows: int) -> dict:
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
-    for i in range(max(args.warmup, 1)):
+    for i in range(max(warmup, 1)):
         if feed is not None:
             feed(i)
         graph.replay()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         if feed is not None:
-            feed(args.warmup + i)
+            feed(warmup + i)
         graph.replay()
     stop.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    log(f"{args.steps} graph replays: {ms:.4f} ms per step")
+    ms = start.elapsed_time(stop) / steps
+    log(f"{steps} graph replays: {ms:.4f} ms per step")
     return {"ms_per_step": ms, "value": rows / (ms * 1e-3),
             "inputs_copied_per_step": feed is not None}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 1 GiB streaming kernel (counter scale reference)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured as one HIP graph and replayed "
-                         "(workloads whose step inputs do not change between steps)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the selection path is data-parallel over independent caches; see the "
-              "sharding notes of the design)", file=sys.stderr)
-        return 2
-    if args.steps < 1 or args.warmup < 0:
-        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
-        return 2
-
+def device_copy_rate(dev) -> float:
+    """The device's own copy rate: 1 GiB read + 1 GiB written per copy, timed
+    on the GPU clock (the path's HBM rate is also given against it)."""
     import torch
-    from query_guided_kv_amd import kvsel as K
-    from query_guided_kv_amd import pipeline, synth
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a visible MI355X GPU", file=sys.stderr)
-        return 2
-    K.load()                                   # fails loudly if the library is missing
-    dev = torch.device("cuda:0")
-    w = synth.workload(args.workload)
-    log(f"workload {w.name}: B={w.B} N={w.N} Hq/H={w.Hq}/{w.H} D={w.D} T={w.T} {w.dtype}")
-
-    if args.copy_probe:
-        # a plain streaming kernel of known size: 1 GiB read, 1 GiB written
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-        log("copy probe: 3 x (1 GiB read + 1 GiB written) done")
-
-    # the device's own copy rate: 1 GiB read + 1 GiB written per
-    # copy, timed on the GPU clock (the path's HBM rate is also given against it)
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -515,40 +471,51 @@ def main() -> int:
         dst.copy_(src)
     b.record()
     torch.cuda.synchronize()
-    copy_GBps = 5 * 2 * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, dst
-    log(f"device copy: {copy_GBps:.0f} GB/s (read + written)")
+    return 5 * 2 * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
 
+
+def host_link_rate(dev) -> dict:
+    """The host link's DMA rate: 1 GiB pinned host -> device, on the GPU clock."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
+    dst = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    return {"dma_copy_GBps": 5 * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9,
+            "peak_GBps": HOST_LINK_GBPS}
+
+
+def measure(w, seed: int, steps: int, warmup: int, graph: bool, copy_GBps: float, dev) -> tuple:
+    """Time ``steps`` steps of workload ``w`` (after ``warmup`` untimed ones)
+    between events on the launch stream, with a (start, end) event pair around
+    every stage; returns (result dict, inputs, rows per step)."""
+    import torch
+    from query_guided_kv_amd import pipeline, synth
+
+    log(f"workload {w.name}: B={w.B} N={w.N} Hq/H={w.Hq}/{w.H} D={w.D} T={w.T} {w.dtype}")
     host_link = None
     if w.l2_host:
-        # the host link's DMA rate: 1 GiB pinned host -> device, timed on the GPU clock
-        src = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
-        dst = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        for _ in range(2):
-            dst.copy_(src, non_blocking=True)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(5):
-            dst.copy_(src, non_blocking=True)
-        b.record()
-        torch.cuda.synchronize()
-        host_link = {"dma_copy_GBps": 5 * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9,
-                     "peak_GBps": HOST_LINK_GBPS}
-        del src, dst
+        host_link = host_link_rate(dev)
         log(f"host link: pinned -> device copy at {host_link['dma_copy_GBps']:.1f} GB/s")
-
     t0 = time.perf_counter()
-    inp = synth.generate(w, args.seed, dev)
+    inp = synth.generate(w, seed, dev)
     torch.cuda.synchronize()
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
     prune = w.recipe == "cachefocus"
     path = pipeline.make_path(w, inp)
+    queries = None
     if prune:
         step = lambda i, m=None: path(inp["q"], inp["q_dec"], m)
     elif w.recompute:
         step = lambda i, m=None: path(inp["q_sel"], m)
     else:
-        queries = make_queries(w, inp, args.warmup + args.steps, args.seed, dev)
+        queries = make_queries(w, inp, warmup + steps, seed, dev)
         step = lambda i, m=None: path(queries[i], m)
 
     # no garbage collection inside the warm-up and timed regions: a collection
@@ -556,46 +523,48 @@ def main() -> int:
     # timed launches leaves the GPU idle (the queue is still empty)
     gc.collect()
     gc.disable()
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"{args.warmup} warm-up steps done")
+    try:
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        log(f"{warmup} warm-up steps done")
+
+        marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for s in path.stages} for _ in range(steps)]
+        if prune:   # the scorer's launches inside the layer loop, one pair per scored layer
+            for mk in marks:
+                mk["score_layers"] = [(torch.cuda.Event(enable_timing=True),
+                                       torch.cuda.Event(enable_timing=True))
+                                      for _ in range(path.n_scored)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # create every event now (torch makes the HIP event on its first
+        # record), so that the timed region only records them
+        for mk in marks:
+            for pairs in mk.values():
+                for pair in (pairs if isinstance(pairs, list) else [pairs]):
+                    for e in pair:
+                        e.record()
+        start.record()
+        stop.record()
+        torch.cuda.synchronize()
+        host_ms = []
+        wall0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            h0 = time.perf_counter()
+            step(warmup + i, marks[i])
+            host_ms.append((time.perf_counter() - h0) * 1e3)
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    finally:
+        gc.enable()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / steps
+    log(f"{steps} timed steps: {total_ms:.2f} ms on the GPU clock, {wall * 1e3:.2f} ms wall")
 
     work = (prune_stage_work(w) if prune else reorder_stage_work(w) if w.reorder
             else recompute_stage_work(w, inp["pos"]) if w.recompute else stage_work(w))
-    marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for s in path.stages} for _ in range(args.steps)]
-    if prune:   # the scorer's launches inside the layer loop, one pair per scored layer
-        for mk in marks:
-            mk["score_layers"] = [(torch.cuda.Event(enable_timing=True),
-                                   torch.cuda.Event(enable_timing=True))
-                                  for _ in range(path.n_scored)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # create every event now (torch makes the HIP event on its first record),
-    # so that the timed region only records them
-    for mk in marks:
-        for pairs in mk.values():
-            for pair in (pairs if isinstance(pairs, list) else [pairs]):
-                for e in pair:
-                    e.record()
-    start.record()
-    stop.record()
-    torch.cuda.synchronize()
-    host_ms = []
-    wall0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        h0 = time.perf_counter()
-        step(args.warmup + i, marks[i])
-        host_ms.append((time.perf_counter() - h0) * 1e3)
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gc.enable()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-    log(f"{args.steps} timed steps: {total_ms:.2f} ms on the GPU clock, {wall * 1e3:.2f} ms wall")
-
     stage_ms = {s: statistics.mean(m[s][0].elapsed_time(m[s][1]) for m in marks)
                 for s in path.stages}
     # per-step times from the first stage's start to the last stage's end
@@ -619,38 +588,28 @@ def main() -> int:
         stage_ms["select_scoring"] = dom_ms
     achieved = quantity / (dom_ms * 1e-3)
     kernel = kernel_of(dom, w)
-    traffic = stored_traffic(kernel, w.name)
     # token-rows scored per step: every cached row once, or for the pruning
     # loop the rows of the documents present at each scored layer
     rows = (w.requests * prune_scored_units(w) * w.unit_len if prune
             else 2 * w.B * w.N if w.reorder
             else work["recompute"][1] // (4 * w.Hq * w.D) if w.recompute else w.B * w.N)
     path_bytes = sum(b for b, _ in work.values())
-
     result = {
-        "metric": "cached KV tokens scored+selected per second",
         "value": rows / (ms_step * 1e-3),
-        "unit": "token-rows/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_step,
         "ms_per_step_median": statistics.median(step_ms),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded, planted relevant units; no datasets or weights)",
         "config": dict({"workload": w.name, "instances": w.B, "cached_rows_per_instance": w.N,
                         "q_heads": w.Hq, "kv_heads": w.H, "head_dim": w.D,
                         "query_tokens": w.T, "unit_len": w.unit_len, "kept_units": w.k,
-                        "seed": args.seed},
+                        "seed": seed},
                        **({"requests": w.requests, "layers": w.layers,
                            "prune_every": w.prune_every, "allocation": w.allocation,
                            "scored_rows_per_step": rows} if prune else {})),
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": traffic, "kernel": kernel,
-                     "stage": dom, "algorithmic_bytes_per_launch": work[dom][0] / launches,
+                     "frac": achieved / peak, "traffic": stored_traffic(kernel, w.name),
+                     "kernel": kernel, "stage": dom,
+                     "algorithmic_bytes_per_launch": work[dom][0] / launches,
                      "algorithmic_flops_per_launch": work[dom][1] / launches,
                      "launches_per_step": launches, "avg_launch_ms": dom_ms / launches},
         "path_hbm": {"algorithmic_bytes_per_step": path_bytes,
@@ -674,23 +633,114 @@ def main() -> int:
                              "unit": "L2 token-rows/s", "l2_tokens_per_l1_entry": w.refill_interval}
     if host_link is not None:
         result["host_link"] = host_link
-    if args.graph:
+    if graph:
         if prune:
-            result["graph"] = time_graph(lambda: path(inp["q"], inp["q_dec"]), None, args, rows)
+            result["graph"] = time_graph(lambda: path(inp["q"], inp["q_dec"]), None, steps,
+                                         warmup, rows)
         elif w.recompute:
-            result["graph"] = time_graph(lambda: path(inp["q_sel"]), None, args, rows)
+            result["graph"] = time_graph(lambda: path(inp["q_sel"]), None, steps, warmup, rows)
         elif w.recipe != "serving":
-            result["graph"] = time_graph(lambda: path(inp["q"]), None, args, rows)
+            result["graph"] = time_graph(lambda: path(inp["q"]), None, steps, warmup, rows)
         else:
             # the captured step reads a static query block; each replay is
             # preceded by a copy of that step's fresh queries into it
             static_q = queries[0].clone()
             result["graph"] = time_graph(lambda: path(static_q),
                                          lambda i: static_q.copy_(queries[i % len(queries)]),
-                                         args, rows)
+                                         steps, warmup, rows)
+    del path
+    return result, inp, rows
+
+
+# Measured beside the default line in the same run: the other bench workloads
+# of the configurations (steps timed, as one line each under "also").
+ALSO = (("acre_bilayer_l1_16k_l2_128k", 200), ("llama2_7b_32docs_x512", 200),
+        ("infoflow_32l_64x1024", 30))
+
+
+def also_entry(res: dict) -> dict:
+    """The summary of one extra workload in the bench line."""
+    keep = ("value", "ms_per_step", "ms_per_step_median", "dtype", "roofline", "stages_ms",
+            "selection", "covered", "graph")
+    out = {k: res[k] for k in keep if k in res}
+    out["workload"] = res["config"]["workload"]
+    out["unit"] = "token-rows/s"
+    out["path_hbm_frac"] = res["path_hbm"]["frac"]
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-also", action="store_true",
+                    help="skip the other workloads measured beside the default one")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB streaming kernel (counter scale reference)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured as one HIP graph and replayed")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the selection path is data-parallel over independent caches; see the "
+              "sharding notes of the design)", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    from query_guided_kv_amd import kvsel as K
+    from query_guided_kv_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible MI355X GPU", file=sys.stderr)
+        return 2
+    K.load()                                   # fails loudly if the library is missing
+    dev = torch.device("cuda:0")
+
+    if args.copy_probe:
+        # a plain streaming kernel of known size: 1 GiB read, 1 GiB written
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy probe: 3 x (1 GiB read + 1 GiB written) done")
+    copy_GBps = device_copy_rate(dev)
+    log(f"device copy: {copy_GBps:.0f} GB/s (read + written)")
+
+    w = synth.workload(args.workload)
+    res, inp, rows = measure(w, args.seed, args.steps, args.warmup, args.graph, copy_GBps, dev)
+    result = dict({"metric": "cached KV tokens scored+selected per second",
+                   "value": res["value"], "unit": "token-rows/s", "n_gpus": 1,
+                   "steps": args.steps, "warmup": args.warmup,
+                   "ms_per_step": res["ms_per_step"],
+                   "ms_per_step_median": res["ms_per_step_median"],
+                   "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                   "dtype": w.dtype,
+                   "data": "synthetic (seeded, planted relevant units; no datasets or weights)"},
+                  **{k: v for k, v in res.items()
+                     if k not in ("value", "ms_per_step", "ms_per_step_median", "dtype")})
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baselines(w, inp, prune)
+        result["cpu_baseline"] = cpu_baselines(w, inp, w.recipe == "cachefocus")
+    del inp
+    if args.workload == DEFAULT_WORKLOAD and not args.no_also:
+        torch.cuda.empty_cache()
+        result["also"] = []
+        for name, steps in ALSO:
+            res_a, inp_a, _ = measure(synth.workload(name), args.seed, steps, 3, True, copy_GBps,
+                                      dev)
+            del inp_a
+            torch.cuda.empty_cache()
+            result["also"].append(also_entry(res_a))
     print(json.dumps(result), flush=True)
     return 0
 

@@ -39,7 +39,20 @@ def assert_cache_close(got: torch.Tensor, want: np.ndarray, dtype: str, ref_norm
     assert g.shape == want.shape, (g.shape, want.shape)
     if dtype == "bf16":
         diff = np.abs(g - want)
-        assert np.all(diff <= bf16_ulp(want) * 1.0001), float(np.max(diff / bf16_ulp(want)))
+        # The oracle rotates twice in fp64 (R(p_new) R(p_old)^T), which leaves an
+        # absolute error of a few 2^-53 of the row's magnitude.  bf16 represents
+        # such tiny values, so where the exact result is 0 (a zero element of a
+        # unit with delta 0, rotated by the identity) the oracle may hold ~1e-17:
+        # that error, bounded by 2^-45 of the row's largest element, is allowed
+        # on top of the one ulp.
+        floor = 2.0 ** -45 * np.abs(want).max(axis=-1, keepdims=True)
+        bad = diff > bf16_ulp(want) * 1.0001 + floor
+        if bad.any():
+            where = np.argwhere(bad)[:8]
+            shown = ", ".join(f"{tuple(int(i) for i in ix)}: got {g[tuple(ix)]!r} want "
+                              f"{want[tuple(ix)]!r}" for ix in where)
+            raise AssertionError(f"{int(bad.sum())} of {bad.size} elements beyond one bf16 ulp "
+                                 f"(worst {float(np.max(diff / bf16_ulp(want))):.4g} ulp); {shown}")
         assert np.mean(g == want) >= 0.999, float(np.mean(g == want))
     else:
         scale = np.abs(want).max(axis=-1, keepdims=True) if ref_norm is None else ref_norm
