@@ -23,7 +23,9 @@
  * --------------------------
  * - Tensor pointers are DEVICE pointers, owned by the caller.  The library
  *   allocates nothing and keeps no state between calls; scratch memory is
- *   passed in as (ws, ws_bytes) and sized by the *_workspace() queries.
+ *   passed in as (ws, ws_bytes) and sized by the *_workspace() queries.  The
+ *   one exception is kvsel_gather_decode_noalloc, whose scratch is a fixed
+ *   array of the library's own device memory (see there).
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *   default stream).  It returns KVSEL_OK once its kernels are enqueued.
  * - Arguments are validated before anything is enqueued.  On a negative status
@@ -469,6 +471,32 @@ size_t kvsel_gather_decode_workspace(int64_t T, int64_t Hq, kvsel_cache kc,
                                      int64_t unit_len, int64_t k,
                                      const kvsel_segment* extra,
                                      int32_t n_extra);
+
+/*
+ * kvsel_gather_decode_noalloc -- for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments and results as kvsel_gather_decode without (ws, ws_bytes):
+ * the split partials live in a fixed array of the library's own device memory,
+ * kvsel_noalloc_scratch_bytes() = 128 MiB per GPU, held from the first use on
+ * that GPU until the process ends.  The call allocates nothing.
+ *   - A shape whose kvsel_gather_decode_workspace() exceeds that size gets
+ *     KVSEL_ERR_WORKSPACE before anything is enqueued (16 requests x 8 layers
+ *     of one-token queries over 64 chunks of 256 tokens needs 65 MiB).
+ *   - The array belongs to the CURRENT device; a stream of another device gets
+ *     KVSEL_ERR_UNSUPPORTED.
+ *   - Every call on one GPU shares its array, which keeps the last call's
+ *     contents: calls that overlap on one GPU (other streams, other host
+ *     threads) race.  Run one at a time per GPU.
+ */
+int kvsel_gather_decode_noalloc(const void* q, int64_t T, int64_t Hq, float scale,
+                                const void* k_src, const void* v_src,
+                                kvsel_cache kc, int64_t unit_len,
+                                const int32_t* idx, int64_t k, int64_t idx_group,
+                                void* k_dst, void* v_dst,
+                                const kvsel_segment* extra, int32_t n_extra,
+                                float* out, float* lse, hipStream_t stream);
+size_t kvsel_noalloc_scratch_bytes(void);
 
 /* Text of a status code; message of the last failed call on this thread. */
 const char* kvsel_status_str(int status);

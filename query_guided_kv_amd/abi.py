@@ -68,6 +68,10 @@ SIGNATURES = {
                                            _P]),
     "kvsel_gather_decode_workspace": (_SZ, [_I64, _I64, Cache, _I64, _I64, ctypes.POINTER(Segment),
                                             _I32]),
+    "kvsel_gather_decode_noalloc": (ctypes.c_int, [_P, _I64, _I64, _F, _P, _P, Cache, _I64, _P,
+                                                   _I64, _I64, _P, _P, ctypes.POINTER(Segment),
+                                                   _I32, _P, _P, _P]),
+    "kvsel_noalloc_scratch_bytes": (_SZ, []),
     "kvsel_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kvsel_last_error": (ctypes.c_char_p, []),
     "kvsel_version": (ctypes.c_int, []),

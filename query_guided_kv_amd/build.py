@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvsel.so")
 
 SOURCES = ["api.cpp", "reposition.hip", "score.hip", "score_mfma.hip", "aggregate.hip",
-           "aggregate_mfma.hip", "topk.hip", "gather.hip", "decode.hip", "index_attn.hip"]
+           "aggregate_mfma.hip", "topk.hip", "gather.hip", "decode.hip", "index_attn.hip", "noalloc.hip"]
 
 ARCH = os.environ.get("KVSEL_ARCH", "gfx950")
 

@@ -585,6 +585,39 @@ def gather_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     return kd, vd, o, lse
 
 
+def gather_decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                          unit_len: int, idx_group: int = 1,
+                          extra: Sequence[Tuple[torch.Tensor, torch.Tensor]] = (),
+                          scale: Optional[float] = None, want_lse: bool = True, *, k_out=None,
+                          v_out=None, out=None, lse_out=None):
+    """kvsel_gather_decode_noalloc -> (k_dst, v_dst, o, lse): kvsel_gather_decode
+    with its scratch in the library's fixed device array (the call allocates
+    nothing; pass every output to allocate nothing here either)."""
+    lib = load()
+    kc = cache_desc(k)
+    dev = q.device
+    _source_device(k, dev, "k")
+    _check_like(v, k, "v")
+    _check_query(q, k, same_device=False)
+    B, T, Hq, D = q.shape
+    _, N, H, _ = k.shape
+    if unit_len < 1 or N % unit_len:
+        raise KvselError(ERR_SHAPE, f"unit_len {unit_len} must divide N={N}")
+    kk = _check_idx(idx, B, idx_group, dev)
+    n_extra = len(extra)
+    segs = _segments(q, extra, "extra")
+    kd = _out(k_out, (B, kk * unit_len, H, D), k.dtype, dev, "k_out")
+    vd = _out(v_out, (B, kk * unit_len, H, D), k.dtype, dev, "v_out")
+    o = _out(out, (B, T, Hq, D), torch.float32, dev, "out")
+    lse = _out(lse_out, (B, Hq, T), torch.float32, dev, "lse") if want_lse else None
+    _gpu(q=q)
+    _check(lib.kvsel_gather_decode_noalloc(_ptr(q), T, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc,
+                                           unit_len, _ptr(idx), kk, idx_group, _ptr(kd),
+                                           _ptr(vd), segs, n_extra, _ptr(o), _ptr(lse),
+                                           _stream(dev)))
+    return kd, vd, o, lse
+
+
 def workspace_bytes(call: str, *args) -> int:
     """The library's workspace query of a call (e.g. ``"gather_decode"``), for
     callers that allocate a workspace once and pass it to every step."""
