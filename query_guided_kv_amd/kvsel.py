@@ -37,6 +37,39 @@ def _check(rc: int) -> None:
         raise KvselError(rc, f"{lib.kvsel_status_str(rc).decode()}: {lib.kvsel_last_error().decode()}")
 
 
+_recorder: Optional[list] = None
+
+
+def _invoke(fn, *args) -> None:
+    """Call a library entry point with its marshalled arguments (recorded
+    first when a :class:`Recording` is active) and check the status."""
+    if _recorder is not None:
+        _recorder.append((fn, args))
+    _check(fn(*args))
+
+
+class Recording:
+    """Collects the (entry point, arguments) of every library call made inside
+    the ``with`` block, so that a caller whose arguments stay the same can
+    replay them with :func:`replay`, skipping the checks that already passed."""
+
+    def __enter__(self) -> list:
+        global _recorder
+        self._prev, self.calls = _recorder, []
+        _recorder = self.calls
+        return self.calls
+
+    def __exit__(self, *exc) -> None:
+        global _recorder
+        _recorder = self._prev
+
+
+def replay(calls: list) -> None:
+    """Make the recorded library calls again, with the same arguments."""
+    for fn, args in calls:
+        _check(fn(*args))
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -217,8 +250,8 @@ def reposition(k: torch.Tensor, delta: torch.Tensor, unit_len: int,
     else:
         _check_like(out, k, "out")
     _gpu(k=k, delta=delta, out=out)
-    _check(lib.kvsel_reposition(_ptr(k), _ptr(out), kc, unit_len, _ptr(delta), per,
-                                rope_base, ROPE[style], _stream(dev)))
+    _invoke(lib.kvsel_reposition, _ptr(k), _ptr(out), kc, unit_len, _ptr(delta), per,
+                                rope_base, ROPE[style], _stream(dev))
     return out
 
 
@@ -245,8 +278,8 @@ def score(q: torch.Tensor, k: torch.Tensor, unit_len: int, scale: Optional[float
     need = lib.kvsel_score_workspace(B, N, Hq, T, unit_len, int(row_stats), int(partials))
     ws = _workspace(need, dev, ws)
     _gpu(q=q, k=k)
-    _check(lib.kvsel_score(_ptr(q), T, Hq, _ptr(k), kc, _scale(scale, D), unit_len, _ptr(rm),
-                           _ptr(rs), _ptr(part), _ptr(ws), _nbytes(ws), _stream(dev)))
+    _invoke(lib.kvsel_score, _ptr(q), T, Hq, _ptr(k), kc, _scale(scale, D), unit_len, _ptr(rm),
+                           _ptr(rs), _ptr(part), _ptr(ws), _nbytes(ws), _stream(dev))
     return rm, rs, part
 
 
@@ -276,10 +309,10 @@ def score_reposition(q: torch.Tensor, k: torch.Tensor, delta: torch.Tensor, rot_
                                                 int(k_out is not None))
     ws = _workspace(need, dev, ws)
     _gpu(q=q, k=k)
-    _check(lib.kvsel_score_reposition(_ptr(q), T, Hq, _ptr(k), _ptr(k_out), kc, _scale(scale, D),
+    _invoke(lib.kvsel_score_reposition, _ptr(q), T, Hq, _ptr(k), _ptr(k_out), kc, _scale(scale, D),
                                       unit_len, rot_unit_len, _ptr(delta), per, rope_base,
                                       ROPE[style], _ptr(rm), _ptr(rs), _ptr(part), _ptr(ws),
-                                      _nbytes(ws), _stream(dev)))
+                                      _nbytes(ws), _stream(dev))
     return rm, rs, part
 
 
@@ -305,10 +338,10 @@ def score_units(q: torch.Tensor, k: torch.Tensor, units: torch.Tensor, unit_len:
     need = lib.kvsel_score_units_workspace(T, Hq, kc, unit_len, n, int(row_stats), int(partials))
     ws = _workspace(need, dev, ws)
     _gpu(q=q, k=k)
-    _check(lib.kvsel_score_units(_ptr(q), T, Hq, _ptr(k), kc, _scale(scale, D), unit_len,
+    _invoke(lib.kvsel_score_units, _ptr(q), T, Hq, _ptr(k), kc, _scale(scale, D), unit_len,
                                  _ptr(units), n, _ptr(delta), per, rope_base, ROPE[style],
                                  _ptr(rm), _ptr(rs), _ptr(part), _ptr(ws), _nbytes(ws),
-                                 _stream(dev)))
+                                 _stream(dev))
     return rm, rs, part
 
 
@@ -366,10 +399,10 @@ def aggregate(unit_len: int, group: int = 1, signal: str = "mass", *,
     need = lib.kvsel_aggregate_workspace(B, N, Hq, T, unit_len, int(chunk), int(row_max is not None))
     ws = _workspace(need, dev, ws)
     _gpu(out=out, part=part, k=k)
-    _check(lib.kvsel_aggregate(_ptr(q), T, Hq, _ptr(k), _ptr(v), kc, _scale(scale, D),
+    _invoke(lib.kvsel_aggregate, _ptr(q), T, Hq, _ptr(k), _ptr(v), kc, _scale(scale, D),
                                _ptr(row_max), _ptr(row_sum), _ptr(part), SIGNAL[signal], unit_len,
                                group, _ptr(out), int(accumulate), _ptr(ws), _nbytes(ws),
-                               _stream(dev)))
+                               _stream(dev))
     return out
 
 
@@ -389,7 +422,7 @@ def topk(scores: torch.Tensor, k: int, values: bool = False, *, idx_out=None, va
     idx = _out(idx_out, (G, k), torch.int32, dev, "idx")
     val = _out(val_out, (G, k), torch.float32, dev, "val") if values else None
     _gpu(scores=scores)
-    _check(lib.kvsel_topk(_ptr(scores), G, M, k, _ptr(idx), _ptr(val), _stream(dev)))
+    _invoke(lib.kvsel_topk, _ptr(scores), G, M, k, _ptr(idx), _ptr(val), _stream(dev))
     return (idx, val) if values else idx
 
 
@@ -405,7 +438,7 @@ def take(src: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
     kk = idx.shape[1]
     out = torch.empty((G, kk), dtype=torch.int32, device=dev)
     _gpu(src=src)
-    _check(lib.kvsel_take(_ptr(src), G, m, _ptr(idx), kk, _ptr(out), _stream(dev)))
+    _invoke(lib.kvsel_take, _ptr(src), G, m, _ptr(idx), kk, _ptr(out), _stream(dev))
     return out
 
 
@@ -423,8 +456,8 @@ def order(scores: torch.Tensor, idx: torch.Tensor, descending: bool = True,
     out = torch.empty((G, kk), dtype=torch.int32, device=dev)
     val = torch.empty((G, kk), dtype=torch.float32, device=dev) if values else None
     _gpu(scores=scores)
-    _check(lib.kvsel_order(_ptr(scores), G, M, _ptr(idx), kk, int(descending), _ptr(out),
-                           _ptr(val), _stream(dev)))
+    _invoke(lib.kvsel_order, _ptr(scores), G, M, _ptr(idx), kk, int(descending), _ptr(out),
+                           _ptr(val), _stream(dev))
     return (out, val) if values else out
 
 
@@ -442,8 +475,8 @@ def index_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Ten
     out = torch.empty((B, S, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if want_lse else None
     _gpu(q=q, k=k)
-    _check(lib.kvsel_index_attn(_ptr(q), S, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc, _ptr(pos),
-                                _ptr(out), _ptr(lse), _stream(dev)))
+    _invoke(lib.kvsel_index_attn, _ptr(q), S, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc, _ptr(pos),
+                                _ptr(out), _ptr(lse), _stream(dev))
     return out, lse
 
 
@@ -458,7 +491,7 @@ def unit_fractions(sel: torch.Tensor, unit_len: int, n_units: int) -> torch.Tens
     G, kk = sel.shape
     r = torch.empty((G, n_units), dtype=torch.float32, device=dev)
     _gpu(sel=sel)
-    _check(lib.kvsel_unit_fractions(_ptr(sel), G, kk, unit_len, n_units, _ptr(r), _stream(dev)))
+    _invoke(lib.kvsel_unit_fractions, _ptr(sel), G, kk, unit_len, n_units, _ptr(r), _stream(dev))
     return r
 
 
@@ -473,8 +506,8 @@ def slot_starts(order: torch.Tensor, unit_len: int, rep: int = 1, base: int = 0)
     G, M = order.shape
     delta = torch.empty((G * rep, M), dtype=torch.int64, device=dev)
     _gpu(order=order)
-    _check(lib.kvsel_slot_starts(_ptr(order), G, M, unit_len, base, rep, _ptr(delta),
-                                 _stream(dev)))
+    _invoke(lib.kvsel_slot_starts, _ptr(order), G, M, unit_len, base, rep, _ptr(delta),
+                                 _stream(dev))
     return delta
 
 
@@ -510,9 +543,9 @@ def gather(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, unit_l
     kd = _out(k_out, (B, rows, H, D), k.dtype, dev, "k_out")
     vd = _out(v_out, (B, rows, H, D), k.dtype, dev, "v_out") if v is not None else None
     _gpu(idx=idx)
-    _check(lib.kvsel_gather(_ptr(k), _ptr(v), kc, unit_len, _ptr(idx), kk, idx_group,
+    _invoke(lib.kvsel_gather, _ptr(k), _ptr(v), kc, unit_len, _ptr(idx), kk, idx_group,
                             _ptr(src_start), align_base, rope_base, ROPE[style], _ptr(proxy_k),
-                            _ptr(proxy_v), pdesc, _ptr(kd), _ptr(vd), _stream(dev)))
+                            _ptr(proxy_v), pdesc, _ptr(kd), _ptr(vd), _stream(dev))
     return kd, vd
 
 
@@ -546,8 +579,8 @@ def decode_attn(q: torch.Tensor, segments: Sequence[Tuple[torch.Tensor, torch.Te
     o = _out(out, (B, T, Hq, D), torch.float32, dev, "out")
     lse = _out(lse_out, (B, Hq, T), torch.float32, dev, "lse") if want_lse else None
     _gpu(q=q)
-    _check(lib.kvsel_decode_attn(_ptr(q), T, Hq, _scale(scale, D), segs, len(segments), _ptr(o),
-                                 _ptr(lse), _ptr(ws), _nbytes(ws), _stream(dev)))
+    _invoke(lib.kvsel_decode_attn, _ptr(q), T, Hq, _scale(scale, D), segs, len(segments), _ptr(o),
+                                 _ptr(lse), _ptr(ws), _nbytes(ws), _stream(dev))
     return o, lse
 
 
@@ -578,10 +611,10 @@ def gather_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     o = _out(out, (B, T, Hq, D), torch.float32, dev, "out")
     lse = _out(lse_out, (B, Hq, T), torch.float32, dev, "lse") if want_lse else None
     _gpu(q=q)
-    _check(lib.kvsel_gather_decode(_ptr(q), T, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc,
+    _invoke(lib.kvsel_gather_decode, _ptr(q), T, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc,
                                    unit_len, _ptr(idx), kk, idx_group, _ptr(kd), _ptr(vd), segs,
                                    n_extra, _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws),
-                                   _stream(dev)))
+                                   _stream(dev))
     return kd, vd, o, lse
 
 
@@ -611,10 +644,10 @@ def gather_decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx
     o = _out(out, (B, T, Hq, D), torch.float32, dev, "out")
     lse = _out(lse_out, (B, Hq, T), torch.float32, dev, "lse") if want_lse else None
     _gpu(q=q)
-    _check(lib.kvsel_gather_decode_noalloc(_ptr(q), T, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc,
+    _invoke(lib.kvsel_gather_decode_noalloc, _ptr(q), T, Hq, _scale(scale, D), _ptr(k), _ptr(v), kc,
                                            unit_len, _ptr(idx), kk, idx_group, _ptr(kd),
                                            _ptr(vd), segs, n_extra, _ptr(o), _ptr(lse),
-                                           _stream(dev)))
+                                           _stream(dev))
     return kd, vd, o, lse
 
 

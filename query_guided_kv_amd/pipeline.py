@@ -117,6 +117,12 @@ class Path:
                             and (s != "gather_decode" or (w.decode and not split)))
         self.buf = {}                                   # outputs kept across calls
         self.ws = {s: K.Workspace() for s in ("score", "aggregate", "decode")}
+        # Launch plans: each call site's library calls, as marshalled on its
+        # first run, are made again as they are while the query block (its
+        # address and shape) and the stream stay the same: every other
+        # argument is this object's own input or buffer.  A short step is
+        # otherwise bound by the host time of the argument checks.
+        self.plans = {}
 
     def _keep(self, *pairs):
         """Record the outputs a call allocated (first call) or filled."""
@@ -128,11 +134,22 @@ class Path:
         w = self.w
         ev = marks or {}
         b = self.buf
+        key = (q.data_ptr(), tuple(q.shape), torch.cuda.current_stream(q.device).cuda_stream)
 
         def mark(stage, i):
             pair = ev.get(stage)
             if pair is not None:
                 pair[i].record()
+
+        def planned(site, fn):
+            plan = self.plans.get(site)
+            if plan is not None and plan[0] == key:
+                K.replay(plan[1])
+                return plan[2]
+            with K.Recording() as calls:
+                res = fn()
+            self.plans[site] = (key, calls, res)
+            return res
 
         out = {}
         k_score = self.k if self.k_rep is None else self.k_rep
@@ -156,24 +173,24 @@ class Path:
             out["k_rep"] = self.k_rep
         if self.chunk:
             mark("score", 0)
-            _, _, part = score(False, True)
+            _, _, part = planned("score", lambda: score(False, True))
             mark("score", 1)
             mark("aggregate", 0)
-            out["unit_score"] = K.aggregate(w.unit_len, w.group, "mass", part=part,
-                                            cache_shape=tuple(k_score.shape), q=q,
-                                            out=b.get("unit_score"), ws=self.ws["aggregate"])
+            out["unit_score"] = planned("aggregate", lambda: K.aggregate(
+                w.unit_len, w.group, "mass", part=part, cache_shape=tuple(k_score.shape), q=q,
+                out=b.get("unit_score"), ws=self.ws["aggregate"]))
             mark("aggregate", 1)
         else:
             mark("score", 0)
-            rm, rs, _ = score(True, False)
+            rm, rs, _ = planned("score", lambda: score(True, False))
             mark("score", 1)
             mark("aggregate", 0)
-            out["unit_score"] = K.aggregate(w.unit_len, w.group, w.signal, q=q, k=k_score,
-                                            v=self.v, row_max=rm, row_sum=rs, scale=w.scale,
-                                            out=b.get("unit_score"), ws=self.ws["aggregate"])
+            out["unit_score"] = planned("aggregate", lambda: K.aggregate(
+                w.unit_len, w.group, w.signal, q=q, k=k_score, v=self.v, row_max=rm, row_sum=rs,
+                scale=w.scale, out=b.get("unit_score"), ws=self.ws["aggregate"]))
             mark("aggregate", 1)
         mark("topk", 0)
-        out["idx"] = K.topk(out["unit_score"], w.k, idx_out=b.get("idx"))
+        out["idx"] = planned("topk", lambda: K.topk(out["unit_score"], w.k, idx_out=b.get("idx")))
         mark("topk", 1)
         self._keep(("unit_score", out["unit_score"]), ("idx", out["idx"]))
         if not w.decode:
@@ -184,29 +201,32 @@ class Path:
             # the copy (re-positioned for "align"), then attention over it
             mark("gather", 0)
             if w.align:
-                gk, gv = K.gather(self.k, self.v, out["idx"], w.unit_len, w.group, align_base=0,
-                                  rope_base=w.rope_base, style=w.rope_style, **gouts)
+                gk, gv = planned("gather", lambda: K.gather(
+                    self.k, self.v, out["idx"], w.unit_len, w.group, align_base=0,
+                    rope_base=w.rope_base, style=w.rope_style, **gouts))
             elif w.refill_interval:     # ACRE: L1 entry j -> its L2 block
-                gk, gv = K.gather(self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group,
-                                  **gouts)
+                gk, gv = planned("gather", lambda: K.gather(
+                    self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group, **gouts))
             else:
-                gk, gv = K.gather(k_score, self.v, out["idx"], w.unit_len, w.group, **gouts)
+                gk, gv = planned("gather", lambda: K.gather(
+                    k_score, self.v, out["idx"], w.unit_len, w.group, **gouts))
             mark("gather", 1)
             mark("decode", 0)
             segs = [(self.k, self.v), (gk, gv)] if w.refill_interval else [(gk, gv)]
-            out["o"], out["lse"] = K.decode_attn(q, segs, w.scale, **douts)
+            out["o"], out["lse"] = planned("decode", lambda: K.decode_attn(q, segs, w.scale,
+                                                                           **douts))
             mark("decode", 1)
         else:
             # refill and attention in one pass over the kept rows
             mark("gather_decode", 0)
             if w.refill_interval:       # ACRE: L1 entry j -> its L2 block, L1 kept as a segment
-                gk, gv, o, lse = K.gather_decode(q, self.l2[0], self.l2[1], out["idx"],
-                                                 w.refill_interval, w.group,
-                                                 extra=[(self.k, self.v)], scale=w.scale,
-                                                 **gouts, **douts)
+                gk, gv, o, lse = planned("gather_decode", lambda: K.gather_decode(
+                    q, self.l2[0], self.l2[1], out["idx"], w.refill_interval, w.group,
+                    extra=[(self.k, self.v)], scale=w.scale, **gouts, **douts))
             else:
-                gk, gv, o, lse = K.gather_decode(q, k_score, self.v, out["idx"], w.unit_len,
-                                                 w.group, scale=w.scale, **gouts, **douts)
+                gk, gv, o, lse = planned("gather_decode", lambda: K.gather_decode(
+                    q, k_score, self.v, out["idx"], w.unit_len, w.group, scale=w.scale,
+                    **gouts, **douts))
             mark("gather_decode", 1)
             out["o"], out["lse"] = o, lse
         out["k_gather"], out["v_gather"] = gk, gv
