@@ -399,3 +399,18 @@ def test_scale_must_be_finite_and_positive(lib):
         assert lib.kvsel_gather_decode(p, 1, 32, bad, p, p, kc, 256, p, 4, 1, p, p, None, 0, p,
                                        None, p, 1 << 40, None) == SHAPE
         assert b"scale" in lib.kvsel_last_error()
+
+
+def test_launch_failure_is_reported(lib):
+    """A call that passes validation but whose launch the runtime rejects
+    returns KVSEL_ERR_HIP with the runtime's message.  Forced here by the
+    absence of a device: on a host with a GPU the fake pointers would be
+    launched on, so the case runs only where the GPU driver's device node is
+    absent (no torch import: this file also runs under the host sanitizer)."""
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU driver is present: the launch would run on fake pointers")
+    p = ctypes.c_void_p(FAKE)
+    assert lib.kvsel_topk(p, 1, 10, 2, p, None, None) == -6
+    assert lib.kvsel_last_error().startswith(b"kvsel_topk:")
+    assert lib.kvsel_take(p, 2, 10, ctypes.c_void_p(FAKE + 4096), 3,
+                          ctypes.c_void_p(FAKE + 8192), None) == -6
