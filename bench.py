@@ -669,16 +669,20 @@ def measure(w, seed: int, steps: int, warmup: int, graph: bool, copy_GBps: float
     return result, inp, rows
 
 
-# Measured beside the default line in the same run: the other bench workloads
-# of the configurations (steps timed, as one line each under "also").
+# Measured beside the default line in the same run (steps timed, one entry
+# each under "also"): the other workloads of the configurations, then the
+# layer-wise pruning loop, the two-stage selection with reordering, the refill
+# from host-resident L2 and the recompute attention of the selected tokens.
 ALSO = (("acre_bilayer_l1_16k_l2_128k", 200), ("llama2_7b_32docs_x512", 200),
-        ("infoflow_32l_64x1024", 30))
+        ("infoflow_32l_64x1024", 30), ("cachefocus_qwen2_28l_40docs_x512", 10),
+        ("infoflow_reorder_32l_64x1024", 10), ("acre_bilayer_host_l2_l1_16k_l2_128k", 50),
+        ("infoflow_recompute_32l_64x1024", 3))
 
 
 def also_entry(res: dict) -> dict:
     """The summary of one extra workload in the bench line."""
     keep = ("value", "ms_per_step", "dtype", "roofline", "stages_ms", "selection", "covered",
-            "graph")
+            "host_link", "graph")
     out = {k: res[k] for k in keep if k in res}
     # the staged pass (an event pair around every stage): its mean and median
     # per-step span include the events' own cost, a fifth of a 0.12 ms step
