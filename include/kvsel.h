@@ -34,7 +34,8 @@
  *   synchronisation, as with any HIP kernel.
  * - Caches are [B][N][H][D]: instance, cached row, kv head, head dim.  Within a
  *   row the H*D elements are contiguous; rows and instances may be strided
- *   (kvsel_cache.stride_n / stride_b, in elements, multiples of 8).  Pointers
+ *   (kvsel_cache.stride_n / stride_b, in elements, multiples of 8; stride_n
+ *   below 2^24, else KVSEL_ERR_UNSUPPORTED).  Pointers
  *   must be 16-byte aligned.  Query blocks are contiguous [B][T][Hq][D] in the
  *   cache dtype.  Per-row statistics are [B][Hq][T] (a "row" is one query head
  *   and query token).  Hq must be a multiple of H; query head h reads kv head
@@ -92,7 +93,7 @@ typedef struct kvsel_cache {
   int64_t H;         /* kv heads                                          */
   int64_t D;         /* head dim: 64 or 128                               */
   int64_t stride_b;  /* elements between instances, >= N * stride_n       */
-  int64_t stride_n;  /* elements between rows, >= H * D                   */
+  int64_t stride_n;  /* elements between rows, >= H * D and < 2^24       */
   int32_t dtype;     /* KVSEL_BF16 or KVSEL_FP32                          */
 } kvsel_cache;
 

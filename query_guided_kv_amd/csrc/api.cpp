@@ -92,6 +92,9 @@ int check_cache(const kvsel_cache& kc, const char* what) {
     return fail(KVSEL_ERR_UNSUPPORTED, "%s: strides must be multiples of 8 elements", what);
   if (kc.B > (int64_t{1} << 24) || kc.N >= (int64_t{1} << 31))
     return fail(KVSEL_ERR_SHAPE, "%s: B or N out of range", what);
+  if (kc.stride_n >= (int64_t{1} << 24))
+    return fail(KVSEL_ERR_UNSUPPORTED, "%s: row stride %lld is not below 2^24 elements", what,
+                (long long)kc.stride_n);
   return KVSEL_OK;
 }
 

@@ -23,6 +23,10 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// so untyped loads return whole dwords and out-of-range ones return zero.
+constexpr int kBufferDword3 = 0x00020000;
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -403,6 +407,94 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   const bf16_t* vb = static_cast<const bf16_t*>(st.v[sg]) + b * st.stride_b[sg] + static_cast<int64_t>(g) * D;
   const int64_t sn = st.stride_n[sg];
 
+  // Tile staging: the next tile's K and V rows are in flight (in registers)
+  // while this tile computes.  With eight waves and head dim 128 the staging is
+  // split by wave: the first four waves load and transpose V (one item of 4
+  // keys x 8 dims per thread), the last four load K (4 vectors per thread), so
+  // every thread issues the same 4 loads, through a buffer resource that covers
+  // rows t0 .. min(t0 + TK, t_end) of its role's cache: rows past the split end
+  // read as zero (their logits are masked below, their values weigh 0) and the
+  // loads carry no clamp or branch.  Otherwise every thread loads K vectors and
+  // the first VITEMS threads V items, rows past the end clamped to the last.
+  constexpr bool SPLIT = (NW == 8 && D == 128);
+  constexpr int KSV = TK * (D / 8) / (NT / 2);   // K vectors per K-staging thread
+  static_assert(!SPLIT || (KSV == 4 && VITEMS == NT / 2), "split staging");
+  constexpr int NBUF = SPLIT ? 4 : KV + 4 * VI;
+  const bool vwave = SPLIT && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < NW / 2;
+  const int te = SPLIT ? (vwave ? threadIdx.x : threadIdx.x - NT / 2) : threadIdx.x;
+  const int tn = SPLIT ? NT / 2 : NT;              // threads of one staging role
+  uint4 bf[NBUF];
+  // split: byte offsets of the thread's 4 rows within a tile (row strides are
+  // below 2^24 elements, so a tile spans less than 2^31 bytes)
+  uint32_t boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = vwave ? (te % KG) * 4 + j : te / (D / 8) + j * (tn / (D / 8));
+    const int ch = vwave ? te / KG : te % (D / 8);
+    boff[j] = static_cast<uint32_t>((row * sn + ch * 8) * static_cast<int64_t>(sizeof(bf16_t)));
+  }
+  const bf16_t* sbase = vwave ? vb : kb;
+  const int64_t koff = (te / (D / 8)) * sn + (te % (D / 8)) * 8;
+  const int64_t kstep = (tn / (D / 8)) * sn;
+  auto fetch_k = [&](uint4* kn, int64_t t0) {
+    if (t0 + TK <= t_end) {   // uniform
+      const bf16_t* kt0 = kb + t0 * sn;
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const uint4 x = *reinterpret_cast<const uint4*>(kt0 + koff + i * kstep);
+        kn[i] = x;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const int e = te + i * tn;
+        const int64_t t = min<int64_t>(t0 + e / (D / 8), t_end - 1);
+        const uint4 x = *reinterpret_cast<const uint4*>(kb + t * sn + (e % (D / 8)) * 8);
+        kn[i] = x;
+      }
+    }
+  };
+  auto fetch_v = [&](uint4* vn, int e, int64_t t0) {   // item e: 4 rows
+    if (t0 + TK <= t_end) {   // uniform
+      const bf16_t* vt0 = vb + t0 * sn + (e % KG) * 4 * sn + (e / KG) * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 y = *reinterpret_cast<const uint4*>(vt0 + j * sn);
+        vn[j] = y;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = min<int64_t>(t0 + (e % KG) * 4 + j, t_end - 1);
+        const uint4 y = *reinterpret_cast<const uint4*>(vb + t * sn + (e / KG) * 8);
+        vn[j] = y;
+      }
+    }
+  };
+  auto fetch = [&](int64_t t0) {
+    if constexpr (SPLIT) {
+      const int64_t rows = max<int64_t>(0, min<int64_t>(TK, t_end - t0));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<bf16_t*>(sbase + t0 * sn), 0,
+          static_cast<int>(rows * sn * static_cast<int64_t>(sizeof(bf16_t))), kBufferDword3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[j], 0, 0));
+    } else {
+      fetch_k(bf, t0);
+#pragma unroll
+      for (int i = 0; i < VI; ++i)
+        if (threadIdx.x + i * NT < VITEMS) fetch_v(bf + KV + 4 * i, threadIdx.x + i * NT, t0);
+    }
+  };
+  auto stage_k = [&](const uint4* kn, int nk) {   // K row-major: (key, 16-byte chunk)
+#pragma unroll
+    for (int i = 0; i < nk; ++i) {
+      const int e = te + i * tn;
+      const int key = e / (D / 8), ch = e % (D / 8);
+      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
+    }
+  };
   // query fragments (B operand: query row col of the row block, 8 dims per k-step)
   uint4 qb[RBW][KS];
   int rb[RBW];
@@ -430,73 +522,25 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     for (int c = 0; c < CB; ++c) o[i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // the next tile's K and V rows are in flight while this tile computes; in a
-  // split's last, partial tile the rows past its end are clamped to its last
-  // row and masked below
-  uint4 kn[KV], vn4[VI][4];
-  const int64_t koff = (threadIdx.x / (D / 8)) * sn + (threadIdx.x % (D / 8)) * 8;
-  const int64_t voff = (threadIdx.x % KG) * 4 * sn + (threadIdx.x / KG) * 8;
-  const int64_t kstep = (NT / (D / 8)) * sn;
-  constexpr int VSTEP = (NT / KG) * 8;   // dims between a thread's V items
-  auto fetch = [&](int64_t t0) {
-    if (t0 + TK <= t_end) {   // uniform
-      const bf16_t* kt0 = kb + t0 * sn;
-      const bf16_t* vt0 = vb + t0 * sn;
-#pragma unroll
-      for (int i = 0; i < KV; ++i) {
-        const uint4 x = *reinterpret_cast<const uint4*>(kt0 + koff + i * kstep);
-        kn[i] = x;
-      }
-#pragma unroll
-      for (int i = 0; i < VI; ++i) {
-        if (threadIdx.x + i * NT < VITEMS) {   // the other threads stage no V
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint4 y = *reinterpret_cast<const uint4*>(vt0 + voff + i * VSTEP + j * sn);
-            vn4[i][j] = y;
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KV; ++i) {
-        const int e = threadIdx.x + i * NT;
-        const int64_t t = min<int64_t>(t0 + e / (D / 8), t_end - 1);
-        const uint4 x = *reinterpret_cast<const uint4*>(kb + t * sn + (e % (D / 8)) * 8);
-        kn[i] = x;
-      }
-#pragma unroll
-      for (int i = 0; i < VI; ++i) {
-        const int e = threadIdx.x + i * NT;
-        if (e < VITEMS) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int64_t t = min<int64_t>(t0 + (e % KG) * 4 + j, t_end - 1);
-            const uint4 y = *reinterpret_cast<const uint4*>(vb + t * sn + (e / KG) * 8);
-            vn4[i][j] = y;
-          }
-        }
-      }
-    }
-  };
-  if (t_begin < t_end) fetch(t_begin);
+  if (SPLIT || t_begin < t_end) fetch(t_begin);
+  __builtin_amdgcn_sched_barrier(0);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TK) {
     __syncthreads();
-    // K row-major: item (key, 16-byte chunk)
+    if constexpr (SPLIT) {
+      if (vwave) stage_vt<VROW>(vt, *reinterpret_cast<const uint4(*)[4]>(bf), te % KG, te / KG);
+      else stage_k(bf, KSV);
+    } else {
+      stage_k(bf, KV);
+      // V transposed: item (4 consecutive keys, 8-dim chunk)
 #pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int e = threadIdx.x + i * NT;
-      const int key = e / (D / 8), ch = e % (D / 8);
-      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
-    }
-    // V transposed: item (4 consecutive keys, 8-dim chunk)
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int e = threadIdx.x + i * NT;
-      if (e < VITEMS) stage_vt<VROW>(vt, vn4[i], e % KG, e / KG);
+      for (int i = 0; i < VI; ++i) {
+        const int e = threadIdx.x + i * NT;
+        if (e < VITEMS)
+          stage_vt<VROW>(vt, *reinterpret_cast<const uint4(*)[4]>(bf + KV + 4 * i), e % KG, e / KG);
+      }
     }
     __syncthreads();
-    if (t0 + TK < t_end) fetch(t0 + TK);
+    if (SPLIT || t0 + TK < t_end) fetch(t0 + TK);
 
     // S^T blocks: key block outer, so one K fragment serves every row block
     f32x4_t sv[RBW][4];

@@ -80,6 +80,8 @@ def test_reposition_validation(lib):
     assert f(cache(), base=0.5) == SHAPE
     assert f(cache(stride_n=1000)) == SHAPE       # < H*D
     assert f(cache(stride_n=1028)) == UNSUP       # not a multiple of 8
+    assert f(cache(B=1, N=2, stride_n=1 << 24)) == UNSUP   # row stride not below 2^24
+    assert b"2^24" in lib.kvsel_last_error()
     assert f(cache(B=0)) == SHAPE
     assert b"unit_len" in lib.kvsel_last_error() or True
 
@@ -274,6 +276,8 @@ def test_decode_validation(lib):
     assert need == 2 * 32 * 1 * 3 * (2 + 128) * 4          # ceil(1300 / 512) = 3 splits
     assert lib.kvsel_decode_attn(p, 1, 32, 0.1, one, 1, out, None, p, need - 4, None) == WS
     assert lib.kvsel_decode_attn(p, 1, 30, 0.1, one, 1, out, None, p, need, None) == SHAPE
+    wide = (K.Segment * 1)(K.Segment(FAKE, FAKE, cache(B=1, N=4, stride_n=1 << 24)))
+    assert lib.kvsel_decode_attn(p, 1, 32, 0.1, wide, 1, out, None, p, 1 << 40, None) == UNSUP
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
