@@ -23,6 +23,10 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// so untyped loads return whole dwords and out-of-range ones return zero.
+constexpr int kBufferDword3 = 0x00020000;
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -469,9 +473,13 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   };
   auto fetch = [&](int64_t t0) {
     if constexpr (SPLIT) {
-      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(sbase + t0 * sn, min<int64_t>(TK, t_end - t0), sn);
+      const int64_t rows = max<int64_t>(0, min<int64_t>(TK, t_end - t0));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<bf16_t*>(sbase + t0 * sn), 0,
+          static_cast<int>(rows * sn * static_cast<int64_t>(sizeof(bf16_t))), kBufferDword3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = load_rsrc(rs, boff[j]);
+      for (int j = 0; j < 4; ++j)
+        bf[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[j], 0, 0));
     } else {
       fetch_k(bf, t0);
 #pragma unroll

@@ -22,24 +22,6 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
-// so untyped loads return whole dwords and out-of-range ones return zero.
-constexpr int kBufferDword3 = 0x00020000;
-
-// A buffer resource over `rows` cache rows of `row_elems` bf16 elements from
-// `base` (rows <= 0: an empty range; every load from it returns zero and
-// touches no memory).  The caller keeps rows * row_elems * 2 below 2^31.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16_t* base, int64_t rows,
-                                                           int64_t row_elems) {
-  const int64_t n = rows > 0 ? rows * row_elems * static_cast<int64_t>(sizeof(bf16_t)) : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, static_cast<int>(n),
-                                           kBufferDword3);
-}
-
-__device__ __forceinline__ uint4 load_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // Padding of a staged row of an LDS tile (keys of the K tile, dims of the
 // transposed V tile): 32 bytes, so that the row stride is 8 dwords past a
 // multiple of 16.  Measured on gfx950 for the 16-byte fragment reads of these
