@@ -356,6 +356,57 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
   }
 }
 
+// One online-softmax step of a wave's RBW row blocks over a 64-key tile: the
+// steps of attn_softmax (mfma.h) for each row block, with a single rescale
+// branch for all of them, so that every exponential and the value products
+// after it fall in one basic block that the scheduler can interleave.  When
+// the branch is taken, each row's reference moves to its new maximum (or stays).
+template <int CB, int RBW>
+__device__ __forceinline__ void attn_softmax_rows(const f32x4_t (&sv)[RBW][4], float scale2,
+                                                  float (&m)[RBW], float (&s)[RBW],
+                                                  f32x4_t (&o)[RBW][CB], uint32_t (&pk)[RBW][4][2]) {
+  float tm[RBW];
+  bool grow = false;
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    float tmax = sv[i][0][0];
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) tmax = fmaxf(tmax, sv[i][kb4][vv]);
+    tm[i] = quad_max(tmax) * scale2;
+    grow = grow || tm[i] > m[i] + kAttnLazy;
+  }
+  if (__any(grow)) {   // uniform: rare once the maxima settle
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      const float mn = fmaxf(m[i], tm[i]);
+      const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[i] - mn);
+      m[i] = mn;
+      s[i] *= alpha;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) o[i][c] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    const float ref = m[i] == -INFINITY ? 0.0f : m[i];
+    float ps = s[i];
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      float p[4];
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv)
+        p[vv] = __builtin_amdgcn_exp2f(fmaf(sv[i][kb4][vv], scale2, -ref));
+      pk[i][kb4][0] = pack2_bf16(p[0], p[1]);
+      pk[i][kb4][1] = pack2_bf16(p[2], p[3]);
+      ps = dot2_bf16(pk[i][kb4][0], kBf16Ones, ps);
+      ps = dot2_bf16(pk[i][kb4][1], kBf16Ones, ps);
+    }
+    s[i] = ps;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // matrix-core variant: bf16, >= 16 query rows per kv head
 // ---------------------------------------------------------------------------
@@ -367,7 +418,7 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
 //                 B = the lane's own probabilities, rounded to bf16): the 32
 //                 keys of two key blocks, in the order the lane holds them.
 // The running max, sum and output of a query row all live in the lanes with
-// l%16 == row, so rescaling is lane-local (and lazy: attn_softmax in mfma.h);
+// l%16 == row, so rescaling is lane-local (and lazy: attn_softmax_rows);
 // the max and the final sum are reduced across the four lane quads.  Waves
 // split the query rows, RBW row blocks each; taller blocks run in passes.
 template <int D, int RBW, int NW>
@@ -524,7 +575,8 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
 
   if (SPLIT || t_begin < t_end) fetch(t_begin);
   __builtin_amdgcn_sched_barrier(0);
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += TK) {
+  // full tiles, then the split's last, partial tile (rows past its end masked)
+  auto tile = [&](int64_t t0, bool partial) {
     __syncthreads();
     if constexpr (SPLIT) {
       if (vwave) stage_vt<VROW>(vt, *reinterpret_cast<const uint4(*)[4]>(bf), te % KG, te / KG);
@@ -558,7 +610,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
         sv[i][kb4] = a;
       }
     }
-    if (t0 + TK > t_end) {   // the split's last, partial tile (uniform)
+    if (partial) {
 #pragma unroll
       for (int i = 0; i < RBW; ++i)
 #pragma unroll
@@ -568,8 +620,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
             if (t0 + kb4 * 16 + quad * 4 + vv >= t_end) sv[i][kb4][vv] = -INFINITY;
     }
     uint32_t pk[RBW][4][2];
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) attn_softmax<CB>(sv[i], scale2, m[i], s[i], o[i], pk[i]);
+    attn_softmax_rows<CB, RBW>(sv, scale2, m, s, o, pk);
     // O^T += V^T P^T: one V^T fragment serves every row block
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
@@ -584,7 +635,10 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
         }
       }
     }
-  }
+  };
+  const int64_t t_full = t_begin + max<int64_t>(0, t_end - t_begin) / TK * TK;
+  for (int64_t t0 = t_begin; t0 < t_full; t0 += TK) tile(t0, false);
+  if (t_full < t_end) tile(t_full, true);
 
   // publish: lane l holds query row rb*16 + l%16, dims c*16 + 4*quad .. +3
 #pragma unroll
