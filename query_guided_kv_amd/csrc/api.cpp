@@ -171,13 +171,19 @@ int64_t split_len_of(int64_t T, int64_t Hq, const kvsel_cache& c, bool gathered,
 
 // (m, s, o) partials of every split of the segments; `gathered` when the last
 // segment is gathered on the fly (the split length depends on the kernel)
+// Decode workspace: the (m, s) pairs of every row and split, then, from a
+// 16-byte boundary, the rows' partial outputs (D floats per row and split).
+int64_t decode_ms_floats(int64_t rows, int64_t n_split) { return (rows * n_split * 2 + 3) / 4 * 4; }
+
 size_t decode_ws(int64_t T, int64_t Hq, const kvsel_segment* segs, int n_seg, bool gathered) {
   if (segs == nullptr || n_seg < 1 || n_seg > kMaxSegments || T < 1 || Hq < 1) return 0;
   for (int i = 0; i < n_seg; ++i)
     if (segs[i].kc.N < 1 || segs[i].kc.B < 1 || segs[i].kc.D < 1) return 0;
   const int64_t n_split =
       decode_splits(segs, n_seg, split_len_of(T, Hq, segs[0].kc, gathered, total_keys(segs, n_seg)));
-  return static_cast<size_t>(segs[0].kc.B * Hq * T * n_split * (2 + segs[0].kc.D)) * sizeof(float);
+  const int64_t rows = segs[0].kc.B * Hq * T;
+  return static_cast<size_t>(decode_ms_floats(rows, n_split) + rows * n_split * segs[0].kc.D) *
+         sizeof(float);
 }
 
 }  // namespace
@@ -651,7 +657,7 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const k
                       int32_t n_seg, float* out, float* lse, void* ws, size_t ws_bytes,
                       hipStream_t stream) {
   KVSEL_TRY(check_ptr(q, "q"));
-  if (out == nullptr) return fail(KVSEL_ERR_NULL, "out is NULL");
+  KVSEL_TRY(check_ptr(out, "out"));
   if (segs == nullptr) return fail(KVSEL_ERR_NULL, "segs is NULL");
   if (n_seg < 1 || n_seg > kMaxSegments)
     return fail(KVSEL_ERR_SHAPE, "kvsel_decode_attn: n_seg=%d not in [1, %d]", n_seg, kMaxSegments);
@@ -678,8 +684,9 @@ int kvsel_decode_attn(const void* q, int64_t T, int64_t Hq, float scale, const k
   const size_t need = kvsel_decode_workspace(T, Hq, segs, n_seg);
   if (ws == nullptr || ws_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "kvsel_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
+  KVSEL_TRY(check_ptr(ws, "ws"));
   float* ws_ms = static_cast<float*>(ws);
-  float* ws_o = ws_ms + c0.B * Hq * T * split * 2;
+  float* ws_o = ws_ms + decode_ms_floats(c0.B * Hq * T, split);
   return launch_decode(q, T, Hq, scale, ds, n_seg, c0.B, c0.H, c0.D, c0.dtype, split, out, lse,
                        ws_ms, ws_o, stream);
 }
@@ -715,7 +722,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
     KVSEL_TRY(check_ptr(k_dst, "k_dst"));
     KVSEL_TRY(check_ptr(v_dst, "v_dst"));
   }
-  if (out == nullptr) return fail(KVSEL_ERR_NULL, "out is NULL");
+  KVSEL_TRY(check_ptr(out, "out"));
   KVSEL_TRY(check_cache(kc, "kvsel_gather_decode"));
   KVSEL_TRY(check_units(kc, unit_len, "kvsel_gather_decode"));
   KVSEL_TRY(check_heads(T, Hq, kc, "kvsel_gather_decode"));
@@ -756,6 +763,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
   if (ws == nullptr || ws_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "kvsel_gather_decode: workspace %zu < %zu bytes", ws_bytes,
                 need);
+  KVSEL_TRY(check_ptr(ws, "ws"));
   if (k > 0) {  // the kept rows may live in pinned host memory
     KVSEL_TRY(resolve_rows(k_src, &k_src, "k_src"));
     KVSEL_TRY(resolve_rows(v_src, &v_src, "v_src"));
@@ -773,7 +781,7 @@ int kvsel_gather_decode(const void* q, int64_t T, int64_t Hq, float scale, const
     }
     const DecodeGather gather{n - 1, idx, unit_len, k, idx_group, M, k_dst, v_dst};
     float* ws_ms = static_cast<float*>(ws);
-    float* ws_o = ws_ms + kc.B * Hq * T * split * 2;
+    float* ws_o = ws_ms + decode_ms_floats(kc.B * Hq * T, split);
     return launch_decode(q, T, Hq, scale, ds, n, kc.B, kc.H, kc.D, kc.dtype, split, out, lse,
                          ws_ms, ws_o, stream, &gather);
   }

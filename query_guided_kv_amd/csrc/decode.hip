@@ -663,33 +663,64 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// merge of the splits: one block of D threads per row
+// merge of the splits: one block of 256 threads per row
 // ---------------------------------------------------------------------------
-__global__ void decode_merge_kernel(const float* __restrict__ ws_ms, const float* __restrict__ ws_o,
-                                    int64_t n_split, int D, int T_, int Hq,
-                                    float* __restrict__ out, float* __restrict__ lse) {
+// The splits are dealt round-robin to NG groups of D / 4 threads; a thread
+// reads 16 bytes (4 dims) of each of its splits' partial outputs, so a row's
+// partials are all in flight at once.  The groups' maxima, sums and outputs
+// meet in LDS.  Partial outputs start at a 16-byte boundary of the workspace.
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_merge_kernel(const float* __restrict__ ws_ms, const float* __restrict__ ws_o,
+                    int64_t n_split, int T_, int Hq, float* __restrict__ out,
+                    float* __restrict__ lse) {
+  constexpr int LPS = D / 4;       // threads per split (4 dims each)
+  constexpr int NG = 256 / LPS;    // split groups
+  __shared__ float gmax[NG], gsum[NG];
+  __shared__ float4 gacc[NG][LPS];
   const int64_t row = blockIdx.x;  // (b*Hq + h)*T + j
-  const int d = threadIdx.x;
+  const int gi = threadIdx.x / LPS, li = threadIdx.x % LPS;
   const float* ms = ws_ms + row * n_split * 2;   // (m_i, s_i) pairs
-  const float* po = ws_o + row * n_split * D + d;
+  const float4* po = reinterpret_cast<const float4*>(ws_o + row * n_split * D) + li;
   float m = -INFINITY;
-#pragma unroll 8
-  for (int64_t i = 0; i < n_split; ++i) m = fmaxf(m, ms[2 * i]);
-  // a split with no keys (m_i = -inf) weighs 0; the loads of several splits
-  // are in flight together
+  for (int64_t i = gi; i < n_split; i += NG) m = fmaxf(m, ms[2 * i]);
+  if (li == 0) gmax[gi] = m;
+  __syncthreads();
+  m = gmax[0];
+#pragma unroll
+  for (int k = 1; k < NG; ++k) m = fmaxf(m, gmax[k]);
+  // a split with no keys (m_i = -inf) weighs 0
   const float ref = m == -INFINITY ? 0.0f : m;
-  float s = 0.0f, acc = 0.0f;
-#pragma unroll 8
-  for (int64_t i = 0; i < n_split; ++i) {
+  float s = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+  for (int64_t i = gi; i < n_split; i += NG) {
     const float a = __builtin_amdgcn_exp2f(ms[2 * i] - ref);
+    const float4 p = po[i * (D / 4)];
     s = fmaf(ms[2 * i + 1], a, s);
-    acc = fmaf(po[i * D], a, acc);
+    acc.x = fmaf(p.x, a, acc.x);
+    acc.y = fmaf(p.y, a, acc.y);
+    acc.z = fmaf(p.z, a, acc.z);
+    acc.w = fmaf(p.w, a, acc.w);
+  }
+  gacc[gi][li] = acc;
+  if (li == 0) gsum[gi] = s;
+  __syncthreads();
+  if (gi != 0) return;
+  float4 t = gacc[0][li];
+  float st = gsum[0];
+#pragma unroll
+  for (int k = 1; k < NG; ++k) {
+    const float4 u = gacc[k][li];
+    t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    st += gsum[k];
   }
   const int64_t j = row % T_;
   const int64_t h = (row / T_) % Hq;
   const int64_t b = row / (static_cast<int64_t>(T_) * Hq);
-  out[((b * T_ + j) * Hq + h) * D + d] = acc / s;
-  if (lse != nullptr && d == 0) lse[row] = (m + log2f(s)) * kLn2;
+  *reinterpret_cast<float4*>(out + ((b * T_ + j) * Hq + h) * D + li * 4) =
+      make_float4(t.x / st, t.y / st, t.z / st, t.w / st);
+  if (lse != nullptr && li == 0) lse[row] = (m + log2f(st)) * kLn2;
 }
 
 template <int D, int H, int R>
@@ -847,9 +878,12 @@ int launch_decode(const void* q, int64_t T, int64_t Hq, float scale, const Decod
   }
   int rc = check_launch("kvsel_decode_attn");
   if (rc != KVSEL_OK) return rc;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(static_cast<unsigned>(B * Hq * T)),
-                     dim3(static_cast<unsigned>(D)), 0, s, ws_ms, ws_o, n_split,
-                     static_cast<int>(D), static_cast<int>(T), static_cast<int>(Hq), out, lse);
+  if (D == 128)
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(static_cast<unsigned>(B * Hq * T)), dim3(256), 0, s,
+                       ws_ms, ws_o, n_split, static_cast<int>(T), static_cast<int>(Hq), out, lse);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(static_cast<unsigned>(B * Hq * T)), dim3(256), 0, s,
+                       ws_ms, ws_o, n_split, static_cast<int>(T), static_cast<int>(Hq), out, lse);
   return check_launch("kvsel_decode_attn (merge)");
 }
 
