@@ -86,8 +86,8 @@ __device__ __forceinline__ void merge_lane(float& m, float& s) {
   merge_ms(m, s, m2, s2);
 }
 
-template <int D, int H, int R, int U>
-__global__ void __launch_bounds__(kThreads)
+template <int D, int H, int R, int U, int NTH>
+__global__ void __launch_bounds__(NTH)
 score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int64_t N,
                     int64_t stride_b, int64_t stride_n, int T, int Hq, float scale2,
                     int64_t seg_len, int64_t nseg, int64_t spb, float* __restrict__ ms,
@@ -100,7 +100,8 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   static_assert(LPH == 8, "head dim 128: 8 lanes per head");
   static_assert(LPT <= 64 && 64 % LPT == 0, "row must tile a wave");
   static_assert(V % 8 == 0 && VL <= U, "need 8 <= U*R <= 8*U");
-  __shared__ float red[kWaves][H * R][2];
+  constexpr int NWV = NTH / 64;
+  __shared__ float red[NWV][H * R][2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -131,7 +132,7 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   }
 
   const bf16_t* kb = k + b * stride_b + g * D + c * 16;
-  constexpr int STEP = kWaves * TPW;
+  constexpr int STEP = NWV * TPW;
   for (int64_t seg = seg0; seg < seg1; ++seg) {
   float m = -INFINITY, s = 0.0f;  // softmax partial of row own_r over this lane's keys
   const int64_t t_begin = seg * seg_len;
@@ -220,10 +221,10 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     red[wave][g * R + own_r][1] = s;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < H * R; i += kThreads) {
+  for (int i = threadIdx.x; i < H * R; i += NTH) {
     float mm = red[0][i][0], ss = red[0][i][1];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) merge_ms(mm, ss, red[w][i][0], red[w][i][1]);
+    for (int w = 1; w < NWV; ++w) merge_ms(mm, ss, red[w][i][0], red[w][i][1]);
     const int gg = i / R, r = i % R;
     const int h = gg * G + r / T, jj = r % T;
     float* o = ms + (((b * Hq + h) * T + jj) * nseg + seg) * 2;
@@ -354,6 +355,11 @@ rowstat_kernel(const float* __restrict__ ms, int64_t rows, int64_t nseg, int nat
 // MI355X: the stream runs at the memory system's rate either way.)
 template <int R> constexpr int stream_unroll() { return R >= 2 ? 4 : 8; }
 constexpr int64_t kStreamSegsPerBlock = 2;
+// Threads of a streaming-scorer workgroup.  Measured on the serving step (two
+// 256-row units of 8 kv heads per workgroup, 1 MiB of keys): 256 threads
+// 5.64-5.74 ms, 512 5.56, 1,024 5.41-5.42; 1,024 threads with one unit per
+// workgroup 5.52, with four 5.38-5.50 (same box).
+constexpr int kStreamThreads = 1024;
 
 template <int D, int H, int R>
 void launch_stream(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_cache& kc,
@@ -364,9 +370,9 @@ void launch_stream(const void* q, int64_t T, int64_t Hq, const void* k, const kv
   int64_t spb = kStreamSegsPerBlock;
   while (spb > 1 && kc.B * ((nseg + spb - 1) / spb) < 8192) spb /= 2;
   const int64_t groups = (nseg + spb - 1) / spb;
-  hipLaunchKernelGGL((score_stream_kernel<D, H, R, stream_unroll<R>()>),
+  hipLaunchKernelGGL((score_stream_kernel<D, H, R, stream_unroll<R>(), kStreamThreads>),
                      dim3(static_cast<unsigned>(kc.B * groups)),
-                     dim3(kThreads), 0, s, static_cast<const bf16_t*>(q),
+                     dim3(kStreamThreads), 0, s, static_cast<const bf16_t*>(q),
                      static_cast<const bf16_t*>(k), kc.N, kc.stride_b, kc.stride_n,
                      static_cast<int>(T), static_cast<int>(Hq), scale2, seg_len, nseg, spb, ms,
                      natural);
