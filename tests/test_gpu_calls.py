@@ -297,6 +297,44 @@ DECODE_CASES = [
 ]
 
 
+def strided(t, pad_heads, pad_rows):
+    """t ([B][N][H][D]) as a view with padded rows (stride_n = (H + pad_heads) * D)
+    and padded instances (pad_rows extra rows each): the layout of a cache
+    slice inside a larger store."""
+    B, N, H, D = t.shape
+    big = torch.zeros((B, N + pad_rows, H + pad_heads, D), dtype=t.dtype, device=t.device)
+    big[:, :N, :H] = t
+    return big[:, :N, :H]
+
+
+# the same calls on strided caches: the tall matrix-core plan (buffer-resource
+# loads at byte offsets of the row stride), the streaming and four-wave plans
+STRIDED_DECODE_CASES = [
+    # name, B, segs N, H, Hq, T, pad_heads, pad_rows
+    ("mfma_R448_strided", 2, (700, 130), 4, 28, 64, 3, 5),
+    ("mfma_R64_strided", 2, (900,), 2, 8, 16, 1, 64),
+    ("stream_R4_strided", 3, (1030,), 8, 32, 1, 2, 9),
+]
+
+
+@pytest.mark.parametrize("case", STRIDED_DECODE_CASES, ids=[c[0] for c in STRIDED_DECODE_CASES])
+def test_decode_strided(case):
+    name, B, Ns, H, Hq, T, ph, pr = case
+    announce("decode_strided", case=name)
+    dev = device()
+    D = 128
+    q = rnd((B, T, Hq, D), "bf16", 27)
+    segs = [(rnd((B, n, H, D), "bf16", 28 + i, 1.5), rnd((B, n, H, D), "bf16", 50 + i))
+            for i, n in enumerate(Ns)]
+    views = [(strided(a.to(dev), ph, pr), strided(b.to(dev), ph, pr)) for a, b in segs]
+    assert views[0][0].stride(1) == (H + ph) * D and not views[0][0].is_contiguous()
+    o, lse = K.decode_attn(q.to(dev), views)
+    torch.cuda.synchronize()
+    wo, wl = O.decode_attention(to64(q), [(to64(a), to64(b)) for a, b in segs], 1.0 / np.sqrt(D))
+    assert_rel(o, wo, 0.0, 5e-3, "o")
+    assert_rel(lse, wl, 0.0, 2e-3, "lse")
+
+
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
 def test_decode(case):
     name, dtype, B, Ns, H, Hq, T, D = case
