@@ -350,10 +350,13 @@ rowstat_kernel(const float* __restrict__ ms, int64_t rows, int64_t nseg, int nat
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-// rows per slot and step: at least 8 (key, row) pairs per lane.  (Double
-// buffering the loads in registers and 8 rows per step measured the same on
-// MI355X: the stream runs at the memory system's rate either way.)
-template <int R> constexpr int stream_unroll() { return R >= 2 ? 4 : 8; }
+// rows per slot and step: at least 8 (key, row) pairs per lane.  With
+// 1,024-thread workgroups the serving shape (4 query rows per kv head) runs
+// fastest at the minimum, 2 rows per step: 5.23-5.33 ms per scoring pass
+// against 5.47-5.50 with 4 rows and 5.66-5.68 with 8 (same box).  (Double
+// buffering the loads in registers measured the same: the stream runs at the
+// memory system's rate.)
+template <int R> constexpr int stream_unroll() { return R == 4 ? 2 : R >= 2 ? 4 : 8; }
 constexpr int64_t kStreamSegsPerBlock = 2;
 // Threads of a streaming-scorer workgroup.  Measured on the serving step (two
 // 256-row units of 8 kv heads per workgroup, 1 MiB of keys): 256 threads
