@@ -356,6 +356,27 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
   }
 }
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// A fragment of V^T (dims 16 c + (l % 16), the lane quad's keys of 32-key half
+// pr, in the order of the probabilities: keys 32 pr + 4 q + 0..3, then
+// 32 pr + 16 + 4 q + 0..3) from a row-major V tile (rows of KROW elements),
+// with two transposing LDS reads.  ds_read_b64_tr_b16 (gfx950, checked on
+// MI355X): in each group of 16 lanes, lane i receives element i % 4 of the
+// 4 elements that lanes i / 4 + 4 k (k = 0..3) point at.  So lane j of the
+// group points at 4 dims 4 (j % 4) of key j / 4, and lane i gets dim i of 4
+// consecutive keys.
+template <int KROW>
+__device__ __forceinline__ uint4 load_vt_tr(const bf16_t* vt, int c, int pr, int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const bf16_t* p = vt + (32 * pr + 4 * q + (j >> 2)) * KROW + c * 16 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) i16x4_t* lds_v4;
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p));
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p + 16 * KROW));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return make_uint4(ua.x, ua.y, ub.x, ub.y);
+}
+
 // One online-softmax step of a wave's RBW row blocks over a 64-key tile: the
 // steps of attn_softmax (mfma.h) for each row block, with a single rescale
 // branch for all of them, so that every exponential and the value products
@@ -437,8 +458,11 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   constexpr int VITEMS = KG * (D / 8);     // V items (4 keys x 8 dims) per tile
   constexpr int VI = (VITEMS + NT - 1) / NT;
   static_assert(KV >= 1 && NT % KG == 0, "tile staging");
+  // eight waves, head dim 128: V staged row-major like K and read back
+  // transposed (ds_read_b64_tr_b16); otherwise V is transposed when staged
+  constexpr bool SPLIT = (NW == 8 && D == 128);
   __shared__ __align__(16) bf16_t kt[TK * KROW];
-  __shared__ __align__(16) bf16_t vt[D * VROW];
+  __shared__ __align__(16) bf16_t vt[SPLIT ? TK * KROW : D * VROW];
 
   const int nwaves = NW;
   int64_t x = blockIdx.x;
@@ -467,7 +491,6 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   // read as zero (their logits are masked below, their values weigh 0) and the
   // loads carry no clamp or branch.  Otherwise every thread loads K vectors and
   // the first VITEMS threads V items, rows past the end clamped to the last.
-  constexpr bool SPLIT = (NW == 8 && D == 128);
   constexpr int KSV = TK * (D / 8) / (NT / 2);   // K vectors per K-staging thread
   static_assert(!SPLIT || (KSV == 4 && VITEMS == NT / 2), "split staging");
   constexpr int NBUF = SPLIT ? 4 : KV + 4 * VI;
@@ -480,8 +503,8 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   uint32_t boff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = vwave ? (te % KG) * 4 + j : te / (D / 8) + j * (tn / (D / 8));
-    const int ch = vwave ? te / KG : te % (D / 8);
+    const int row = te / (D / 8) + j * (tn / (D / 8));
+    const int ch = te % (D / 8);
     boff[j] = static_cast<uint32_t>((row * sn + ch * 8) * static_cast<int64_t>(sizeof(bf16_t)));
   }
   const bf16_t* sbase = vwave ? vb : kb;
@@ -538,12 +561,13 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
         if (threadIdx.x + i * NT < VITEMS) fetch_v(bf + KV + 4 * i, threadIdx.x + i * NT, t0);
     }
   };
-  auto stage_k = [&](const uint4* kn, int nk) {   // K row-major: (key, 16-byte chunk)
+  // a row-major tile (K, and V in the split plan): item (key, 16-byte chunk)
+  auto stage_k = [&](bf16_t* tile, const uint4* kn, int nk) {
 #pragma unroll
     for (int i = 0; i < nk; ++i) {
       const int e = te + i * tn;
       const int key = e / (D / 8), ch = e % (D / 8);
-      *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
+      *reinterpret_cast<uint4*>(&tile[key * KROW + ch * 8]) = kn[i];
     }
   };
   // query fragments (B operand: query row col of the row block, 8 dims per k-step)
@@ -579,10 +603,9 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   auto tile = [&](int64_t t0, bool partial) {
     __syncthreads();
     if constexpr (SPLIT) {
-      if (vwave) stage_vt<VROW>(vt, *reinterpret_cast<const uint4(*)[4]>(bf), te % KG, te / KG);
-      else stage_k(bf, KSV);
+      stage_k(vwave ? vt : kt, bf, KSV);
     } else {
-      stage_k(bf, KV);
+      stage_k(kt, bf, KV);
       // V transposed: item (4 consecutive keys, 8-dim chunk)
 #pragma unroll
       for (int i = 0; i < VI; ++i) {
@@ -626,7 +649,9 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const uint4 va = load_vt<VROW>(vt, c, pr, col, quad);
+        uint4 va;
+        if constexpr (SPLIT) va = load_vt_tr<KROW>(vt, c, pr, lane);
+        else va = load_vt<VROW>(vt, c, pr, col, quad);
 #pragma unroll
         for (int i = 0; i < RBW; ++i) {
           const uint4 pb = make_uint4(pk[i][2 * pr][0], pk[i][2 * pr][1], pk[i][2 * pr + 1][0],
