@@ -47,7 +47,10 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   static_assert(VI == 1, "one V item per thread at most");
   static_assert(VITEMS <= NL, "V is staged by the lead threads");
   __shared__ __align__(16) bf16_t kt[TK * KROW];
-  __shared__ __align__(16) bf16_t vt2[2][D * VROW];   // V of tiles t (t / TK even, odd)
+  // V of tiles t (t / TK even, odd): with head dim 128 row-major like K and
+  // read back transposed (ds_read_b64_tr_b16), else transposed when staged
+  constexpr bool VROWMAJ = D == 128;
+  __shared__ __align__(16) bf16_t vt2[2][VROWMAJ ? TK * KROW : D * VROW];
   __shared__ int wave_lim[NW];
 
   int64_t x = blockIdx.x;
@@ -126,7 +129,13 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         const uint4 x = *reinterpret_cast<const uint4*>(kt0 + koff + i * kstep);
         kn[i] = x;
       }
-      if (threadIdx.x < VITEMS) {   // the other threads stage no V
+      if constexpr (VROWMAJ) {      // V rows as the K rows
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          const uint4 y = *reinterpret_cast<const uint4*>(vt0 + koff + i * kstep);
+          vn4[0][i] = y;
+        }
+      } else if (threadIdx.x < VITEMS) {   // the other threads stage no V
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint4 y = *reinterpret_cast<const uint4*>(vt0 + voff + j * stride_n);
@@ -141,7 +150,15 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         const uint4 x = *reinterpret_cast<const uint4*>(kb + t * stride_n + (e % (D / 8)) * 8);
         kn[i] = x;
       }
-      if (threadIdx.x < VITEMS) {
+      if constexpr (VROWMAJ) {
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          const int e = threadIdx.x + i * NL;
+          const int64_t t = min<int64_t>(t0 + e / (D / 8), N - 1);
+          const uint4 y = *reinterpret_cast<const uint4*>(vb + t * stride_n + (e % (D / 8)) * 8);
+          vn4[0][i] = y;
+        }
+      } else if (threadIdx.x < VITEMS) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int64_t t = min<int64_t>(t0 + (threadIdx.x % KG) * 4 + j, N - 1);
@@ -191,7 +208,9 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const uint4 va = load_vt<VROW>(vtt, c, pr, col, quad);
+        uint4 va;
+        if constexpr (VROWMAJ) va = load_vt_tr<KROW>(vtt, c, pr, lane);
+        else va = load_vt<VROW>(vtt, c, pr, col, quad);
 #pragma unroll
         for (int i = 0; i < RBW; ++i) {
           const uint4 pb = make_uint4(pk[i][2 * pr][0], pk[i][2 * pr][1], pk[i][2 * pr + 1][0],
@@ -216,9 +235,14 @@ index_attn_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
       }
       bf16_t* vt = vt2[(t0 / TK) & 1];
-      if (threadIdx.x < VITEMS) {
-        const int kg = threadIdx.x % KG, ch = threadIdx.x / KG;
-        stage_vt<VROW>(vt, vn4[0], kg, ch);
+      if constexpr (VROWMAJ) {
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          const int e = threadIdx.x + i * NL;
+          *reinterpret_cast<uint4*>(&vt[(e / (D / 8)) * KROW + (e % (D / 8)) * 8]) = vn4[0][i];
+        }
+      } else if (threadIdx.x < VITEMS) {
+        stage_vt<VROW>(vt, vn4[0], threadIdx.x % KG, threadIdx.x / KG);
       }
       __syncthreads();
       if (t0 + TK < t_end) fetch(t0 + TK);

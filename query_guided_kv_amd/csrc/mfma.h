@@ -110,6 +110,27 @@ __device__ __forceinline__ uint4 load_vt(const bf16_t* vt, int c, int pr, int co
   return *reinterpret_cast<const uint4*>(&vt[(c * 16 + col) * VROW + pr * 32 + quad * 8]);
 }
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// A fragment of V^T (dims 16 c + (l % 16), the lane quad's keys of 32-key half
+// pr, in the order of the probabilities: keys 32 pr + 4 q + 0..3, then
+// 32 pr + 16 + 4 q + 0..3) from a row-major V tile (rows of KROW elements),
+// with two transposing LDS reads.  ds_read_b64_tr_b16 (gfx950, checked on
+// MI355X): in each group of 16 lanes, lane i receives element i % 4 of the
+// 4 elements that lanes i / 4 + 4 k (k = 0..3) point at.  So lane j of the
+// group points at 4 dims 4 (j % 4) of key j / 4, and lane i gets dim i of 4
+// consecutive keys.
+template <int KROW>
+__device__ __forceinline__ uint4 load_vt_tr(const bf16_t* vt, int c, int pr, int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const bf16_t* p = vt + (32 * pr + 4 * q + (j >> 2)) * KROW + c * 16 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) i16x4_t* lds_v4;
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p));
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p + 16 * KROW));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return make_uint4(ua.x, ua.y, ub.x, ub.y);
+}
+
 // One online-softmax step of a row block over a 64-key tile.  sv holds the
 // lane's logits (keys 16 kb4 + 4 (l / 16) + v; -inf where masked); m, s and o
 // are the row's reference, sum and output accumulators.  The probabilities come
