@@ -414,9 +414,11 @@ __device__ __forceinline__ void attn_softmax_rows(const f32x4_t (&sv)[RBW][4], f
 //   S^T = K Q^T  (A = 16 keys x 32 dims from the LDS K tile, B = 32 dims x 16
 //                 query rows held in registers): lane l gets query row l%16
 //                 and keys 4*(l/16) .. +3 of the key block;
-//   O^T += V^T P^T  (A = 16 dims x 32 keys from a transposed LDS V tile,
-//                 B = the lane's own probabilities, rounded to bf16): the 32
-//                 keys of two key blocks, in the order the lane holds them.
+//   O^T += V^T P^T  (A = 16 dims x 32 keys of V^T: from a V tile transposed
+//                 when staged, or, in the eight-wave plan, from a row-major V
+//                 tile through transposing LDS reads; B = the lane's own
+//                 probabilities, rounded to bf16): the 32 keys of two key
+//                 blocks, in the order the lane holds them.
 // The running max, sum and output of a query row all live in the lanes with
 // l%16 == row, so rescaling is lane-local (and lazy: attn_softmax_rows);
 // the max and the final sum are reduced across the four lane quads.  Waves
