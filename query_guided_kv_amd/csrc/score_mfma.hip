@@ -74,11 +74,15 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   __shared__ float red[NWK][ROWS_PASS][2];
   __shared__ double2 cs[ROT ? D / 2 : 1];
 
+  // workgroups are dealt kv head fastest: those running together read the
+  // heads of the same cached rows, so their 256-byte pieces of each row are
+  // fetched close together (32 kv heads, 8 KiB rows: 43.8 -> 41.5 us; no
+  // change with 4 or 8 kv heads)
   int64_t x = blockIdx.x;
+  const int g = static_cast<int>(x % H); x /= H;
   const int64_t grp = x % groups; x /= groups;
-  const int pass = static_cast<int>(x % passes); x /= passes;
-  const int g = static_cast<int>(x % H);
-  const int64_t b = x / H;
+  const int pass = static_cast<int>(x % passes);
+  const int64_t b = x / passes;
   const int G = Hq / H;
   const int R = G * T;
   const int lane = threadIdx.x & 63;
