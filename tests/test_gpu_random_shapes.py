@@ -1,0 +1,171 @@
+"""Seeded random shapes for the scorer, the aggregate, the top-k, the gather
+and the decode attention, against the oracle: rows per kv head drawn across
+every plan boundary (the streaming kernels up to 8 rows, one 16-row block,
+four-wave plans up to 128 rows, eight-wave plans of two row blocks, several
+row passes), head dim 64 and 128, bf16 and fp32, ragged cache lengths, units
+of 1 to 256 rows, instance groups, one or two decode segments, top-k rows of
+1 to 120,000 scores with heavy ties.  Each case draws its shape from its own
+seed, so a failure names a shape that reproduces.  Tolerances as in the
+per-call tests: scores within relative 2e-3, decode outputs within 5e-3
+absolute, indices, values and copies bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import announce, assert_rel, device
+from oracle.pipeline import to64
+from query_guided_kv_amd import kvsel as K
+
+pytestmark = pytest.mark.gpu
+
+TD = {"bf16": torch.bfloat16, "fp32": torch.float32}
+N_CASES = 64
+
+
+def rnd(shape, dtype, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (scale * torch.randn(shape, generator=g)).to(TD[dtype])
+
+
+def draw(seed: int) -> dict:
+    """A shape: rows per kv head (query heads per kv head x tokens) spread
+    over 1 .. 448, with the oracle's work kept to a few hundred MFLOP."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = "fp32" if rng.random() < 0.15 else "bf16"
+    D = int(rng.choice([64, 128, 128]))
+    H = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 7, 8]))
+    rows = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 100, 128, 160, 224, 300, 448]))
+    T = max(1, rows // G)
+    B = int(rng.choice([1, 2]))
+    unit = int(rng.choice([1, 64, 128, 256]))
+    budget = 4e8 / (B * H * G * T * D)          # cached rows the oracle can afford
+    n_units = max(1, int(rng.integers(1, max(2, int(budget // unit) + 1))))
+    n_units = min(n_units, max(1, 3000 // unit))
+    N = unit * n_units if unit > 1 else int(rng.integers(33, max(34, min(3000, int(budget)))))
+    split = int(rng.integers(1, N)) if N > 1 and rng.random() < 0.5 else N
+    return dict(dtype=dtype, D=D, H=H, G=G, T=T, B=B, N=N, unit=unit, split=split)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_score(seed):
+    c = draw(seed)
+    announce("random_score", seed=seed, **c)
+    dev = device()
+    B, N, H, D, T, Hq = c["B"], c["N"], c["H"], c["D"], c["T"], c["H"] * c["G"]
+    q = rnd((B, T, Hq, D), c["dtype"], 2 * seed)
+    k = rnd((B, N, H, D), c["dtype"], 2 * seed + 1, scale=1.5)
+    scale = 1.0 / np.sqrt(D)
+    unit = c["unit"]
+    rm, rs, part = K.score(q.to(dev), k.to(dev), unit, scale, row_stats=True, partials=unit > 1)
+    torch.cuda.synchronize()
+    m, Z, p = O.score(to64(q), to64(k), scale, unit)
+    assert_rel(rm, m, 2e-3, 2e-3, "row_max")
+    assert_rel(rs, Z, 2e-3, 0.0, "row_sum")
+    if unit > 1:
+        assert_rel(part[..., 0], p[..., 0], 2e-3, 2e-3, "m_u")
+        assert_rel(part[..., 1], p[..., 1], 2e-3, 0.0, "S_u")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_decode(seed):
+    c = draw(seed)
+    announce("random_decode", seed=seed, **c)
+    dev = device()
+    B, N, H, D, T, Hq = c["B"], c["N"], c["H"], c["D"], c["T"], c["H"] * c["G"]
+    q = rnd((B, T, Hq, D), c["dtype"], 3 * seed)
+    k = rnd((B, N, H, D), c["dtype"], 3 * seed + 1)
+    v = rnd((B, N, H, D), c["dtype"], 3 * seed + 2)
+    # one segment, or the cache cut in two at a random row (the second
+    # segment a separate allocation, as a refilled part would be)
+    s = c["split"]
+    pairs = [(k[:, :s].contiguous(), v[:, :s].contiguous())]
+    if s < N:
+        pairs.append((k[:, s:].contiguous(), v[:, s:].contiguous()))
+    scale = 1.0 / np.sqrt(D)
+    o, lse = K.decode_attn(q.to(dev), [(a.to(dev), b.to(dev)) for a, b in pairs], scale)
+    torch.cuda.synchronize()
+    want_o, want_lse = O.decode_attention(to64(q), [(to64(a), to64(b)) for a, b in pairs], scale)
+    assert_rel(o, want_o, 0.0, 5e-3, "decode output")
+    assert_rel(lse, want_lse, 0.0, 2e-3, "lse")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_aggregate(seed):
+    """Per-unit attention mass or mass x |v| (token path), or the chunk
+    combine of the scorer's partials (chunk path), grouped over instances."""
+    c = draw(seed)
+    rng = np.random.default_rng(2000 + seed)
+    signal = "vnorm" if rng.random() < 0.5 else "mass"
+    unit = c["unit"] if c["unit"] > 1 or rng.random() < 0.5 else int(rng.choice([1, 5]))
+    path = "chunk" if unit % 64 == 0 and signal == "mass" and rng.random() < 0.5 else "token"
+    B, H, D, T, Hq = c["B"], c["H"], c["D"], c["T"], c["H"] * c["G"]
+    N = c["N"] - c["N"] % unit if unit > 1 else c["N"]
+    group = B if rng.random() < 0.5 else 1
+    announce("random_aggregate", seed=seed, signal=signal, path=path, unit=unit, N=N, group=group,
+             **{k: c[k] for k in ("dtype", "D", "H", "G", "T", "B")})
+    dev = device()
+    q = rnd((B, T, Hq, D), c["dtype"], 5 * seed).to(dev)
+    k = rnd((B, N, H, D), c["dtype"], 5 * seed + 1, scale=1.5).to(dev)
+    v = rnd((B, N, H, D), c["dtype"], 5 * seed + 2).to(dev)
+    scale = 1.0 / np.sqrt(D)
+    if path == "chunk":
+        rm, rs, part = K.score(q, k, unit, scale, row_stats=True, partials=True)
+        got = K.aggregate(unit, group, "mass", part=part, row_max=rm, row_sum=rs, k=k)
+    else:
+        rm, rs, _ = K.score(q, k, unit, scale, row_stats=True, partials=False)
+        got = K.aggregate(unit, group, signal, q=q, k=k, v=v, row_max=rm, row_sum=rs)
+    torch.cuda.synchronize()
+    want = O.aggregate(to64(q), to64(k), to64(v), scale, signal, unit, group)
+    assert_rel(got, want, 2e-3, 0.0, "unit_score")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_topk(seed):
+    """Rows of random length and k, with continuous scores, heavy ties or
+    values packed into a narrow band: indices and values bit-exact."""
+    rng = np.random.default_rng(3000 + seed)
+    G = int(rng.integers(1, 5))
+    M = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 20000)),
+                        int(rng.integers(20000, 120000))]))
+    k = int(rng.integers(0, M + 1))
+    kind = str(rng.choice(["float", "ties", "band"]))
+    announce("random_topk", seed=seed, G=G, M=M, k=k, kind=kind)
+    if kind == "float":
+        s = rng.standard_normal((G, M)).astype(np.float32)
+    elif kind == "ties":
+        s = rng.integers(0, int(rng.integers(2, 200)), size=(G, M)).astype(np.float32)
+    else:
+        s = (3.0 + 1e-5 * rng.standard_normal((G, M))).astype(np.float32)
+    dev = device()
+    idx, val = K.topk(torch.from_numpy(s).to(dev), k, values=True)
+    torch.cuda.synchronize()
+    want = O.topk(s.astype(np.float64), k)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert np.array_equal(val.cpu().numpy(), np.take_along_axis(s, want, axis=1))
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_gather(seed):
+    """Kept units of random length gathered into the compact layout: bit-exact."""
+    c = draw(seed)
+    rng = np.random.default_rng(4000 + seed)
+    unit = int(rng.choice([1, 3, 64, 256]))
+    M = int(rng.integers(1, max(2, 3000 // unit)))
+    group = c["B"] if rng.random() < 0.5 else 1
+    kept = int(rng.integers(1, M + 1))
+    B, H, D = c["B"], c["H"], c["D"]
+    N = M * unit
+    announce("random_gather", seed=seed, unit=unit, M=M, kept=kept, group=group,
+             **{k: c[k] for k in ("dtype", "D", "H", "B")})
+    k = rnd((B, N, H, D), c["dtype"], 7 * seed)
+    v = rnd((B, N, H, D), c["dtype"], 7 * seed + 1)
+    idx = np.stack([np.sort(rng.choice(M, kept, replace=False)) for _ in range(B // group)])
+    dev = device()
+    gk, gv = K.gather(k.to(dev), v.to(dev), torch.from_numpy(idx).int().to(dev), unit, group)
+    torch.cuda.synchronize()
+    wk, wv = O.gather(to64(k), to64(v), idx, unit, group)
+    assert np.array_equal(to64(gk), wk) and np.array_equal(to64(gv), wv)
