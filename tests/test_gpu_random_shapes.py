@@ -1,5 +1,6 @@
-"""Seeded random shapes for the scorer, the aggregate, the top-k, the gather
-and the decode attention, against the oracle: rows per kv head drawn across
+"""Seeded random shapes for the scorer (plain and with re-positioning fused),
+the aggregate, the top-k, the gather, the decode attention (plain and with the
+refill fused) and the index-based causal attention, against the oracle: rows per kv head drawn across
 every plan boundary (the streaming kernels up to 8 rows, one 16-row block,
 four-wave plans up to 128 rows, eight-wave plans of two row blocks, several
 row passes), head dim 64 and 128, bf16 and fp32, ragged cache lengths, units
@@ -169,3 +170,108 @@ def test_random_gather(seed):
     torch.cuda.synchronize()
     wk, wv = O.gather(to64(k), to64(v), idx, unit, group)
     assert np.array_equal(to64(gk), wk) and np.array_equal(to64(gv), wv)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_score_reposition(seed):
+    """Re-positioning fused into the scorer: the same row statistics, bit for
+    bit, as re-positioning then scoring (and the same K' where it is kept),
+    and the oracle on the re-positioned keys."""
+    c = draw(seed)
+    rng = np.random.default_rng(5000 + seed)
+    rot = int(rng.choice([1, 8, 64, 128, 256, 512]))
+    M = int(rng.integers(1, max(2, 3000 // rot)))
+    N = M * rot
+    style = str(rng.choice(["half", "interleaved"]))
+    per_inst = bool(rng.random() < 0.5)
+    keep = bool(rng.random() < 0.5)
+    B, H, D, T, Hq = c["B"], c["H"], c["D"], c["T"], c["H"] * c["G"]
+    announce("random_score_reposition", seed=seed, rot=rot, N=N, style=style, per_inst=per_inst,
+             keep=keep, **{k: c[k] for k in ("dtype", "D", "H", "G", "T", "B")})
+    dev = device()
+    q = rnd((B, T, Hq, D), c["dtype"], 11 * seed).to(dev)
+    k = rnd((B, N, H, D), c["dtype"], 11 * seed + 1, 1.5).to(dev)
+    delta = torch.from_numpy(rng.integers(0, 66000, size=(B, M) if per_inst else (M,))).to(dev)
+    k_out = torch.empty_like(k) if keep else None
+    rm, rs, _ = K.score_reposition(q, k, delta, rot, 1, k_out=k_out, row_stats=True,
+                                   partials=False, style=style)
+    k_ref = K.reposition(k, delta, rot, style=style)
+    rm2, rs2, _ = K.score(q, k_ref, 1, row_stats=True, partials=False)
+    torch.cuda.synchronize()
+    assert torch.equal(rm, rm2) and torch.equal(rs, rs2)
+    if keep:
+        assert torch.equal(k_out, k_ref)
+    p_old = np.tile(np.arange(rot), M)
+    dl = delta.cpu().numpy() if per_inst else np.broadcast_to(delta.cpu().numpy(), (B, M))
+    p_new = p_old[None] + np.repeat(dl, rot, axis=1)
+    want_k = O.reposition(to64(k), np.broadcast_to(p_old, (B, N)), p_new, 10000.0, style,
+                          c["dtype"])
+    m, Z, _ = O.score(to64(q), want_k, 1.0 / np.sqrt(D), 1)
+    assert_rel(rm, m, 2e-3, 2e-3, "row_max")
+    assert_rel(rs, Z, 2e-3, 0.0, "row_sum")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_gather_decode(seed):
+    """Refill and decode in one call: the compact cache bit-exact, the
+    attention over it (after any extra segments) within tolerance."""
+    c = draw(seed)
+    rng = np.random.default_rng(6000 + seed)
+    unit = int(rng.choice([1, 3, 64, 256]))
+    M = int(rng.integers(1, max(2, 2500 // unit)))
+    kept = int(rng.integers(0, M + 1))
+    group = c["B"] if rng.random() < 0.5 else 1
+    n_extra = int(rng.integers(0 if kept else 1, 3))
+    extra_n = [int(rng.integers(1, 600)) for _ in range(n_extra)]
+    B, H, D, T, Hq = c["B"], c["H"], c["D"], c["T"], c["H"] * c["G"]
+    N = M * unit
+    announce("random_gather_decode", seed=seed, unit=unit, M=M, kept=kept, group=group,
+             extra=extra_n, **{k: c[k] for k in ("dtype", "D", "H", "G", "T", "B")})
+    dev = device()
+    q = rnd((B, T, Hq, D), c["dtype"], 13 * seed)
+    k = rnd((B, N, H, D), c["dtype"], 13 * seed + 1, 1.5)
+    v = rnd((B, N, H, D), c["dtype"], 13 * seed + 2)
+    extra = [(rnd((B, n, H, D), c["dtype"], 13 * seed + 3 + 2 * i, 1.5),
+              rnd((B, n, H, D), c["dtype"], 13 * seed + 4 + 2 * i)) for i, n in enumerate(extra_n)]
+    idx = np.stack([np.sort(rng.choice(M, kept, replace=False)) for _ in range(B // group)])
+    idx_t = torch.from_numpy(idx).int().to(dev).reshape(B // group, kept)
+    kd, vd, o, lse = K.gather_decode(q.to(dev), k.to(dev), v.to(dev), idx_t, unit, group,
+                                     extra=[(a.to(dev), b.to(dev)) for a, b in extra])
+    torch.cuda.synchronize()
+    wk, wv = O.gather(to64(k), to64(v), idx, unit, group)
+    assert np.array_equal(to64(kd), wk) and np.array_equal(to64(vd), wv)
+    segs = [(to64(a), to64(b)) for a, b in extra] + ([(wk, wv)] if kept else [])
+    wo, wl = O.decode_attention(to64(q), segs, 1.0 / np.sqrt(D))
+    assert_rel(o, wo, 0.0, 5e-3, "o")
+    assert_rel(lse, wl, 0.0, 2e-3, "lse")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_index_attn(seed):
+    """Selected tokens attending causally to the context, positions anywhere
+    (some before the first row, some past the last)."""
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.integers(1, 3))
+    H = int(rng.choice([1, 2, 4]))
+    Hq = H * int(rng.choice([1, 4, 7]))
+    D = int(rng.choice([64, 128, 128]))
+    N = int(rng.integers(1, 2500))
+    S = int(rng.integers(1, 300))
+    announce("random_index_attn", seed=seed, B=B, H=H, Hq=Hq, D=D, N=N, S=S)
+    dev = device()
+    g = torch.Generator().manual_seed(8000 + seed)
+    q = torch.randn((B, S, Hq, D), generator=g).to(torch.bfloat16)
+    k = (1.5 * torch.randn((B, N, H, D), generator=g)).to(torch.bfloat16)
+    v = torch.randn((B, N, H, D), generator=g).to(torch.bfloat16)
+    pos = rng.integers(-3, N + 3, size=(B, S))
+    if rng.random() < 0.5:
+        pos = np.sort(pos, axis=1)
+    pos = pos.astype(np.int32)
+    o, lse = K.index_attn(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(pos).to(dev))
+    torch.cuda.synchronize()
+    wo, wl = O.index_causal_attention(to64(q), to64(k), to64(v), pos, 1 / np.sqrt(D))
+    assert_rel(o, wo, 0.0, 5e-3, "output")
+    fin = np.isfinite(wl)
+    got_l = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert_rel(got_l[fin], wl[fin], 0.0, 5e-3, "lse")
