@@ -1,5 +1,5 @@
-"""Seeded random shapes for the scorer (plain and with re-positioning fused),
-the aggregate, the top-k, the gather, the decode attention (plain and with the
+"""Seeded random shapes for the scorer (plain, with re-positioning fused, and
+over listed units), the aggregate, the top-k, the gather, the decode attention (plain and with the
 refill fused) and the index-based causal attention, against the oracle: rows per kv head drawn across
 every plan boundary (the streaming kernels up to 8 rows, one 16-row block,
 four-wave plans up to 128 rows, eight-wave plans of two row blocks, several
@@ -275,3 +275,48 @@ def test_random_index_attn(seed):
     got_l = lse.cpu().numpy().astype(np.float64)
     assert np.array_equal(np.isfinite(got_l), fin)
     assert_rel(got_l[fin], wl[fin], 0.0, 5e-3, "lse")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_score_units(seed):
+    """Listed units of a cache (repeats allowed), re-positioned to random
+    positions or not, scored in place: row statistics and per-unit partials
+    against the oracle on the concatenated, re-positioned copy."""
+    c = draw(seed)
+    rng = np.random.default_rng(9000 + seed)
+    U = int(rng.choice([64, 96, 128, 256, 512]))
+    n_src = int(rng.integers(1, max(2, 2500 // U)))
+    n = int(rng.integers(1, 2 * n_src + 1))
+    dmode = str(rng.choice(["none", "shared", "inst"]))
+    style = str(rng.choice(["half", "interleaved"]))
+    B, H, D, T, Hq = c["B"], c["H"], c["D"], c["T"], c["H"] * c["G"]
+    announce("random_score_units", seed=seed, U=U, n_src=n_src, n=n, dmode=dmode, style=style,
+             **{k: c[k] for k in ("dtype", "D", "H", "G", "T", "B")})
+    dev = device()
+    k = rnd((B, n_src * U, H, D), c["dtype"], 17 * seed, 1.5)
+    q = rnd((B, T, Hq, D), c["dtype"], 17 * seed + 1)
+    units = rng.integers(0, n_src, size=(B, n))
+    if dmode == "shared":
+        delta = rng.integers(0, 60000, size=(n,))
+    elif dmode == "inst":
+        delta = rng.integers(-40000, 40000, size=(B, n))
+    else:
+        delta = None
+    scale = 1.0 / np.sqrt(D)
+    rm, rs, part = K.score_units(q.to(dev), k.to(dev), torch.from_numpy(units.astype(np.int32)).to(dev),
+                                 U, delta=None if delta is None else torch.from_numpy(delta).to(dev),
+                                 scale=scale, style=style)
+    torch.cuda.synchronize()
+    k64 = to64(k)
+    rows = (units[:, :, None] * U + np.arange(U)[None, None, :]).reshape(B, n * U)
+    concat = np.stack([k64[b, rows[b]] for b in range(B)])
+    if delta is not None:
+        p_old = np.tile(np.arange(U), n)
+        p_new = p_old[None] + np.repeat(np.broadcast_to(delta, (B, n)), U, axis=1)
+        concat = O.reposition(concat, np.broadcast_to(p_old, (B, n * U)), p_new, 10000.0, style,
+                              c["dtype"])
+    m, Z, p = O.score(to64(q), concat, scale, U)
+    assert_rel(rm, m, 2e-3, 2e-3, "row_max")
+    assert_rel(rs, Z, 2e-3, 0.0, "row_sum")
+    assert_rel(part[..., 0], p[..., 0], 2e-3, 2e-3, "m_u")
+    assert_rel(part[..., 1], p[..., 1], 2e-3, 0.0, "S_u")
