@@ -675,6 +675,8 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
 // reads 16 bytes (4 dims) of each of its splits' partial outputs, so a row's
 // partials are all in flight at once.  The groups' maxima, sums and outputs
 // meet in LDS.  Partial outputs start at a 16-byte boundary of the workspace.
+// A thread's first PF splits (every split of up to PF * NG) are loaded whole
+// before the row's maximum is known, so the partials take one trip to memory.
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const float* __restrict__ ws_ms, const float* __restrict__ ws_o,
@@ -682,14 +684,30 @@ decode_merge_kernel(const float* __restrict__ ws_ms, const float* __restrict__ w
                     float* __restrict__ lse) {
   constexpr int LPS = D / 4;       // threads per split (4 dims each)
   constexpr int NG = 256 / LPS;    // split groups
+  constexpr int PF = 4;            // splits per thread held in registers
   __shared__ float gmax[NG], gsum[NG];
   __shared__ float4 gacc[NG][LPS];
   const int64_t row = blockIdx.x;  // (b*Hq + h)*T + j
   const int gi = threadIdx.x / LPS, li = threadIdx.x % LPS;
   const float* ms = ws_ms + row * n_split * 2;   // (m_i, s_i) pairs
   const float4* po = reinterpret_cast<const float4*>(ws_o + row * n_split * D) + li;
+  float pm[PF], psum[PF];
+  float4 pov[PF];
   float m = -INFINITY;
-  for (int64_t i = gi; i < n_split; i += NG) m = fmaxf(m, ms[2 * i]);
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int64_t i = gi + j * NG;
+    pm[j] = -INFINITY;   // past the last split: weight 0
+    psum[j] = 0.0f;
+    pov[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (i < n_split) {
+      pm[j] = ms[2 * i];
+      psum[j] = ms[2 * i + 1];
+      pov[j] = po[i * (D / 4)];
+    }
+    m = fmaxf(m, pm[j]);
+  }
+  for (int64_t i = gi + PF * NG; i < n_split; i += NG) m = fmaxf(m, ms[2 * i]);
   if (li == 0) gmax[gi] = m;
   __syncthreads();
   m = gmax[0];
@@ -699,8 +717,17 @@ decode_merge_kernel(const float* __restrict__ ws_ms, const float* __restrict__ w
   const float ref = m == -INFINITY ? 0.0f : m;
   float s = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const float a = __builtin_amdgcn_exp2f(pm[j] - ref);
+    s = fmaf(psum[j], a, s);
+    acc.x = fmaf(pov[j].x, a, acc.x);
+    acc.y = fmaf(pov[j].y, a, acc.y);
+    acc.z = fmaf(pov[j].z, a, acc.z);
+    acc.w = fmaf(pov[j].w, a, acc.w);
+  }
 #pragma unroll 4
-  for (int64_t i = gi; i < n_split; i += NG) {
+  for (int64_t i = gi + PF * NG; i < n_split; i += NG) {
     const float a = __builtin_amdgcn_exp2f(ms[2 * i] - ref);
     const float4 p = po[i * (D / 4)];
     s = fmaf(ms[2 * i + 1], a, s);
