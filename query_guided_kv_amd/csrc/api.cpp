@@ -22,6 +22,13 @@ void set_error(const char* fmt, ...) {
   va_end(ap);
 }
 
+RopeTheta rope_theta(double base, int64_t D) {
+  RopeTheta th{};
+  for (int64_t i = 0; i < D / 2 && i < 64; ++i)
+    th.t[i] = std::pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(D));
+  return th;
+}
+
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess) return KVSEL_OK;

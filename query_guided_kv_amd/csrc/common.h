@@ -136,12 +136,12 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
 }
 
 // ---------------------------------------------------------------------------
-// RoPE: per-pair cos/sin of delta * theta_i in fp64, theta_i = base^(-2i/D).
-// The 2x2 rotation is also done in fp64 and rounded once to the cache dtype,
-// so a re-positioned key is the correctly rounded rotation of the stored one.
+// RoPE: per-pair cos/sin of delta * theta_i in fp64, theta_i = base^(-2i/D)
+// (the table comes from the host, RopeTheta).  The 2x2 rotation is also done
+// in fp64 and rounded once to the cache dtype, so a re-positioned key is the
+// correctly rounded rotation of the stored one.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double2 rope_cs(int64_t delta, int i, int D, double base) {
-  const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(D));
+__device__ __forceinline__ double2 rope_cs(int64_t delta, double theta) {
   const double ang = static_cast<double>(delta) * theta;
   double s, c;
   sincos(ang, &s, &c);

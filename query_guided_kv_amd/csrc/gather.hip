@@ -25,7 +25,7 @@ __global__ void __launch_bounds__(kThreads)
 gather_kernel(const T* __restrict__ ksrc, const T* __restrict__ vsrc, int H, int64_t stride_b,
               int64_t stride_n, int64_t U, const int32_t* __restrict__ idx, int64_t k,
               int64_t idx_group, const int64_t* __restrict__ src_start, int64_t align_base,
-              double base, int64_t chunks, int64_t rows_per_chunk, int64_t dst_rows,
+              RopeTheta th, int64_t chunks, int64_t rows_per_chunk, int64_t dst_rows,
               int64_t M, T* __restrict__ kdst, T* __restrict__ vdst) {
   constexpr int V = Elem<T>::kPerVec;
   constexpr int HALF = D / 2;
@@ -44,7 +44,7 @@ gather_kernel(const T* __restrict__ ksrc, const T* __restrict__ vsrc, int H, int
 
   if constexpr (ALIGN) {
     const int64_t delta = align_base + r * U - (src_start ? src_start[u] : 0);
-    for (int i = threadIdx.x; i < HALF; i += kThreads) cs[i] = rope_cs(delta, i, D, base);
+    for (int i = threadIdx.x; i < HALF; i += kThreads) cs[i] = rope_cs(delta, th.t[i]);
     __syncthreads();
   }
 
@@ -148,7 +148,8 @@ void launch_g(const void* k_src, const void* v_src, const kvsel_cache& kc, int64
                      dim3(static_cast<unsigned>(kc.B * k * chunks)), dim3(kThreads), 0, s,
                      static_cast<const T*>(k_src), static_cast<const T*>(v_src),
                      static_cast<int>(kc.H), kc.stride_b, kc.stride_n, U, idx, k, idx_group,
-                     src_start, align_base, base, chunks, rows_per_chunk, dst_rows, kc.N / U,
+                     src_start, align_base, ALIGN ? rope_theta(base, D) : RopeTheta{}, chunks,
+                     rows_per_chunk, dst_rows, kc.N / U,
                      static_cast<T*>(k_dst), static_cast<T*>(v_dst));
 }
 

@@ -20,6 +20,14 @@ constexpr int kMfmaTileKeys = 64;
 // decode_split_len gives the length a call actually uses).
 constexpr int kDecodeSplit = 512;
 
+// The RoPE frequencies theta_i = base^(-2i/D), i < D/2, formed once per call
+// on the host in fp64 (the C library's pow) and passed to the kernels by value,
+// so that no workgroup spends its start on a pow chain.
+struct RopeTheta {
+  double t[64];
+};
+RopeTheta rope_theta(double base, int64_t D);
+
 int launch_reposition(const void* k_in, void* k_out, const kvsel_cache& kc, int64_t unit_len,
                       const int64_t* delta, int per_instance, double base, int style,
                       hipStream_t s);

@@ -19,7 +19,7 @@ template <typename T, int D, int STYLE>
 __global__ void __launch_bounds__(kThreads)
 reposition_kernel(const T* kin, T* kout, int64_t N, int H, int64_t stride_b,
                   int64_t stride_n, int64_t unit_len, const int64_t* __restrict__ delta,
-                  int64_t delta_stride_b, int64_t tiles, double base) {
+                  int64_t delta_stride_b, int64_t tiles, RopeTheta th) {
   constexpr int V = Elem<T>::kPerVec;
   constexpr int HALF = D / 2;
   __shared__ double2 cs[kRows][HALF];
@@ -32,7 +32,7 @@ reposition_kernel(const T* kin, T* kout, int64_t N, int H, int64_t stride_b,
   const int64_t* db = delta + b * delta_stride_b;
   for (int e = threadIdx.x; e < nu * HALF; e += kThreads) {
     const int uu = e / HALF, i = e - uu * HALF;
-    cs[uu][i] = rope_cs(db[u0 + uu], i, D, base);
+    cs[uu][i] = rope_cs(db[u0 + uu], th.t[i]);
   }
   __syncthreads();
 
@@ -82,7 +82,7 @@ void launch_t(const void* k_in, void* k_out, const kvsel_cache& kc, int64_t unit
   hipLaunchKernelGGL((reposition_kernel<T, D, STYLE>), dim3(static_cast<unsigned>(kc.B * tiles)),
                      dim3(kThreads), 0, s, static_cast<const T*>(k_in), static_cast<T*>(k_out),
                      kc.N, static_cast<int>(kc.H), kc.stride_b, kc.stride_n, unit_len, delta,
-                     per_instance ? M : int64_t{0}, tiles, base);
+                     per_instance ? M : int64_t{0}, tiles, rope_theta(base, D));
 }
 
 }  // namespace

@@ -45,8 +45,8 @@ struct ScoreRot {
   const int64_t* delta;      // [M] or [B][M] (delta_stride_b = M)
   int64_t delta_stride_b;
   int64_t rot_len;
-  double base;
   bf16_t* kout;              // same layout as k, or NULL
+  RopeTheta theta;           // theta_i of the call's base and head dim
 };
 
 // D: head dim; RBW: row blocks per wave; NWR: waves across row blocks; NW:
@@ -246,7 +246,7 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
     if constexpr (ROT != 0) {
       if (rc.u != cs_unit) {
         const int64_t delta = rot.delta[b * rot.delta_stride_b + rc.u];
-        for (int i = threadIdx.x; i < D / 2; i += kThreads) cs[i] = rope_cs(delta, i, D, rot.base);
+        for (int i = threadIdx.x; i < D / 2; i += kThreads) cs[i] = rope_cs(delta, rot.theta.t[i]);
         cs_unit = rc.u;
         __syncthreads();
         load_cs();
@@ -458,7 +458,7 @@ bool score_mfma_rot_ok(int dtype, int64_t rows_per_kv, int64_t seg_len, int64_t 
 void launch_score_mfma(const void* q, int64_t T, int64_t Hq, const void* k,
                        const kvsel_cache& kc, float scale2, int64_t seg_len, int64_t nseg,
                        float* ms, int natural, hipStream_t s) {
-  const ScoreRot none{nullptr, 0, 1, 0.0, nullptr};
+  const ScoreRot none{nullptr, 0, 1, nullptr, RopeTheta{}};
   const UnitMap all{nullptr, 0, 1, 0};
   if (kc.D == 128)
     dispatch<128, 0, false>(q, T, Hq, k, kc, scale2, seg_len, nseg, ms, natural, none, all, s);
@@ -471,8 +471,8 @@ void launch_score_mfma_rot(const void* q, int64_t T, int64_t Hq, const void* k, 
                            float* ms, int natural, int64_t rot_len, const int64_t* delta,
                            int per_instance, double base, int style, hipStream_t s) {
   const float scale2 = scale * kLog2e;
-  const ScoreRot rot{delta, per_instance ? kc.N / rot_len : 0, rot_len, base,
-                     static_cast<bf16_t*>(k_out)};
+  const ScoreRot rot{delta, per_instance ? kc.N / rot_len : 0, rot_len,
+                     static_cast<bf16_t*>(k_out), rope_theta(base, kc.D)};
   const bool w = k_out != nullptr;
   const UnitMap all{nullptr, 0, 1, 0};
 #define KVSEL_SR(D_, ST)                                                                   \
@@ -494,7 +494,8 @@ void launch_score_mfma_units(const void* q, int64_t T, int64_t Hq, const void* k
   const float scale2 = scale * kLog2e;
   kvsel_cache kv = kc;  // N = scored rows; strides stay the source's
   kv.N = map.n_units * map.unit_len;
-  const ScoreRot rot{delta, per_instance ? map.n_units : 0, map.unit_len, base, nullptr};
+  const ScoreRot rot{delta, per_instance ? map.n_units : 0, map.unit_len, nullptr,
+                     delta != nullptr ? rope_theta(base, kc.D) : RopeTheta{}};
 #define KVSEL_SU(D_, ST) \
   dispatch<D_, ST, false>(q, T, Hq, k, kv, scale2, seg_len, nseg, ms, natural, rot, map, s);
   if (kc.D == 128) {
