@@ -40,9 +40,9 @@ agg_chunk_kernel(const float* __restrict__ part, const float* __restrict__ row_m
   static_assert(kThreads == 4 * kAggChunkRows, "4 lanes per row derive its statistics");
   __shared__ float red[kAggRowLanes][kAggUnits];
   __shared__ float s_m[DERIVE ? kAggChunkRows : 1], s_iz[DERIVE ? kAggChunkRows : 1];
-  const int64_t uc = blockIdx.x % n_uc;
-  const int64_t rc = (blockIdx.x / n_uc) % n_rc;
-  const int64_t gi = blockIdx.x / (n_uc * n_rc);
+  const int64_t uc = blockIdx.x % static_cast<uint32_t>(n_uc);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t rc = (blockIdx.x / static_cast<uint32_t>(n_uc)) % static_cast<uint32_t>(n_rc);
+  const int64_t gi = blockIdx.x / static_cast<uint32_t>(n_uc * n_rc);
   const int ul = threadIdx.x % kAggUnits, rl = threadIdx.x / kAggUnits;
   const int64_t u = uc * kAggUnits + ul;
   const int64_t r0 = rc * kAggChunkRows;
@@ -113,8 +113,8 @@ agg_token_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   __shared__ __align__(16) float qs[kQRows][D + kPad];
   __shared__ float mz[kQRows][2];
 
-  const int64_t b = blockIdx.x / tiles;
-  const int64_t t = (blockIdx.x % tiles) * TPB + threadIdx.x / TPR;
+  const int64_t b = blockIdx.x / static_cast<uint32_t>(tiles);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t t = static_cast<int64_t>(blockIdx.x % static_cast<uint32_t>(tiles)) * TPB + threadIdx.x / TPR;
   const int p = threadIdx.x % TPR;
   const bool t_ok = t < N;
   const int G = Hq / H;
@@ -182,8 +182,8 @@ __global__ void __launch_bounds__(kThreads)
 unit_sum_kernel(const float* __restrict__ per_token, int64_t parts, int64_t part_stride,
                 int64_t N, int64_t unit_len, int64_t M, int64_t group, int64_t mblocks,
                 int accumulate, float* __restrict__ out) {
-  const int64_t gi = blockIdx.x / mblocks;
-  const int64_t u = (blockIdx.x % mblocks) * kThreads + threadIdx.x;
+  const int64_t gi = blockIdx.x / static_cast<uint32_t>(mblocks);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t u = static_cast<int64_t>(blockIdx.x % static_cast<uint32_t>(mblocks)) * kThreads + threadIdx.x;
   if (u >= M) return;
   float acc = 0.0f;
   for (int64_t p = 0; p < parts; ++p) {

@@ -50,10 +50,10 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ float part[NW][kTileKeys];
   __shared__ float tot[kMaxRange];
 
-  int64_t x = blockIdx.x;
-  const int64_t grp = x % parts; x /= parts;
-  const int64_t b = x / ranges;
-  const int64_t t_begin = (x % ranges) * range;
+  uint32_t x = blockIdx.x;   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t grp = x % static_cast<uint32_t>(parts); x /= static_cast<uint32_t>(parts);
+  const int64_t b = x / static_cast<uint32_t>(ranges);
+  const int64_t t_begin = static_cast<int64_t>(x % static_cast<uint32_t>(ranges)) * range;
   const int64_t t_end = min(N, t_begin + range);
   const int G = Hq / H;
   const int R = G * T;

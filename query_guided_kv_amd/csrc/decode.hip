@@ -83,8 +83,8 @@ decode_stream_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64
   const int slot = lane / LPT;
   const int g = (lane % LPT) / LPH;
   const int c = lane % LPH;
-  const int64_t b = blockIdx.x / n_split;
-  const int64_t sp = blockIdx.x % n_split;
+  const int64_t b = blockIdx.x / static_cast<uint32_t>(n_split);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t sp = blockIdx.x % static_cast<uint32_t>(n_split);
   const int sg = find_seg(st, n_seg, sp);
   const int64_t t_begin = (sp - st.split_begin[sg]) * st.split_len;
   const int64_t t_end = min(st.N[sg], t_begin + st.split_len);
@@ -283,11 +283,11 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
   __shared__ __align__(16) float ks[kTileKeys][D + kPad];
   __shared__ __align__(16) float vs[kTileKeys][D + kPad];
 
-  int64_t x = blockIdx.x;
-  const int64_t sp = x % n_split; x /= n_split;
-  const int64_t pass = x % passes; x /= passes;
-  const int g = static_cast<int>(x % H);
-  const int64_t b = x / H;
+  uint32_t x = blockIdx.x;   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t sp = x % static_cast<uint32_t>(n_split); x /= static_cast<uint32_t>(n_split);
+  const int64_t pass = x % static_cast<uint32_t>(passes); x /= static_cast<uint32_t>(passes);
+  const int g = static_cast<int>(x % static_cast<uint32_t>(H));
+  const int64_t b = x / static_cast<uint32_t>(H);
   const int sg = find_seg(st, n_seg, sp);
   const int64_t t_begin = (sp - st.split_begin[sg]) * st.split_len;
   const int64_t t_end = min(st.N[sg], t_begin + st.split_len);
@@ -446,11 +446,11 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   __shared__ __align__(16) bf16_t vt[SPLIT ? TK * KROW : D * VROW];
 
   const int nwaves = NW;
-  int64_t x = blockIdx.x;
-  const int64_t sp = x % n_split; x /= n_split;
-  const int pass = static_cast<int>(x % passes); x /= passes;
-  const int g = static_cast<int>(x % H);
-  const int64_t b = x / H;
+  uint32_t x = blockIdx.x;   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t sp = x % static_cast<uint32_t>(n_split); x /= static_cast<uint32_t>(n_split);
+  const int pass = static_cast<int>(x % static_cast<uint32_t>(passes)); x /= static_cast<uint32_t>(passes);
+  const int g = static_cast<int>(x % static_cast<uint32_t>(H));
+  const int64_t b = x / static_cast<uint32_t>(H);
   const int sg = find_seg(st, n_seg, sp);
   const int64_t t_begin = (sp - st.split_begin[sg]) * st.split_len;
   const int64_t t_end = min(st.N[sg], t_begin + st.split_len);

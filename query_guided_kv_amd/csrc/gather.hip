@@ -31,10 +31,10 @@ gather_kernel(const T* __restrict__ ksrc, const T* __restrict__ vsrc, int H, int
   constexpr int HALF = D / 2;
   __shared__ double2 cs[ALIGN ? HALF : 1];
 
-  const int64_t chunk = blockIdx.x % chunks;
-  const int64_t br = blockIdx.x / chunks;
-  const int64_t r = br % k;
-  const int64_t b = br / k;
+  const int64_t chunk = blockIdx.x % static_cast<uint32_t>(chunks);   // 32-bit: the grid is below 2^32 workgroups
+  const uint32_t br = blockIdx.x / static_cast<uint32_t>(chunks);
+  const int64_t r = br % static_cast<uint32_t>(k);
+  const int64_t b = br / static_cast<uint32_t>(k);
   const int64_t u = idx[(b / idx_group) * k + r];
   if (u < 0 || u >= M) return;  // invalid index: leave the slot untouched
   const int64_t t0 = chunk * rows_per_chunk;
@@ -106,8 +106,8 @@ proxy_copy_kernel(const T* __restrict__ kp, const T* __restrict__ vp, int64_t m,
                   T* __restrict__ kdst, T* __restrict__ vdst) {
   constexpr int V = Elem<T>::kPerVec;
   __shared__ int64_t dst_row[kProxyRows];
-  const int64_t b = blockIdx.x / tiles;
-  const int64_t j0 = (blockIdx.x % tiles) * kProxyRows;
+  const int64_t b = blockIdx.x / static_cast<uint32_t>(tiles);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x % static_cast<uint32_t>(tiles)) * kProxyRows;
   const int rows = static_cast<int>(min<int64_t>(kProxyRows, m - j0));
   const int32_t* sel = idx + (b / idx_group) * k;
   if (threadIdx.x < rows) {

@@ -24,8 +24,8 @@ reposition_kernel(const T* kin, T* kout, int64_t N, int H, int64_t stride_b,
   constexpr int HALF = D / 2;
   __shared__ double2 cs[kRows][HALF];
 
-  const int64_t b = blockIdx.x / tiles;
-  const int64_t r0 = (blockIdx.x % tiles) * kRows;
+  const int64_t b = blockIdx.x / static_cast<uint32_t>(tiles);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x % static_cast<uint32_t>(tiles)) * kRows;
   const int rows = static_cast<int>(min<int64_t>(kRows, N - r0));
   const int64_t u0 = r0 / unit_len;
   const int nu = static_cast<int>((r0 + rows - 1) / unit_len - u0 + 1);

@@ -111,8 +111,8 @@ score_stream_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   // a workgroup scores spb consecutive segments (one partial each): the
   // query slices are loaded once and the per-segment fixed cost is shared
   const int64_t groups = (nseg + spb - 1) / spb;
-  const int64_t b = blockIdx.x / groups;
-  const int64_t seg0 = (blockIdx.x % groups) * spb;
+  const int64_t b = blockIdx.x / static_cast<uint32_t>(groups);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t seg0 = static_cast<int64_t>(blockIdx.x % static_cast<uint32_t>(groups)) * spb;
   const int64_t seg1 = min(nseg, seg0 + spb);
   const int G = Hq / H;
   // the block of (row, key) pairs this lane owns after the scatter
@@ -250,10 +250,10 @@ score_tile_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t N, i
   constexpr int V = Elem<T>::kPerVec;
   __shared__ __align__(16) float ks[kTileKeys][D + kPad];
 
-  const int64_t seg = blockIdx.x % nseg;
-  const int64_t bg = blockIdx.x / nseg;
-  const int g = static_cast<int>(bg % H);
-  const int64_t b = bg / H;
+  const int64_t seg = blockIdx.x % static_cast<uint32_t>(nseg);   // 32-bit: the grid is below 2^32 workgroups
+  const uint32_t bg = blockIdx.x / static_cast<uint32_t>(nseg);
+  const int g = static_cast<int>(bg % static_cast<uint32_t>(H));
+  const int64_t b = bg / static_cast<uint32_t>(H);
   const int G = Hq / H;
   const int R = G * T_;
   const int rl = threadIdx.x / TPR;

@@ -78,11 +78,13 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   // heads of the same cached rows, so their 256-byte pieces of each row are
   // fetched close together (32 kv heads, 8 KiB rows: 43.8 -> 41.5 us; no
   // change with 4 or 8 kv heads)
-  int64_t x = blockIdx.x;
-  const int g = static_cast<int>(x % H); x /= H;
-  const int64_t grp = x % groups; x /= groups;
-  const int pass = static_cast<int>(x % passes);
-  const int64_t b = x / passes;
+  // in 32 bits (the grid is below 2^32 workgroups): a 64-bit division by a
+  // runtime value is a long scalar sequence that every workgroup would run
+  uint32_t x = blockIdx.x;
+  const int g = static_cast<int>(x % static_cast<uint32_t>(H)); x /= static_cast<uint32_t>(H);
+  const int64_t grp = x % static_cast<uint32_t>(groups); x /= static_cast<uint32_t>(groups);
+  const int pass = static_cast<int>(x % static_cast<uint32_t>(passes));
+  const int64_t b = x / static_cast<uint32_t>(passes);
   const int G = Hq / H;
   const int R = G * T;
   const int lane = threadIdx.x & 63;
@@ -136,7 +138,9 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
     }
   };
   auto cursor_at = [&](int64_t len) {
-    const int64_t u = t_begin / len;
+    const int64_t u = (t_begin >> 32) == 0 && (len >> 32) == 0
+                          ? static_cast<int64_t>(static_cast<uint32_t>(t_begin) / static_cast<uint32_t>(len))
+                          : t_begin / len;
     return Cursor{u, t_begin - u * len, len};
   };
   // per-thread offsets of the tile's vectors from the tile's first row

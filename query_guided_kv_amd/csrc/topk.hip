@@ -351,8 +351,8 @@ order_kernel(const float* __restrict__ score, int64_t M, const int32_t* __restri
              float* __restrict__ val_out) {
   __shared__ uint32_t skey[kOrderTile];
   __shared__ int32_t sidx[kOrderTile];
-  const int64_t g = blockIdx.x / jblocks;
-  const int64_t j = (blockIdx.x % jblocks) * kOrderThreads + threadIdx.x;
+  const int64_t g = blockIdx.x / static_cast<uint32_t>(jblocks);   // 32-bit: the grid is below 2^32 workgroups
+  const int64_t j = static_cast<int64_t>(blockIdx.x % static_cast<uint32_t>(jblocks)) * kOrderThreads + threadIdx.x;
   const int32_t* in = idx + g * k;
   const float* sc = score + g * M;
   auto key_of = [&](int32_t i) -> uint32_t { return (i >= 0 && i < M) ? order_key(sc[i]) : 0u; };
