@@ -238,7 +238,7 @@ def kernel_of(stage: str, w) -> str:
     return {"score": "score_stream_kernel" if stream else
                      "score_mfma_kernel" if mfma else "score_tile_kernel",
             "aggregate": "agg_mfma_kernel" if mfma else "agg_token_kernel",
-            "topk": "topk_reg_kernel" if w.N // w.unit_len <= 16384 else "topk_stream_kernel",
+            "topk": "topk_reg_kernel" if w.N // w.unit_len <= 65536 else "topk_stream_kernel",
             "gather": "gather_kernel",
             "decode": decode_kernel(w, rows) + MERGE,
             "gather_decode": "decode_stream_kernel" + MERGE}[stage]

@@ -13,10 +13,11 @@
 //     indices; a block-wide exclusive scan of both counts gives every kept
 //     index its output slot, so the kept set is written in ascending index
 //     order with no sort.
-// Rows of up to 16 * 1024 scores keep each thread's slice in registers and
-// read the scores once; longer rows read them again for every pass (coalesced
-// reads of a row the L2 holds), since their slices would not fit in the
-// registers of a 1024-thread workgroup.
+// Rows of up to 64 * 1024 scores keep each thread's slice in registers and
+// read the scores once, with 16-byte loads that are all in flight together;
+// longer rows read them again for every pass (coalesced reads of a row the L2
+// holds), since their slices would not fit in the registers of a 1024-thread
+// workgroup.
 #include "common.h"
 #include "internal.h"
 
@@ -28,7 +29,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kFastBits = 11;
 constexpr int kFastBins = 1 << kFastBits;
 constexpr int kFastCand = 256;
-constexpr int kRegKeys = 16;   // keys per thread held in registers, at most
+constexpr int kRegKeys = 64;   // keys per thread held in registers, at most
 static_assert(kFastBins == 2 * kThreads, "two bins per thread in the bin scan");
 static_assert(kFastCand <= kThreads, "one candidate per thread in the ranking");
 
@@ -77,15 +78,25 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
   pb = sb[wave] + ib - b;
 }
 
-// Keys of a row held in registers: indices i0 .. i0 + KPT - 1 of this thread.
+// Row indices stay below 2^31 (the int32 output), so a slice's indices and
+// counts are 32-bit: 64-bit index arithmetic per unrolled key would cost
+// registers.  The number of a slice's KPT indices from i0 that lie in a row
+// of M:
+template <int KPT>
+__device__ __forceinline__ int slice_valid(uint32_t i0, uint32_t M) {
+  return i0 >= M ? 0 : static_cast<int>(min(static_cast<uint32_t>(KPT), M - i0));
+}
+
+// Keys of a row held in registers: this thread's slice of KPT indices, the
+// first nv of them inside the row.
 template <int KPT>
 struct RegKeys {
   uint32_t key[KPT];
-  int64_t i0, M;
+  int nv;
   template <typename F>
   __device__ __forceinline__ void each(F f) const {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) f(i0 + e < M, key[e]);
+    for (int e = 0; e < KPT; ++e) f(e < nv, key[e]);
   }
 };
 
@@ -96,18 +107,18 @@ constexpr int kBatch = 16;
 // Keys of a row read for every pass: indices threadIdx.x + r * kThreads.
 struct StreamKeys {
   const float* s;
-  int64_t M;
+  uint32_t M;
   template <typename F>
   __device__ __forceinline__ void each(F f) const {
-    for (int64_t i0 = threadIdx.x; i0 < M; i0 += kBatch * kThreads) {
+    for (uint32_t i0 = threadIdx.x; i0 < M; i0 += kBatch * kThreads) {
       uint32_t key[kBatch];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        const int64_t i = i0 + static_cast<int64_t>(b) * kThreads;
+        const uint32_t i = i0 + static_cast<uint32_t>(b) * kThreads;
         key[b] = i < M ? order_key(s[i]) : 0u;
       }
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) f(i0 + static_cast<int64_t>(b) * kThreads < M, key[b]);
+      for (int b = 0; b < kBatch; ++b) f(i0 + static_cast<uint32_t>(b) * kThreads < M, key[b]);
     }
   }
 };
@@ -213,11 +224,12 @@ __device__ __forceinline__ void range_select(const Keys& keys, uint32_t k, TopkS
   need_eq = sm.need;
 }
 
-// KPT consecutive keys of indices i0 .. i0 + KPT - 1 (those past M read as 0).
+// KPT consecutive keys of indices i0 .. i0 + KPT - 1, the first nv inside the
+// row (the rest read as 0).
 template <int KPT>
-__device__ __forceinline__ void load_slice(const float* s, int64_t i0, int64_t M,
+__device__ __forceinline__ void load_slice(const float* s, uint32_t i0, int nv,
                                            uint32_t (&key)[KPT]) {
-  if (KPT % 4 == 0 && i0 + KPT <= M && (reinterpret_cast<uintptr_t>(s + i0) & 15u) == 0) {
+  if (KPT % 4 == 0 && nv == KPT && (reinterpret_cast<uintptr_t>(s + i0) & 15u) == 0) {
     // a whole 16-byte aligned slice: vector loads (a quarter of the requests)
 #pragma unroll
     for (int e = 0; e < KPT; e += 4) {
@@ -231,7 +243,7 @@ __device__ __forceinline__ void load_slice(const float* s, int64_t i0, int64_t M
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) key[e] = i0 + e < M ? order_key(s[i0 + e]) : 0u;
+    for (int e = 0; e < KPT; ++e) key[e] = e < nv ? order_key(s[i0 + e]) : 0u;
   }
 }
 
@@ -239,15 +251,15 @@ __device__ __forceinline__ void load_slice(const float* s, int64_t i0, int64_t M
 // owns the slice tile0 + t * KPT .. + KPT - 1.  gt_run / eq_run count the kept
 // keys (> K*, == K*) of earlier tiles and are advanced past this one.
 template <int KPT>
-__device__ __forceinline__ void write_tile(const uint32_t (&key)[KPT], int64_t tile0, int64_t M,
+__device__ __forceinline__ void write_tile(const uint32_t (&key)[KPT], uint32_t tile0, int nv,
                                            uint32_t kstar, uint32_t need_eq, uint32_t& gt_run,
                                            uint32_t& eq_run, TopkShared& sm, const float* s,
                                            int32_t* out_i, float* out_v) {
-  const int64_t i0 = tile0 + static_cast<int64_t>(threadIdx.x) * KPT;
+  const uint32_t i0 = tile0 + threadIdx.x * KPT;
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
-    const bool in = i0 + e < M;
+    const bool in = e < nv;
     n_gt += in && key[e] > kstar;
     n_eq += in && key[e] == kstar;
   }
@@ -257,14 +269,14 @@ __device__ __forceinline__ void write_tile(const uint32_t (&key)[KPT], int64_t t
   gt_before += gt_run;
   eq_before += eq_run;
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    if (i0 + e >= M) break;
-    if (key[e] > kstar) {
+  for (int e = 0; e < KPT; ++e) {   // a fixed trip count, so the keys stay in registers
+    const bool in = e < nv;
+    if (in && key[e] > kstar) {
       const uint32_t pos = gt_before + min(eq_before, need_eq);
       out_i[pos] = static_cast<int32_t>(i0 + e);
       if (out_v) out_v[pos] = s[i0 + e];
       ++gt_before;
-    } else if (key[e] == kstar) {
+    } else if (in && key[e] == kstar) {
       if (eq_before < need_eq) {
         const uint32_t pos = gt_before + eq_before;
         out_i[pos] = static_cast<int32_t>(i0 + e);
@@ -279,7 +291,8 @@ __device__ __forceinline__ void write_tile(const uint32_t (&key)[KPT], int64_t t
 }
 
 // Rows of up to KPT * 1024 scores (KPT <= kRegKeys): each thread keeps its
-// contiguous slice of KPT keys in registers, so the scores are read once.
+// contiguous slice of KPT keys in registers, so the scores are read once and
+// compacted in one tile.
 template <int KPT>
 __global__ void __launch_bounds__(kThreads)
 topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* __restrict__ idx,
@@ -289,13 +302,13 @@ topk_reg_kernel(const float* __restrict__ score, int64_t M, int64_t k, int32_t* 
   int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
   float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
   RegKeys<KPT> keys;
-  keys.i0 = static_cast<int64_t>(threadIdx.x) * KPT;
-  keys.M = M;
-  load_slice<KPT>(s, keys.i0, M, keys.key);
+  const uint32_t i0 = threadIdx.x * KPT;
+  keys.nv = slice_valid<KPT>(i0, static_cast<uint32_t>(M));
+  load_slice<KPT>(s, i0, keys.nv, keys.key);
   uint32_t kstar, need_eq;
   range_select(keys, static_cast<uint32_t>(k), sm, kstar, need_eq);
   uint32_t gt_run = 0, eq_run = 0;
-  write_tile<KPT>(keys.key, 0, M, kstar, need_eq, gt_run, eq_run, sm, s, out_i, out_v);
+  write_tile<KPT>(keys.key, 0u, keys.nv, kstar, need_eq, gt_run, eq_run, sm, s, out_i, out_v);
 }
 
 // Longer rows: the selection reads the row again for every pass; the
@@ -308,14 +321,17 @@ topk_stream_kernel(const float* __restrict__ score, int64_t M, int64_t k,
   int32_t* out_i = idx + static_cast<int64_t>(blockIdx.x) * k;
   float* out_v = val ? val + static_cast<int64_t>(blockIdx.x) * k : nullptr;
   uint32_t kstar, need_eq;
-  range_select(StreamKeys{s, M}, static_cast<uint32_t>(k), sm, kstar, need_eq);
+  const uint32_t m = static_cast<uint32_t>(M);
+  range_select(StreamKeys{s, m}, static_cast<uint32_t>(k), sm, kstar, need_eq);
 
   // tiles of kThreads * kRegKeys indices, in ascending order
   uint32_t gt_run = 0, eq_run = 0;
-  for (int64_t tile0 = 0; tile0 < M; tile0 += static_cast<int64_t>(kThreads) * kRegKeys) {
+  for (uint32_t tile0 = 0; tile0 < m; tile0 += kThreads * kRegKeys) {
     uint32_t key[kRegKeys];
-    load_slice<kRegKeys>(s, tile0 + static_cast<int64_t>(threadIdx.x) * kRegKeys, M, key);
-    write_tile<kRegKeys>(key, tile0, M, kstar, need_eq, gt_run, eq_run, sm, s, out_i, out_v);
+    const uint32_t i0 = tile0 + threadIdx.x * kRegKeys;
+    const int nv = slice_valid<kRegKeys>(i0, m);
+    load_slice<kRegKeys>(s, i0, nv, key);
+    write_tile<kRegKeys>(key, tile0, nv, kstar, need_eq, gt_run, eq_run, sm, s, out_i, out_v);
   }
 }
 
@@ -465,9 +481,9 @@ int launch_topk(const float* score, int64_t G, int64_t M, int64_t k, int32_t* id
   const int64_t per = (M + kThreads - 1) / kThreads;
 #define KVSEL_TK(KPT) \
   if (per <= KPT) { hipLaunchKernelGGL(topk_reg_kernel<KPT>, grid, block, 0, s, score, M, k, idx, val); return check_launch("kvsel_topk"); }
-  KVSEL_TK(1) KVSEL_TK(2) KVSEL_TK(4) KVSEL_TK(8) KVSEL_TK(16)
+  KVSEL_TK(1) KVSEL_TK(2) KVSEL_TK(4) KVSEL_TK(8) KVSEL_TK(16) KVSEL_TK(32) KVSEL_TK(64)
 #undef KVSEL_TK
-  static_assert(kRegKeys == 16, "the register variants above end at kRegKeys");
+  static_assert(kRegKeys == 64, "the register variants above end at kRegKeys");
   hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, s, score, M, k, idx, val);
   return check_launch("kvsel_topk");
 }

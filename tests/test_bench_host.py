@@ -39,8 +39,10 @@ def test_stage_kernels_are_known(name):
 def test_topk_kernel_follows_row_length():
     serving = synth.workload("serving_16req_8l_128k")        # 512 units per row
     infoflow = synth.workload("infoflow_32l_64x1024")        # 65,536 tokens per row
+    longer = synth.workload("infoflow_32l_64x1024", N=131072)
     assert bench.kernel_of("topk", serving) == "topk_reg_kernel"
-    assert bench.kernel_of("topk", infoflow) == "topk_stream_kernel"
+    assert bench.kernel_of("topk", infoflow) == "topk_reg_kernel"   # 64 keys per thread
+    assert bench.kernel_of("topk", longer) == "topk_stream_kernel"
 
 
 def test_host_cpu_record():

@@ -172,6 +172,10 @@ TOPK_CASES = [
     (2, 20000, 300, "ties100"), (1, 16384, 2048, "cluster"), (3, 4096, 1000, "signed"),
     # rows re-read per pass: 19 compaction tiles with a ragged tail; several rows
     (1, 300007, 12345, "cluster"), (2, 40000, 5000, "signed"), (1, 100000, 99999, "ties100"),
+    # the largest rows held in registers (32 and 64 keys per thread) and one
+    # past each; ragged slices, unaligned rows when G > 1
+    (1, 32768, 4000, "signed"), (2, 32769, 100, "ties"), (1, 65535, 65535, "float"),
+    (3, 50001, 7, "cluster"), (1, 65536, 1, "ties_few"), (2, 65537, 30000, "signed"),
 ]
 
 
