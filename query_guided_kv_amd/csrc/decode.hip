@@ -18,6 +18,8 @@
 #include "internal.h"
 #include "mfma.h"
 
+#include <type_traits>
+
 namespace kvsel {
 namespace {
 
@@ -356,19 +358,21 @@ decode_tile_kernel(const T* __restrict__ q, SegTable st, int n_seg, int64_t n_sp
   }
 }
 
-// One online-softmax step of a wave's RBW row blocks over a 64-key tile: the
-// steps of attn_softmax (mfma.h) for each row block, with a single rescale
-// branch for all of them, so that every exponential and the value products
-// after it fall in one basic block that the scheduler can interleave.  When
-// the branch is taken, each row's reference moves to its new maximum (or stays).
-template <int CB, int RBW>
-__device__ __forceinline__ void attn_softmax_rows(const f32x4_t (&sv)[RBW][4], float scale2,
+// One online-softmax step of the first NB of a wave's RBW row blocks over a
+// 64-key tile: the steps of attn_softmax (mfma.h) for each row block, with a
+// single rescale branch for all of them, so that every exponential and the
+// value products after it fall in one basic block that the scheduler can
+// interleave.  When the branch is taken, each row's reference moves to its new
+// maximum (or stays).
+template <int CB, int RBW, int NB>
+__device__ __forceinline__ void attn_softmax_rows(const f32x4_t (&sv)[NB][4], float scale2,
                                                   float (&m)[RBW], float (&s)[RBW],
-                                                  f32x4_t (&o)[RBW][CB], uint32_t (&pk)[RBW][4][2]) {
-  float tm[RBW];
+                                                  f32x4_t (&o)[RBW][CB], uint32_t (&pk)[NB][4][2]) {
+  static_assert(NB <= RBW, "active row blocks");
+  float tm[NB];
   bool grow = false;
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < NB; ++i) {
     float tmax = sv[i][0][0];
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4)
@@ -379,7 +383,7 @@ __device__ __forceinline__ void attn_softmax_rows(const f32x4_t (&sv)[RBW][4], f
   }
   if (__any(grow)) {   // uniform: rare once the maxima settle
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const float mn = fmaxf(m[i], tm[i]);
       const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[i] - mn);
       m[i] = mn;
@@ -389,7 +393,7 @@ __device__ __forceinline__ void attn_softmax_rows(const f32x4_t (&sv)[RBW][4], f
     }
   }
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const float ref = m[i] == -INFINITY ? 0.0f : m[i];
     float ps = s[i];
 #pragma unroll
@@ -552,11 +556,18 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     }
   };
   // query fragments (B operand: query row col of the row block, 8 dims per k-step)
+  // Row block of slot i: a pass fills slot 0 of every wave, then slot 1, so
+  // the padding of a pass's last, partial set of blocks lands in the second
+  // slot of the last waves, at most one such wave per SIMD (waves w and
+  // w + NW / 2 share one).  Those waves run the one-block loop below and
+  // skip the padding's products and exponentials.
   uint4 qb[RBW][KS];
   int rb[RBW];
+  int nb = 0;                      // row blocks of this wave holding query rows
 #pragma unroll
   for (int i = 0; i < RBW; ++i) {
-    rb[i] = (pass * nwaves + wave) * RBW + i;
+    rb[i] = (pass * RBW + i) * nwaves + wave;
+    nb += rb[i] * 16 < R ? 1 : 0;
     const int r = rb[i] * 16 + col;
     if (r < R) {
       const int h = g * G + r / T_, j = r % T_;
@@ -581,7 +592,8 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   if (SPLIT || t_begin < t_end) fetch(t_begin);
   __builtin_amdgcn_sched_barrier(0);
   // full tiles, then the split's last, partial tile (rows past its end masked)
-  auto tile = [&](int64_t t0, bool partial) {
+  auto tile = [&](auto nbc, int64_t t0, bool partial) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nbc)::value;   // active row blocks (the first NB slots)
     __syncthreads();
     if constexpr (SPLIT) {
       stage_k(vwave ? vt : kt, bf, KSV);
@@ -599,7 +611,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     if (SPLIT || t0 + TK < t_end) fetch(t0 + TK);
 
     // S^T blocks: key block outer, so one K fragment serves every row block
-    f32x4_t sv[RBW][4];
+    f32x4_t sv[NB][4];
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4) {
       uint4 ka[KS];
@@ -607,7 +619,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
       for (int s2 = 0; s2 < KS; ++s2)
         ka[s2] = *reinterpret_cast<const uint4*>(&kt[(kb4 * 16 + col) * KROW + s2 * 32 + quad * 8]);
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) {
+      for (int i = 0; i < NB; ++i) {
         f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) a = mfma16x16x32(ka[s2], qb[i][s2], a);
@@ -616,15 +628,15 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     }
     if (partial) {
 #pragma unroll
-      for (int i = 0; i < RBW; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
           for (int vv = 0; vv < 4; ++vv)
             if (t0 + kb4 * 16 + quad * 4 + vv >= t_end) sv[i][kb4][vv] = -INFINITY;
     }
-    uint32_t pk[RBW][4][2];
-    attn_softmax_rows<CB, RBW>(sv, scale2, m, s, o, pk);
+    uint32_t pk[NB][4][2];
+    attn_softmax_rows<CB, RBW, NB>(sv, scale2, m, s, o, pk);
     // O^T += V^T P^T: one V^T fragment serves every row block
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
@@ -634,7 +646,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
         if constexpr (SPLIT) va = load_vt_tr<KROW>(vt, c, pr, lane);
         else va = load_vt<VROW>(vt, c, pr, col, quad);
 #pragma unroll
-        for (int i = 0; i < RBW; ++i) {
+        for (int i = 0; i < NB; ++i) {
           const uint4 pb = make_uint4(pk[i][2 * pr][0], pk[i][2 * pr][1], pk[i][2 * pr + 1][0],
                                       pk[i][2 * pr + 1][1]);
           o[i][c] = mfma16x16x32(va, pb, o[i][c]);
@@ -643,8 +655,15 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     }
   };
   const int64_t t_full = t_begin + max<int64_t>(0, t_end - t_begin) / TK * TK;
-  for (int64_t t0 = t_begin; t0 < t_full; t0 += TK) tile(t0, false);
-  if (t_full < t_end) tile(t_full, true);
+  auto run = [&](auto nbc) __attribute__((always_inline)) {
+    for (int64_t t0 = t_begin; t0 < t_full; t0 += TK) tile(nbc, t0, false);
+    if (t_full < t_end) tile(nbc, t_full, true);
+  };
+  // every wave passes the same barriers in either loop; a wave with no query
+  // rows (a short last pass) runs the one-block loop on zero queries
+  if constexpr (RBW == 1) run(std::integral_constant<int, 1>{});
+  else if (nb == RBW) run(std::integral_constant<int, RBW>{});
+  else run(std::integral_constant<int, 1>{});
 
   // publish: lane l holds query row rb*16 + l%16, dims c*16 + 4*quad .. +3
 #pragma unroll
