@@ -145,15 +145,17 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         *reinterpret_cast<uint4*>(&kt[key * KROW + ch * 8]) = kn[i];
       }
       if constexpr (VNORM) {
-        float ss = 0.0f;
+        // squares summed with the packed bf16 dot, two elements an
+        // instruction with no unpacking (a bf16 square is exact in fp32)
+        float ss = 0.0f, st = 0.0f;
 #pragma unroll
         for (int i = 0; i < VV; ++i) {
-          float f[8];
-          unpack16<bf16_t>(vr[i], f);
-#pragma unroll
-          for (int d = 0; d < 8; ++d) ss = fmaf(f[d], f[d], ss);
+          ss = dot2_bf16(vr[i].x, vr[i].x, ss);
+          st = dot2_bf16(vr[i].y, vr[i].y, st);
+          ss = dot2_bf16(vr[i].z, vr[i].z, ss);
+          st = dot2_bf16(vr[i].w, vr[i].w, st);
         }
-        ss = group_sum<4>(ss);
+        ss = group_sum<4>(ss + st);
         if ((threadIdx.x & 3) == 0) vn[threadIdx.x >> 2] = sqrtf(ss);
       }
       __syncthreads();
