@@ -298,6 +298,12 @@ DECODE_CASES = [
     # two row blocks per wave: one pass with idle waves, a segment shorter than a tile
     ("mfma_R224_one_pass_short_seg", "bf16", 2, (1030, 5), 4, 28, 32, 128),
     ("mfma_R200_d64_one_pass", "bf16", 1, (2100,), 2, 10, 40, 64),
+    # a pass fills every wave's first row block, then the second: 12 blocks
+    # leave four waves one block; 17 leave a second pass of one block (seven
+    # waves without query rows); 32 fill two passes
+    ("mfma_R192_one_pass_four_single", "bf16", 2, (900,), 2, 24, 16, 128),
+    ("mfma_R272_one_block_last_pass", "bf16", 1, (1500, 40), 4, 68, 16, 128),
+    ("mfma_R512_two_full_passes", "bf16", 1, (800,), 2, 32, 32, 128),
 ]
 
 
