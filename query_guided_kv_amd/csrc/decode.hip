@@ -556,11 +556,12 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
     }
   };
   // query fragments (B operand: query row col of the row block, 8 dims per k-step)
-  // Row block of slot i: a pass fills slot 0 of every wave, then slot 1, so
-  // the padding of a pass's last, partial set of blocks lands in the second
-  // slot of the last waves, at most one such wave per SIMD (waves w and
-  // w + NW / 2 share one).  Those waves run the one-block loop below and
-  // skip the padding's products and exponentials.
+  // Row block of slot i: a pass fills slot 0 of every wave, then slot 1, and
+  // so on, so the padding of a pass's last, partial set of blocks lands in
+  // the last slots of the last waves; with two slots, at most one such wave
+  // per SIMD (waves w and w + NW / 2 share one).  A wave with at most one
+  // block of query rows runs the one-block loop below and skips the
+  // padding's products and exponentials.
   uint4 qb[RBW][KS];
   int rb[RBW];
   int nb = 0;                      // row blocks of this wave holding query rows
@@ -662,7 +663,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, SegTable st, int n_seg, int64_t
   // every wave passes the same barriers in either loop; a wave with no query
   // rows (a short last pass) runs the one-block loop on zero queries
   if constexpr (RBW == 1) run(std::integral_constant<int, 1>{});
-  else if (nb == RBW) run(std::integral_constant<int, RBW>{});
+  else if (nb > 1) run(std::integral_constant<int, RBW>{});   // padded slots too, if any
   else run(std::integral_constant<int, 1>{});
 
   // publish: lane l holds query row rb*16 + l%16, dims c*16 + 4*quad .. +3

@@ -20,6 +20,8 @@
 #include "internal.h"
 #include "mfma.h"
 
+#include <type_traits>
+
 namespace kvsel {
 namespace {
 
@@ -92,11 +94,17 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
   const int wr = wave % NWR, wk = wave / NWR;
   const int col = lane & 15, quad = lane >> 4;
 
-  // query fragments of this wave's row blocks (rows past R are zero)
+  // query fragments of this wave's row blocks (rows past R are zero).  A pass
+  // fills the first slot of every wave row, then the second, and so on, so a
+  // last, partial pass leaves its padding in the last slots of the last wave
+  // rows; with eight waves of two slots, one such wave per SIMD.  A wave with
+  // at most one block of query rows runs the one-block loop below.
   uint4 qa[RBW][KS];
+  int nb = 0;                      // row blocks of this wave holding query rows
 #pragma unroll
   for (int i = 0; i < RBW; ++i) {
     const int r = (pass * NWR * RBW + wr + i * NWR) * 16 + col;
+    nb += (pass * NWR * RBW + wr + i * NWR) * 16 < R ? 1 : 0;
     if (r < R) {
       const int h = g * G + r / T, j = r % T;
       const uint4* qp = reinterpret_cast<const uint4*>(q + ((b * T + j) * Hq + h) * D + quad * 8);
@@ -280,7 +288,9 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
     }
   }
   // one tile: sb holds it (rotated), rb the next tile's raw rows
-  auto body = [&](uint4 (&sb)[VPT], bool& sb_ok, uint4 (&rb)[VPT], int64_t t0) {
+  auto body = [&](auto nbc, uint4 (&sb)[VPT], bool& sb_ok, uint4 (&rb)[VPT], int64_t t0)
+      __attribute__((always_inline)) {
+    constexpr int NB = decltype(nbc)::value;   // active row blocks (the first NB slots)
     __syncthreads();               // previous tile fully read
     if constexpr (ROT != 0 && !PIPE) {
       unit_cs();
@@ -296,7 +306,7 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
       fc.advance();
     }
 
-    f32x4_t acc[RBW][KBW];
+    f32x4_t acc[NB][KBW];
 #pragma unroll
     for (int jb = 0; jb < KBW; ++jb) {
       const int key = (wk + jb * NWK) * 16 + col;
@@ -305,7 +315,7 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
       for (int st = 0; st < KS; ++st)
         bk[st] = *reinterpret_cast<const uint4*>(&kt[key * KROW + st * 32 + quad * 8]);
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) {
+      for (int i = 0; i < NB; ++i) {
         f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st)
@@ -329,7 +339,7 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
       for (int jb = 0; jb < KBW; ++jb) {
         if (!tile_ok || (wk + jb * NWK) * 16 + col >= rem) {
 #pragma unroll
-          for (int i = 0; i < RBW; ++i)
+          for (int i = 0; i < NB; ++i)
             acc[i][jb] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
       }
@@ -337,7 +347,7 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
     // online softmax, branch-free: while a row has seen only masked keys its
     // max stays -inf and the reference 0 keeps every exp at exp2(-inf) = 0
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
+    for (int i = 0; i < NB; ++i) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float tmax = acc[i][0][v];
@@ -357,13 +367,14 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
     // end of a segment: merge and publish its partials
     seg_off += kTileKeys;
     if (seg_off == seg_len || t0 + kTileKeys >= t_end) {
+      // a skipped slot holds only padded rows, which are not published
 #pragma unroll
-      for (int i = 0; i < RBW; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) merge_cols(m[i][v], s[i][v]);
       if (col == 0) {
 #pragma unroll
-        for (int i = 0; i < RBW; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int rl = (wr + i * NWR) * 16 + quad * 4 + v;  // row within the pass
@@ -391,14 +402,21 @@ score_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, in
       seg_off = 0;
     }
   };
-  if constexpr (PIPE) {
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kTileKeys) {
-      body(bufA, okA, bufB, t0);
-      if (t0 + kTileKeys < t_end) body(bufB, okB, bufA, t0 + kTileKeys);
+  auto run = [&](auto nbc) __attribute__((always_inline)) {
+    if constexpr (PIPE) {
+      for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kTileKeys) {
+        body(nbc, bufA, okA, bufB, t0);
+        if (t0 + kTileKeys < t_end) body(nbc, bufB, okB, bufA, t0 + kTileKeys);
+      }
+    } else {
+      for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) body(nbc, bufA, okA, bufA, t0);
     }
-  } else {
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kTileKeys) body(bufA, okA, bufA, t0);
-  }
+  };
+  // every wave passes the same barriers in either loop; a wave with no query
+  // rows (a short last pass) runs the one-block loop on zero queries
+  if constexpr (RBW == 1) run(std::integral_constant<int, 1>{});
+  else if (nb > 1) run(std::integral_constant<int, RBW>{});   // padded slots too, if any
+  else run(std::integral_constant<int, 1>{});
 }
 
 template <int D, int RBW, int NWR, int NW, int ROT, bool WRITE>

@@ -92,6 +92,12 @@ SCORE_CASES = [
     ("mfma_R64_chunks", "bf16", 2, 4096, 8, 16, 32, 128, 256),
     ("mfma_R128_tokens_ragged", "bf16", 2, 2000, 4, 16, 32, 128, 1),
     ("mfma_R300_two_passes_ragged", "bf16", 1, 700, 1, 10, 30, 128, 1),
+    # a pass fills every wave row's first row block, then the next: 12 blocks
+    # leave four single-block waves; 17 leave a second pass of one block;
+    # head dim 64 with 14 blocks in four slots leaves waves of three
+    ("mfma_R192_single_block_waves", "bf16", 2, 1088, 2, 24, 16, 128, 64),
+    ("mfma_R272_one_block_last_pass", "bf16", 1, 900, 2, 34, 8, 128, 1),
+    ("mfma_R224_d64_three_of_four", "bf16", 2, 1024, 2, 16, 14, 64, 128),
 ]
 
 
