@@ -452,11 +452,11 @@ void dispatch(const void* q, int64_t T, int64_t Hq, const void* k, const kvsel_c
   }
   // up to 1024 keys per workgroup (segments of 256 go four to a block), fewer
   // when that leaves under ~2048 workgroups for the 256 CUs, but not fewer
-  // than 512: a workgroup loads its query fragments once for at least 8
-  // tiles (448 rows per kv head over 16,384 keys: 28.5 -> 25.8 us against 256
-  // keys per workgroup; shorter ranges for 512-key segments were faster)
+  // than 256: a workgroup loads its query fragments once for at least 4
+  // tiles.  448 rows per kv head over 16,384 keys: 512 workgroups of 256 keys,
+  // two to a CU (122 VGPRs), 22.3 -> 20.0 us against 256 of 512 keys
   int64_t spb = seg_len >= 1024 ? 1 : 1024 / seg_len;
-  while (spb > 1 && spb * seg_len > 512 && kc.B * kc.H * p.passes * ((nseg + spb - 1) / spb) < 2048)
+  while (spb > 1 && spb * seg_len > 256 && kc.B * kc.H * p.passes * ((nseg + spb - 1) / spb) < 2048)
     spb /= 2;
 #define KVSEL_SM(RBW, NWR, NW)                                                             \
   if (p.rbw == RBW && p.nwr == NWR && nw == NW)                                            \
