@@ -28,8 +28,8 @@ namespace {
 constexpr int kTileKeys = kMfmaTileKeys;
 constexpr int kPad = kMfmaPad;
 constexpr int kMaxRange = 1024;   // cached rows per workgroup
-constexpr int kSmallRange = 512;  // cached rows per workgroup for small caches
-constexpr int kTargetBlocks = 256;
+constexpr int kSmallRange = 256;  // cached rows per workgroup for small caches
+constexpr int kTargetBlocks = 512;
 
 template <int D, int RBW, int NWR, int NW, bool VNORM>
 __global__ void __launch_bounds__(64 * NW)
@@ -208,7 +208,8 @@ agg_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 // items split over groups.  Large caches: one group, ranges sized to fill the
 // chip.  Small caches (B * N < kAggSplitRows): ranges of kSmallRange rows and
 // up to kAggMaxParts groups, so each workgroup keeps its query fragments for
-// several tiles instead of reloading them for every tile.
+// several tiles instead of reloading them for every tile; about two
+// workgroups per CU, which the eight-wave plan's registers allow.
 struct AggPlan {
   int64_t range, ranges, parts;
   int hp_per_block, passes, rbw, nwr, nw;
